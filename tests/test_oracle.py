@@ -1,0 +1,506 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Each pin checks the oracle against something other than itself: closed forms
+derived by hand (tests/golden), exactly rounded brute force on tiny inputs,
+invariants of the softmax, the tiled online-softmax recurrence of the pages,
+special cases that reduce to other calls, an independent library (PyTorch's
+fp64 CPU attention, scipy's logsumexp, torch.autograd), and central finite
+differences for the gradients.  A final test plants plausible mistakes in a
+copy of the oracle's source and checks that at least one pin catches each.
+
+Pages: "Is a full-day context better than a 10-minute context? Flash attention
+and the sequence-length question" (marketmaker.cc) -- sections "Why attention
+is memory-bound" (definition), "The Flash Attention algorithm" (tiled
+pseudocode), "Online softmax recurrence" (exactness), "Causal masking",
+"Backward pass: recompute instead of store"; "Flash-Attention 2 for
+performance optimisation" (Medium) -- "Attention" (rows sum to one),
+"Flash Attention 2" (deferred rescaling, stored L).
+"""
+import json
+import math
+import os
+import types
+
+import numpy as np
+import pytest
+
+import oracle.attention as ORA
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _rand(seed, *shape):
+    return _rng(seed).standard_normal(shape)
+
+
+def _close(a, b, tol, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    fa, fb = np.isfinite(a), np.isfinite(b)
+    assert np.array_equal(fa, fb), (what, "finite pattern differs")
+    assert np.array_equal(a[~fa], b[~fb]), (what, "non-finite values differ")
+    if fa.any():
+        err = np.max(np.abs(a[fa] - b[fb]))
+        assert err <= tol, (what, float(err), tol)
+
+
+# ---------------------------------------------------------------- pins ----
+
+def pin_golden(m):
+    """Hand-derived closed-form cases (tests/golden/closed_forms.json)."""
+    with open(os.path.join(GOLDEN, "closed_forms.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        q = np.array(c["q"], dtype=np.float64)[None, None]
+        k = np.array(c["k"], dtype=np.float64)[None, None]
+        v = np.array(c["v"], dtype=np.float64)[None, None]
+        kv = None if c["kv_len"] is None else np.array(c["kv_len"])
+        o, lse = m.attention_fwd(q, k, v, c["scale"], c["causal"], kv)
+        _close(o[0, 0], c["o"], 1e-14, c["name"] + " O")
+        lse_exp = np.array([float(x) for x in c["lse"]])
+        _close(lse[0, 0], lse_exp, 1e-14, c["name"] + " LSE")
+        if "do" in c:
+            do = np.array(c["do"], dtype=np.float64)[None, None]
+            dq, dk, dv = m.attention_bwd(q, k, v, do, c["scale"], c["causal"],
+                                         kv)
+            _close(dq[0, 0], c["dq"], 1e-14, c["name"] + " dQ")
+            _close(dk[0, 0], c["dk"], 1e-14, c["name"] + " dK")
+            _close(dv[0, 0], c["dv"], 1e-14, c["name"] + " dV")
+
+
+def _brute_fwd(q, k, v, scale, causal, kv_len):
+    """Explicit loops, exactly rounded sums (math.fsum), math.exp."""
+    B, H, N, d = q.shape
+    o = np.zeros((B, H, N, v.shape[-1]))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        L = N if kv_len is None else int(kv_len[b])
+        for h in range(H):
+            for i in range(N):
+                vis = [j for j in range(N)
+                       if j < L and (not causal or j <= i)]
+                if not vis:
+                    lse[b, h, i] = -math.inf
+                    continue
+                s = [scale * math.fsum(float(q[b, h, i, c]) * float(k[b, h, j, c])
+                                       for c in range(d)) for j in vis]
+                mx = max(s)
+                e = [math.exp(x - mx) for x in s]
+                den = math.fsum(e)
+                for c in range(v.shape[-1]):
+                    o[b, h, i, c] = math.fsum(
+                        e[t] * float(v[b, h, j, c]) for t, j in enumerate(vis)) / den
+                lse[b, h, i] = mx + math.log(den)
+    return o, lse
+
+
+def pin_bruteforce(m):
+    """Whole forward and both masks against exactly rounded loops."""
+    seed = 0
+    for N, d in [(1, 1), (2, 2), (3, 3), (5, 8), (17, 3)]:
+        for causal in (False, True):
+            for kv in (None, np.array([N, max(1, N // 2)]),
+                       np.array([0, N - 1])):
+                seed += 1
+                q = _rand(seed, 2, 2, N, d) * 1.7
+                k = _rand(seed + 100, 2, 2, N, d)
+                v = _rand(seed + 200, 2, 2, N, d)
+                scale = 0.37
+                o, lse = m.attention_fwd(q, k, v, scale, causal, kv)
+                ob, lb = _brute_fwd(q, k, v, scale, causal, kv)
+                _close(o, ob, 1e-13, f"brute O N={N} d={d} c={causal}")
+                _close(lse, lb, 1e-13, f"brute LSE N={N} d={d} c={causal}")
+
+
+def _n_visible(N, causal, L):
+    i = np.arange(N)
+    n = np.full(N, L) if not causal else np.minimum(i + 1, L)
+    return np.maximum(n, 0)
+
+
+def pin_closed_forms(m):
+    """Equal scores give the mean of visible V; N=1; two keys."""
+    B, H, N, d = 2, 3, 23, 8
+    v = _rand(1, B, H, N, d)
+    k = _rand(2, B, H, N, d)
+    for causal in (False, True):
+        kv = np.array([N, 9])
+        # Q = 0: all scores 0 -> mean of visible V rows, lse = ln n_i.
+        o, lse = m.attention_fwd(np.zeros((B, H, N, d)), k, v, 0.3, causal, kv)
+        for b in range(B):
+            n = _n_visible(N, causal, int(kv[b]))
+            cs = np.cumsum(v[b], axis=1)           # [H, N, d]
+            for i in range(N):
+                mean = cs[:, n[i] - 1] / n[i]
+                _close(o[b, :, i], mean, 1e-13, "Q=0 mean")
+                _close(lse[b, :, i], np.full(H, math.log(n[i])), 1e-13,
+                       "Q=0 lse")
+        # All K rows equal: s_ij = scale q_i.k0 for every j.
+        k0 = np.broadcast_to(_rand(3, B, H, 1, d), (B, H, N, d)).copy()
+        q = _rand(4, B, H, N, d)
+        o, lse = m.attention_fwd(q, k0, v, 0.3, causal, kv)
+        for b in range(B):
+            n = _n_visible(N, causal, int(kv[b]))
+            cs = np.cumsum(v[b], axis=1)
+            for i in range(N):
+                _close(o[b, :, i], cs[:, n[i] - 1] / n[i], 1e-12, "equal K")
+                s = 0.3 * np.sum(q[b, :, i] * k0[b, :, 0], axis=-1)
+                _close(lse[b, :, i], s + math.log(n[i]), 1e-12, "equal K lse")
+    # N = 1: O = V, lse = scale q.k.
+    q1, k1, v1 = _rand(5, 2, 2, 1, 4), _rand(6, 2, 2, 1, 4), _rand(7, 2, 2, 1, 4)
+    o, lse = m.attention_fwd(q1, k1, v1, 0.8, True)
+    _close(o, v1, 1e-15, "N=1 O")
+    _close(lse, 0.8 * np.sum(q1 * k1, axis=-1), 1e-14, "N=1 lse")
+    # Two keys: p1 = sigmoid(s1 - s2).
+    q2, k2, v2 = _rand(8, 1, 1, 2, 3), _rand(9, 1, 1, 2, 3), _rand(10, 1, 1, 2, 3)
+    o, lse = m.attention_fwd(q2, k2, v2, 0.9, False)
+    for i in range(2):
+        s1 = 0.9 * float(q2[0, 0, i] @ k2[0, 0, 0])
+        s2 = 0.9 * float(q2[0, 0, i] @ k2[0, 0, 1])
+        p1 = 1.0 / (1.0 + math.exp(s2 - s1))
+        _close(o[0, 0, i], p1 * v2[0, 0, 0] + (1 - p1) * v2[0, 0, 1], 1e-14,
+               "two keys O")
+        _close(lse[0, 0, i], max(s1, s2) + math.log1p(math.exp(-abs(s1 - s2))),
+               1e-14, "two keys lse")
+
+
+def pin_prob_rows(m):
+    """With V = I, O is P: rows sum to one, P >= 0, masked P = 0, and
+    log P_ij - log P_ik = scale q_i.(k_j - k_k) for visible j, k."""
+    N = 11
+    q, k = _rand(11, 2, 2, N, 5), _rand(12, 2, 2, N, 5)
+    eye = np.broadcast_to(np.eye(N), (2, 2, N, N)).copy()
+    for causal in (False, True):
+        kv = np.array([N, 6])
+        P, _ = m.attention_fwd(q, k, eye, 0.7, causal, kv)
+        P2 = m.attention_probs(q, k, 0.7, causal, kv)
+        _close(P, P2, 1e-15, "probs vs O with V=I")
+        assert (P >= 0).all()
+        _close(P.sum(-1), np.ones((2, 2, N)), 1e-14, "row sums")
+        for b in range(2):
+            L = int(kv[b])
+            for i in range(N):
+                for j in range(N):
+                    visible = j < L and (not causal or j <= i)
+                    if not visible:
+                        assert P[b, :, i, j].max() == 0.0
+                        continue
+                    # compare with key 0 (always visible here)
+                    want = 0.7 * np.sum(q[b, :, i] * (k[b, :, j] - k[b, :, 0]),
+                                        axis=-1)
+                    got = np.log(P[b, :, i, j]) - np.log(P[b, :, i, 0])
+                    _close(got, want, 1e-12, "log-ratio")
+
+
+def pin_shift(m):
+    """Adding c_i to every score of row i leaves O and adds c_i to LSE.
+
+    The shift is built by appending a column: q' = [q, c/scale], k' = [k, 1].
+    With |c| ~ 1e3 this also shows the max subtraction keeps exp finite.
+    """
+    B, H, N, d = 1, 2, 19, 6
+    q, k, v = _rand(21, B, H, N, d), _rand(22, B, H, N, d), _rand(23, B, H, N, d)
+    c = _rng(24).uniform(500.0, 1500.0, (B, H, N))
+    scale = 0.5
+    qa = np.concatenate([q, (c / scale)[..., None]], axis=-1)
+    ka = np.concatenate([k, np.ones((B, H, N, 1))], axis=-1)
+    for causal in (False, True):
+        o, lse = m.attention_fwd(q, k, v, scale, causal)
+        o2, lse2 = m.attention_fwd(qa, ka, v, scale, causal)
+        _close(o2, o, 1e-11, "shift O")
+        _close(lse2 - c, lse, 1e-9, "shift LSE")
+
+
+def pin_permutation(m):
+    """Non-causal: permuting K,V rows jointly changes nothing; permuting Q
+    rows permutes O and LSE."""
+    B, H, N, d = 2, 2, 13, 4
+    q, k, v = _rand(31, B, H, N, d), _rand(32, B, H, N, d), _rand(33, B, H, N, d)
+    o, lse = m.attention_fwd(q, k, v, 0.6, False)
+    pk = _rng(34).permutation(N)
+    o2, lse2 = m.attention_fwd(q, k[:, :, pk], v[:, :, pk], 0.6, False)
+    _close(o2, o, 1e-13, "perm KV O")
+    _close(lse2, lse, 1e-13, "perm KV LSE")
+    pq = _rng(35).permutation(N)
+    o3, lse3 = m.attention_fwd(q[:, :, pq], k, v, 0.6, False)
+    _close(o3, o[:, :, pq], 1e-13, "perm Q O")
+    _close(lse3, lse[:, :, pq], 1e-13, "perm Q LSE")
+
+
+def _tiled_attention(q, k, v, scale, causal, kv_len, Br, Bc, deferred):
+    """Tiled online softmax over Br x Bc tiles, fp64.
+
+    deferred=False: O_i is kept normalised after every KV tile (the pages'
+    FlashAttention pseudocode).  deferred=True: O_i accumulates unnormalised
+    and is divided by l once at the end, with only the max rescale in the
+    loop (the FA2 schedule).  Wholly masked tiles are skipped.
+    """
+    B, H, N, d = q.shape
+    o = np.zeros((B, H, N, v.shape[-1]))
+    lse = np.full((B, H, N), -np.inf)
+    for b in range(B):
+        L = N if kv_len is None else int(kv_len[b])
+        for h in range(H):
+            for r0 in range(0, N, Br):
+                r1 = min(N, r0 + Br)
+                Qi = q[b, h, r0:r1]
+                mi = np.full(r1 - r0, -np.inf)
+                li = np.zeros(r1 - r0)
+                Oi = np.zeros((r1 - r0, v.shape[-1]))
+                for c0 in range(0, N, Bc):
+                    c1 = min(N, c0 + Bc)
+                    if c0 >= L or (causal and c0 > r1 - 1):
+                        continue                      # tile wholly masked
+                    S = scale * Qi @ k[b, h, c0:c1].T
+                    ii = np.arange(r0, r1)[:, None]
+                    jj = np.arange(c0, c1)[None, :]
+                    vis = (jj < L) & ((jj <= ii) if causal else True)
+                    S = np.where(vis, S, -np.inf)
+                    mij = S.max(axis=1)
+                    mnew = np.maximum(mi, mij)
+                    ref = np.where(np.isfinite(mnew), mnew, 0.0)
+                    Pij = np.exp(S - ref[:, None])
+                    lij = Pij.sum(axis=1)
+                    alpha = np.exp(np.where(np.isfinite(mi), mi - ref, -np.inf))
+                    lnew = alpha * li + lij
+                    if deferred:
+                        Oi = alpha[:, None] * Oi + Pij @ v[b, h, c0:c1]
+                    else:
+                        safe = np.where(lnew > 0, lnew, 1.0)
+                        Oi = ((alpha * li / safe)[:, None] * Oi
+                              + (Pij @ v[b, h, c0:c1]) / safe[:, None])
+                    mi, li = mnew, lnew
+                if deferred:
+                    Oi = Oi / np.where(li > 0, li, 1.0)[:, None]
+                o[b, h, r0:r1] = Oi
+                with np.errstate(divide="ignore"):
+                    lse[b, h, r0:r1] = np.where(li > 0, mi + np.log(
+                        np.where(li > 0, li, 1.0)), -np.inf)
+    return o, lse
+
+
+def pin_tiled_recurrence(m):
+    """The pages' tiled recurrence (both schedules, ragged tiles) equals the
+    two-pass oracle to 1e-12: the method is exact in exact arithmetic."""
+    B, H, N, d = 2, 2, 37, 8
+    q, k, v = _rand(41, B, H, N, d) * 2, _rand(42, B, H, N, d), _rand(43, B, H, N, d)
+    for causal in (False, True):
+        for kv in (None, np.array([37, 12]), np.array([5, 0])):
+            o, lse = m.attention_fwd(q, k, v, 0.45, causal, kv)
+            for Br, Bc in [(8, 5), (16, 16), (37, 3)]:
+                for deferred in (False, True):
+                    ot, lt = _tiled_attention(q, k, v, 0.45, causal, kv, Br, Bc,
+                                              deferred)
+                    _close(o, ot, 1e-12, f"tiled O {Br}x{Bc} def={deferred}")
+                    _close(lse, lt, 1e-12, f"tiled LSE {Br}x{Bc}")
+
+
+def pin_reductions(m):
+    """Causal row i = non-causal attention over keys 0..i; a padded row =
+    non-causal attention over the first kv_len keys."""
+    B, H, N, d = 2, 2, 15, 4
+    q, k, v = _rand(51, B, H, N, d), _rand(52, B, H, N, d), _rand(53, B, H, N, d)
+    o, lse = m.attention_fwd(q, k, v, 0.5, True)
+    for i in range(N):
+        oi, li = m.attention_fwd(q[:, :, i:i + 1], k[:, :, :i + 1],
+                                 v[:, :, :i + 1], 0.5, False)
+        _close(o[:, :, i:i + 1], oi, 1e-13, "causal row reduction")
+        _close(lse[:, :, i:i + 1], li, 1e-13, "causal row lse")
+    kv = np.array([7, 15])
+    o, lse = m.attention_fwd(q, k, v, 0.5, False, kv)
+    for b in range(B):
+        L = int(kv[b])
+        ob, lb = m.attention_fwd(q[b:b + 1], k[b:b + 1, :, :L],
+                                 v[b:b + 1, :, :L], 0.5, False)
+        _close(o[b:b + 1], ob, 1e-13, "padding reduction")
+        _close(lse[b:b + 1], lb, 1e-13, "padding lse")
+
+
+def _torch_mask(N, causal, kv_len, B):
+    import torch
+    i = torch.arange(N)[:, None]
+    j = torch.arange(N)[None, :]
+    masks = []
+    for b in range(B):
+        L = N if kv_len is None else int(kv_len[b])
+        mk = j < L
+        if causal:
+            mk = mk & (j <= i)
+        masks.append(mk)
+    return torch.stack(masks)[:, None]          # [B,1,N,N], True = attend
+
+
+def pin_torch_sdpa(m):
+    """Independent library: PyTorch's fp64 CPU attention for O, scipy's
+    logsumexp for LSE."""
+    import torch
+    from scipy.special import logsumexp
+    B, H, N, d = 2, 3, 29, 16
+    q, k, v = _rand(61, B, H, N, d), _rand(62, B, H, N, d), _rand(63, B, H, N, d)
+    for causal in (False, True):
+        for kv in (None, np.array([29, 10])):
+            o, lse = m.attention_fwd(q, k, v, 0.3, causal, kv)
+            mask = _torch_mask(N, causal, kv, B)
+            ot = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                attn_mask=mask, scale=0.3).numpy()
+            _close(o, ot, 1e-12, "sdpa O")
+            s = 0.3 * np.einsum("bhid,bhjd->bhij", q, k)
+            s = np.where(mask.numpy(), s, -np.inf)
+            _close(lse, logsumexp(s, axis=-1), 1e-12, "logsumexp")
+
+
+def _loss(m, q, k, v, do, scale, causal, kv):
+    o, _ = m.attention_fwd(q, k, v, scale, causal, kv)
+    return float(np.sum(o * do))
+
+
+def pin_finite_diff(m):
+    """Central finite differences of <dO, O> pin every gradient element."""
+    N, d = 7, 3
+    for causal, kv in ((False, None), (True, None), (False, np.array([4]))):
+        q, k, v = _rand(71, 1, 1, N, d), _rand(72, 1, 1, N, d), _rand(73, 1, 1, N, d)
+        do = _rand(74, 1, 1, N, d)
+        grads = m.attention_bwd(q, k, v, do, 0.8, causal, kv)
+        h = 1e-6
+        for which, g in zip(range(3), grads):
+            num = np.zeros_like(g)
+            for idx in np.ndindex(*g.shape):
+                args = [q.copy(), k.copy(), v.copy()]
+                args[which][idx] += h
+                lp = _loss(m, *args, do, 0.8, causal, kv)
+                args[which][idx] -= 2 * h
+                lm = _loss(m, *args, do, 0.8, causal, kv)
+                num[idx] = (lp - lm) / (2 * h)
+            scale_ = max(1.0, np.abs(num).max())
+            _close(g / scale_, num / scale_, 1e-6, f"finite diff {which}")
+
+
+def pin_torch_autograd(m):
+    """Independent library: torch.autograd through PyTorch's fp64 CPU
+    attention."""
+    import torch
+    B, H, N, d = 2, 2, 21, 8
+    for causal in (False, True):
+        for kv in (None, np.array([21, 9])):
+            q, k, v = _rand(81, B, H, N, d), _rand(82, B, H, N, d), _rand(83, B, H, N, d)
+            do = _rand(84, B, H, N, d)
+            dq, dk, dv = m.attention_bwd(q, k, v, do, 0.4, causal, kv)
+            tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+            ot = torch.nn.functional.scaled_dot_product_attention(
+                tq, tk, tv, attn_mask=_torch_mask(N, causal, kv, B), scale=0.4)
+            ot.backward(torch.from_numpy(do))
+            _close(dq, tq.grad.numpy(), 1e-11, "autograd dQ")
+            _close(dk, tk.grad.numpy(), 1e-11, "autograd dK")
+            _close(dv, tv.grad.numpy(), 1e-11, "autograd dV")
+
+
+def pin_grad_invariants(m):
+    """sum_j dK_j = 0 (rows of dS sum to zero) and sum_j dV_j = sum of dO
+    over the rows that see at least one key."""
+    B, H, N, d = 2, 2, 33, 8
+    q, k, v, do = (_rand(s, B, H, N, d) for s in (91, 92, 93, 94))
+    for causal in (False, True):
+        kv = np.array([33, 0]) if not causal else np.array([20, 33])
+        dq, dk, dv = m.attention_bwd(q, k, v, do, 0.5, causal, kv)
+        _close(dk.sum(axis=2), np.zeros((B, H, d)), 1e-11, "sum dK")
+        for b in range(B):
+            rows_with_key = int(kv[b]) > 0
+            want = do[b].sum(axis=1) if rows_with_key else np.zeros((H, d))
+            _close(dv[b].sum(axis=1), want, 1e-11, "sum dV")
+            if not rows_with_key:
+                _close(dq[b], np.zeros_like(dq[b]), 0.0, "dQ without keys")
+
+
+def pin_visible_pairs(m):
+    for N in (1, 5, 64, 100):
+        for causal in (False, True):
+            for kv in (None, [N, N // 2, 0]):
+                B = 1 if kv is None else 3
+                want = int(sum(
+                    ORA_brute_vis(N, causal, None if kv is None else kv[b])
+                    for b in range(B))) * 2
+                assert m.visible_pairs(N, causal, kv, B=B, H=2) == want
+    assert m.visible_pairs(1024, True) == 1024 * 1025 // 2
+
+
+def ORA_brute_vis(N, causal, L):
+    L = N if L is None else L
+    return sum(1 for i in range(N) for j in range(N)
+               if j < L and (not causal or j <= i))
+
+
+PINS = [pin_golden, pin_bruteforce, pin_closed_forms, pin_prob_rows,
+        pin_shift, pin_permutation, pin_tiled_recurrence, pin_reductions,
+        pin_torch_sdpa, pin_finite_diff, pin_torch_autograd,
+        pin_grad_invariants, pin_visible_pairs]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    pin(ORA)
+
+
+def test_pages_score_matrix_figure():
+    """The pages' 12.9 GB (12 fp16 heads, N=23,400) is approximate: the
+    exact count is 13.14e9 bytes."""
+    with open(os.path.join(GOLDEN, "pages_figures.json")) as f:
+        g = json.load(f)
+    exact = g["N"] ** 2 * g["heads"] * g["bytes_per_score"]
+    assert exact == g["exact_bytes"] == 13_141_440_000
+    assert abs(exact / 1e9 - g["pages_figure_GB"]) < 0.25
+
+
+# ------------------------------------------------- planted mistakes ----
+
+MUTANTS = [
+    ("drop_scale", "s = scale * (qr @ kh.T)", "s = (qr @ kh.T)"),
+    ("transposed_scores", "s = scale * (qr @ kh.T)", "s = scale * (kh @ qr.T)"),
+    ("causal_direction", "vis &= j <= i", "vis &= j >= i"),
+    ("causal_hides_diagonal", "vis &= j <= i", "vis &= j < i"),
+    ("kv_len_off_by_one", "vis &= j < int(kv_len_b)", "vis &= j <= int(kv_len_b)"),
+    ("mask_with_zero", "s = np.where(vis, s, -np.inf)", "s = np.where(vis, s, 0.0)"),
+    ("lse_log2", "m + np.log(np.where(l > 0, l, 1))",
+     "m + np.log2(np.where(l > 0, l, 1))"),
+    ("lse_without_max", "m + np.log(np.where(l > 0, l, 1))",
+     "np.log(np.where(l > 0, l, 1))"),
+    ("no_max_subtraction", "e = np.exp(s - m_ref[:, None])", "e = np.exp(s)"),
+    ("no_normalisation", "p = e / np.where(empty, 1.0, l)[:, None]", "p = e"),
+    ("dv_transposed", "dv[b, h] += p.T @ dor", "dv[b, h] += p @ dor"),
+    ("ds_sign", "ds = p * (dp - D[:, None])", "ds = p * (D[:, None] - dp)"),
+    ("ds_without_D", "ds = p * (dp - D[:, None])", "ds = p * dp"),
+    ("dk_without_scale", "dk[b, h] += scale * (ds.T @ q[b, h, c0:c1])",
+     "dk[b, h] += (ds.T @ q[b, h, c0:c1])"),
+    ("dq_uses_v", "dq[b, h, c0:c1] = scale * (ds @ k[b, h])",
+     "dq[b, h, c0:c1] = scale * (ds @ v[b, h])"),
+    ("dq_transposed_ds", "dq[b, h, c0:c1] = scale * (ds @ k[b, h])",
+     "dq[b, h, c0:c1] = scale * (ds.T @ k[b, h])"),
+]
+
+
+def _mutant(old, new):
+    with open(ORA.__file__) as f:
+        src = f.read()
+    assert src.count(old) >= 1, old
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(name, old, new):
+    mod = _mutant(old, new)
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mod)
+        except Exception:
+            return
+    pytest.fail(f"no pin caught the planted mistake {name}")
