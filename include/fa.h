@@ -1,0 +1,159 @@
+/*
+ * fa.h -- C ABI of libfa.so: exact IO-aware tiled attention for AMD Instinct
+ * MI355X (gfx950), forward and backward.
+ *
+ * Pages cited (titles as the pages give them):
+ *   [MM] "Is a full-day context better than a 10-minute context? Flash
+ *        attention and the sequence-length question" (marketmaker.cc blog)
+ *   [TW] "Flash-Attention 2 for performance optimisation" (Medium blog)
+ *   [ZN] "Paper summary: FlashAttention" (zenn.dev)
+ *
+ * Operation.  O = softmax(scale * Q K^T) V per (batch, head) ([MM] "Why
+ * attention is memory-bound"), computed tile by tile with the online-softmax
+ * recurrence so that the N x N score matrix never reaches HBM ([MM] "The
+ * Flash Attention algorithm", "Online softmax recurrence"; [ZN] "Proposed
+ * method": tiling).  The forward also returns the per-row natural-log
+ * log-sum-exp LSE_i = m_i + ln(l_i) ([TW] "Flash Attention 2": one statistic
+ * L per row instead of m and l).  The backward recomputes P tile by tile from
+ * Q, K and LSE instead of storing it ([MM] "Backward pass: recompute instead
+ * of store"; [TW] "Recomputation").
+ *
+ * Visibility.  Key j is visible to query i iff (causal == 0 or j <= i) and
+ * j < kv_len[b] (kv_len absent: N).  With causal != 0, key tiles wholly in
+ * the future of a query tile are neither loaded nor computed ([MM] "Causal
+ * masking").  A query row with no visible key gets O = 0 and LSE = -inf.
+ *
+ * Layout.  Q, K, V, O, dO, dQ, dK, dV are contiguous row-major [B, H, N, d]
+ * (the (batch, heads, seq, head_dim) shape of [MM] "Integration").  LSE is
+ * [B, H, N] float32.  kv_len is int32 [B].  bf16 tensors are passed as raw
+ * 16-bit patterns (uint16_t).  Accumulation is float32 throughout.
+ *
+ * Ownership.  Every pointer except `stream` is a DEVICE pointer owned by the
+ * caller.  The library allocates nothing, frees nothing and keeps no mutable
+ * global state; it is safe to call from several host threads.  Outputs must
+ * not alias inputs.  Outputs are fully overwritten.
+ *
+ * Execution.  Calls are asynchronous: they validate arguments, enqueue
+ * kernels on `stream` (a hipStream_t passed as void*; NULL = the default
+ * stream) and return without synchronising.  Device-side faults surface at
+ * the caller's next synchronisation.
+ *
+ * Errors.  Every entry point returns FA_OK (0) or a negative FA_ERR_* code.
+ * Argument errors are detected before any HIP call is made (so they are
+ * testable without a GPU).  FA_ERR_HIP reports a launch failure
+ * (hipGetLastError after the launch).  `scale` is not validated; NaN or Inf
+ * inputs propagate.  kv_len values are read on the device, not validated, and
+ * clamped to [0, N].  There is no fallback path: an unsupported case is an
+ * error, never a silent slower route.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,      /* a required pointer is NULL                     */
+  FA_ERR_SHAPE = -2,     /* B, H or N <= 0, or B*H*N > 2^31-1              */
+  FA_ERR_HEADDIM = -3,   /* d is not 64 or 128 (backward: not 128)         */
+  FA_ERR_ALIGN = -4,     /* a tensor pointer is not 16-byte aligned        */
+  FA_ERR_WORKSPACE = -5, /* workspace NULL, too small or not 256-B aligned */
+  FA_ERR_HIP = -6        /* the HIP runtime reported a launch error        */
+};
+
+/* Library version, as 10000*major + 100*minor + patch. */
+int fa_version(void);
+
+/* Human-readable text for a status code (never NULL; static storage). */
+const char* fa_status_string(int status);
+
+/*
+ * Forward, bf16 inputs/outputs, float32 accumulation and LSE.
+ *   q, k, v : [B,H,N,d] bf16, read only.
+ *   o       : [B,H,N,d] bf16, written.
+ *   lse     : [B,H,N] float32, written (natural log).
+ *   scale   : multiplies Q K^T (1/sqrt(d) for standard attention).
+ *   causal  : nonzero = key j visible to query i only when j <= i.
+ * d must be 64 or 128.  Equivalent to fa_fwd_kvlen with kv_len = NULL.
+ */
+int fa_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+           uint16_t* o, float* lse, int B, int H, int N, int d, float scale,
+           int causal, void* stream);
+
+/*
+ * Forward with per-sequence key padding: in batch b only keys
+ * j < kv_len[b] are visible (for every head).  kv_len is a device int32 [B]
+ * array, or NULL for no padding.  All N query rows are produced.
+ */
+int fa_fwd_kvlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                 const int32_t* kv_len, uint16_t* o, float* lse, int B, int H,
+                 int N, int d, float scale, int causal, void* stream);
+
+/*
+ * Forward, float32 inputs and outputs (no reduced precision anywhere):
+ * float32 matrix-core products, float32 softmax.  Same shapes and semantics
+ * as fa_fwd.
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
+               float* lse, int B, int H, int N, int d, float scale,
+               int causal, void* stream);
+
+/*
+ * The backward entry points below support head dimension d = 128 only; any
+ * other d returns FA_ERR_HEADDIM (and fa_bwd_workspace_size returns 0).
+ *
+ * Bytes of device workspace fa_bwd needs: D [B,H,N] float32 followed by the
+ * float32 dQ accumulator [B,H,N,d], each starting on a 256-byte boundary.
+ * Returns 0 for invalid shapes.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/*
+ * Backward of the bf16 forward (no key padding).
+ *   q, k, v, o, dO : [B,H,N,d] bf16; o is the forward's output.
+ *   lse            : [B,H,N] float32 from the forward.
+ *   dq, dk, dv     : [B,H,N,d] bf16, written.
+ *   workspace      : device buffer of at least fa_bwd_workspace_size() bytes,
+ *                    256-byte aligned, owned by the caller; its contents on
+ *                    entry do not matter and are clobbered.
+ * P is recomputed tile by tile as exp(scale*Q K^T - LSE).  The gradient is
+ * that of <dO, O>:  dV = P^T dO,  dS = P * (dO V^T - D) with
+ * D_i = dO_i . O_i,  dQ = scale dS K,  dK = scale dS^T Q.
+ * dQ is accumulated in float32 with atomic adds, so its low bits may differ
+ * from run to run; dK and dV are deterministic.
+ * Equivalent to fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq_convert in order.
+ */
+int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+           const uint16_t* o, const uint16_t* dO, const float* lse,
+           uint16_t* dq, uint16_t* dk, uint16_t* dv, void* workspace,
+           size_t workspace_bytes, int B, int H, int N, int d, float scale,
+           int causal, void* stream);
+
+/* Backward stage 1: D_i = dO_i . O_i into the workspace, and zero the dQ
+ * accumulator. */
+int fa_bwd_preprocess(const uint16_t* o, const uint16_t* dO, void* workspace,
+                      size_t workspace_bytes, int B, int H, int N, int d,
+                      void* stream);
+
+/* Backward stage 2: one workgroup per key block; recomputes P, writes dK and
+ * dV, and atomically adds dQ into the workspace accumulator. */
+int fa_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                const uint16_t* dO, const float* lse, uint16_t* dk,
+                uint16_t* dv, void* workspace, size_t workspace_bytes, int B,
+                int H, int N, int d, float scale, int causal, void* stream);
+
+/* Backward stage 3: dq = bf16(scale * dQ accumulator). */
+int fa_bwd_dq_convert(const void* workspace, size_t workspace_bytes,
+                      uint16_t* dq, int B, int H, int N, int d, float scale,
+                      void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

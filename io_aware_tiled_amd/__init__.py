@@ -1,0 +1,252 @@
+"""Python binding of libfa: exact IO-aware tiled attention on MI355X (gfx950).
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of libfa.so (built in-tree by ``python -m io_aware_tiled_amd.build``);
+PyTorch is used for device memory and for the current HIP stream.  There is
+no CPU path and no fallback: if the library is missing or a tensor is not on
+the GPU, the call raises.
+
+The functions named like the C ABI (``fa_fwd``, ``fa_fwd_kvlen``,
+``fa_fwd_f32``, ``fa_bwd``, ``fa_bwd_preprocess``, ``fa_bwd_dkdv``,
+``fa_bwd_dq_convert``, ``fa_bwd_workspace_size``, ``fa_status_string``,
+``fa_version``) take caller-allocated tensors exactly as the C calls take
+pointers.  ``forward`` and ``backward`` allocate the outputs with
+``torch.empty`` on the inputs' device and call them.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "FAError", "lib", "lib_path", "fa_version", "fa_status_string",
+    "fa_fwd", "fa_fwd_kvlen", "fa_fwd_f32", "fa_bwd_workspace_size",
+    "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq_convert",
+    "forward", "backward", "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfa.so")
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_S = ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/fa.h
+_SIGS = {
+    "fa_version": (_I, []),
+    "fa_status_string": (ctypes.c_char_p, [_I]),
+    "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_fwd_kvlen": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_bwd_workspace_size": (_S, [_I, _I, _I, _I]),
+    "fa_bwd": (_I, [_P] * 10 + [_S, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_bwd_preprocess": (_I, [_P, _P, _P, _S, _I, _I, _I, _I, _P]),
+    "fa_bwd_dkdv": (_I, [_P] * 8 + [_S, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_bwd_dq_convert": (_I, [_P, _S, _P, _I, _I, _I, _I, _F, _P]),
+}
+EXPORTED_SYMBOLS = tuple(_SIGS)
+
+
+class FAError(RuntimeError):
+    """A libfa call returned a non-zero status."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fa_status_string(status)} (status {status})")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with "
+                "`python -m io_aware_tiled_amd.build` (no fallback exists)")
+        handle = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def fa_version() -> int:
+    return int(lib().fa_version())
+
+
+def fa_status_string(status: int) -> str:
+    return lib().fa_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise FAError(status, where)
+
+
+# ---------------------------------------------------------------- marshalling
+
+def _ptr(t):
+    """Device pointer of a tensor (None -> NULL).  Refuses host tensors."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libfa takes GPU tensors only (no CPU path exists)")
+    if not t.is_contiguous():
+        raise ValueError("libfa takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(t, stream):
+    import torch
+    if stream is not None:
+        return stream
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _bhnd(q):
+    if q.dim() != 4:
+        raise ValueError(f"expected [B,H,N,d], got shape {tuple(q.shape)}")
+    return tuple(int(x) for x in q.shape)
+
+
+def _expect(t, dtype, shape, name):
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {shape}, got {tuple(t.shape)}")
+
+
+def fa_fwd(q, k, v, o, lse, scale, causal, stream=None):
+    """C fa_fwd on bf16 tensors [B,H,N,d]; lse float32 [B,H,N]."""
+    fa_fwd_kvlen(q, k, v, None, o, lse, scale, causal, stream)
+
+
+def fa_fwd_kvlen(q, k, v, kv_len, o, lse, scale, causal, stream=None):
+    """C fa_fwd_kvlen; kv_len is a device int32 [B] tensor or None."""
+    import torch
+    B, H, N, d = _bhnd(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _expect(t, torch.bfloat16, (B, H, N, d), n)
+    _expect(lse, torch.float32, (B, H, N), "lse")
+    if kv_len is not None:
+        _expect(kv_len, torch.int32, (B,), "kv_len")
+    st = lib().fa_fwd_kvlen(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), _ptr(o),
+                            _ptr(lse), B, H, N, d, float(scale), int(bool(causal)),
+                            _stream(q, stream))
+    _check(st, "fa_fwd_kvlen")
+
+
+def fa_fwd_f32(q, k, v, o, lse, scale, causal, stream=None):
+    """C fa_fwd_f32 on float32 tensors [B,H,N,d]."""
+    import torch
+    B, H, N, d = _bhnd(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _expect(t, torch.float32, (B, H, N, d), n)
+    _expect(lse, torch.float32, (B, H, N), "lse")
+    st = lib().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                          B, H, N, d, float(scale), int(bool(causal)),
+                          _stream(q, stream))
+    _check(st, "fa_fwd_f32")
+
+
+def fa_bwd_workspace_size(B, H, N, d) -> int:
+    return int(lib().fa_bwd_workspace_size(int(B), int(H), int(N), int(d)))
+
+
+def _ws(workspace):
+    import torch
+    if workspace.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 tensor")
+    return _ptr(workspace), workspace.numel()
+
+
+def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, workspace, scale, causal,
+           stream=None):
+    """C fa_bwd; workspace is a device uint8 tensor of at least
+    fa_bwd_workspace_size bytes (torch allocations are 256-B aligned)."""
+    import torch
+    B, H, N, d = _bhnd(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO"),
+                 (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _expect(t, torch.bfloat16, (B, H, N, d), n)
+    _expect(lse, torch.float32, (B, H, N), "lse")
+    wp, wn = _ws(workspace)
+    st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
+                      _ptr(dq), _ptr(dk), _ptr(dv), wp, wn, B, H, N, d,
+                      float(scale), int(bool(causal)), _stream(q, stream))
+    _check(st, "fa_bwd")
+
+
+def fa_bwd_preprocess(o, dO, workspace, stream=None):
+    B, H, N, d = _bhnd(o)
+    wp, wn = _ws(workspace)
+    st = lib().fa_bwd_preprocess(_ptr(o), _ptr(dO), wp, wn, B, H, N, d,
+                                 _stream(o, stream))
+    _check(st, "fa_bwd_preprocess")
+
+
+def fa_bwd_dkdv(q, k, v, dO, lse, dk, dv, workspace, scale, causal,
+                stream=None):
+    B, H, N, d = _bhnd(q)
+    wp, wn = _ws(workspace)
+    st = lib().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse),
+                           _ptr(dk), _ptr(dv), wp, wn, B, H, N, d,
+                           float(scale), int(bool(causal)), _stream(q, stream))
+    _check(st, "fa_bwd_dkdv")
+
+
+def fa_bwd_dq_convert(workspace, dq, scale, stream=None):
+    B, H, N, d = _bhnd(dq)
+    wp, wn = _ws(workspace)
+    st = lib().fa_bwd_dq_convert(wp, wn, _ptr(dq), B, H, N, d, float(scale),
+                                 _stream(dq, stream))
+    _check(st, "fa_bwd_dq_convert")
+
+
+# ------------------------------------------------------------- convenience
+
+def forward(q, k, v, *, causal=False, scale=None, kv_len=None, stream=None):
+    """Returns (o, lse).  bf16 inputs use fa_fwd_kvlen, float32 use
+    fa_fwd_f32 (which has no key padding)."""
+    import torch
+    B, H, N, d = _bhnd(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if q.dtype == torch.float32:
+        if kv_len is not None:
+            raise ValueError("fa_fwd_f32 has no key-padding variant")
+        fa_fwd_f32(q, k, v, o, lse, scale, causal, stream)
+    else:
+        fa_fwd_kvlen(q, k, v, kv_len, o, lse, scale, causal, stream)
+    return o, lse
+
+
+def backward(q, k, v, o, lse, dO, *, causal=False, scale=None, stream=None,
+             workspace=None):
+    """Returns (dq, dk, dv) for the bf16 forward."""
+    import torch
+    B, H, N, d = _bhnd(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nbytes = fa_bwd_workspace_size(B, H, N, d)
+    if nbytes == 0:
+        raise FAError(-3 if d != 128 else -2, "fa_bwd_workspace_size")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, workspace, scale, causal, stream)
+    return dq, dk, dv

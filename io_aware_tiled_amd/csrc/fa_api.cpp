@@ -1,0 +1,194 @@
+// C ABI of libfa (declared in include/fa.h): argument validation, workspace
+// layout and dispatch to the gfx950 kernels.  Every argument check runs before
+// the first HIP call, so argument errors are reported without touching a GPU.
+#include "fa.h"
+
+#include <stdint.h>
+
+#include "fa_launch.h"
+
+namespace {
+
+constexpr int kVersion = 10000;   // 1.0.0
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape check shared by all entry points: positive extents, a supported head
+// dimension, at most 2^31-1 rows (B*H*N) so every grid fits HIP's 32-bit
+// workgroup count.
+int check_shape(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_SHAPE;
+  const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
+  const unsigned long long rows = bh * (unsigned long long)N;
+  if (rows > 0x7fffffffull) return FA_ERR_SHAPE;
+  const unsigned long long qblk = bh * (((unsigned long long)N + 127) / 128);
+  if (qblk > 0x7fffffffull) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  return FA_OK;
+}
+
+// The backward kernels exist for head dimension 128 only.
+int check_shape_bwd(int B, int H, int N, int d) {
+  const int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  return d == 128 ? FA_OK : FA_ERR_HEADDIM;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Workspace {
+  float* D;
+  float* dq_acc;
+};
+
+size_t ws_d_bytes(int B, int H, int N) {
+  return align256((size_t)B * H * N * sizeof(float));
+}
+
+size_t ws_bytes(int B, int H, int N, int d) {
+  return ws_d_bytes(B, H, N) + align256((size_t)B * H * N * d * sizeof(float));
+}
+
+int check_workspace(const void* ws, size_t bytes, int B, int H, int N, int d) {
+  if (ws == nullptr) return FA_ERR_WORKSPACE;
+  if (((uintptr_t)ws & 255u) != 0) return FA_ERR_WORKSPACE;
+  if (bytes < ws_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
+  return FA_OK;
+}
+
+Workspace carve(void* ws, int B, int H, int N) {
+  Workspace w;
+  w.D = (float*)ws;
+  w.dq_acc = (float*)((char*)ws + ws_d_bytes(B, H, N));
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return kVersion; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE:
+      return "FA_ERR_SHAPE: B, H or N is not positive, or the problem is too large";
+    case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension d must be 64 or 128";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
+    case FA_ERR_WORKSPACE:
+      return "FA_ERR_WORKSPACE: workspace is NULL, not 256-byte aligned or too small";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported a launch error";
+    default: return "unknown fa status code";
+  }
+}
+
+int fa_fwd_kvlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                 const int32_t* kv_len, uint16_t* o, float* lse, int B, int H,
+                 int N, int d, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(lse) || ((uintptr_t)kv_len & 3u) != 0)
+    return FA_ERR_ALIGN;
+  return fa::launch_fwd_bf16(q, k, v, kv_len, o, lse, B, H, N, d, scale,
+                             causal != 0, (hipStream_t)stream);
+}
+
+int fa_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+           uint16_t* o, float* lse, int B, int H, int N, int d, float scale,
+           int causal, void* stream) {
+  return fa_fwd_kvlen(q, k, v, nullptr, o, lse, B, H, N, d, scale, causal,
+                      stream);
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
+               float* lse, int B, int H, int N, int d, float scale,
+               int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(lse))
+    return FA_ERR_ALIGN;
+  return fa::launch_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal != 0,
+                            (hipStream_t)stream);
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
+  if (check_shape_bwd(B, H, N, d) != FA_OK) return 0;
+  return ws_bytes(B, H, N, d);
+}
+
+int fa_bwd_preprocess(const uint16_t* o, const uint16_t* dO, void* workspace,
+                      size_t workspace_bytes, int B, int H, int N, int d,
+                      void* stream) {
+  if (!o || !dO) return FA_ERR_NULL;
+  int st = check_shape_bwd(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned16(o) || !aligned16(dO)) return FA_ERR_ALIGN;
+  st = check_workspace(workspace, workspace_bytes, B, H, N, d);
+  if (st != FA_OK) return st;
+  const Workspace w = carve(workspace, B, H, N);
+  return fa::launch_bwd_preprocess(o, dO, w.D, w.dq_acc, B, H, N, d,
+                                   (hipStream_t)stream);
+}
+
+int fa_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                const uint16_t* dO, const float* lse, uint16_t* dk,
+                uint16_t* dv, void* workspace, size_t workspace_bytes, int B,
+                int H, int N, int d, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !dO || !lse || !dk || !dv) return FA_ERR_NULL;
+  int st = check_shape_bwd(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) ||
+      !aligned16(lse) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_ALIGN;
+  st = check_workspace(workspace, workspace_bytes, B, H, N, d);
+  if (st != FA_OK) return st;
+  const Workspace w = carve(workspace, B, H, N);
+  return fa::launch_bwd_dkdv(q, k, v, dO, lse, w.D, w.dq_acc, dk, dv, B, H, N,
+                             d, scale, causal != 0, (hipStream_t)stream);
+}
+
+int fa_bwd_dq_convert(const void* workspace, size_t workspace_bytes,
+                      uint16_t* dq, int B, int H, int N, int d, float scale,
+                      void* stream) {
+  if (!dq) return FA_ERR_NULL;
+  int st = check_shape_bwd(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned16(dq)) return FA_ERR_ALIGN;
+  st = check_workspace(workspace, workspace_bytes, B, H, N, d);
+  if (st != FA_OK) return st;
+  const Workspace w = carve(const_cast<void*>(workspace), B, H, N);
+  return fa::launch_bwd_dq_convert(w.dq_acc, dq, (size_t)B * H * N * d,
+                                   scale, (hipStream_t)stream);
+}
+
+int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+           const uint16_t* o, const uint16_t* dO, const float* lse,
+           uint16_t* dq, uint16_t* dk, uint16_t* dv, void* workspace,
+           size_t workspace_bytes, int B, int H, int N, int d, float scale,
+           int causal, void* stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv)
+    return FA_ERR_NULL;
+  int st = check_shape_bwd(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(dO) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv))
+    return FA_ERR_ALIGN;
+  st = check_workspace(workspace, workspace_bytes, B, H, N, d);
+  if (st != FA_OK) return st;
+  st = fa_bwd_preprocess(o, dO, workspace, workspace_bytes, B, H, N, d, stream);
+  if (st != FA_OK) return st;
+  st = fa_bwd_dkdv(q, k, v, dO, lse, dk, dv, workspace, workspace_bytes, B, H,
+                   N, d, scale, causal, stream);
+  if (st != FA_OK) return st;
+  return fa_bwd_dq_convert(workspace, workspace_bytes, dq, B, H, N, d, scale,
+                           stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// Shared device-side helpers of libfa (gfx950 / CDNA4 only).
+//
+// Matrix-core lane layouts used throughout (checked on gfx950 with an
+// in-bounds probe):
+//   v_mfma_f32_32x32x16_bf16  C = A(32x16) * B(16x32) + C
+//     A: lane l holds A[l%32][k-slot (l/32, e)], e = 0..7   (8 bf16)
+//     B: lane l holds B[k-slot (l/32, e)][l%32]            (8 bf16)
+//     C: lane l register r holds C[8*(r/4) + 4*(l/32) + r%4][l%32]
+//   The k-slot (l/32, e) is the same for A and B, so any consistent
+//   assignment of contraction indices to slots gives the same product.
+//   v_mfma_f32_32x32x2_f32: A lane l holds A[l%32][slot l/32], B likewise,
+//   C as above.
+//   ds_read_b64_tr_b16: inside each group of 16 lanes, lane r addresses four
+//   consecutive 16-bit values M[r][0..3]; lane i receives
+//   M[4e + i/4][i%4] for e = 0..3.  Pointing lane r at row (base + r/4),
+//   column (cbase + 4*(r%4)) of a row-major tile gives lane i the column
+//   (cbase + i) of rows base..base+3: a transposed read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32x2f(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Transposed 4 x 16-bit read from LDS (see the layout note above).
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+// Concatenate two transposed reads into one MFMA operand.  Built with a
+// whole-vector shuffle and bit cast: assembling a __bf16 vector element by
+// element is miscompiled by the ROCm 7.2 compiler (it broadcasts element 0).
+__device__ __forceinline__ bf16x8 join_bf16(i16x4 lo, i16x4 hi) {
+  const i16x8 r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Halves of an 8-element bf16 vector (whole-vector shuffles, see above).
+__device__ __forceinline__ bf16x4 lo4(bf16x8 x) {
+  const i16x8 r = __builtin_bit_cast(i16x8, x);
+  return __builtin_bit_cast(bf16x4, __builtin_shufflevector(r, r, 0, 1, 2, 3));
+}
+__device__ __forceinline__ bf16x4 hi4(bf16x8 x) {
+  const i16x8 r = __builtin_bit_cast(i16x8, x);
+  return __builtin_bit_cast(bf16x4, __builtin_shufflevector(r, r, 4, 5, 6, 7));
+}
+
+// Round-to-nearest-even float32 -> bf16 of 8 values.
+__device__ __forceinline__ bf16x8 to_bf16x8(f32x8 x) {
+  return __builtin_convertvector(x, bf16x8);
+}
+
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
+  return __builtin_convertvector(x, bf16x4);
+}
+
+// Value of the other half-wave's lane (l ^ 32).
+__device__ __forceinline__ float xor32(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+// Workgroup index remap so that consecutive logical indices stay on one
+// XCD: the hardware deals workgroups round-robin over the 8 XCDs, so
+// physical id p runs on XCD p % 8.  Logical id = (p % 8) * per + p / 8 for
+// the full part of the grid; the remainder maps to itself.
+__device__ __forceinline__ int xcd_remap(int p, int n) {
+  constexpr int kXcd = 8;
+  const int per = n / kXcd;
+  const int full = per * kXcd;
+  if (p >= full) return p;
+  return (p % kXcd) * per + p / kXcd;
+}
+
+}  // namespace fa

@@ -1,0 +1,33 @@
+// Internal launchers of libfa (not part of the C ABI).  Arguments are
+// validated by the C-ABI layer before any of these is called; each returns 0
+// or -6 (a HIP launch error).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+int launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    const int32_t* kv_len, uint16_t* o, float* lse, int B,
+                    int H, int N, int d, float scale, int causal,
+                    hipStream_t stream);
+
+int launch_fwd_f32(const float* q, const float* k, const float* v, float* o,
+                   float* lse, int B, int H, int N, int d, float scale,
+                   int causal, hipStream_t stream);
+
+int launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, float* D,
+                          float* dq_acc, int B, int H, int N, int d,
+                          hipStream_t stream);
+
+int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    const uint16_t* dO, const float* lse, const float* D,
+                    float* dq_acc, uint16_t* dk, uint16_t* dv, int B, int H,
+                    int N, int d, float scale, int causal, hipStream_t stream);
+
+int launch_bwd_dq_convert(const float* dq_acc, uint16_t* dq, size_t n,
+                          float scale, hipStream_t stream);
+
+}  // namespace fa

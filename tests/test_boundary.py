@@ -1,0 +1,137 @@
+"""C-ABI boundary checks that need no GPU.
+
+The library must load, export every function include/fa.h declares, and
+reject bad arguments with the documented status codes before making any HIP
+call (so these run on a machine without a GPU).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import io_aware_tiled_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+OK, NULL, SHAPE, HEADDIM, ALIGN, WORKSPACE, HIP = 0, -1, -2, -3, -4, -5, -6
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fa.lib_path()),
+                                reason="libfa.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(fa_[a-z0-9_]+)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_expected_calls():
+    names = _declared_functions()
+    for want in ["fa_fwd", "fa_fwd_kvlen", "fa_fwd_f32", "fa_bwd",
+                 "fa_bwd_workspace_size", "fa_status_string", "fa_version",
+                 "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq_convert"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    raw = ctypes.CDLL(fa.lib_path())
+    for name in _declared_functions():
+        assert hasattr(raw, name), name
+    assert set(_declared_functions()) == set(fa.EXPORTED_SYMBOLS)
+
+
+def test_version_and_status_strings():
+    assert fa.fa_version() == 10000
+    seen = set()
+    for code in (OK, NULL, SHAPE, HEADDIM, ALIGN, WORKSPACE, HIP):
+        s = fa.fa_status_string(code)
+        assert s.startswith("FA_"), s
+        seen.add(s)
+    assert len(seen) == 7
+    assert "unknown" in fa.fa_status_string(12345)
+
+
+# Fake, never-dereferenced device addresses: validation fails before use.
+A = 0x10000          # 16-byte aligned
+MIS = 0x10002        # misaligned
+
+
+def _fwd(q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=64, d=64, scale=0.125,
+         causal=0, kv=None):
+    return fa.lib().fa_fwd_kvlen(q, k, v, kv, o, lse, B, H, N, d, scale,
+                                 causal, None)
+
+
+def test_fwd_argument_errors():
+    assert _fwd(q=None) == NULL
+    assert _fwd(o=None) == NULL
+    assert _fwd(lse=None) == NULL
+    assert _fwd(B=0) == SHAPE
+    assert _fwd(H=-1) == SHAPE
+    assert _fwd(N=0) == SHAPE
+    assert _fwd(B=1 << 16, H=1 << 16, N=1 << 16) == SHAPE
+    assert _fwd(d=32) == HEADDIM
+    assert _fwd(d=96) == HEADDIM
+    assert _fwd(d=256) == HEADDIM
+    assert _fwd(q=MIS) == ALIGN
+    assert _fwd(lse=MIS) == ALIGN
+    assert _fwd(kv=0x10001) == ALIGN
+    L = fa.lib()
+    assert L.fa_fwd(None, A, A, A, A, 1, 1, 64, 64, 0.1, 1, None) == NULL
+    assert L.fa_fwd(A, A, A, A, A, 1, 1, 64, 48, 0.1, 1, None) == HEADDIM
+    assert L.fa_fwd_f32(A, A, None, A, A, 1, 1, 64, 64, 0.1, 0, None) == NULL
+    assert L.fa_fwd_f32(A, A, A, A, MIS, 1, 1, 64, 64, 0.1, 0, None) == ALIGN
+    assert L.fa_fwd_f32(A, A, A, A, A, 1, 0, 64, 64, 0.1, 0, None) == SHAPE
+
+
+def test_workspace_size():
+    ws = fa.fa_bwd_workspace_size
+    def a256(x):
+        return (x + 255) // 256 * 256
+    for B, H, N in [(1, 1, 1), (4, 16, 4096), (2, 3, 1000)]:
+        want = a256(B * H * N * 4) + a256(B * H * N * 128 * 4)
+        assert ws(B, H, N, 128) == want
+    assert ws(1, 1, 64, 64) == 0          # backward: head dim 128 only
+    assert ws(0, 1, 64, 128) == 0
+    assert ws(1, 1, -5, 128) == 0
+
+
+def test_bwd_argument_errors():
+    L = fa.lib()
+    nbytes = fa.fa_bwd_workspace_size(1, 1, 64, 128)
+    W = 0x100000                          # 256-byte aligned fake address
+
+    def bwd(ptrs=None, ws=W, wsb=nbytes, d=128, N=64):
+        p = ptrs or [A] * 9
+        return L.fa_bwd(*p, ws, wsb, 1, 1, N, d, 0.088, 1, None)
+    for i in range(9):
+        p = [A] * 9
+        p[i] = None
+        assert bwd(p) == NULL, i
+    assert bwd(d=64) == HEADDIM
+    assert bwd(N=0) == SHAPE
+    assert bwd(ws=None) == WORKSPACE
+    assert bwd(ws=W + 16) == WORKSPACE    # not 256-byte aligned
+    assert bwd(wsb=nbytes - 1) == WORKSPACE
+    p = [A] * 9
+    p[4] = MIS
+    assert bwd(p) == ALIGN
+    assert L.fa_bwd_preprocess(A, None, W, nbytes, 1, 1, 64, 128, None) == NULL
+    assert L.fa_bwd_preprocess(A, A, W, 16, 1, 1, 64, 128, None) == WORKSPACE
+    assert L.fa_bwd_dkdv(A, A, A, A, A, A, None, W, nbytes, 1, 1, 64, 128,
+                         0.1, 1, None) == NULL
+    assert L.fa_bwd_dq_convert(W, nbytes, None, 1, 1, 64, 128, 0.1,
+                               None) == NULL
+    assert L.fa_bwd_dq_convert(W, nbytes, A, 1, 1, 64, 64, 0.1,
+                               None) == HEADDIM
+
+
+def test_python_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q)
