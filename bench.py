@@ -1,0 +1,255 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+for the default workload (causal, B=4, H=16, N=4096, d=128) that is the
+forward (fa_fwd) and the three backward stages (fa_bwd_preprocess,
+fa_bwd_dkdv, fa_bwd_dq_convert).  Forward-only workloads run fa_fwd (or
+fa_fwd_f32 / fa_fwd_kvlen).  Inputs are resident in HBM before timing starts.
+
+Throughput is algorithmic: 4d FLOP per visible (query, key) pair for the
+forward and 10d for the backward (causal: N(N+1)/2 pairs per head); masked
+work, exp and max/sum operations are not counted.  Rank 0 prints one JSON
+line with a "roofline" object for the dominant kernel (its average launch
+duration from HIP events recorded on the launch stream during the timed
+steps) and a "cpu_baseline" object (the fp64 oracle timed on a bounded
+sample of heads on the host cores).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synthetic as S  # noqa: E402
+
+METRIC = ("attention fwd(+bwd) TFLOP/s bf16 causal, N=1K-23.4K; "
+          "% of MFMA peak")
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix peak (published)
+PEAK_F32_TFLOPS = 157.3         # MI355X fp32 matrix peak (published)
+DEFAULT_WORKLOAD = "causal_fwd_bwd_d128"
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
+
+
+def _sources_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "io_aware_tiled_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def visible_pairs(w: S.Workload, kv_len) -> int:
+    if w.causal:
+        per = w.N * (w.N + 1) // 2
+        return per * w.B * w.H
+    if kv_len is None:
+        return w.N * w.N * w.B * w.H
+    return int(sum(w.N * int(L) for L in kv_len)) * w.H
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w: S.Workload, inp: dict, target_s: float = 15.0) -> dict:
+    """Time the fp64 oracle (as it stands) on a bounded sample of heads."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    nh = 1
+    # one head first, then grow the sample toward target_s of CPU work
+    sl = (slice(0, 1), slice(0, nh))
+    q, k, v = (inp[n][sl] for n in ("q", "k", "v"))
+    kv = None if inp["kv_len"] is None else inp["kv_len"][:1]
+    t0 = time.perf_counter()
+    oracle.attention_fwd(q, k, v, inp["scale"], inp["causal"], kv,
+                         workers=cores)
+    if w.backward:
+        oracle.attention_bwd(q, k, v, inp["do"][sl], inp["scale"],
+                             inp["causal"], kv, workers=cores)
+    t1 = time.perf_counter() - t0
+    nh = int(max(1, min(w.H, cores, target_s // max(t1, 1e-3))))
+    if nh > 1:
+        sl = (slice(0, 1), slice(0, nh))
+        q, k, v = (inp[n][sl] for n in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        oracle.attention_fwd(q, k, v, inp["scale"], inp["causal"], kv,
+                             workers=cores)
+        if w.backward:
+            oracle.attention_bwd(q, k, v, inp["do"][sl], inp["scale"],
+                                 inp["causal"], kv, workers=cores)
+        t1 = time.perf_counter() - t0
+    sw = S.Workload(w.name, 1, nh, w.N, w.d, w.dtype, w.causal, w.seeds,
+                    w.backward)
+    pairs = visible_pairs(sw, kv)
+    flops = pairs * w.d * (4 + (10 if w.backward else 0))
+    return {"value": flops / t1 / 1e12, "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": (f"fp64 numpy oracle, {'forward+backward' if w.backward else 'forward'}"
+                       f" of batch 0, heads 0..{nh - 1} of {w.name} "
+                       f"(N={w.N}, d={w.d}); {t1:.2f} s; {cores} threads "
+                       "(BLAS pool + one worker thread per head)")}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    choices=sorted(S.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (profiling runs)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU "
+              f"path (asked for --gpus {args.gpus}); run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import io_aware_tiled_amd as fa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    w = S.WORKLOADS[args.workload]
+    log(f"[bench] generating {w.name} inputs")
+    inp = S.make_inputs(w)
+
+    def up(name):
+        bits = inp[name + "_bits"]
+        if w.dtype == "bf16":
+            return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(bits).to(dev)
+
+    q, k, v = up("q"), up("k"), up("v")
+    do = up("do") if w.backward else None
+    kv = None if inp["kv_len"] is None else torch.from_numpy(inp["kv_len"]).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    scale, causal = inp["scale"], inp["causal"]
+    if w.backward:
+        ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.N, w.d),
+                         dtype=torch.uint8, device=dev)
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    names = ["fwd"] + (["bwd_preprocess", "bwd_dkdv", "bwd_dq_convert"]
+                       if w.backward else [])
+
+    def step(events=None):
+        def mark(i):
+            if events is not None:
+                events[i].record(stream)
+        mark(0)
+        if w.dtype == "f32":
+            fa.fa_fwd_f32(q, k, v, o, lse, scale, causal)
+        else:
+            fa.fa_fwd_kvlen(q, k, v, kv, o, lse, scale, causal)
+        mark(1)
+        if w.backward:
+            fa.fa_bwd_preprocess(o, do, ws)
+            mark(2)
+            fa.fa_bwd_dkdv(q, k, v, do, lse, dk, dv, ws, scale, causal)
+            mark(3)
+            fa.fa_bwd_dq_convert(ws, dq, scale)
+            mark(4)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+          for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    per_kernel = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]))
+                  for j, n in enumerate(names)}
+    pairs = visible_pairs(w, inp["kv_len"])
+    fwd_flops = 4.0 * w.d * pairs
+    bwd_flops = 10.0 * w.d * pairs if w.backward else 0.0
+    step_flops = fwd_flops + bwd_flops
+    value = step_flops / (ms_step * 1e-3) / 1e12
+    peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+
+    if w.backward:
+        dom, dom_flops, src = "bwd_dkdv", bwd_flops, ["fa_bwd.hip", "fa_common.h"]
+    else:
+        dom, dom_flops, src = "fwd", fwd_flops, ["fa_fwd.hip", "fa_common.h"]
+    dom_ms = per_kernel[dom]
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        ent = tr.get(w.name, {}).get(dom)
+        if ent and ent.get("source_digest") == _sources_digest(src):
+            traffic = ent["bytes_per_launch"]
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2),
+                "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic,
+                "kernel": dom, "kernel_ms": round(dom_ms, 4),
+                "algorithmic_flop_per_launch": dom_flops}
+
+    # outputs of the timed run must be finite (parity itself is the tests' job)
+    check = {"o_finite": bool(torch.isfinite(o.float()).all()),
+             "lse_finite_or_neg_inf": bool((torch.isfinite(lse) | (lse == -float("inf"))).all())}
+    if w.backward:
+        check["grads_finite"] = bool(all(torch.isfinite(t.float()).all()
+                                         for t in (dq, dk, dv)))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on a sample (cpu_baseline)")
+        cpu = cpu_baseline(w, inp)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if w.dtype == "f32" else "bf16",
+        "data": "synthetic (seeded iid N(0,1) inputs of the workload's shape)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal,
+                   "pass": "forward+backward" if w.backward else "forward",
+                   "parallelism": "single GPU"},
+        "frac_of_peak": round(value / peak, 4),
+        "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},
+        "fwd_tflops": round(fwd_flops / (per_kernel["fwd"] * 1e-3) / 1e12, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "sanity": check,
+    }
+    if w.backward:
+        bwd_ms = sum(per_kernel[n] for n in names[1:])
+        out["bwd_tflops"] = round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
