@@ -5,7 +5,7 @@
 A step is one pass of the whole hot path over one batch of synthetic input:
 for the default workload (causal, B=4, H=16, N=4096, d=128) that is the
 forward (fa_fwd) and the three backward stages (fa_bwd_preprocess,
-fa_bwd_dkdv, fa_bwd_dq_convert).  Forward-only workloads run fa_fwd (or
+fa_bwd_dkdv, fa_bwd_dq).  Forward-only workloads run fa_fwd (or
 fa_fwd_f32 / fa_fwd_kvlen).  Inputs are resident in HBM before timing starts.
 
 Throughput is algorithmic: 4d FLOP per visible (query, key) pair for the
@@ -149,7 +149,7 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
-    names = ["fwd"] + (["bwd_preprocess", "bwd_dkdv", "bwd_dq_convert"]
+    names = ["fwd"] + (["bwd_preprocess", "bwd_dkdv", "bwd_dq"]
                        if w.backward else [])
 
     def step(events=None):
@@ -167,7 +167,7 @@ def main(argv=None) -> int:
             mark(2)
             fa.fa_bwd_dkdv(q, k, v, do, lse, dk, dv, ws, scale, causal)
             mark(3)
-            fa.fa_bwd_dq_convert(ws, dq, scale)
+            fa.fa_bwd_dq(q, k, v, do, lse, dq, ws, scale, causal)
             mark(4)
 
     log(f"[bench] warmup {args.warmup} steps")

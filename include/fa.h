@@ -107,9 +107,9 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
  * The backward entry points below support head dimension d = 128 only; any
  * other d returns FA_ERR_HEADDIM (and fa_bwd_workspace_size returns 0).
  *
- * Bytes of device workspace fa_bwd needs: D [B,H,N] float32 followed by the
- * float32 dQ accumulator [B,H,N,d], each starting on a 256-byte boundary.
- * Returns 0 for invalid shapes.
+ * Bytes of device workspace the backward needs: D [B,H,N] float32 (the row
+ * dot products dO_i . O_i), rounded up to 256 bytes.  Returns 0 for invalid
+ * shapes.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 
@@ -123,10 +123,10 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  *                    entry do not matter and are clobbered.
  * P is recomputed tile by tile as exp(scale*Q K^T - LSE).  The gradient is
  * that of <dO, O>:  dV = P^T dO,  dS = P * (dO V^T - D) with
- * D_i = dO_i . O_i,  dQ = scale dS K,  dK = scale dS^T Q.
- * dQ is accumulated in float32 with atomic adds, so its low bits may differ
- * from run to run; dK and dV are deterministic.
- * Equivalent to fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq_convert in order.
+ * D_i = dO_i . O_i,  dQ = scale dS K,  dK = scale dS^T Q.  Accumulation is
+ * float32 in registers with no atomics, so results are bitwise
+ * reproducible.  Equivalent to fa_bwd_preprocess, fa_bwd_dkdv and fa_bwd_dq
+ * in that order on one stream.
  */
 int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
            const uint16_t* o, const uint16_t* dO, const float* lse,
@@ -134,23 +134,25 @@ int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
            size_t workspace_bytes, int B, int H, int N, int d, float scale,
            int causal, void* stream);
 
-/* Backward stage 1: D_i = dO_i . O_i into the workspace, and zero the dQ
- * accumulator. */
+/* Backward stage 1: D_i = dO_i . O_i (float32) into the workspace. */
 int fa_bwd_preprocess(const uint16_t* o, const uint16_t* dO, void* workspace,
                       size_t workspace_bytes, int B, int H, int N, int d,
                       void* stream);
 
-/* Backward stage 2: one workgroup per key block; recomputes P, writes dK and
- * dV, and atomically adds dQ into the workspace accumulator. */
+/* Backward stage 2: one workgroup per 128-key block; recomputes S, P, dP and
+ * dS per query tile and writes dK and dV.  Reads D from the workspace. */
 int fa_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                 const uint16_t* dO, const float* lse, uint16_t* dk,
-                uint16_t* dv, void* workspace, size_t workspace_bytes, int B,
-                int H, int N, int d, float scale, int causal, void* stream);
+                uint16_t* dv, const void* workspace, size_t workspace_bytes,
+                int B, int H, int N, int d, float scale, int causal,
+                void* stream);
 
-/* Backward stage 3: dq = bf16(scale * dQ accumulator). */
-int fa_bwd_dq_convert(const void* workspace, size_t workspace_bytes,
-                      uint16_t* dq, int B, int H, int N, int d, float scale,
-                      void* stream);
+/* Backward stage 3: one workgroup per 128-row query block; recomputes S, P,
+ * dP and dS per key tile and writes dQ.  Reads D from the workspace. */
+int fa_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+              const uint16_t* dO, const float* lse, uint16_t* dq,
+              const void* workspace, size_t workspace_bytes, int B, int H,
+              int N, int d, float scale, int causal, void* stream);
 
 #ifdef __cplusplus
 }

@@ -8,7 +8,7 @@ the GPU, the call raises.
 
 The functions named like the C ABI (``fa_fwd``, ``fa_fwd_kvlen``,
 ``fa_fwd_f32``, ``fa_bwd``, ``fa_bwd_preprocess``, ``fa_bwd_dkdv``,
-``fa_bwd_dq_convert``, ``fa_bwd_workspace_size``, ``fa_status_string``,
+``fa_bwd_dq``, ``fa_bwd_workspace_size``, ``fa_status_string``,
 ``fa_version``) take caller-allocated tensors exactly as the C calls take
 pointers.  ``forward`` and ``backward`` allocate the outputs with
 ``torch.empty`` on the inputs' device and call them.
@@ -22,7 +22,7 @@ import os
 __all__ = [
     "FAError", "lib", "lib_path", "fa_version", "fa_status_string",
     "fa_fwd", "fa_fwd_kvlen", "fa_fwd_f32", "fa_bwd_workspace_size",
-    "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq_convert",
+    "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
     "forward", "backward", "EXPORTED_SYMBOLS",
 ]
 
@@ -46,7 +46,7 @@ _SIGS = {
     "fa_bwd": (_I, [_P] * 10 + [_S, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_preprocess": (_I, [_P, _P, _P, _S, _I, _I, _I, _I, _P]),
     "fa_bwd_dkdv": (_I, [_P] * 8 + [_S, _I, _I, _I, _I, _F, _I, _P]),
-    "fa_bwd_dq_convert": (_I, [_P, _S, _P, _I, _I, _I, _I, _F, _P]),
+    "fa_bwd_dq": (_I, [_P] * 7 + [_S, _I, _I, _I, _I, _F, _I, _P]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -205,12 +205,13 @@ def fa_bwd_dkdv(q, k, v, dO, lse, dk, dv, workspace, scale, causal,
     _check(st, "fa_bwd_dkdv")
 
 
-def fa_bwd_dq_convert(workspace, dq, scale, stream=None):
-    B, H, N, d = _bhnd(dq)
+def fa_bwd_dq(q, k, v, dO, lse, dq, workspace, scale, causal, stream=None):
+    B, H, N, d = _bhnd(q)
     wp, wn = _ws(workspace)
-    st = lib().fa_bwd_dq_convert(wp, wn, _ptr(dq), B, H, N, d, float(scale),
-                                 _stream(dq, stream))
-    _check(st, "fa_bwd_dq_convert")
+    st = lib().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse),
+                         _ptr(dq), wp, wn, B, H, N, d, float(scale),
+                         int(bool(causal)), _stream(q, stream))
+    _check(st, "fa_bwd_dq")
 
 
 # ------------------------------------------------------------- convenience

@@ -36,31 +36,16 @@ int check_shape_bwd(int B, int H, int N, int d) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-struct Workspace {
-  float* D;
-  float* dq_acc;
-};
-
-size_t ws_d_bytes(int B, int H, int N) {
+// The backward workspace holds D [B,H,N] float32 only.
+size_t ws_bytes(int B, int H, int N) {
   return align256((size_t)B * H * N * sizeof(float));
 }
 
-size_t ws_bytes(int B, int H, int N, int d) {
-  return ws_d_bytes(B, H, N) + align256((size_t)B * H * N * d * sizeof(float));
-}
-
-int check_workspace(const void* ws, size_t bytes, int B, int H, int N, int d) {
+int check_workspace(const void* ws, size_t bytes, int B, int H, int N) {
   if (ws == nullptr) return FA_ERR_WORKSPACE;
   if (((uintptr_t)ws & 255u) != 0) return FA_ERR_WORKSPACE;
-  if (bytes < ws_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
+  if (bytes < ws_bytes(B, H, N)) return FA_ERR_WORKSPACE;
   return FA_OK;
-}
-
-Workspace carve(void* ws, int B, int H, int N) {
-  Workspace w;
-  w.D = (float*)ws;
-  w.dq_acc = (float*)((char*)ws + ws_d_bytes(B, H, N));
-  return w;
 }
 
 }  // namespace
@@ -119,7 +104,7 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   if (check_shape_bwd(B, H, N, d) != FA_OK) return 0;
-  return ws_bytes(B, H, N, d);
+  return ws_bytes(B, H, N);
 }
 
 int fa_bwd_preprocess(const uint16_t* o, const uint16_t* dO, void* workspace,
@@ -129,42 +114,44 @@ int fa_bwd_preprocess(const uint16_t* o, const uint16_t* dO, void* workspace,
   int st = check_shape_bwd(B, H, N, d);
   if (st != FA_OK) return st;
   if (!aligned16(o) || !aligned16(dO)) return FA_ERR_ALIGN;
-  st = check_workspace(workspace, workspace_bytes, B, H, N, d);
+  st = check_workspace(workspace, workspace_bytes, B, H, N);
   if (st != FA_OK) return st;
-  const Workspace w = carve(workspace, B, H, N);
-  return fa::launch_bwd_preprocess(o, dO, w.D, w.dq_acc, B, H, N, d,
+  return fa::launch_bwd_preprocess(o, dO, (float*)workspace, B, H, N, d,
                                    (hipStream_t)stream);
 }
 
 int fa_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                 const uint16_t* dO, const float* lse, uint16_t* dk,
-                uint16_t* dv, void* workspace, size_t workspace_bytes, int B,
-                int H, int N, int d, float scale, int causal, void* stream) {
+                uint16_t* dv, const void* workspace, size_t workspace_bytes,
+                int B, int H, int N, int d, float scale, int causal,
+                void* stream) {
   if (!q || !k || !v || !dO || !lse || !dk || !dv) return FA_ERR_NULL;
   int st = check_shape_bwd(B, H, N, d);
   if (st != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) ||
       !aligned16(lse) || !aligned16(dk) || !aligned16(dv))
     return FA_ERR_ALIGN;
-  st = check_workspace(workspace, workspace_bytes, B, H, N, d);
+  st = check_workspace(workspace, workspace_bytes, B, H, N);
   if (st != FA_OK) return st;
-  const Workspace w = carve(workspace, B, H, N);
-  return fa::launch_bwd_dkdv(q, k, v, dO, lse, w.D, w.dq_acc, dk, dv, B, H, N,
-                             d, scale, causal != 0, (hipStream_t)stream);
+  return fa::launch_bwd_dkdv(q, k, v, dO, lse, (const float*)workspace, dk,
+                             dv, B, H, N, d, scale, causal != 0,
+                             (hipStream_t)stream);
 }
 
-int fa_bwd_dq_convert(const void* workspace, size_t workspace_bytes,
-                      uint16_t* dq, int B, int H, int N, int d, float scale,
-                      void* stream) {
-  if (!dq) return FA_ERR_NULL;
+int fa_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+              const uint16_t* dO, const float* lse, uint16_t* dq,
+              const void* workspace, size_t workspace_bytes, int B, int H,
+              int N, int d, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !dO || !lse || !dq) return FA_ERR_NULL;
   int st = check_shape_bwd(B, H, N, d);
   if (st != FA_OK) return st;
-  if (!aligned16(dq)) return FA_ERR_ALIGN;
-  st = check_workspace(workspace, workspace_bytes, B, H, N, d);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) ||
+      !aligned16(lse) || !aligned16(dq))
+    return FA_ERR_ALIGN;
+  st = check_workspace(workspace, workspace_bytes, B, H, N);
   if (st != FA_OK) return st;
-  const Workspace w = carve(const_cast<void*>(workspace), B, H, N);
-  return fa::launch_bwd_dq_convert(w.dq_acc, dq, (size_t)B * H * N * d,
-                                   scale, (hipStream_t)stream);
+  return fa::launch_bwd_dq(q, k, v, dO, lse, (const float*)workspace, dq, B,
+                           H, N, d, scale, causal != 0, (hipStream_t)stream);
 }
 
 int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -180,15 +167,15 @@ int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
       !aligned16(dO) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) ||
       !aligned16(dv))
     return FA_ERR_ALIGN;
-  st = check_workspace(workspace, workspace_bytes, B, H, N, d);
+  st = check_workspace(workspace, workspace_bytes, B, H, N);
   if (st != FA_OK) return st;
   st = fa_bwd_preprocess(o, dO, workspace, workspace_bytes, B, H, N, d, stream);
   if (st != FA_OK) return st;
   st = fa_bwd_dkdv(q, k, v, dO, lse, dk, dv, workspace, workspace_bytes, B, H,
                    N, d, scale, causal, stream);
   if (st != FA_OK) return st;
-  return fa_bwd_dq_convert(workspace, workspace_bytes, dq, B, H, N, d, scale,
-                           stream);
+  return fa_bwd_dq(q, k, v, dO, lse, dq, workspace, workspace_bytes, B, H, N,
+                   d, scale, causal, stream);
 }
 
 }  // extern "C"

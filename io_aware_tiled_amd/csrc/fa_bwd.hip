@@ -17,28 +17,33 @@
 //   dV = P^T dO,  dP = dO V^T,  D_i = dO_i . O_i,  dS = P * (dP - D),
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
-// Kernels (three launches on one stream):
-//   1. bwd_preprocess: D_i from the bf16 O and dO, and zero the float32 dQ
-//      accumulator.
-//   2. bwd_dkdv: one workgroup per (batch, head, 128-key block); 4
-//      wavefronts own 32 keys each and walk the 32-row query tiles that can
-//      see those keys (causal: tiles wholly before the key block are
-//      skipped).  dK and dV accumulate in registers; dQ is accumulated with
-//      float32 atomic adds.
-//   3. bwd_dq_convert: dQ accumulator * scale -> bf16.
+// Kernels (three launches on one stream, no atomics, deterministic):
+//   1. bwd_preprocess: D_i = dO_i . O_i from the bf16 O and dO.
+//   2. bwd_dkdv: one workgroup per (batch, head, 128-key block); 8
+//      wavefronts, each owning 32 keys and one half of every 64-row query
+//      tile that can see them (causal: tiles wholly before the key block are
+//      skipped).  S, dP, P and dS are recomputed per tile and dK^T, dV^T
+//      accumulate in registers; the two query halves' partials are added
+//      through LDS at the end.
+//   3. bwd_dq: one workgroup per (batch, head, 128-row query block),
+//      streaming K/V tiles like the forward; it recomputes S^T and dP^T and
+//      accumulates dQ^T in registers.
+// Splitting dQ from dK/dV costs 4d extra matrix FLOP per (query, key) pair
+// (14d instead of 10d) but removes the float32 atomics that a fused kernel
+// needs for dQ: device-scope atomics are resolved at the memory side, not in
+// an XCD's L2, and on gfx950 they cost more than the recomputation.
 //
-// gfx950 mapping in bwd_dkdv (head dim 128):
-//   * S = Q_i K_j^T and dP = dO_i V_j^T on v_mfma_f32_32x32x16_bf16 with
-//     K_j / V_j as register-resident B operands; the accumulator layout puts
-//     one key per lane and 16 queries per lane, so P and dS are directly the
-//     B operands of dV^T += dO_i^T P and dK^T += Q_i^T dS.
-//   * dO_i^T and Q_i^T come from the row-major LDS tiles through
-//     ds_read_b64_tr_b16; Q_i, dO_i and K_j use a 16-byte-chunk XOR swizzle
-//     that keeps both the row reads (ds_read_b128) and the transposed reads
-//     free of bank conflicts.
-//   * dS^T goes to LDS with 8-byte stores; dQ_i += dS K_j reads it back
-//     transposed (ds_read_b64_tr_b16), each wavefront producing 32 columns
-//     of dQ over all 128 keys.
+// gfx950 mapping (head dim 128):
+//   * bwd_dkdv computes S = Q_i K_j^T and dP = dO_i V_j^T on
+//     v_mfma_f32_32x32x16_bf16 so the accumulator puts one key per lane and
+//     16 queries per lane; P and dS are then directly the B operands of
+//     dV^T += dO_i^T P and dK^T += Q_i^T dS, with dO_i^T and Q_i^T read from
+//     the row-major LDS tiles by ds_read_b64_tr_b16.
+//   * bwd_dq computes S^T and dP^T with one query per lane (as the forward),
+//     so P^T and dS^T need only the lane's own LSE and D, and dS^T is the B
+//     operand of dQ^T += K_j^T dS^T with K_j^T read transposed from LDS.
+//   * LDS rows are padded to 304 bytes: conflict-free 16-byte row reads and
+//     at most 2-way transposed reads.
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -48,25 +53,13 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBK = 128;   // keys per workgroup (32 per wavefront)
-constexpr int kBQ = 32;    // query rows per tile
 constexpr int kD = 128;    // head dimension of the backward kernel
-
-// 16-byte chunk swizzle of a 256-byte row: rows 0..15 at one chunk land in
-// 16 distinct chunks, and rows 4a..4a+3 map any aligned group of 4 chunks to
-// 4 distinct groups.
-__device__ __forceinline__ int swz(int row) {
-  return ((row & 3) << 2) | ((row >> 2) & 3);
-}
-// Element offset of (row, col) in a swizzled [rows][128] bf16 tile.
-__device__ __forceinline__ int sw_off(int row, int col) {
-  return row * kD + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
-}
 
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(
     const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-    float* __restrict__ Dv, float* __restrict__ dq_acc, size_t rows) {
+    float* __restrict__ Dv, size_t rows) {
   constexpr int TPR = D / 8;                 // threads per row
   constexpr int RPB = kThreads / TPR;        // rows per block
   const int t = threadIdx.x % TPR;
@@ -77,47 +70,51 @@ __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(
     const bf16x8 g = *(const bf16x8*)(dO + row * D + 8 * t);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc += (float)o[e] * (float)g[e];
-    f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-    *(f32x4*)(dq_acc + row * D + 8 * t) = z;
-    *(f32x4*)(dq_acc + row * D + 8 * t + 4) = z;
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (row < rows && t == 0) Dv[row] = acc;
 }
 
-__global__ __launch_bounds__(kThreads) void bwd_dq_convert_kernel(
-    const float* __restrict__ acc, uint16_t* __restrict__ dq, size_t n8,
-    float scale) {
-  const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= n8) return;
-  f32x8 x;
-  const f32x4 a = *(const f32x4*)(acc + 8 * i);
-  const f32x4 b = *(const f32x4*)(acc + 8 * i + 4);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[e] = a[e] * scale;
-    x[e + 4] = b[e] * scale;
-  }
-  *(bf16x8*)(dq + 8 * i) = to_bf16x8(x);
-}
-
 // ---------------------------------------------------------------------------
+// dK/dV kernel: 8 wavefronts (two per SIMD).  Wavefront w owns the 32 keys
+// of key slice ks = w % 4 and the 32 query rows of half qh = w / 4 of each
+// 64-row query tile, so wave pairs (ks, 0) and (ks, 1) hold partial dK/dV of
+// the same keys and add them through LDS once at the end.
+constexpr int kBwdThreads = 512;
+constexpr int kBQ2 = 64;   // query rows per tile
+
+// Padded row stride (elements): 304-byte rows for the 256-byte K/V/Q/dO rows
+// keep the 16-byte row reads conflict-free and the transposed 8-byte reads at
+// most 2-way.  Linear layouts let every operand address be one per-lane base
+// plus an immediate offset.
+constexpr int kRS = 152;   // K, V, Q, dO row stride
+
 template <bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dv,
-    float* __restrict__ dq_acc, uint16_t* __restrict__ dK,
-    uint16_t* __restrict__ dV, int N, int n_kblk, float c_log2,
-    float scale) {
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kblk,
+    float c_log2, float scale) {
   constexpr int D = kD;
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kBK * D];     // 32 KB
-  __shared__ __attribute__((aligned(16))) uint16_t lds_q[kBQ * D];     //  8 KB
-  __shared__ __attribute__((aligned(16))) uint16_t lds_do[kBQ * D];    //  8 KB
-  __shared__ __attribute__((aligned(16))) uint16_t lds_dst[kBK * kBQ]; //  8 KB
-  __shared__ __attribute__((aligned(16))) float lds_lse[kBQ];
-  __shared__ __attribute__((aligned(16))) float lds_d[kBQ];
+  constexpr int KB = kBK * kRS;        // elements of the K (or V) block
+  constexpr int QB = kBQ2 * kRS;       // elements of a Q (or dO) tile
+  // K | V | Q0 | dO0 | Q1 | dO1 (bf16), then LSE and D (float), the query
+  // tiles double-buffered so one barrier per tile suffices.  After the main
+  // loop the K|V region (64 KB) is reused for the dK/dV pair reduction.
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * KB + 4 * QB];
+  __shared__ __attribute__((aligned(16))) float lds_lse[2][kBQ2];
+  __shared__ __attribute__((aligned(16))) float lds_d[2][kBQ2];
+  // Tile bases are opaque scalars: ds_read/ds_write immediate offsets are
+  // 16-bit, so with bases folded in as constants every operand address of a
+  // tile past 64 KB would need its own register.
+  uint16_t* lds_k = smem;
+  uint16_t* lds_v = smem + __builtin_amdgcn_readfirstlane(KB);
+  uint16_t* const lds_q0 = smem + __builtin_amdgcn_readfirstlane(2 * KB);
+  const int qbuf = __builtin_amdgcn_readfirstlane(2 * QB);   // buffer stride
+  const int dooff = __builtin_amdgcn_readfirstlane(QB);      // Q -> dO
+  float* red = (float*)smem;
 
   const int BH = gridDim.x / n_kblk;
   // Key blocks with the most visible queries (smallest index) go first.
@@ -126,14 +123,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = wave_id();   // wave-uniform (scalar register)
+  const int ks = w & 3;          // key slice
+  const int qh = w >> 2;         // query half of each tile
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int r16 = lane & 15;
   const int dsub = (lane >> 4) & 1;
 
   const int kb0 = jb * kBK;
-  const int mykey = kb0 + 32 * w + l32;      // this lane's key
+  const int wk0 = kb0 + 32 * ks;            // first key of this wavefront
+  const int mykey = wk0 + l32;              // this lane's key
   const size_t head = (size_t)bh * N * D;
   const uint16_t* Qh = Q + head;
   const uint16_t* Kh = K + head;
@@ -141,29 +141,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const uint16_t* dOh = dO + head;
   const float* LSEh = LSE + (size_t)bh * N;
   const float* Dh = Dv + (size_t)bh * N;
-  float* dQh = dq_acc + head;
 
-  // ---- K_j into LDS (swizzled), K_j and V_j fragments into registers.
+  // ---- K_j and V_j into LDS (padded rows), rows past N are zero.
 #pragma unroll
-  for (int r = 0; r < kBK * D / 8 / kThreads; ++r) {
-    const int c = tid + kThreads * r;
+  for (int r = 0; r < kBK * D / 8 / kBwdThreads; ++r) {
+    const int c = tid + kBwdThreads * r;
     const int row = c / (D / 8);
     const int col = 8 * (c % (D / 8));
     const int key = kb0 + row;
-    u32x4 x = u32x4{0, 0, 0, 0};
-    if (key < N) x = *(const u32x4*)(Kh + (size_t)key * D + col);
-    *(u32x4*)(&lds_k[sw_off(row, col)]) = x;
-  }
-  bf16x8 kf[D / 16], vf[D / 16];   // lane: key mykey, d = 16kk + 8hh + 0..7
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    if (mykey < N) {
-      kf[kk] = *(const bf16x8*)(Kh + (size_t)mykey * D + 16 * kk + 8 * hh);
-      vf[kk] = *(const bf16x8*)(Vh + (size_t)mykey * D + 16 * kk + 8 * hh);
-    } else {
-      kf[kk] = bf16x8{};
-      vf[kk] = bf16x8{};
+    u32x4 xk = u32x4{0, 0, 0, 0}, xv = u32x4{0, 0, 0, 0};
+    if (key < N) {
+      xk = *(const u32x4*)(Kh + (size_t)key * D + col);
+      xv = *(const u32x4*)(Vh + (size_t)key * D + col);
     }
+    *(u32x4*)(&lds_k[row * kRS + col]) = xk;
+    *(u32x4*)(&lds_v[row * kRS + col]) = xv;
   }
 
   f32x16 dk_acc[D / 32], dv_acc[D / 32];
@@ -173,154 +165,171 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     dv_acc[i] = f32x16{};
   }
 
-  const int n_qt = (N + kBQ - 1) / kBQ;
-  const int it0 = CAUSAL ? kb0 / kBQ : 0;
+  const int n_qt = (N + kBQ2 - 1) / kBQ2;
+  const int it0 = CAUSAL ? kb0 / kBQ2 : 0;
 
   // Query-tile staging: 2 chunks of Q and 2 of dO per thread, plus LSE / D.
+  // Rows past N load row N-1 (in bounds) and are replaced by zeros with a
+  // select, so the loads need no branch.
   u32x4 qreg[2], doreg[2];
   float lse_r = 0.f, d_r = 0.f;
   auto load_qtile = [&](int it) {
+    const int qt0 = it * kBQ2;
+    const uint16_t* qb = Qh + (size_t)qt0 * D;      // wave-uniform bases
+    const uint16_t* gb = dOh + (size_t)qt0 * D;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int c = tid + kThreads * r;
+      const int c = tid + kBwdThreads * r;
       const int row = c / (D / 8);
       const int col = 8 * (c % (D / 8));
-      const int q = it * kBQ + row;
-      if (q < N) {
-        qreg[r] = *(const u32x4*)(Qh + (size_t)q * D + col);
-        doreg[r] = *(const u32x4*)(dOh + (size_t)q * D + col);
-      } else {
-        qreg[r] = u32x4{0, 0, 0, 0};
-        doreg[r] = u32x4{0, 0, 0, 0};
-      }
+      const bool ok = qt0 + row < N;
+      const unsigned off = (unsigned)(min(row, N - 1 - qt0) * D + col);
+      const u32x4 a = *(const u32x4*)(qb + off);
+      const u32x4 g = *(const u32x4*)(gb + off);
+      const u32x4 z = u32x4{0, 0, 0, 0};
+      qreg[r] = ok ? a : z;
+      doreg[r] = ok ? g : z;
     }
-    if (tid < kBQ) {
-      const int q = it * kBQ + tid;
+    if (w == 0) {
+      const int q = qt0 + lane;
+      const int qc = min(q, N - 1);
       // Rows past N (and rows without any visible key) get +inf so that
       // exp2(s - lse) = 0 for every key.
-      float l = q < N ? LSEh[q] : INFINITY;
+      const float l = q < N ? LSEh[qc] : INFINITY;
       lse_r = (l == -INFINITY) ? INFINITY : l * kLog2e;
-      d_r = q < N ? Dh[q] : 0.f;
+      d_r = q < N ? Dh[qc] : 0.f;
     }
   };
-  auto store_qtile = [&]() {
+  auto store_qtile = [&](int buf) {
+    uint16_t* lq_ = lds_q0 + (buf ? qbuf : 0);
+    uint16_t* ld_ = lq_ + dooff;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int c = tid + kThreads * r;
+      const int c = tid + kBwdThreads * r;
       const int row = c / (D / 8);
       const int col = 8 * (c % (D / 8));
-      *(u32x4*)(&lds_q[sw_off(row, col)]) = qreg[r];
-      *(u32x4*)(&lds_do[sw_off(row, col)]) = doreg[r];
+      *(u32x4*)(&lq_[row * kRS + col]) = qreg[r];
+      *(u32x4*)(&ld_[row * kRS + col]) = doreg[r];
     }
-    if (tid < kBQ) {
-      lds_lse[tid] = lse_r;
-      lds_d[tid] = d_r;
+    if (w == 0) {
+      lds_lse[buf][lane] = lse_r;
+      lds_d[buf][lane] = d_r;
     }
   };
 
   if (it0 < n_qt) load_qtile(it0);
   for (int it = it0; it < n_qt; ++it) {
-    store_qtile();
-    __syncthreads();                      // (A) Q_i, dO_i, LSE, D, K ready
+    const int buf = (it - it0) & 1;
+    store_qtile(buf);
+    // Q_i, dO_i, LSE, D (and K, V) ready; also every wavefront has finished
+    // reading the other buffer, which the next iteration overwrites.
+    __syncthreads();
     if (it + 1 < n_qt) load_qtile(it + 1);
+    const uint16_t* lds_q = lds_q0 + (buf ? qbuf : 0);
+    const uint16_t* lds_do = lds_q + dooff;
+    const float* lse_t = lds_lse[buf];
+    const float* d_t = lds_d[buf];
 
-    const int q0 = it * kBQ;
-    const int wk0 = kb0 + 32 * w;        // first key of this wavefront
-    const bool active = !(CAUSAL && wk0 > q0 + kBQ - 1) && wk0 < N;
+    const int q0 = it * kBQ2;
+    const int qw0 = q0 + 32 * qh;         // first query row of this wavefront
 
-    bf16x8 dsb[2];
-    if (active) {
-      // ---- S = Q_i K_j^T and dP = dO_i V_j^T (queries x keys).
-      f32x16 s = f32x16{}, dp = f32x16{};
+    // ---- S = Q K^T and dP = dO V^T for 32 queries x 32 keys.  (A block
+    // wholly in the causal future only occurs on the diagonal tile; it is
+    // computed and masked to zero rather than branched around.)
+    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const int off = sw_off(l32, 16 * kk + 8 * hh);
-        const bf16x8 qa = *(const bf16x8*)(&lds_q[off]);
-        const bf16x8 ga = *(const bf16x8*)(&lds_do[off]);
-        s = mfma32x16(qa, kf[kk], s);
-        dp = mfma32x16(ga, vf[kk], dp);
-      }
-      // ---- P = exp2(s*c - lse2), dS = P (dP - D).  Register r holds query
-      // q0 + 8(r/4) + 4hh + r%4 of this lane's key.
-      const bool need_mask =
-          (CAUSAL && wk0 + 31 > q0) || (wk0 + 32 > N);
-      f32x8 pv[2], dsv[2];
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const int qo = (32 * qh + l32) * kRS + 16 * kk + 8 * hh;
+      const int ko = (32 * ks + l32) * kRS + 16 * kk + 8 * hh;
+      const bf16x8 qa = *(const bf16x8*)(&lds_q[qo]);
+      const bf16x8 ga = *(const bf16x8*)(&lds_do[qo]);
+      const bf16x8 kf = *(const bf16x8*)(&lds_k[ko]);
+      const bf16x8 vf = *(const bf16x8*)(&lds_v[ko]);
+      s = mfma32x16(qa, kf, s);
+      dp = mfma32x16(ga, vf, dp);
+    }
+    // ---- P = exp2(s*c - lse2), dS = P (dP - D).  Register r holds query
+    // qw0 + 8(r/4) + 4hh + r%4 of this lane's key.
+    const bool need_mask = (CAUSAL && wk0 + 31 > qw0) || (wk0 + 32 > N);
+    bf16x8 pb[2], dsb[2];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 l4 = *(const f32x4*)(&lds_lse[8 * g + 4 * hh]);
-        const f32x4 d4 = *(const f32x4*)(&lds_d[8 * g + 4 * hh]);
+    for (int c = 0; c < 2; ++c) {
+      f32x8 pv, dsv;
+#pragma unroll
+      for (int g2 = 0; g2 < 2; ++g2) {
+        const int g = 2 * c + g2;
+        const f32x4 l4 = *(const f32x4*)(&lse_t[32 * qh + 8 * g + 4 * hh]);
+        const f32x4 d4 = *(const f32x4*)(&d_t[32 * qh + 8 * g + 4 * hh]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
           float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l4[e]));
           if (need_mask) {
-            const int q = q0 + 8 * g + 4 * hh + e;
+            const int q = qw0 + 8 * g + 4 * hh + e;
             if ((CAUSAL && mykey > q) || mykey >= N) p = 0.f;
           }
-          const float ds = p * (dp[r] - d4[e]);
-          pv[r >> 3][r & 7] = p;
-          dsv[r >> 3][r & 7] = ds;
+          pv[4 * g2 + e] = p;
+          dsv[4 * g2 + e] = p * (dp[r] - d4[e]);
         }
       }
-      const bf16x8 pb[2] = {to_bf16x8(pv[0]), to_bf16x8(pv[1])};
-      dsb[0] = to_bf16x8(dsv[0]);
-      dsb[1] = to_bf16x8(dsv[1]);
-
-      // ---- dV^T += dO_i^T P and dK^T += Q_i^T dS (d x keys).
-      // Operand slot (hh, e) <-> query 16c + 8(e/4) + 4hh + e%4.
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int col = 32 * db + 16 * dsub + 4 * (r16 & 3);
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int row = 16 * c + 4 * hh + (r16 >> 2);
-          const i16x4 g_lo = lds_read_tr16(&lds_do[sw_off(row, col)]);
-          const i16x4 g_hi = lds_read_tr16(&lds_do[sw_off(row + 8, col)]);
-          const i16x4 q_lo = lds_read_tr16(&lds_q[sw_off(row, col)]);
-          const i16x4 q_hi = lds_read_tr16(&lds_q[sw_off(row + 8, col)]);
-          dv_acc[db] = mfma32x16(join_bf16(g_lo, g_hi), pb[c], dv_acc[db]);
-          dk_acc[db] = mfma32x16(join_bf16(q_lo, q_hi), dsb[c], dk_acc[db]);
-        }
-      }
-    } else {
-      dsb[0] = bf16x8{};
-      dsb[1] = bf16x8{};
+      pb[c] = to_bf16x8(pv);
+      dsb[c] = to_bf16x8(dsv);
     }
 
-    // ---- dS^T to LDS: row = key (32w + l32), 4 consecutive queries per store.
+    // ---- dV^T += dO^T P and dK^T += Q^T dS (d x keys).
+    // Operand slot (hh, e) <-> query row 32qh + 16c + 8(e/4) + 4hh + e%4.
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const bf16x4 x = (g & 1) ? hi4(dsb[g >> 1]) : lo4(dsb[g >> 1]);
-      *(bf16x4*)(&lds_dst[(32 * w + l32) * kBQ + 8 * g + 4 * hh]) = x;
+    for (int db = 0; db < D / 32; ++db) {
+      const int col = 32 * db + 16 * dsub + 4 * (r16 & 3);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int row = 32 * qh + 16 * c + 4 * hh + (r16 >> 2);
+        const i16x4 g_lo = lds_read_tr16(&lds_do[row * kRS + col]);
+        const i16x4 g_hi = lds_read_tr16(&lds_do[(row + 8) * kRS + col]);
+        dv_acc[db] = mfma32x16(join_bf16(g_lo, g_hi), pb[c], dv_acc[db]);
+      }
     }
-    __syncthreads();                      // (B) dS^T complete
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int col = 32 * db + 16 * dsub + 4 * (r16 & 3);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int row = 32 * qh + 16 * c + 4 * hh + (r16 >> 2);
+        const i16x4 q_lo = lds_read_tr16(&lds_q[row * kRS + col]);
+        const i16x4 q_hi = lds_read_tr16(&lds_q[(row + 8) * kRS + col]);
+        dk_acc[db] = mfma32x16(join_bf16(q_lo, q_hi), dsb[c], dk_acc[db]);
+      }
+    }
 
-    // ---- dQ_i[:, 32w .. 32w+31] += dS K_j over the 128 keys.
-    // Slot (hh, e) <-> key 16kc + 8(e/4) + 4hh + e%4 for both operands.
-    if (!(CAUSAL && kb0 > q0 + kBQ - 1)) {
-      f32x16 dq = f32x16{};
-      const int qcol = 16 * dsub + 4 * (r16 & 3);
-      const int dcol = 32 * w + 16 * dsub + 4 * (r16 & 3);
-#pragma unroll
-      for (int kc = 0; kc < kBK / 16; ++kc) {
-        const int krow = 16 * kc + 4 * hh + (r16 >> 2);
-        const i16x4 a_lo = lds_read_tr16(&lds_dst[krow * kBQ + qcol]);
-        const i16x4 a_hi = lds_read_tr16(&lds_dst[(krow + 8) * kBQ + qcol]);
-        const i16x4 b_lo = lds_read_tr16(&lds_k[sw_off(krow, dcol)]);
-        const i16x4 b_hi = lds_read_tr16(&lds_k[sw_off(krow + 8, dcol)]);
-        dq = mfma32x16(join_bf16(a_lo, a_hi), join_bf16(b_lo, b_hi), dq);
-      }
-      // Register r holds query q0 + 8(r/4) + 4hh + r%4, column 32w + l32.
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = q0 + 8 * (r / 4) + 4 * hh + (r % 4);
-        if (q < N) unsafeAtomicAdd(&dQh[(size_t)q * D + 32 * w + l32], dq[r]);
-      }
-    }
   }
 
+  // ---- add the two query halves' partial dK^T, dV^T through LDS.
+  __syncthreads();                        // K/V region free
+  auto red_idx = [&](int db, int r) { return ((ks * 4 + db) * 16 + r) * 64 + lane; };
+  if (qh == 1) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[red_idx(db, r)] = dv_acc[db][r];
+  }
+  __syncthreads();
+  if (qh == 0) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dv_acc[db][r] += red[red_idx(db, r)];
+  }
+  __syncthreads();
+  if (qh == 1) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[red_idx(db, r)] = dk_acc[db][r];
+  }
+  __syncthreads();
+
   // ---- epilogue: dK = scale * dK^T, dV = dV^T (lane = key, regs = d).
-  if (mykey < N) {
+  if (qh == 0 && mykey < N) {
     uint16_t* dkr = dK + head + (size_t)mykey * D;
     uint16_t* dvr = dV + head + (size_t)mykey * D;
 #pragma unroll
@@ -330,7 +339,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         f32x4 a, b;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          a[e] = dk_acc[db][4 * g + e] * scale;
+          a[e] = (dk_acc[db][4 * g + e] + red[red_idx(db, 4 * g + e)]) * scale;
           b[e] = dv_acc[db][4 * g + e];
         }
         *(bf16x4*)(dkr + 32 * db + 8 * g + 4 * hh) = to_bf16x4(a);
@@ -340,51 +349,248 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// dQ kernel: one workgroup per (batch, head, 128-row query block), 4
+// wavefronts of 32 query rows, streaming 64-key tiles of K and V through LDS
+// (double-buffered) exactly like the forward.  Per tile it recomputes
+// S^T = K Q^T and dP^T = V dO^T, forms P^T = exp2(S^T c - lse2) and
+// dS^T = P^T (dP^T - D) in-lane (one query per lane), and accumulates
+// dQ^T += K^T dS^T with K^T read transposed from LDS.  No atomics: dQ is
+// written once, deterministically.
+constexpr int kDqBR = 128;
+constexpr int kDqBC = 64;
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Dv,
+    uint16_t* __restrict__ dQ, int N, int n_qblk, float c_log2,
+    float scale) {
+  constexpr int D = kD;
+  constexpr int TE = kDqBC * kRS;      // elements per K (or V) tile buffer
+  constexpr int CPT = kDqBC * D / 8 / kThreads;   // 16-byte chunks per thread
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TE];
+  // buffers: K0 | V0 | K1 | V1 (bases opaque: see bwd_dkdv_kernel)
+  const int vbase = __builtin_amdgcn_readfirstlane(TE);
+  const int buf1 = __builtin_amdgcn_readfirstlane(2 * TE);
+
+  const int BH = gridDim.x / n_qblk;
+  int bh, qb;
+  if (CAUSAL) {
+    qb = n_qblk - 1 - (int)blockIdx.x / BH;
+    bh = blockIdx.x % BH;
+  } else {
+    bh = blockIdx.x / n_qblk;
+    qb = blockIdx.x % n_qblk;
+  }
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = wave_id();
+  const int lq = lane & 31;
+  const int hh = lane >> 5;
+  const int r16 = lane & 15;
+  const int dsub = (lane >> 4) & 1;
+  const int q0 = qb * kDqBR;
+  const int qw0 = q0 + 32 * w;
+  const int qw1 = qw0 + 31;
+  const int qrow = qw0 + lq;
+
+  const size_t head = (size_t)bh * N * D;
+  const uint16_t* Qh = Q + head;
+  const uint16_t* Kh = K + head;
+  const uint16_t* Vh = V + head;
+  const uint16_t* dOh = dO + head;
+
+  int kend = N;
+  if (CAUSAL) kend = min(kend, q0 + kDqBR);
+  const int ntiles = (kend + kDqBC - 1) / kDqBC;
+
+  // Q and dO fragments of this lane's query (B operands), LSE and D.
+  bf16x8 qf[D / 16], gf[D / 16];
+  const int qc = min(qrow, N - 1);
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const bf16x8 a = *(const bf16x8*)(Qh + (size_t)qc * D + 16 * kk + 8 * hh);
+    const bf16x8 g = *(const bf16x8*)(dOh + (size_t)qc * D + 16 * kk + 8 * hh);
+    qf[kk] = qrow < N ? a : bf16x8{};
+    gf[kk] = qrow < N ? g : bf16x8{};
+  }
+  float lse2 = INFINITY, dd = 0.f;
+  if (qrow < N) {
+    const float l = LSE[(size_t)bh * N + qrow];
+    lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+    dd = Dv[(size_t)bh * N + qrow];
+  }
+
+  u32x4 kreg[CPT], vreg[CPT];
+  auto load_tile = [&](int j) {
+    const int k0 = j * kDqBC;
+    const uint16_t* kb = Kh + (size_t)k0 * D;
+    const uint16_t* vb = Vh + (size_t)k0 * D;
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+      const int c = tid + kThreads * r;
+      const int row = c / (D / 8);
+      const int col = 8 * (c % (D / 8));
+      const bool ok = k0 + row < N;
+      const unsigned off = (unsigned)(min(row, N - 1 - k0) * D + col);
+      const u32x4 a = *(const u32x4*)(kb + off);
+      const u32x4 b = *(const u32x4*)(vb + off);
+      const u32x4 z = u32x4{0, 0, 0, 0};
+      kreg[r] = ok ? a : z;
+      vreg[r] = ok ? b : z;
+    }
+  };
+  auto store_tile = [&](int buf) {
+    uint16_t* kt = smem + (buf ? buf1 : 0);
+    uint16_t* vt = kt + vbase;
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+      const int c = tid + kThreads * r;
+      const int row = c / (D / 8);
+      const int col = 8 * (c % (D / 8));
+      *(u32x4*)(&kt[row * kRS + col]) = kreg[r];
+      *(u32x4*)(&vt[row * kRS + col]) = vreg[r];
+    }
+  };
+
+  f32x16 dq_acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) dq_acc[i] = f32x16{};
+
+  if (ntiles > 0) load_tile(0);
+  for (int j = 0; j < ntiles; ++j) {
+    const int buf = j & 1;
+    store_tile(buf);
+    __syncthreads();
+    if (j + 1 < ntiles) load_tile(j + 1);
+    const int k0 = j * kDqBC;
+    if (CAUSAL && k0 > qw1) continue;     // tile wholly in this wave's future
+    const uint16_t* kt = smem + (buf ? buf1 : 0);
+    const uint16_t* vt = kt + vbase;
+
+    // ---- S^T = K Q^T and dP^T = V dO^T (keys x queries), two 32-key blocks.
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const int o = (32 * kb + lq) * kRS + 16 * kk + 8 * hh;
+        s[kb] = mfma32x16(*(const bf16x8*)(&kt[o]), qf[kk], s[kb]);
+        dp[kb] = mfma32x16(*(const bf16x8*)(&vt[o]), gf[kk], dp[kb]);
+      }
+    }
+    // ---- P^T and dS^T in-lane; register r of block kb holds key
+    // k0 + 32kb + 8(r/4) + 4hh + r%4 for this lane's query.
+    const bool need_mask = (CAUSAL && k0 + kDqBC - 1 > qw0) || (k0 + kDqBC > N);
+    bf16x8 dsb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        f32x8 x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * c + e;
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c_log2, -lse2));
+          if (need_mask) {
+            const int key = k0 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
+            if ((CAUSAL && key > qrow) || key >= N) p = 0.f;
+          }
+          x[e] = p * (dp[kb][r] - dd);
+        }
+        dsb[kb][c] = to_bf16x8(x);
+      }
+    }
+    // ---- dQ^T += K^T dS^T.  A operand lane (d, hh) element e is
+    // K[32kb + 16c + 8(e/4) + 4hh + e%4][d], read transposed.
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int col = 32 * db + 16 * dsub + 4 * (r16 & 3);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int row = 32 * kb + 16 * c + 4 * hh + (r16 >> 2);
+          const i16x4 lo = lds_read_tr16(&kt[row * kRS + col]);
+          const i16x4 hi = lds_read_tr16(&kt[(row + 8) * kRS + col]);
+          dq_acc[db] = mfma32x16(join_bf16(lo, hi), dsb[kb][c], dq_acc[db]);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: dQ = scale * dQ^T (lane = query, regs = d).
+  if (qrow < N) {
+    uint16_t* out = dQ + head + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = dq_acc[db][4 * g + e] * scale;
+        *(bf16x4*)(out + 32 * db + 8 * g + 4 * hh) = to_bf16x4(x);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 int launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, float* D,
-                          float* dq_acc, int B, int H, int N, int d,
-                          hipStream_t stream) {
+                          int B, int H, int N, int d, hipStream_t stream) {
   const size_t rows = (size_t)B * H * N;
   if (d == 128) {
     constexpr int RPB = kThreads / (128 / 8);
     const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
     hipLaunchKernelGGL(bwd_preprocess_kernel<128>, grid, dim3(kThreads), 0,
-                       stream, o, dO, D, dq_acc, rows);
+                       stream, o, dO, D, rows);
   } else {
     constexpr int RPB = kThreads / (64 / 8);
     const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
     hipLaunchKernelGGL(bwd_preprocess_kernel<64>, grid, dim3(kThreads), 0,
-                       stream, o, dO, D, dq_acc, rows);
+                       stream, o, dO, D, rows);
   }
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
 int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const uint16_t* dO, const float* lse, const float* D,
-                    float* dq_acc, uint16_t* dk, uint16_t* dv, int B, int H,
-                    int N, int d, float scale, int causal,
-                    hipStream_t stream) {
+                    uint16_t* dk, uint16_t* dv, int B, int H, int N, int d,
+                    float scale, int causal, hipStream_t stream) {
   if (d != kD) return -3;
   const int n_kblk = (N + kBK - 1) / kBK;
-  const dim3 grid((unsigned)(B * H * n_kblk)), block(kThreads);
+  const dim3 grid((unsigned)(B * H * n_kblk)), block(kBwdThreads);
   const float c = (float)((double)scale * 1.4426950408889634);
   if (causal) {
     hipLaunchKernelGGL(bwd_dkdv_kernel<true>, grid, block, 0, stream, q, k, v,
-                       dO, lse, D, dq_acc, dk, dv, N, n_kblk, c, scale);
+                       dO, lse, D, dk, dv, N, n_kblk, c, scale);
   } else {
     hipLaunchKernelGGL(bwd_dkdv_kernel<false>, grid, block, 0, stream, q, k,
-                       v, dO, lse, D, dq_acc, dk, dv, N, n_kblk, c, scale);
+                       v, dO, lse, D, dk, dv, N, n_kblk, c, scale);
   }
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
-int launch_bwd_dq_convert(const float* dq_acc, uint16_t* dq, size_t n,
-                          float scale, hipStream_t stream) {
-  const size_t n8 = n / 8;
-  const dim3 grid((unsigned)((n8 + kThreads - 1) / kThreads));
-  hipLaunchKernelGGL(bwd_dq_convert_kernel, grid, dim3(kThreads), 0, stream,
-                     dq_acc, dq, n8, scale);
+int launch_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                  const uint16_t* dO, const float* lse, const float* D,
+                  uint16_t* dq, int B, int H, int N, int d, float scale,
+                  int causal, hipStream_t stream) {
+  if (d != kD) return -3;
+  const int n_qblk = (N + kDqBR - 1) / kDqBR;
+  const dim3 grid((unsigned)(B * H * n_qblk)), block(kThreads);
+  const float c = (float)((double)scale * 1.4426950408889634);
+  if (causal) {
+    hipLaunchKernelGGL(bwd_dq_kernel<true>, grid, block, 0, stream, q, k, v,
+                       dO, lse, D, dq, N, n_qblk, c, scale);
+  } else {
+    hipLaunchKernelGGL(bwd_dq_kernel<false>, grid, block, 0, stream, q, k, v,
+                       dO, lse, D, dq, N, n_qblk, c, scale);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

@@ -78,6 +78,13 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
   return __builtin_convertvector(x, bf16x4);
 }
 
+// Index of this wavefront in its workgroup, as a wave-uniform value: the
+// compiler cannot infer that threadIdx.x / 64 is uniform, and per-wave
+// decisions (causal skips, tile ownership) must be scalar branches.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 // Value of the other half-wave's lane (l ^ 32).
 __device__ __forceinline__ float xor32(float x) {
   return __shfl_xor(x, 32, 64);

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = wave_id();   // wave-uniform (scalar register)
   const int lq = lane & 31;     // query column of the accumulator
   const int hh = lane >> 5;     // half-wave
   const int q0 = qb * kBR;
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = wave_id();   // wave-uniform (scalar register)
   const int lq = lane & 31;
   const int hh = lane >> 5;
   const int q0 = qb * kBR;

@@ -19,15 +19,16 @@ int launch_fwd_f32(const float* q, const float* k, const float* v, float* o,
                    int causal, hipStream_t stream);
 
 int launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, float* D,
-                          float* dq_acc, int B, int H, int N, int d,
-                          hipStream_t stream);
+                          int B, int H, int N, int d, hipStream_t stream);
 
 int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const uint16_t* dO, const float* lse, const float* D,
-                    float* dq_acc, uint16_t* dk, uint16_t* dv, int B, int H,
-                    int N, int d, float scale, int causal, hipStream_t stream);
+                    uint16_t* dk, uint16_t* dv, int B, int H, int N, int d,
+                    float scale, int causal, hipStream_t stream);
 
-int launch_bwd_dq_convert(const float* dq_acc, uint16_t* dq, size_t n,
-                          float scale, hipStream_t stream);
+int launch_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                  const uint16_t* dO, const float* lse, const float* D,
+                  uint16_t* dq, int B, int H, int N, int d, float scale,
+                  int causal, hipStream_t stream);
 
 }  // namespace fa

@@ -33,7 +33,7 @@ def test_header_declares_expected_calls():
     names = _declared_functions()
     for want in ["fa_fwd", "fa_fwd_kvlen", "fa_fwd_f32", "fa_bwd",
                  "fa_bwd_workspace_size", "fa_status_string", "fa_version",
-                 "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq_convert"]:
+                 "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq"]:
         assert want in names
 
 
@@ -93,8 +93,7 @@ def test_workspace_size():
     def a256(x):
         return (x + 255) // 256 * 256
     for B, H, N in [(1, 1, 1), (4, 16, 4096), (2, 3, 1000)]:
-        want = a256(B * H * N * 4) + a256(B * H * N * 128 * 4)
-        assert ws(B, H, N, 128) == want
+        assert ws(B, H, N, 128) == a256(B * H * N * 4)
     assert ws(1, 1, 64, 64) == 0          # backward: head dim 128 only
     assert ws(0, 1, 64, 128) == 0
     assert ws(1, 1, -5, 128) == 0
@@ -124,10 +123,12 @@ def test_bwd_argument_errors():
     assert L.fa_bwd_preprocess(A, A, W, 16, 1, 1, 64, 128, None) == WORKSPACE
     assert L.fa_bwd_dkdv(A, A, A, A, A, A, None, W, nbytes, 1, 1, 64, 128,
                          0.1, 1, None) == NULL
-    assert L.fa_bwd_dq_convert(W, nbytes, None, 1, 1, 64, 128, 0.1,
-                               None) == NULL
-    assert L.fa_bwd_dq_convert(W, nbytes, A, 1, 1, 64, 64, 0.1,
-                               None) == HEADDIM
+    assert L.fa_bwd_dq(A, A, A, A, A, None, W, nbytes, 1, 1, 64, 128, 0.1,
+                       1, None) == NULL
+    assert L.fa_bwd_dq(A, A, A, A, A, A, W, nbytes, 1, 1, 64, 64, 0.1,
+                       1, None) == HEADDIM
+    assert L.fa_bwd_dq(A, A, A, A, A, A, W, 0, 1, 1, 64, 128, 0.1,
+                       1, None) == WORKSPACE
 
 
 def test_python_binding_refuses_host_tensors():
