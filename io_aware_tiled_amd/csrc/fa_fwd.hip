@@ -46,6 +46,8 @@ namespace {
 constexpr int kBR = 128;   // query rows per workgroup (32 per wavefront)
 constexpr int kBC = 64;    // keys per K/V tile
 constexpr int kThreads = 256;
+// Growth of the running max (log2 units) tolerated before O is rescaled.
+constexpr float kRescaleSlack = 8.f;
 
 template <int D>
 struct FwdTile {
@@ -205,6 +207,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     }
 
     // ---- online softmax statistics (scaled log2 domain; c_log2 >= 0).
+    // The reference max m_run only moves when some lane's tile max exceeds
+    // it by more than kRescaleSlack (then every lane moves to its true
+    // running max and rescales O and l); otherwise the exponentials are taken
+    // against the stale reference and stay below 2^kRescaleSlack.  Exact in
+    // exact arithmetic: O and l share the reference, which cancels in O/l.
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -212,12 +219,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = fmaxf(mx, xor32(mx));
     const float mt = (mx == -INFINITY) ? -INFINITY : mx * c_log2;
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    if (__any(mt > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(
+          m_run - ((m_new == -INFINITY) ? 0.f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
-    float lsum = 0.f;
+    // P^T in bf16 for the P V product; l sums the float32 weights (a sum of
+    // the bf16-rounded weights would move LSE by up to 2^-9 relative).
     bf16x8 pb[2][2];
     auto probs = [&](auto masked) {
 #pragma unroll
@@ -233,16 +247,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
               if (x == -INFINITY) pe = 0.f;
             }
             p[e] = pe;
-            lsum += pe;
+            l_run += pe;
           }
           pb[kb][c] = to_bf16x8(p);
         }
       }
     };
     if (need_mask) probs(std::true_type{}); else probs(std::false_type{});
-    l_run = l_run * alpha + lsum;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
 
     // ---- O^T += V_j^T P^T.  A operand lane (d, hh) element e is
     // V[32kb + 16c + 8(e/4) + 4hh + e%4][d], read with two transposed reads.
