@@ -90,6 +90,24 @@ __device__ __forceinline__ float xor32(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// max(x[l], x[l ^ 32]) in every lane, without an LDS round trip:
+// v_permlane32_swap of (x, x) yields the lower half-wave's x in the first
+// result and the upper half-wave's x in the second, in every lane.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(
+      __builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false,
+      false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]),
+               __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(
+      __builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false,
+      false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) +
+         __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
 // Workgroup index remap so that consecutive logical indices stay on one
 // XCD: the hardware deals workgroups round-robin over the 8 XCDs, so
 // physical id p runs on XCD p % 8.  Logical id = (p % 8) * per + p / 8 for

@@ -129,22 +129,27 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     c_log2 = -c_log2;
   }
 
-  // Cooperative tile loads: chunk c = tid + 256*r -> row c/(D/8), col 8*(c%(D/8)).
+  // Cooperative tile loads: chunk c = tid + 256*r -> row c/(D/8), col
+  // 8*(c%(D/8)).  Rows past N read row N-1 (in bounds) and are replaced by
+  // zeros with a select; addresses are a wave-uniform tile base plus a 32-bit
+  // per-lane offset.
   u32x4 kreg[T::CPT], vreg[T::CPT];
   auto load_tile = [&](int j) {
+    const int k0 = j * kBC;
+    const uint16_t* kb = Kh + (size_t)k0 * D;
+    const uint16_t* vb = Vh + (size_t)k0 * D;
 #pragma unroll
     for (int r = 0; r < T::CPT; ++r) {
       const int c = tid + kThreads * r;
       const int row = c / (D / 8);
       const int col = 8 * (c % (D / 8));
-      const int key = j * kBC + row;
-      if (key < N) {
-        kreg[r] = *(const u32x4*)(Kh + (size_t)key * D + col);
-        vreg[r] = *(const u32x4*)(Vh + (size_t)key * D + col);
-      } else {
-        kreg[r] = u32x4{0, 0, 0, 0};
-        vreg[r] = u32x4{0, 0, 0, 0};
-      }
+      const bool ok = k0 + row < N;
+      const unsigned off = (unsigned)(min(row, N - 1 - k0) * D + col);
+      const u32x4 a = *(const u32x4*)(kb + off);
+      const u32x4 b = *(const u32x4*)(vb + off);
+      const u32x4 z = u32x4{0, 0, 0, 0};
+      kreg[r] = ok ? a : z;
+      vreg[r] = ok ? b : z;
     }
   };
   auto store_tile = [&](int buf) {
@@ -172,7 +177,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const int buf = j & 1;
     store_tile(buf);
     __syncthreads();
-    if (j + 1 < ntiles) load_tile(j + 1);
+    // Prefetch the next tile (the last iteration reloads its own tile: an
+    // in-bounds load that keeps the loop free of a branch).
+    load_tile(min(j + 1, ntiles - 1));
 
     const int k0 = j * kBC;
     // Tiles wholly in this wavefront's causal future are skipped.
@@ -184,11 +191,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
       const uint16_t* kp = &lds_k[buf][(32 * kb + lq) * T::KST + 8 * hh];
+      bf16x8 a[D / 16];
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 a = *(const bf16x8*)(kp + 16 * kk);
-        s[kb] = mfma32x16(a, qf[kk], s[kb]);
-      }
+      for (int kk = 0; kk < D / 16; ++kk) a[kk] = *(const bf16x8*)(kp + 16 * kk);
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) s[kb] = mfma32x16(a[kk], qf[kk], s[kb]);
     }
 
     // ---- mask: causal diagonal, ragged tail, key padding.
@@ -217,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, xor32(mx));
+    mx = max_halves(mx);
     const float mt = (mx == -INFINITY) ? -INFINITY : mx * c_log2;
     if (__any(mt > m_run + kRescaleSlack)) {
       const float m_new = fmaxf(m_run, mt);
@@ -262,22 +269,25 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const int dcol = 32 * db + 16 * dsub + 4 * (r16 & 3);
+      bf16x8 a[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const int key = 32 * kb + 16 * c + 4 * hh + (r16 >> 2);
-          const i16x4 lo = lds_read_tr16(&lds_v[buf][key * T::VST + dcol]);
-          const i16x4 hi =
-              lds_read_tr16(&lds_v[buf][(key + 8) * T::VST + dcol]);
-          oacc[db] = mfma32x16(join_bf16(lo, hi), pb[kb][c], oacc[db]);
+          a[kb][c] = join_bf16(lds_read_tr16(&lds_v[buf][key * T::VST + dcol]),
+                               lds_read_tr16(&lds_v[buf][(key + 8) * T::VST + dcol]));
         }
       }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) oacc[db] = mfma32x16(a[kb][c], pb[kb][c], oacc[db]);
     }
   }
 
   // ---- epilogue: combine half-wave sums, normalise, store O and LSE.
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = sum_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < N) {
     uint16_t* orow = O + head + (size_t)qrow * D;
