@@ -10,7 +10,10 @@ fa_fwd_f32 / fa_fwd_kvlen).  Inputs are resident in HBM before timing starts.
 
 Throughput is algorithmic: 4d FLOP per visible (query, key) pair for the
 forward and 10d for the backward (causal: N(N+1)/2 pairs per head); masked
-work, exp and max/sum operations are not counted.  Rank 0 prints one JSON
+work, exp and max/sum operations are not counted, and neither is the
+backward's second recomputation of S and dP in fa_bwd_dq (the backward
+kernels execute 14d per pair).  The roofline's dominant kernel is fa_bwd_dkdv
+(8d per pair) for forward+backward workloads and fa_fwd otherwise.  Rank 0 prints one JSON
 line with a "roofline" object for the dominant kernel (its average launch
 duration from HIP events recorded on the launch stream during the timed
 steps) and a "cpu_baseline" object (the fp64 oracle timed on a bounded
@@ -102,6 +105,121 @@ def cpu_baseline(w: S.Workload, inp: dict, target_s: float = 15.0) -> dict:
                        "(BLAS pool + one worker thread per head)")}
 
 
+KERNEL_KEYS = (("bwd_dkdv_kernel", "bwd_dkdv"), ("bwd_dq_kernel", "bwd_dq"),
+               ("bwd_preprocess_kernel", "bwd_preprocess"),
+               ("fwd_bf16_kernel", "fwd"), ("fwd_f32_kernel", "fwd"))
+
+
+def algorithmic_bytes(w: S.Workload, kernel: str) -> int:
+    """Bytes a kernel must move to and from HBM at least once: its inputs and
+    outputs, each read or written exactly once."""
+    el = 4 if w.dtype == "f32" else 2
+    t = w.B * w.H * w.N * w.d * el          # one [B,H,N,d] tensor
+    r = w.B * w.H * w.N * 4                 # one float32 [B,H,N] row vector
+    return {"fwd": 3 * t + t + r,             # Q,K,V -> O, LSE
+            "bwd_preprocess": 2 * t + r,      # O, dO -> D
+            "bwd_dkdv": 4 * t + 2 * r + 2 * t,  # Q,K,V,dO,LSE,D -> dK,dV
+            "bwd_dq": 4 * t + 2 * r + t}[kernel]  # Q,K,V,dO,LSE,D -> dQ
+
+
+def _pmc_per_kernel(path, counter):
+    """Average counter value per dispatch, keyed by kernel short name."""
+    import csv
+    vals = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            key = None
+            for frag, k in KERNEL_KEYS:
+                if "fa::" in name and frag in name:
+                    key = k
+            if "neg_kernel" in name:
+                key = "copy_calibration"
+            if key is not None:
+                vals.setdefault(key, []).append(float(r["Counter_Value"]))
+    return {k: (float(np.mean(v)), len(v)) for k, v in vals.items()}
+
+
+def write_traffic(w: S.Workload, csvs, command, mib) -> int:
+    fetch = _pmc_per_kernel(csvs[0], "FETCH_SIZE")
+    write = _pmc_per_kernel(csvs[1], "WRITE_SIZE")
+    if "copy_calibration" not in fetch or "copy_calibration" not in write:
+        print("no calibration kernel in the counter files", file=sys.stderr)
+        return 1
+    # The calibration dispatch reads and writes mib MiB.
+    cal_bytes = mib * (1 << 20)
+    f_scale = cal_bytes / (fetch["copy_calibration"][0] * 1024.0)
+    w_scale = cal_bytes / (write["copy_calibration"][0] * 1024.0)
+    src = {"fwd": ["fa_fwd.hip", "fa_common.h"]}
+    entry = {}
+    for k in fetch:
+        if k == "copy_calibration" or k not in write:
+            continue
+        fb = fetch[k][0] * 1024.0 * f_scale
+        wb = write[k][0] * 1024.0 * w_scale
+        entry[k] = {
+            "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
+            "bytes_per_launch": round(fb + wb),
+            "algorithmic_bytes_per_launch": algorithmic_bytes(w, k),
+            "dispatches": fetch[k][1],
+            "source_digest": _sources_digest(src.get(k, ["fa_bwd.hip", "fa_common.h"])),
+        }
+    tr = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+    tr[w.name] = {"kernels": entry, "command": command,
+                  "calibration": {"bytes": cal_bytes,
+                                  "fetch_kib_measured": fetch["copy_calibration"][0],
+                                  "write_kib_measured": write["copy_calibration"][0],
+                                  "fetch_scale": f_scale, "write_scale": w_scale}}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(tr, f, indent=1, sort_keys=True)
+    md = os.path.join(PROFILES, f"traffic_{w.name}.md")
+    with open(md, "w") as f:
+        f.write(f"# HBM traffic per launch: {w.name} (B={w.B} H={w.H} N={w.N} "
+                f"d={w.d}, causal={w.causal})\n\nCommands (repository root, one "
+                f"MI355X):\n\n```\n{command}\n```\n\n"
+                "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by the "
+                f"calibration copy of {mib} MiB: fetch x{f_scale:.4f}, write "
+                f"x{w_scale:.4f} (measured {fetch['copy_calibration'][0]:.0f} / "
+                f"{write['copy_calibration'][0]:.0f} KiB).\n\n"
+                "| kernel | fetch MB | write MB | total MB | algorithmic MB | "
+                "total / algorithmic |\n|---|---|---|---|---|---|\n")
+        for k, e in sorted(entry.items()):
+            f.write(f"| {k} | {e['fetch_bytes_per_launch']/1e6:.1f} | "
+                    f"{e['write_bytes_per_launch']/1e6:.1f} | "
+                    f"{e['bytes_per_launch']/1e6:.1f} | "
+                    f"{e['algorithmic_bytes_per_launch']/1e6:.1f} | "
+                    f"{e['bytes_per_launch']/e['algorithmic_bytes_per_launch']:.2f} |\n")
+    print(open(md).read())
+    return 0
+
+
+def summarize_trace(w: S.Workload, path, command) -> int:
+    import csv
+    with open(path) as f:
+        rows = [r for r in csv.DictReader(f) if "fa::" in r["Name"]]
+    md = os.path.join(PROFILES, f"kernels_{w.name}.md")
+    with open(md, "w") as f:
+        f.write(f"# Kernel trace: {w.name} (B={w.B} H={w.H} N={w.N} d={w.d}, "
+                f"causal={w.causal}, {'forward+backward' if w.backward else 'forward'})"
+                f"\n\nCommand (repository root, one MI355X):\n\n```\n{command}"
+                "\n```\n\nrocprofv3 kernel statistics, libfa kernels only "
+                "(durations in microseconds):\n\n| kernel | calls | average | "
+                "min | max | share of GPU time |\n|---|---|---|---|---|---|\n")
+        for r in rows:
+            name = (r["Name"].replace("(anonymous namespace)::", "")
+                    .split("(")[0].replace("void ", ""))
+            f.write(f"| `{name}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.1f}"
+                    f" | {float(r['MinNs'])/1e3:.1f} | {float(r['MaxNs'])/1e3:.1f}"
+                    f" | {float(r['Percentage']):.1f}% |\n")
+    print(open(md).read())
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,7 +229,32 @@ def main(argv=None) -> int:
                     choices=sorted(S.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run an elementwise copy (y = -x, float32) of "
+                         "MIB MiB three times after the warmup: the known-size "
+                         "kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn two rocprofv3 --pmc counter "
+                         "collections (FETCH_SIZE, then WRITE_SIZE) of a "
+                         "--copy-calibration run into profiles/traffic.json "
+                         "(give the same --copy-calibration MIB)")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
+                    help="no GPU work: write the libfa rows of a rocprofv3 "
+                         "--kernel-trace --stats kernel_stats.csv to "
+                         "profiles/kernels_<workload>.md")
+    ap.add_argument("--command", default="",
+                    help="with --traffic-from / --summarize-trace: the "
+                         "command that made the CSVs")
     args = ap.parse_args(argv)
+
+    if args.summarize_trace:
+        return summarize_trace(S.WORKLOADS[args.workload], args.summarize_trace,
+                               args.command)
+    if args.traffic_from:
+        if not args.copy_calibration:
+            ap.error("--traffic-from needs the run's --copy-calibration MIB")
+        return write_traffic(S.WORKLOADS[args.workload], args.traffic_from,
+                             args.command, args.copy_calibration)
 
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU "
@@ -174,6 +317,15 @@ def main(argv=None) -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        cx = torch.ones(n, dtype=torch.float32, device=dev)
+        cy = torch.empty_like(cx)
+        for _ in range(3):
+            torch.neg(cx, out=cy)
+        torch.cuda.synchronize()
+        del cx, cy
+        log(f"[bench] copy calibration: 3 x {args.copy_calibration} MiB")
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
           for _ in range(args.steps)]
@@ -196,7 +348,10 @@ def main(argv=None) -> int:
     peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
 
     if w.backward:
-        dom, dom_flops, src = "bwd_dkdv", bwd_flops, ["fa_bwd.hip", "fa_common.h"]
+        # fa_bwd_dkdv produces dK and dV: S = Q K^T, dP = dO V^T, dV += P^T dO
+        # and dK += dS^T Q, 2d FLOP each per visible pair.
+        dom, dom_flops, src = ("bwd_dkdv", 8.0 * w.d * pairs,
+                               ["fa_bwd.hip", "fa_common.h"])
     else:
         dom, dom_flops, src = "fwd", fwd_flops, ["fa_fwd.hip", "fa_common.h"]
     dom_ms = per_kernel[dom]
@@ -205,7 +360,7 @@ def main(argv=None) -> int:
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        ent = tr.get(w.name, {}).get(dom)
+        ent = tr.get(w.name, {}).get("kernels", {}).get(dom)
         if ent and ent.get("source_digest") == _sources_digest(src):
             traffic = ent["bytes_per_launch"]
     roofline = {"bound": "mfma", "achieved": round(achieved, 2),

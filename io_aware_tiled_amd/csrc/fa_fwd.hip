@@ -20,7 +20,7 @@
 // wavefront owns a distinct slice of the query block and shares the K/V
 // tiles, so no reduction crosses wavefronts (item 3; [TW] "Flash Attention 2").
 //
-// gfx950 mapping (one workgroup = 4 wavefronts = 128 query rows):
+// gfx950 mapping (one workgroup = 4 or 8 wavefronts, 32 query rows each):
 //   * S^T = K_j Q_i^T on v_mfma_f32_32x32x16_bf16: the accumulator layout
 //     puts one query per lane (two lanes per query, one per half-wave), so
 //     the row max and row sum are in-lane reductions plus one exchange
@@ -49,7 +49,7 @@ constexpr int kThreads = 256;
 // Growth of the running max (log2 units) tolerated before O is rescaled.
 constexpr float kRescaleSlack = 8.f;
 
-template <int D>
+template <int D, int NW>
 struct FwdTile {
   // K rows padded by 16 B: row stride = 4 (mod 64) banks, conflict-free for
   // the 16-row phases of ds_read_b128.
@@ -60,7 +60,9 @@ struct FwdTile {
   static constexpr int KELEMS = kBC * KST;
   static constexpr int VELEMS = kBC * VST;
   static constexpr int CHUNKS = kBC * D / 8;           // 16-byte chunks per tile
-  static constexpr int CPT = CHUNKS / kThreads;        // chunks per thread
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int CPT = CHUNKS / THREADS;         // chunks per thread
+  static constexpr int BR = 32 * NW;                   // query rows per workgroup
 };
 
 // Map a workgroup index to (bh, query block): causal grids run the longest
@@ -76,13 +78,13 @@ __device__ __forceinline__ void fwd_schedule(int wg, int n_qblk, int BH,
   }
 }
 
-template <int D, bool CAUSAL, bool KVLEN>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
+template <int D, int NW, bool CAUSAL, bool KVLEN>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
     float* __restrict__ LSE, const int32_t* __restrict__ kv_len, int H,
     int N, int n_qblk, float c_log2) {
-  using T = FwdTile<D>;
+  using T = FwdTile<D, NW>;
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][T::KELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][T::VELEMS];
 
@@ -96,13 +98,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int w = wave_id();   // wave-uniform (scalar register)
   const int lq = lane & 31;     // query column of the accumulator
   const int hh = lane >> 5;     // half-wave
-  const int q0 = qb * kBR;
+  const int q0 = qb * T::BR;
   const int qrow = q0 + w * 32 + lq;
 
   int kvlim = N;
   if (KVLEN) kvlim = min(max(kv_len[b], 0), N);
   int kend = kvlim;
-  if (CAUSAL) kend = min(kend, q0 + kBR);
+  if (CAUSAL) kend = min(kend, q0 + T::BR);
   const int ntiles = kend > 0 ? (kend + kBC - 1) / kBC : 0;
 
   const size_t head = (size_t)bh * N * D;
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     c_log2 = -c_log2;
   }
 
-  // Cooperative tile loads: chunk c = tid + 256*r -> row c/(D/8), col
+  // Cooperative tile loads: chunk c = tid + THREADS*r -> row c/(D/8), col
   // 8*(c%(D/8)).  Rows past N read row N-1 (in bounds) and are replaced by
   // zeros with a select; addresses are a wave-uniform tile base plus a 32-bit
   // per-lane offset.
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const uint16_t* vb = Vh + (size_t)k0 * D;
 #pragma unroll
     for (int r = 0; r < T::CPT; ++r) {
-      const int c = tid + kThreads * r;
+      const int c = tid + T::THREADS * r;
       const int row = c / (D / 8);
       const int col = 8 * (c % (D / 8));
       const bool ok = k0 + row < N;
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int r = 0; r < T::CPT; ++r) {
-      const int c = tid + kThreads * r;
+      const int c = tid + T::THREADS * r;
       const int row = c / (D / 8);
       const int col = 8 * (c % (D / 8));
       *(u32x4*)(&lds_k[buf][row * T::KST + col]) = kreg[r];
@@ -497,13 +499,27 @@ int launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const int32_t* kv_len, uint16_t* o, float* lse, int B,
                     int H, int N, int d, float scale, int causal,
                     hipStream_t stream) {
-  const int n_qblk = (N + kBR - 1) / kBR;
-  const dim3 grid((unsigned)(B * H * n_qblk)), block(kThreads);
+  // Head dim 128 on grids with at least two 256-row workgroups per CU uses
+  // 256-row workgroups of 8 wavefronts: each K/V tile staged in LDS then
+  // feeds twice as many query rows.  Everything else uses 128-row
+  // workgroups of 4 wavefronts, two per CU.
+  constexpr int kCUs = 256;
+  const long long wide_grid = (long long)B * H * ((N + 255) / 256);
+  const bool wide = d == 128 && wide_grid >= 2 * kCUs;
+  const int br = wide ? 256 : 128;
+  const int n_qblk = (N + br - 1) / br;
+  const dim3 grid((unsigned)(B * H * n_qblk)), block(wide ? 512 : 256);
   const float c = (float)((double)scale * 1.4426950408889634);
   const bool kv = kv_len != nullptr;
-#define FA_FWD_LAUNCH(DD, CC, KK)                                          \
-  hipLaunchKernelGGL((fwd_bf16_kernel<DD, CC, KK>), grid, block, 0, stream, \
-                     q, k, v, o, lse, kv_len, H, N, n_qblk, c)
+#define FA_FWD_LAUNCH(DD, CC, KK)                                              \
+  do {                                                                         \
+    if (wide)                                                                  \
+      hipLaunchKernelGGL((fwd_bf16_kernel<DD, 8, CC, KK>), grid, block, 0,     \
+                         stream, q, k, v, o, lse, kv_len, H, N, n_qblk, c);    \
+    else                                                                       \
+      hipLaunchKernelGGL((fwd_bf16_kernel<DD, 4, CC, KK>), grid, block, 0,     \
+                         stream, q, k, v, o, lse, kv_len, H, N, n_qblk, c);    \
+  } while (0)
   if (d == 64) {
     if (causal) {
       if (kv) FA_FWD_LAUNCH(64, true, true); else FA_FWD_LAUNCH(64, true, false);
