@@ -48,6 +48,12 @@ constexpr int kBC = 64;    // keys per K/V tile
 constexpr int kThreads = 256;
 // Growth of the running max (log2 units) tolerated before O is rescaled.
 constexpr float kRescaleSlack = 8.f;
+// Largest per-lane tile sum of weights accepted against a stale reference.
+// Small on purpose: it keeps the reference within a few units of the true
+// running max, so that a row's dominant weight stays near 1, where its bf16
+// rounding error is smallest (a dominant weight of 2^20 would round with
+// the full 2^-8 relative error of bf16 and show in near one-hot rows).
+constexpr float kSumLimit = 0x1p8f;
 
 template <int D, int NW>
 struct FwdTile {
@@ -313,6 +319,409 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Software-pipelined forward for large grids.  One workgroup = 4 wavefronts
+// = 256 query rows; each wavefront owns two 32-row blocks (rows
+// q0 + 32w + 0..31 and q0 + 128 + 32w + 0..31, which balances the causal
+// work of the wavefronts) and runs them in lockstep, so every K or V operand
+// read from LDS feeds one MFMA of each block.  The key axis is walked in
+// half-tiles of 32 keys, t = 2j + kb, and each step overlaps three of them:
+//   step t:  S_{t+1} = K_{t+1} Q^T  and  O += V_{t-1}^T P_{t-1}^T  on the
+//            matrix cores, while the VALU turns S_t into P_t,
+// with MFMAs and exponentials interleaved one by one in issue order (a
+// wavefront issues in order, so a run of MFMAs would leave its VALU work
+// waiting).  Only the masking of S_{t+1} on diagonal, ragged or padded tiles
+// and the rare move of the softmax reference sit between steps.  A tile's
+// two steps need K_j, K_{j+1}, V_{j-1} and V_j in LDS, so K and V rotate
+// through three stages each with one barrier per tile: a stage is
+// overwritten two barriers after its last read.  Tile loads are raw buffer
+// loads whose descriptor ends at the last key of the head, so keys past N
+// read as zero without per-lane selects.
+
+template <int D>
+struct PipeTile {
+  static constexpr int KST = D + 8;    // as FwdTile: conflict-free reads
+  static constexpr int VST = D + 32;
+  static constexpr int KELEMS = kBC * KST;
+  static constexpr int VELEMS = kBC * VST;
+  static constexpr int THREADS = 256;
+  static constexpr int BR = 256;
+  static constexpr int CPT = kBC * D / 8 / THREADS;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* p,
+                                                            int bytes) {
+  // 0x00020000: raw 32-bit data format (untyped loads), range-checked.
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, bytes,
+                                           0x00020000);
+}
+
+template <int D, bool CAUSAL, bool KVLEN>
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_pipe_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+    float* __restrict__ LSE, const int32_t* __restrict__ kv_len, int H,
+    int N, int n_qblk, float c_log2) {
+  using T = PipeTile<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[3][T::KELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[3][T::VELEMS];
+
+  const int BH = gridDim.x / n_qblk;
+  int bh, qb;
+  fwd_schedule(blockIdx.x, n_qblk, BH, CAUSAL, bh, qb);
+  const int b = bh / H;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = wave_id();
+  const int lq = lane & 31;
+  const int hh = lane >> 5;
+  const int r16 = lane & 15;
+  const int dsub = (lane >> 4) & 1;
+  const int q0 = qb * T::BR;
+  int qlo[2], qrow[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    qlo[c] = q0 + 32 * (w + 4 * c);
+    qrow[c] = qlo[c] + lq;
+  }
+
+  int kvlim = N;
+  if (KVLEN) kvlim = min(max(kv_len[b], 0), N);
+  int kend = kvlim;
+  if (CAUSAL) kend = min(kend, q0 + T::BR);
+  const int ntiles = kend > 0 ? (kend + kBC - 1) / kBC : 0;
+  // Tiles this wavefront computes (its block 1 sees the most keys; block 0
+  // is masked on the at most two extra tiles).
+  int kend_w = kvlim;
+  if (CAUSAL) kend_w = min(kend_w, qlo[1] + 32);
+  const int nt_w = kend_w > 0 ? (kend_w + kBC - 1) / kBC : 0;
+
+  const size_t head = (size_t)bh * N * D;
+  const uint16_t* Qh = Q + head;
+  const uint16_t* Kh = K + head;
+  const uint16_t* Vh = V + head;
+
+  bf16x8 qf[2][D / 16];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      qf[c][kk] = qrow[c] < N
+                      ? *(const bf16x8*)(Qh + (size_t)qrow[c] * D + 16 * kk + 8 * hh)
+                      : bf16x8{};
+  if (c_log2 < 0.f) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) qf[c][kk] = -qf[c][kk];
+    c_log2 = -c_log2;
+  }
+  // A zero scale becomes a tiny positive one: every visible weight is then
+  // exp2(0) to fp32 precision and masked scores (-inf) still give 0.
+  c_log2 = fmaxf(c_log2, 1e-30f);
+
+  // ---- tile loads: thread chunk r covers row (tid + 256r) / (D/8).
+  unsigned voff[T::CPT];
+  int lds_off_k[T::CPT], lds_off_v[T::CPT];
+#pragma unroll
+  for (int r = 0; r < T::CPT; ++r) {
+    const int cidx = tid + T::THREADS * r;
+    const int row = cidx / (D / 8);
+    const int col = 8 * (cidx % (D / 8));
+    voff[r] = (unsigned)((row * D + col) * 2);
+    lds_off_k[r] = row * T::KST + col;
+    lds_off_v[r] = row * T::VST + col;
+  }
+  u32x4 kreg[T::CPT], vreg[T::CPT];
+  auto load_k = [&](int j) {
+    const int k0 = j * kBC;
+    const auto rs = tile_rsrc(Kh + (size_t)k0 * D, min(N - k0, kBC) * D * 2);
+#pragma unroll
+    for (int r = 0; r < T::CPT; ++r)
+      kreg[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[r], 0, 0));
+  };
+  auto load_v = [&](int j) {
+    const int k0 = j * kBC;
+    const auto rs = tile_rsrc(Vh + (size_t)k0 * D, min(N - k0, kBC) * D * 2);
+#pragma unroll
+    for (int r = 0; r < T::CPT; ++r)
+      vreg[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[r], 0, 0));
+  };
+  auto store_k = [&](int st) {
+#pragma unroll
+    for (int r = 0; r < T::CPT; ++r)
+      *(u32x4*)(&lds_k[st][lds_off_k[r]]) = kreg[r];
+  };
+  auto store_v = [&](int st) {
+#pragma unroll
+    for (int r = 0; r < T::CPT; ++r)
+      *(u32x4*)(&lds_v[st][lds_off_v[r]]) = vreg[r];
+  };
+
+  f32x16 oacc[2][D / 32];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) oacc[c][i] = f32x16{};
+  float m_ref[2] = {-INFINITY, -INFINITY};   // reference max (scaled log2)
+  float m_use[2] = {0.f, 0.f};               // m_ref, or 0 while m_ref = -inf
+  float l_run[2] = {0.f, 0.f};
+  // Per half-tile parity x: S^T (32 keys x 32 queries) of each block, and
+  // P^T of each block in bf16 (two 16-key halves).
+  f32x16 s[2][2];
+  bf16x8 pb[2][2][2];
+  float tsum[2];
+
+  // ---- one step.  xs: parity of S_{t+1} (= parity of P_{t-1}); the
+  // exponentials take S_t (parity 1 - xs).  stk/kbs: K stage and 32-key
+  // half of S_{t+1}; stv/kbv: V stage and half of P_{t-1}.
+  auto step = [&](auto xs_tag, int stk, int kbs, int stv, int kbv) {
+    constexpr int XS = decltype(xs_tag)::value;
+    constexpr int XE = 1 - XS;
+    constexpr int kS = D / 16;             // S MFMAs per block
+    constexpr int kP = 2 * (D / 32);       // PV MFMAs per block
+    constexpr int kN = kS + kP;            // operand reads (each used twice)
+    constexpr int kPf = 3;
+    auto fetch = [&](int i) -> bf16x8 {
+      if (i < kS)
+        return *(const bf16x8*)(&lds_k[stk][(32 * kbs + lq) * T::KST + 8 * hh + 16 * i]);
+      const int pi = i - kS;
+      const int db = pi / 2, h = pi % 2;
+      const int dcol = 32 * db + 16 * dsub + 4 * (r16 & 3);
+      const int key = 32 * kbv + 16 * h + 4 * hh + (r16 >> 2);
+      return join_bf16(lds_read_tr16(&lds_v[stv][key * T::VST + dcol]),
+                       lds_read_tr16(&lds_v[stv][(key + 8) * T::VST + dcol]));
+    };
+    bf16x8 op[kPf];
+#pragma unroll
+    for (int i = 0; i < kPf; ++i) op[i] = fetch(i);
+    // The 32 exponentials of the step (16 per block, element el -> block
+    // el / 16, half (el / 8) % 2, register el % 8) run as a three-stage
+    // pipeline across MFMA slots: slot m takes the FMA of one element group,
+    // the exp2 of the group before it and the row-sum adds (and, at the end
+    // of an 8-element half, the bf16 conversion) of the group before that,
+    // so no instruction waits on the one just issued.
+    constexpr int kM = 2 * kN;                      // MFMA slots
+    constexpr int kG = 32 / kM > 0 ? 32 / kM : 1;   // elements per slot
+    constexpr int kSlots = 32 / kG;                 // slots with VALU work
+    float x[32], pe[32];
+    float t[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    auto el_fma = [&](int g) {
+#pragma unroll
+      for (int u = 0; u < kG; ++u) {
+        const int el = g * kG + u, ce = el / 16, h = (el / 8) % 2, e = el % 8;
+        x[el] = __builtin_fmaf(s[XE][ce][8 * h + e], c_log2, -m_use[ce]);
+      }
+    };
+    auto el_exp = [&](int g) {
+#pragma unroll
+      for (int u = 0; u < kG; ++u) pe[g * kG + u] = __builtin_amdgcn_exp2f(x[g * kG + u]);
+    };
+    auto el_sum = [&](int g) {
+#pragma unroll
+      for (int u = 0; u < kG; ++u) {
+        const int el = g * kG + u, ce = el / 16;
+        t[ce][el & 1] += pe[el];
+        if (el % 8 == 7) {
+          f32x8 v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = pe[el - 7 + e];
+          pb[XE][ce][(el / 8) % 2] = to_bf16x8(v);
+        }
+      }
+    };
+#pragma unroll
+    for (int m = 0; m < kM + 2; ++m) {
+      if (m < kM) {
+        const int i = m / 2, c = m % 2;
+        const bf16x8 a = op[i % kPf];
+        if (c == 1 && i + kPf < kN) op[i % kPf] = fetch(i + kPf);
+        if (i < kS) {
+          s[XS][c] = mfma32x16(a, qf[c][i], i == 0 ? f32x16{} : s[XS][c]);
+        } else {
+          const int pi = i - kS;
+          oacc[c][pi / 2] = mfma32x16(a, pb[XS][c][pi % 2], oacc[c][pi / 2]);
+        }
+      }
+      if (m < kSlots) el_fma(m);
+      if (m >= 1 && m - 1 < kSlots) el_exp(m - 1);
+      if (m >= 2 && m - 2 < kSlots) el_sum(m - 2);
+      // Without a use here the compiler moves the adds to the step's end.
+      asm volatile("" : "+v"(t[0][0]), "+v"(t[0][1]), "+v"(t[1][0]), "+v"(t[1][1]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const float t0 = t[0][0] + t[0][1], t1 = t[1][0] + t[1][1];
+    tsum[0] = t0;
+    tsum[1] = t1;
+  };
+
+  // ---- P_t of block c recomputed against the current reference.
+  auto probs = [&](int xe, int c) {
+    float t = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x8 p;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(
+            __builtin_fmaf(s[xe][c][8 * h + e], c_log2, -m_use[c]));
+        t += p[e];
+      }
+      pb[xe][c][h] = to_bf16x8(p);
+    }
+    tsum[c] = t;
+  };
+
+  // ---- Reference bookkeeping without a per-step max.  The weights are
+  // taken against a reference m_ref that only has to keep them finite and
+  // near 1: O and l share it, so it cancels in O / l and in
+  // LSE = m_ref + log l.  While every lane's half-tile sum stays below
+  // kSumLimit the step is kept.  Otherwise (and on a row's first step,
+  // m_ref = -inf) the reference moves to the true running max, O and l are
+  // rescaled by exp2(m_ref_old - m_ref_new) as in the online-softmax
+  // recurrence, and the step's weights are recomputed.
+  auto settle = [&](int xe) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      asm volatile("" : "+v"(pb[xe][c][0]), "+v"(pb[xe][c][1]), "+v"(tsum[c]));
+      if (__any(tsum[c] > kSumLimit || m_ref[c] == -INFINITY)) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[xe][c][r]);
+        mx = max_halves(mx);
+        const float mt = (mx == -INFINITY) ? -INFINITY : mx * c_log2;
+        const float m_new = fmaxf(m_ref[c], mt);
+        const float alpha = __builtin_amdgcn_exp2f(
+            m_ref[c] - ((m_new == -INFINITY) ? 0.f : m_new));
+        l_run[c] *= alpha;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) oacc[c][i] *= alpha;
+        m_ref[c] = m_new;
+        m_use[c] = (m_new == -INFINITY) ? 0.f : m_new;
+        probs(xe, c);
+      }
+      l_run[c] += tsum[c];
+    }
+  };
+
+  // ---- mask half-tile t = 2j + kb (parity x) where needed.
+  auto mask_half = [&](int x, int j, int kb) {
+    const int k0 = j * kBC + 32 * kb;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bool need_mask =
+          (CAUSAL && k0 + 31 > qlo[c]) || (k0 + 32 > kvlim);
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 8 * (r / 4) + 4 * hh + (r % 4);
+          const bool hide = (CAUSAL && key > qrow[c]) || key >= kvlim;
+          if (hide) s[x][c][r] = -INFINITY;
+        }
+      }
+    }
+  };
+
+  // ---- O += V^T P^T for the last half-tile (no exponentials left).
+  auto pv_only = [&](int x, int stv, int kbv) {
+#pragma unroll
+    for (int pi = 0; pi < 2 * (D / 32); ++pi) {
+      const int db = pi / 2, h = pi % 2;
+      const int dcol = 32 * db + 16 * dsub + 4 * (r16 & 3);
+      const int key = 32 * kbv + 16 * h + 4 * hh + (r16 >> 2);
+      const bf16x8 a =
+          join_bf16(lds_read_tr16(&lds_v[stv][key * T::VST + dcol]),
+                    lds_read_tr16(&lds_v[stv][(key + 8) * T::VST + dcol]));
+#pragma unroll
+      for (int c = 0; c < 2; ++c) oacc[c][db] = mfma32x16(a, pb[x][c][h], oacc[c][db]);
+    }
+  };
+
+  if (ntiles > 0) {
+    const int last = ntiles - 1;
+    // Prologue: K_0 in stage 0, zeros in V stage 2 (the V_{-1} that the
+    // first step multiplies by P = 0), S_0 (half 0 of tile 0) and its mask;
+    // K_1, V_0 in registers for tile 0's stores.
+    load_k(0);
+#pragma unroll
+    for (int r = 0; r < T::CPT; ++r) vreg[r] = u32x4{0, 0, 0, 0};
+    store_v(2);
+    store_k(0);
+    load_k(min(1, last));
+    load_v(0);
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) pb[x][c][h] = bf16x8{};
+    __syncthreads();
+    if (nt_w > 0) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        s[0][c] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+          s[0][c] = mfma32x16(*(const bf16x8*)(&lds_k[0][lq * T::KST + 8 * hh + 16 * kk]),
+                              qf[c][kk], s[0][c]);
+      }
+      mask_half(0, 0, 0);
+    }
+    // Stages: K_j and V_j in stage j % 3.  Tile j stores K_{j+1} and V_j,
+    // then loads K_{j+2} and V_{j+1}.
+    int st0 = 0, st1 = 1, stm = 2;   // j % 3, (j+1) % 3, (j-1) % 3
+    for (int j = 0; j < ntiles; ++j) {
+      store_k(st1);
+      store_v(st0);
+      __syncthreads();
+      load_k(min(j + 2, last));
+      load_v(min(j + 1, last));
+      if (j < nt_w) {
+        // step 2j: S of (j, half 1) || P of (j, half 0); O += (j-1, half 1)
+        step(std::integral_constant<int, 1>{}, st0, 1, stm, 1);
+        settle(0);
+        mask_half(1, j, 1);
+        // step 2j+1: S of (j+1, half 0) || P of (j, half 1); O += (j, half 0)
+        step(std::integral_constant<int, 0>{}, st1, 0, st0, 0);
+        settle(1);
+        if (j + 1 < nt_w) mask_half(0, j + 1, 0);
+      } else if (j == nt_w) {
+        pv_only(1, stm, 1);
+      }
+      const int tmp = stm;
+      stm = st0;
+      st0 = st1;
+      st1 = tmp;
+    }
+    if (nt_w == ntiles && nt_w > 0) pv_only(1, stm, 1);
+  }
+
+  // ---- epilogue: combine half-wave sums, normalise, store O and LSE.
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const float l_tot = sum_halves(l_run[c]);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qrow[c] < N) {
+      uint16_t* orow = O + head + (size_t)qrow[c] * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = oacc[c][db][4 * g + e] * inv;
+          *(bf16x4*)(orow + 32 * db + 8 * g + 4 * hh) = to_bf16x4(x);
+        }
+      if (hh == 0) {
+        LSE[(size_t)bh * N + qrow[c]] =
+            l_tot > 0.f ? (m_ref[c] + __builtin_amdgcn_logf(l_tot)) * kLn2
+                        : -INFINITY;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // float32 forward: v_mfma_f32_32x32x2_f32 (true fp32 products), 32-key tiles.
 // The contraction slot (l/32) of the fp32 instruction takes d in two halves:
 // slot h, step kk <-> d = kk + (D/2)*h, the same for the K and Q operands.
@@ -499,21 +908,26 @@ int launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const int32_t* kv_len, uint16_t* o, float* lse, int B,
                     int H, int N, int d, float scale, int causal,
                     hipStream_t stream) {
-  // Head dim 128 on grids with at least two 256-row workgroups per CU uses
-  // 256-row workgroups of 8 wavefronts: each K/V tile staged in LDS then
-  // feeds twice as many query rows.  Everything else uses 128-row
-  // workgroups of 4 wavefronts, two per CU.
+  // Head dim 64 on grids with at least one 256-row workgroup per CU: the
+  // pipelined kernel (two workgroups per CU).  Head dim 128 on grids with
+  // at least two 256-row workgroups per CU: 8-wavefront workgroups of the
+  // plain kernel.  Everything else: 4-wavefront workgroups (128 rows).
   constexpr int kCUs = 256;
-  const long long wide_grid = (long long)B * H * ((N + 255) / 256);
-  const bool wide = d == 128 && wide_grid >= 2 * kCUs;
-  const int br = wide ? 256 : 128;
+  const long long grid256 = (long long)B * H * ((N + 255) / 256);
+  const int kind = (d == 64 && grid256 >= kCUs)         ? 2
+                   : (d == 128 && grid256 >= 2 * kCUs) ? 1
+                                                       : 0;
+  const int br = kind ? 256 : 128;
   const int n_qblk = (N + br - 1) / br;
-  const dim3 grid((unsigned)(B * H * n_qblk)), block(wide ? 512 : 256);
+  const dim3 grid((unsigned)(B * H * n_qblk)), block(kind == 1 ? 512 : 256);
   const float c = (float)((double)scale * 1.4426950408889634);
   const bool kv = kv_len != nullptr;
 #define FA_FWD_LAUNCH(DD, CC, KK)                                              \
   do {                                                                         \
-    if (wide)                                                                  \
+    if (kind == 2)                                                             \
+      hipLaunchKernelGGL((fwd_bf16_pipe_kernel<DD, CC, KK>), grid, block, 0,   \
+                         stream, q, k, v, o, lse, kv_len, H, N, n_qblk, c);    \
+    else if (kind == 1)                                                        \
       hipLaunchKernelGGL((fwd_bf16_kernel<DD, 8, CC, KK>), grid, block, 0,     \
                          stream, q, k, v, o, lse, kv_len, H, N, n_qblk, c);    \
     else                                                                       \

@@ -120,6 +120,61 @@ def test_fwd_bitwise_repeatable():
         assert torch.equal(o, o0) and torch.equal(lse, l0)
 
 
+# ------------------------------------------- wide grids (256-row kernels)
+# Grids of at least 256 workgroups of 256 rows select the 256-row kernels
+# (head dim 64: the pipelined kernel; head dim 128 from 512 such
+# workgroups: the 8-wavefront kernel).  Many heads at small N reach them
+# with an oracle that still runs every row.
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d,BH,N", [(64, (16, 16), 1), (64, (16, 16), 65),
+                                    (64, (16, 16), 200), (64, (8, 32), 300),
+                                    (64, (4, 64), 513), (128, (32, 16), 1),
+                                    (128, (32, 16), 65), (128, (16, 32), 200),
+                                    (128, (16, 16), 300)])
+def test_fwd_wide_grid_ragged(causal, d, BH, N):
+    B, H = BH
+    inp = S.make_case(B, H, N, d, "bf16", causal, seed=N + d + 3 * causal)
+    _check(f"wide d={d} B={B} H={H} N={N} causal={causal}", inp)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_wide_grid_kvlen(d, causal):
+    N = 300
+    B = 64 if d == 64 else 128
+    rng = np.random.default_rng(77 + d)
+    kv = rng.integers(0, N + 1, B)
+    kv[:8] = [0, 1, 63, 64, 65, 256, 299, 300]
+    inp = S.make_case(B, 4, N, d, "bf16", causal, seed=12 + d,
+                      kv_len=kv.tolist())
+    _check(f"wide kvlen d={d} causal={causal}", inp)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_wide_grid_large_magnitude_and_scale(d):
+    H = 16 if d == 64 else 32
+    inp = S.make_case(16, H, 257, d, "bf16", True, seed=9, q_scale=30.0)
+    _check(f"wide Q*30 d={d}", inp)
+    for scale in (-0.125, 0.0):
+        inp = S.make_case(16, H, 200, d, "bf16", True, seed=4, scale=scale)
+        _check(f"wide scale={scale} d={d}", inp)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_growing_scores(d, causal):
+    """Scores that grow by ~100 (log2 units) along the keys: the reference
+    max of a row must move many times, far past any fixed headroom."""
+    H = 16 if d == 64 else 32
+    N = 700
+    inp = S.make_case(16, H, N, d, "bf16", causal, seed=61 + d)
+    ramp = np.linspace(0.0, 60.0, N, dtype=np.float32)[None, None, :, None]
+    kb = S.bf16_round_bits(inp["k"] + ramp)
+    inp = dict(inp, k_bits=kb, k=S.bf16_bits_to_f32(kb))
+    _check(f"growing scores d={d} causal={causal}", inp)
+
+
 # ---------------------------------------------------------- full workloads
 
 def test_workload_tiny_f32():
