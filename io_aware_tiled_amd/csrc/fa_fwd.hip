@@ -337,14 +337,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
 // loads whose descriptor ends at the last key of the head, so keys past N
 // read as zero without per-lane selects.
 
-template <int D>
+template <int D, int NW, int NB>
 struct PipeTile {
   static constexpr int KST = D + 8;    // as FwdTile: conflict-free reads
   static constexpr int VST = D + 32;
   static constexpr int KELEMS = kBC * KST;
   static constexpr int VELEMS = kBC * VST;
-  static constexpr int THREADS = 256;
-  static constexpr int BR = 256;
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int BR = 32 * NW * NB;
   static constexpr int CPT = kBC * D / 8 / THREADS;
 };
 
@@ -355,13 +355,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* p,
                                            0x00020000);
 }
 
-template <int D, bool CAUSAL, bool KVLEN>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_pipe_kernel(
+template <int D, int NW, int NB, bool CAUSAL, bool KVLEN>
+__global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf16_pipe_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
     float* __restrict__ LSE, const int32_t* __restrict__ kv_len, int H,
     int N, int n_qblk, float c_log2) {
-  using T = PipeTile<D>;
+  using T = PipeTile<D, NW, NB>;
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[3][T::KELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[3][T::VELEMS];
 
@@ -378,10 +378,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_pipe_kernel(
   const int r16 = lane & 15;
   const int dsub = (lane >> 4) & 1;
   const int q0 = qb * T::BR;
-  int qlo[2], qrow[2];
+  int qlo[NB], qrow[NB];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    qlo[c] = q0 + 32 * (w + 4 * c);
+  for (int c = 0; c < NB; ++c) {
+    qlo[c] = q0 + 32 * (w + NW * c);
     qrow[c] = qlo[c] + lq;
   }
 
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_pipe_kernel(
   // Tiles this wavefront computes (its block 1 sees the most keys; block 0
   // is masked on the at most two extra tiles).
   int kend_w = kvlim;
-  if (CAUSAL) kend_w = min(kend_w, qlo[1] + 32);
+  if (CAUSAL) kend_w = min(kend_w, qlo[NB - 1] + 32);
   const int nt_w = kend_w > 0 ? (kend_w + kBC - 1) / kBC : 0;
 
   const size_t head = (size_t)bh * N * D;
@@ -401,9 +401,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_pipe_kernel(
   const uint16_t* Kh = K + head;
   const uint16_t* Vh = V + head;
 
-  bf16x8 qf[2][D / 16];
+  bf16x8 qf[NB][D / 16];
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int c = 0; c < NB; ++c)
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
       qf[c][kk] = qrow[c] < N
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_pipe_kernel(
                       : bf16x8{};
   if (c_log2 < 0.f) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < NB; ++c)
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) qf[c][kk] = -qf[c][kk];
     c_log2 = -c_log2;
@@ -458,19 +458,23 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_pipe_kernel(
       *(u32x4*)(&lds_v[st][lds_off_v[r]]) = vreg[r];
   };
 
-  f32x16 oacc[2][D / 32];
+  f32x16 oacc[NB][D / 32];
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int c = 0; c < NB; ++c)
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) oacc[c][i] = f32x16{};
-  float m_ref[2] = {-INFINITY, -INFINITY};   // reference max (scaled log2)
-  float m_use[2] = {0.f, 0.f};               // m_ref, or 0 while m_ref = -inf
-  float l_run[2] = {0.f, 0.f};
+  float m_ref[NB], m_use[NB], l_run[NB];
+#pragma unroll
+  for (int c = 0; c < NB; ++c) {
+    m_ref[c] = -INFINITY;   // reference max (scaled log2)
+    m_use[c] = 0.f;         // m_ref, or 0 while m_ref = -inf
+    l_run[c] = 0.f;
+  }
   // Per half-tile parity x: S^T (32 keys x 32 queries) of each block, and
   // P^T of each block in bf16 (two 16-key halves).
-  f32x16 s[2][2];
-  bf16x8 pb[2][2][2];
-  float tsum[2];
+  f32x16 s[2][NB];
+  bf16x8 pb[2][NB][2];
+  float tsum[NB];
 
   // ---- one step.  xs: parity of S_{t+1} (= parity of P_{t-1}); the
   // exponentials take S_t (parity 1 - xs).  stk/kbs: K stage and 32-key
@@ -495,17 +499,20 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_pipe_kernel(
     bf16x8 op[kPf];
 #pragma unroll
     for (int i = 0; i < kPf; ++i) op[i] = fetch(i);
-    // The 32 exponentials of the step (16 per block, element el -> block
+    // The 16 NB exponentials of the step (16 per block, element el -> block
     // el / 16, half (el / 8) % 2, register el % 8) run as a three-stage
     // pipeline across MFMA slots: slot m takes the FMA of one element group,
     // the exp2 of the group before it and the row-sum adds (and, at the end
     // of an 8-element half, the bf16 conversion) of the group before that,
     // so no instruction waits on the one just issued.
-    constexpr int kM = 2 * kN;                      // MFMA slots
-    constexpr int kG = 32 / kM > 0 ? 32 / kM : 1;   // elements per slot
-    constexpr int kSlots = 32 / kG;                 // slots with VALU work
-    float x[32], pe[32];
-    float t[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    constexpr int kEl = 16 * NB;                    // exponentials
+    constexpr int kM = NB * kN;                     // MFMA slots
+    constexpr int kG = kEl / kM > 0 ? kEl / kM : 1; // elements per slot
+    constexpr int kSlots = kEl / kG;                // slots with VALU work
+    float x[kEl], pe[kEl];
+    float t[NB][2];
+#pragma unroll
+    for (int c = 0; c < NB; ++c) t[c][0] = t[c][1] = 0.f;
     auto el_fma = [&](int g) {
 #pragma unroll
       for (int u = 0; u < kG; ++u) {
@@ -533,9 +540,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_pipe_kernel(
 #pragma unroll
     for (int m = 0; m < kM + 2; ++m) {
       if (m < kM) {
-        const int i = m / 2, c = m % 2;
+        const int i = m / NB, c = m % NB;
         const bf16x8 a = op[i % kPf];
-        if (c == 1 && i + kPf < kN) op[i % kPf] = fetch(i + kPf);
+        if (c == NB - 1 && i + kPf < kN) op[i % kPf] = fetch(i + kPf);
         if (i < kS) {
           s[XS][c] = mfma32x16(a, qf[c][i], i == 0 ? f32x16{} : s[XS][c]);
         } else {
@@ -547,12 +554,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_pipe_kernel(
       if (m >= 1 && m - 1 < kSlots) el_exp(m - 1);
       if (m >= 2 && m - 2 < kSlots) el_sum(m - 2);
       // Without a use here the compiler moves the adds to the step's end.
-      asm volatile("" : "+v"(t[0][0]), "+v"(t[0][1]), "+v"(t[1][0]), "+v"(t[1][1]));
+#pragma unroll
+      for (int c = 0; c < NB; ++c) asm volatile("" : "+v"(t[c][0]), "+v"(t[c][1]));
       __builtin_amdgcn_sched_barrier(0);
     }
-    const float t0 = t[0][0] + t[0][1], t1 = t[1][0] + t[1][1];
-    tsum[0] = t0;
-    tsum[1] = t1;
+#pragma unroll
+    for (int c = 0; c < NB; ++c) tsum[c] = t[c][0] + t[c][1];
   };
 
   // ---- P_t of block c recomputed against the current reference.
@@ -582,7 +589,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_pipe_kernel(
   // recurrence, and the step's weights are recomputed.
   auto settle = [&](int xe) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < NB; ++c) {
       asm volatile("" : "+v"(pb[xe][c][0]), "+v"(pb[xe][c][1]), "+v"(tsum[c]));
       if (__any(tsum[c] > kSumLimit || m_ref[c] == -INFINITY)) {
         float mx = -INFINITY;
@@ -608,7 +615,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_pipe_kernel(
   auto mask_half = [&](int x, int j, int kb) {
     const int k0 = j * kBC + 32 * kb;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < NB; ++c) {
       const bool need_mask =
           (CAUSAL && k0 + 31 > qlo[c]) || (k0 + 32 > kvlim);
       if (need_mask) {
@@ -633,7 +640,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_pipe_kernel(
           join_bf16(lds_read_tr16(&lds_v[stv][key * T::VST + dcol]),
                     lds_read_tr16(&lds_v[stv][(key + 8) * T::VST + dcol]));
 #pragma unroll
-      for (int c = 0; c < 2; ++c) oacc[c][db] = mfma32x16(a, pb[x][c][h], oacc[c][db]);
+      for (int c = 0; c < NB; ++c) oacc[c][db] = mfma32x16(a, pb[x][c][h], oacc[c][db]);
     }
   };
 
@@ -652,13 +659,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_pipe_kernel(
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < NB; ++c)
 #pragma unroll
         for (int h = 0; h < 2; ++h) pb[x][c][h] = bf16x8{};
     __syncthreads();
     if (nt_w > 0) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < NB; ++c) {
         s[0][c] = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
@@ -698,7 +705,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd_bf16_pipe_kernel(
 
   // ---- epilogue: combine half-wave sums, normalise, store O and LSE.
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < NB; ++c) {
     const float l_tot = sum_halves(l_run[c]);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow[c] < N) {
@@ -908,28 +915,27 @@ int launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const int32_t* kv_len, uint16_t* o, float* lse, int B,
                     int H, int N, int d, float scale, int causal,
                     hipStream_t stream) {
-  // Head dim 64 on grids with at least one 256-row workgroup per CU: the
-  // pipelined kernel (two workgroups per CU).  Head dim 128 on grids with
-  // at least two 256-row workgroups per CU: 8-wavefront workgroups of the
-  // plain kernel.  Everything else: 4-wavefront workgroups (128 rows).
+  // Grids with at least one 256-row workgroup per CU use the pipelined
+  // kernel: head dim 64 with 4 wavefronts of two 32-row blocks (two
+  // workgroups per CU), head dim 128 with 8 wavefronts of one block (its two
+  // blocks would not fit two wavefronts per SIMD).  Smaller grids use the
+  // plain kernel with 128-row workgroups, two per CU.
   constexpr int kCUs = 256;
   const long long grid256 = (long long)B * H * ((N + 255) / 256);
-  const int kind = (d == 64 && grid256 >= kCUs)         ? 2
-                   : (d == 128 && grid256 >= 2 * kCUs) ? 1
-                                                       : 0;
-  const int br = kind ? 256 : 128;
+  const bool pipe = grid256 >= kCUs;
+  const int br = pipe ? 256 : 128;
   const int n_qblk = (N + br - 1) / br;
-  const dim3 grid((unsigned)(B * H * n_qblk)), block(kind == 1 ? 512 : 256);
+  const dim3 grid((unsigned)(B * H * n_qblk));
+  const dim3 block(pipe && d == 128 ? 512 : 256);
   const float c = (float)((double)scale * 1.4426950408889634);
   const bool kv = kv_len != nullptr;
 #define FA_FWD_LAUNCH(DD, CC, KK)                                              \
   do {                                                                         \
-    if (kind == 2)                                                             \
-      hipLaunchKernelGGL((fwd_bf16_pipe_kernel<DD, CC, KK>), grid, block, 0,   \
-                         stream, q, k, v, o, lse, kv_len, H, N, n_qblk, c);    \
-    else if (kind == 1)                                                        \
-      hipLaunchKernelGGL((fwd_bf16_kernel<DD, 8, CC, KK>), grid, block, 0,     \
-                         stream, q, k, v, o, lse, kv_len, H, N, n_qblk, c);    \
+    if (pipe)                                                                  \
+      hipLaunchKernelGGL((fwd_bf16_pipe_kernel<DD, DD == 64 ? 4 : 8,           \
+                                               DD == 64 ? 2 : 1, CC, KK>),     \
+                         grid, block, 0, stream, q, k, v, o, lse, kv_len, H,   \
+                         N, n_qblk, c);                                        \
     else                                                                       \
       hipLaunchKernelGGL((fwd_bf16_kernel<DD, 4, CC, KK>), grid, block, 0,     \
                          stream, q, k, v, o, lse, kv_len, H, N, n_qblk, c);    \
