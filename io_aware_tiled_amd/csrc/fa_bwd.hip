@@ -47,6 +47,8 @@
 #include "fa_common.h"
 #include "fa_launch.h"
 
+#include <type_traits>
+
 namespace fa {
 
 namespace {
@@ -539,6 +541,263 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined dQ kernel: one workgroup per (batch, head, 256-row query block),
+// 8 wavefronts of 32 query rows (two per SIMD).  The key axis is walked in
+// half-tiles of 32 keys, t = 2j + kb; step t issues
+//   S^T_{t+1} = K Q^T and dP^T_{t+1} = V dO^T on the matrix cores while the
+//   VALU forms P_t = exp2(c S^T_t - lse) and dS^T_t = P_t (dP^T_t - D),
+//   then dQ^T += K_t^T dS^T_t,
+// with MFMAs and VALU work interleaved one by one in issue order.  K and V
+// tile j are read in tiles j-1 and j, so they rotate through three LDS
+// stages with one barrier per tile.  Tile loads are raw buffer loads whose
+// descriptor ends at the head's last key: keys past N read as zero.
+constexpr int kDqPBR = 256;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bwd_rsrc(const uint16_t* p,
+                                                           int bytes) {
+  // 0x00020000: raw 32-bit data format (untyped loads), range-checked.
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, bytes,
+                                           0x00020000);
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Dv,
+    uint16_t* __restrict__ dQ, int N, int n_qblk, float c_log2,
+    float scale) {
+  constexpr int D = kD;
+  constexpr int TE = kDqBC * kRS;                 // elements per tile stage
+  constexpr int THREADS = 512;
+  constexpr int CPT = kDqBC * D / 8 / THREADS;    // 16-byte chunks per thread
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[3][TE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[3][TE];
+
+  const int BH = gridDim.x / n_qblk;
+  int bh, qb;
+  if (CAUSAL) {
+    qb = n_qblk - 1 - (int)blockIdx.x / BH;
+    bh = blockIdx.x % BH;
+  } else {
+    bh = blockIdx.x / n_qblk;
+    qb = blockIdx.x % n_qblk;
+  }
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = wave_id();
+  const int lq = lane & 31;
+  const int hh = lane >> 5;
+  const int r16 = lane & 15;
+  const int dsub = (lane >> 4) & 1;
+  const int q0 = qb * kDqPBR;
+  const int qlo = q0 + 32 * w;
+  const int qrow = qlo + lq;
+
+  int kend = N;
+  if (CAUSAL) kend = min(kend, q0 + kDqPBR);
+  const int ntiles = (kend + kDqBC - 1) / kDqBC;
+  int kend_w = N;
+  if (CAUSAL) kend_w = min(kend_w, qlo + 32);
+  const int nt_w = (kend_w + kDqBC - 1) / kDqBC;
+
+  const size_t head = (size_t)bh * N * D;
+  const uint16_t* Qh = Q + head;
+  const uint16_t* Kh = K + head;
+  const uint16_t* Vh = V + head;
+  const uint16_t* dOh = dO + head;
+
+  // Q and dO fragments of this lane's query (B operands), LSE and D.
+  bf16x8 qf[D / 16], gf[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    qf[kk] = qrow < N ? *(const bf16x8*)(Qh + (size_t)qrow * D + 16 * kk + 8 * hh)
+                      : bf16x8{};
+    gf[kk] = qrow < N ? *(const bf16x8*)(dOh + (size_t)qrow * D + 16 * kk + 8 * hh)
+                      : bf16x8{};
+  }
+  // The sign of the scale is folded into Q (bf16 negation is exact), so the
+  // exponent scale is positive and masked scores (-inf) give P = 0; a zero
+  // scale becomes a tiny positive one.  dQ keeps the caller's scale.
+  if (c_log2 < 0.f) {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = -qf[kk];
+    c_log2 = -c_log2;
+  }
+  c_log2 = fmaxf(c_log2, 1e-30f);
+  float lse2 = INFINITY, dd = 0.f;   // rows past N (and empty rows): P = 0
+  if (qrow < N) {
+    const float l = LSE[(size_t)bh * N + qrow];
+    lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+    dd = Dv[(size_t)bh * N + qrow];
+  }
+
+  unsigned voff[CPT];
+  int lds_off[CPT];
+#pragma unroll
+  for (int r = 0; r < CPT; ++r) {
+    const int cidx = tid + THREADS * r;
+    const int row = cidx / (D / 8);
+    const int col = 8 * (cidx % (D / 8));
+    voff[r] = (unsigned)((row * D + col) * 2);
+    lds_off[r] = row * kRS + col;
+  }
+  u32x4 kreg[CPT], vreg[CPT];
+  auto load_kv = [&](int j) {
+    const int k0 = j * kDqBC;
+    const int bytes = min(N - k0, kDqBC) * D * 2;
+    const auto rk = bwd_rsrc(Kh + (size_t)k0 * D, bytes);
+    const auto rv = bwd_rsrc(Vh + (size_t)k0 * D, bytes);
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+      kreg[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff[r], 0, 0));
+      vreg[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[r], 0, 0));
+    }
+  };
+  auto store_kv = [&](int st) {
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+      *(u32x4*)(&lds_k[st][lds_off[r]]) = kreg[r];
+      *(u32x4*)(&lds_v[st][lds_off[r]]) = vreg[r];
+    }
+  };
+
+  f32x16 dq_acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) dq_acc[i] = f32x16{};
+  f32x16 s[2], dp[2];        // S^T, dP^T of a half-tile, by parity
+  bf16x8 dsb[2];             // dS^T in bf16, 16-key halves
+
+  // ---- one step.  XS: parity receiving S^T, dP^T of the next half-tile
+  // (stage stn, 32-key half kbn); the VALU and dQ take the current one
+  // (parity 1 - XS, K stage stc, half kbc).
+  auto step = [&](auto xs_tag, int stn, int kbn, int stc, int kbc) {
+    constexpr int XS = decltype(xs_tag)::value;
+    constexpr int XE = 1 - XS;
+    constexpr int kS = D / 16;           // MFMAs for S^T (and for dP^T)
+    constexpr int kQ = 2 * (D / 32);     // MFMAs for dQ^T
+    constexpr int kN = 2 * kS + kQ;
+    constexpr int kPf = 3;
+    auto fetch = [&](int i) -> bf16x8 {
+      if (i < kS)
+        return *(const bf16x8*)(&lds_k[stn][(32 * kbn + lq) * kRS + 8 * hh + 16 * i]);
+      if (i < 2 * kS)
+        return *(const bf16x8*)(&lds_v[stn][(32 * kbn + lq) * kRS + 8 * hh + 16 * (i - kS)]);
+      const int pi = i - 2 * kS;
+      const int h = pi / (D / 32), db = pi % (D / 32);
+      const int col = 32 * db + 16 * dsub + 4 * (r16 & 3);
+      const int row = 32 * kbc + 16 * h + 4 * hh + (r16 >> 2);
+      return join_bf16(lds_read_tr16(&lds_k[stc][row * kRS + col]),
+                       lds_read_tr16(&lds_k[stc][(row + 8) * kRS + col]));
+    };
+    bf16x8 op[kPf];
+#pragma unroll
+    for (int i = 0; i < kPf; ++i) op[i] = fetch(i);
+    // VALU: 16 elements as a three-stage pipeline over the MFMA slots
+    // (FMA, then exp2, then dS and, per 8 elements, the bf16 conversion);
+    // the dQ MFMAs come last, after each half of dS^T is converted.
+    float x[16], pe[16], dsv[16];
+#pragma unroll
+    for (int m = 0; m < kN; ++m) {
+      const bf16x8 a = op[m % kPf];
+      if (m + kPf < kN) op[m % kPf] = fetch(m + kPf);
+      if (m < kS) {
+        s[XS] = mfma32x16(a, qf[m], m == 0 ? f32x16{} : s[XS]);
+      } else if (m < 2 * kS) {
+        const int kk = m - kS;
+        dp[XS] = mfma32x16(a, gf[kk], kk == 0 ? f32x16{} : dp[XS]);
+      } else {
+        // Half 0 of dS^T (converted in slot 9) feeds the first D/32 of
+        // these MFMAs, half 1 (converted in slot 17) the last D/32, which
+        // start at slot 2 kS + D/32 = 20: each half is ready before use.
+        const int pi = m - 2 * kS;
+        dq_acc[pi % (D / 32)] = mfma32x16(a, dsb[pi / (D / 32)], dq_acc[pi % (D / 32)]);
+      }
+      if (m < 16) x[m] = __builtin_fmaf(s[XE][m], c_log2, -lse2);
+      if (m >= 1 && m - 1 < 16) pe[m - 1] = __builtin_amdgcn_exp2f(x[m - 1]);
+      if (m >= 2 && m - 2 < 16) {
+        const int el = m - 2;
+        dsv[el] = pe[el] * (dp[XE][el] - dd);
+        if (el % 8 == 7) {
+          f32x8 v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = dsv[el - 7 + e];
+          dsb[el / 8] = to_bf16x8(v);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- mask the half-tile (j, kb) held in parity x where needed.
+  auto mask_half = [&](int x, int j, int kb) {
+    const int k0 = j * kDqBC + 32 * kb;
+    const bool need_mask = (CAUSAL && k0 + 31 > qlo) || (k0 + 32 > N);
+    if (need_mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 8 * (r / 4) + 4 * hh + (r % 4);
+        if ((CAUSAL && key > qrow) || key >= N) s[x][r] = -INFINITY;
+      }
+    }
+  };
+
+  if (ntiles > 0) {
+    const int last = ntiles - 1;
+    // Prologue: K_0, V_0 in stage 0; S^T, dP^T of half-tile (0, 0); K_1, V_1
+    // in registers for tile 0's stores.
+    load_kv(0);
+    store_kv(0);
+    load_kv(min(1, last));
+    __syncthreads();
+    if (nt_w > 0) {
+      s[0] = f32x16{};
+      dp[0] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const int o = lq * kRS + 8 * hh + 16 * kk;
+        s[0] = mfma32x16(*(const bf16x8*)(&lds_k[0][o]), qf[kk], s[0]);
+        dp[0] = mfma32x16(*(const bf16x8*)(&lds_v[0][o]), gf[kk], dp[0]);
+      }
+      mask_half(0, 0, 0);
+    }
+    // K_j, V_j in stage j % 3.  Tile j stores K_{j+1}, V_{j+1}, then loads
+    // K_{j+2}, V_{j+2}.
+    int st0 = 0, st1 = 1;
+    for (int j = 0; j < ntiles; ++j) {
+      store_kv(st1);
+      __syncthreads();
+      load_kv(min(j + 2, last));
+      if (j < nt_w) {
+        // step 2j: S^T, dP^T of (j, 1) || dS of (j, 0), dQ += (j, 0)
+        step(std::integral_constant<int, 1>{}, st0, 1, st0, 0);
+        mask_half(1, j, 1);
+        // step 2j+1: S^T, dP^T of (j+1, 0) || dS of (j, 1), dQ += (j, 1)
+        step(std::integral_constant<int, 0>{}, st1, 0, st0, 1);
+        if (j + 1 < nt_w) mask_half(0, j + 1, 0);
+      }
+      st0 = st1;
+      st1 = st1 == 2 ? 0 : st1 + 1;
+    }
+  }
+
+  // ---- epilogue: dQ = scale * dQ^T (lane = query, regs = d).
+  if (qrow < N) {
+    uint16_t* out = dQ + head + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 xo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xo[e] = dq_acc[db][4 * g + e] * scale;
+        *(bf16x4*)(out + 32 * db + 8 * g + 4 * hh) = to_bf16x4(xo);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 int launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, float* D,
@@ -581,9 +840,24 @@ int launch_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   uint16_t* dq, int B, int H, int N, int d, float scale,
                   int causal, hipStream_t stream) {
   if (d != kD) return -3;
+  const float c = (float)((double)scale * 1.4426950408889634);
+  // Grids with at least one 256-row workgroup per CU: the pipelined kernel;
+  // smaller ones: 128-row workgroups, two per CU.
+  const long long grid256 = (long long)B * H * ((N + kDqPBR - 1) / kDqPBR);
+  if (grid256 >= 256) {
+    const int n_qblk = (N + kDqPBR - 1) / kDqPBR;
+    const dim3 grid((unsigned)(B * H * n_qblk)), block(512);
+    if (causal) {
+      hipLaunchKernelGGL(bwd_dq_pipe_kernel<true>, grid, block, 0, stream, q,
+                         k, v, dO, lse, D, dq, N, n_qblk, c, scale);
+    } else {
+      hipLaunchKernelGGL(bwd_dq_pipe_kernel<false>, grid, block, 0, stream, q,
+                         k, v, dO, lse, D, dq, N, n_qblk, c, scale);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+  }
   const int n_qblk = (N + kDqBR - 1) / kDqBR;
   const dim3 grid((unsigned)(B * H * n_qblk)), block(kThreads);
-  const float c = (float)((double)scale * 1.4426950408889634);
   if (causal) {
     hipLaunchKernelGGL(bwd_dq_kernel<true>, grid, block, 0, stream, q, k, v,
                        dO, lse, D, dq, N, n_qblk, c, scale);

@@ -46,6 +46,23 @@ def test_bwd_ragged(causal, N):
     _check_bwd(f"bwd causal={causal} N={N}", inp)
 
 
+# Grids of at least 256 workgroups of 256 query rows select the pipelined dQ
+# kernel; many heads at small N reach it with a full oracle comparison.
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 65, 200])
+def test_bwd_wide_grid(causal, N):
+    inp = S.make_case(16, 16, N, 128, "bf16", causal, seed=300 + N + causal,
+                      backward=True)
+    _check_bwd(f"wide bwd causal={causal} N={N}", inp)
+
+
+@pytest.mark.parametrize("scale", [-0.08, 0.0])
+def test_bwd_wide_grid_scales(scale):
+    inp = S.make_case(16, 16, 100, 128, "bf16", True, seed=17, backward=True,
+                      scale=scale)
+    _check_bwd(f"wide bwd scale={scale}", inp)
+
+
 def test_bwd_bitwise_repeatable():
     """No atomics anywhere in the backward: dQ, dK and dV are bit-identical
     across runs."""
