@@ -23,10 +23,12 @@ ARCH = "gfx950"
 
 SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp"]
 
-# Per-source flags.  The forward's VALU reads every MFMA result (scores), so
-# its accumulators are kept in VGPRs rather than AGPRs (which the VALU can
-# only reach through copies).
-SOURCE_FLAGS = {"fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source flags.  The VALU reads the score MFMAs' results, so MFMA
+# results are kept in VGPRs rather than AGPRs (which the VALU can only reach
+# through copies); the backward's long-lived dK/dV accumulators are placed in
+# AGPRs explicitly.
+SOURCE_FLAGS = {"fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

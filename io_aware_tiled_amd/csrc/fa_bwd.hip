@@ -541,6 +541,351 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   }
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bwd_rsrc(const uint16_t* p,
+                                                           int bytes) {
+  // 0x00020000: raw 32-bit data format (untyped loads), range-checked.
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, bytes,
+                                           0x00020000);
+}
+
+// dV^T / dK^T accumulation of the pipelined dK/dV kernel: the accumulators
+// live in AGPRs, which only MFMAs touch until the epilogue, while the
+// score MFMAs of the same kernel write VGPRs that the VALU reads.  The
+// compiler assigns one register file to all MFMAs of a kernel, so this one
+// is written out.  Hazards: back-to-back accumulation into the same AGPRs
+// needs no wait states; the AGPR writes of the zero fill before the loop
+// and the reads of the epilogue are separated from these MFMAs by explicit
+// s_nop padding (agpr_hazard_pad).
+__device__ __forceinline__ void mfma_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+               : "+a"(acc)
+               : "v"(a), "v"(b));
+}
+// Wait states between an MFMA that writes AGPRs and an instruction that
+// reads them (or between a VALU write of AGPRs and an MFMA reading them as
+// C), with margin: three s_nop 7 give 24.
+__device__ __forceinline__ void agpr_hazard_pad() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined dK/dV kernel: one workgroup per (batch, head, 128-key block), 4
+// wavefronts (one per SIMD) of 32 keys.  The K and V fragments of a
+// wavefront's keys stay in registers for the whole kernel, so LDS only
+// carries the streamed 64-row query tiles (Q, dO, LSE, D).  A tile is two
+// 32-row blocks; work item A_c is S = Q_c K^T and dP = dO_c V^T, V_c the
+// VALU turning them into P and dS, B_c the products dV^T += dO_c^T P and
+// dK^T += Q_c^T dS.  Tile i runs two phases, each 32 MFMAs with one
+// block's VALU work interleaved in issue order:
+//   phase 1:  A_1(i), B_1(i-1)  ||  V_0(i)
+//   phase 2:  B_0(i), A_0(i+1)  ||  V_1(i)
+// Tile i is read from iteration i-1 to i+1, so query tiles rotate through
+// four LDS stages with one barrier per tile.
+constexpr int kKvPBK = 128;
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Dv,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kblk,
+    float c_log2, float scale) {
+  constexpr int D = kD;
+  constexpr int QE = kBQ2 * kRS;                 // elements per tile stage
+  constexpr int THREADS = 256;
+  constexpr int CPT = kBQ2 * D / 8 / THREADS;    // 16-byte chunks per thread
+  __shared__ __attribute__((aligned(16))) uint16_t lds_q[4][QE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_g[4][QE];   // dO
+  __shared__ __attribute__((aligned(16))) float lds_lse[4][kBQ2];
+  __shared__ __attribute__((aligned(16))) float lds_d[4][kBQ2];
+
+  const int BH = gridDim.x / n_kblk;
+  // Key blocks with the most visible queries (smallest index) go first.
+  const int jb = blockIdx.x / BH;
+  const int bh = blockIdx.x % BH;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = wave_id();
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int r16 = lane & 15;
+  const int dsub = (lane >> 4) & 1;
+
+  const int kb0 = jb * kKvPBK;
+  const int wk0 = kb0 + 32 * w;             // first key of this wavefront
+  const int mykey = wk0 + l32;              // this lane's key
+  const size_t head = (size_t)bh * N * D;
+  const uint16_t* Qh = Q + head;
+  const uint16_t* dOh = dO + head;
+  const float* LSEh = LSE + (size_t)bh * N;
+  const float* Dh = Dv + (size_t)bh * N;
+
+  // K and V fragments of this lane's key (B operands), zero past N.  The
+  // sign of the scale is folded into K (exact for bf16), so the exponent
+  // scale is positive and masked scores (-inf) give P = 0; a zero scale
+  // becomes a tiny positive one.  dK keeps the caller's scale.
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    kf[kk] = mykey < N ? *(const bf16x8*)(K + head + (size_t)mykey * D + 16 * kk + 8 * hh)
+                       : bf16x8{};
+    vf[kk] = mykey < N ? *(const bf16x8*)(V + head + (size_t)mykey * D + 16 * kk + 8 * hh)
+                       : bf16x8{};
+  }
+  if (c_log2 < 0.f) {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) kf[kk] = -kf[kk];
+    c_log2 = -c_log2;
+  }
+  c_log2 = fmaxf(c_log2, 1e-30f);
+
+  const int n_qt = (N + kBQ2 - 1) / kBQ2;
+  const int it0 = CAUSAL ? kb0 / kBQ2 : 0;
+
+  // ---- query-tile staging (buffer loads: rows past N read as zero).
+  unsigned voff[CPT];
+  int lds_off[CPT];
+#pragma unroll
+  for (int r = 0; r < CPT; ++r) {
+    const int cidx = tid + THREADS * r;
+    const int row = cidx / (D / 8);
+    const int col = 8 * (cidx % (D / 8));
+    voff[r] = (unsigned)((row * D + col) * 2);
+    lds_off[r] = row * kRS + col;
+  }
+  u32x4 qreg[CPT], greg[CPT];
+  float lse_r = INFINITY, d_r = 0.f;
+  auto load_tile = [&](int it) {
+    const int qt0 = it * kBQ2;
+    const int bytes = min(N - qt0, kBQ2) * D * 2;
+    const auto rq = bwd_rsrc(Qh + (size_t)qt0 * D, bytes);
+    const auto rg = bwd_rsrc(dOh + (size_t)qt0 * D, bytes);
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+      qreg[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, voff[r], 0, 0));
+      greg[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, voff[r], 0, 0));
+    }
+    if (w == 0) {
+      // Rows past N (and rows without any visible key) get +inf, so that
+      // exp2(s - lse) = 0 for every key.
+      const int q = qt0 + lane;
+      const float l = q < N ? LSEh[min(q, N - 1)] : INFINITY;
+      lse_r = (l == -INFINITY) ? INFINITY : l * kLog2e;
+      d_r = q < N ? Dh[min(q, N - 1)] : 0.f;
+    }
+  };
+  auto store_tile = [&](int st) {
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+      *(u32x4*)(&lds_q[st][lds_off[r]]) = qreg[r];
+      *(u32x4*)(&lds_g[st][lds_off[r]]) = greg[r];
+    }
+    if (w == 0) {
+      lds_lse[st][lane] = lse_r;
+      lds_d[st][lane] = d_r;
+    }
+  };
+
+  f32x16 dk_acc[D / 32], dv_acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    dk_acc[i] = f32x16{};
+    dv_acc[i] = f32x16{};
+  }
+  f32x16 s[2], dp[2];          // S, dP of each block (lane = key)
+  bf16x8 pb[2][2], dsb[2][2];  // P, dS of each block in bf16, 16-row halves
+
+  // ---- one phase.  A: S, dP of block ca from stage sta.  B: dV, dK of
+  // block cb from stage stb.  VALU: P, dS of block cv with LSE / D from
+  // stage stv.  B_FIRST orders the B products before the A ones.
+  auto phase = [&](auto b_first, int sta, int ca, int stb, int cb,
+                   int stv, int cv) {
+    constexpr bool BF = decltype(b_first)::value;
+    constexpr int kA = 2 * (D / 16);       // S and dP MFMAs
+    constexpr int kB = 4 * (D / 32);       // dV and dK MFMAs
+    constexpr int kN = kA + kB;
+    constexpr int kPf = 4;
+    auto fetch = [&](int i) -> bf16x8 {
+      const bool is_a = BF ? (i >= kB) : (i < kA);
+      if (is_a) {
+        const int ai = BF ? i - kB : i;
+        const int kk = ai / 2;
+        const uint16_t* t = (ai % 2 == 0) ? lds_q[sta] : lds_g[sta];
+        return *(const bf16x8*)(&t[(32 * ca + l32) * kRS + 16 * kk + 8 * hh]);
+      }
+      const int bi = BF ? i : i - kA;
+      const int which = bi / (kB / 2);           // 0: dO^T (dV), 1: Q^T (dK)
+      const int h = (bi % (kB / 2)) / (D / 32), db = bi % (D / 32);
+      const uint16_t* t = which == 0 ? lds_g[stb] : lds_q[stb];
+      const int col = 32 * db + 16 * dsub + 4 * (r16 & 3);
+      const int row = 32 * cb + 16 * h + 4 * hh + (r16 >> 2);
+      return join_bf16(lds_read_tr16(&t[row * kRS + col]),
+                       lds_read_tr16(&t[(row + 8) * kRS + col]));
+    };
+    bf16x8 op[kPf];
+#pragma unroll
+    for (int i = 0; i < kPf; ++i) op[i] = fetch(i);
+    // LSE / D of the lane's 16 rows of block cv: register r <-> row
+    // 32 cv + 8 (r / 4) + 4 hh + r % 4.
+    f32x4 l4[4], d4[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      l4[g] = *(const f32x4*)(&lds_lse[stv][32 * cv + 8 * g + 4 * hh]);
+      d4[g] = *(const f32x4*)(&lds_d[stv][32 * cv + 8 * g + 4 * hh]);
+    }
+    // VALU: 16 elements as a three-stage pipeline over the MFMA slots
+    // (FMA, then exp2, then dS and, per 8 elements, the bf16 conversions).
+    float x[16], pe[16], dsv[16];
+#pragma unroll
+    for (int m = 0; m < kN; ++m) {
+      const bf16x8 a = op[m % kPf];
+      if (m + kPf < kN) op[m % kPf] = fetch(m + kPf);
+      const bool is_a = BF ? (m >= kB) : (m < kA);
+      if (is_a) {
+        const int ai = BF ? m - kB : m;
+        const int kk = ai / 2;
+        if (ai % 2 == 0)
+          s[ca] = mfma32x16(a, kf[kk], kk == 0 ? f32x16{} : s[ca]);
+        else
+          dp[ca] = mfma32x16(a, vf[kk], kk == 0 ? f32x16{} : dp[ca]);
+      } else {
+        const int bi = BF ? m : m - kA;
+        const int which = bi / (kB / 2);
+        const int h = (bi % (kB / 2)) / (D / 32), db = bi % (D / 32);
+        if (which == 0)
+          mfma_agpr(dv_acc[db], a, pb[cb][h]);
+        else
+          mfma_agpr(dk_acc[db], a, dsb[cb][h]);
+      }
+      if (m < 16) x[m] = __builtin_fmaf(s[cv][m], c_log2, -l4[m / 4][m % 4]);
+      if (m >= 1 && m - 1 < 16) pe[m - 1] = __builtin_amdgcn_exp2f(x[m - 1]);
+      if (m >= 2 && m - 2 < 16) {
+        const int el = m - 2;
+        dsv[el] = pe[el] * (dp[cv][el] - d4[el / 4][el % 4]);
+        if (el % 8 == 7) {
+          f32x8 vp, vd;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            vp[e] = pe[el - 7 + e];
+            vd[e] = dsv[el - 7 + e];
+          }
+          pb[cv][el / 8] = to_bf16x8(vp);
+          dsb[cv][el / 8] = to_bf16x8(vd);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Keep the VALU work in this phase: without a use here the compiler
+    // sinks it past the masking branch that follows.
+    asm volatile("" : "+v"(pb[cv][0]), "+v"(pb[cv][1]), "+v"(dsb[cv][0]),
+                 "+v"(dsb[cv][1]));
+  };
+
+  // ---- mask block c of query tile it where needed (causal diagonal, keys
+  // past N; rows past N already have P = 0 through LSE = +inf).
+  auto mask_block = [&](int c, int it) {
+    const int qb0 = it * kBQ2 + 32 * c;
+    const bool need_mask = (CAUSAL && wk0 + 31 > qb0) || (wk0 + 32 > N);
+    if (need_mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = qb0 + 8 * (r / 4) + 4 * hh + (r % 4);
+        if ((CAUSAL && mykey > q) || mykey >= N) s[c][r] = -INFINITY;
+      }
+    }
+  };
+
+  // ---- dV, dK of block 1 of the last tile (no VALU work left).
+  auto b_only = [&](int stb) {
+#pragma unroll
+    for (int bi = 0; bi < 4 * (D / 32); ++bi) {
+      const int which = bi / (2 * (D / 32));
+      const int h = (bi % (2 * (D / 32))) / (D / 32), db = bi % (D / 32);
+      const uint16_t* t = which == 0 ? lds_g[stb] : lds_q[stb];
+      const int col = 32 * db + 16 * dsub + 4 * (r16 & 3);
+      const int row = 32 + 16 * h + 4 * hh + (r16 >> 2);
+      const bf16x8 a = join_bf16(lds_read_tr16(&t[row * kRS + col]),
+                                 lds_read_tr16(&t[(row + 8) * kRS + col]));
+      if (which == 0)
+        mfma_agpr(dv_acc[db], a, pb[1][h]);
+      else
+        mfma_agpr(dk_acc[db], a, dsb[1][h]);
+    }
+  };
+
+  if (it0 < n_qt) {
+    const int last = n_qt - 1;
+    // Prologue: tile it0 in stage 0; zeros in stage 3 (the tile before it0,
+    // whose block 1 the first phase multiplies by P = dS = 0); A_0(it0).
+    load_tile(it0);
+    store_tile(0);
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+      qreg[r] = u32x4{0, 0, 0, 0};
+      greg[r] = u32x4{0, 0, 0, 0};
+    }
+    store_tile(3);
+    load_tile(min(it0 + 1, last));
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        pb[c][h] = bf16x8{};
+        dsb[c][h] = bf16x8{};
+      }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const int o = l32 * kRS + 16 * kk + 8 * hh;
+      s[0] = mfma32x16(*(const bf16x8*)(&lds_q[0][o]), kf[kk], kk == 0 ? f32x16{} : s[0]);
+      dp[0] = mfma32x16(*(const bf16x8*)(&lds_g[0][o]), vf[kk], kk == 0 ? f32x16{} : dp[0]);
+    }
+    mask_block(0, it0);
+    agpr_hazard_pad();   // zero-filled accumulators -> first MFMA
+
+    // Tile i in stage (i - it0) % 4.  Iteration i stores tile i+1, then
+    // loads tile i+2.
+    int sp = 3, s0 = 0, s1 = 1;   // stages of tiles i-1, i, i+1
+    for (int it = it0; it < n_qt; ++it) {
+      store_tile(s1);
+      __syncthreads();
+      load_tile(min(it + 2, last));
+      // phase 1: A_1(i), B_1(i-1) || V_0(i)
+      phase(std::false_type{}, s0, 1, sp, 1, s0, 0);
+      mask_block(1, it);
+      // phase 2: B_0(i), A_0(i+1) || V_1(i)
+      phase(std::true_type{}, s1, 0, s0, 0, s0, 1);
+      if (it + 1 < n_qt) mask_block(0, it + 1);
+      sp = s0;
+      s0 = s1;
+      s1 = (s1 + 1) & 3;
+    }
+    b_only(sp);
+    agpr_hazard_pad();   // last MFMA -> epilogue reads
+  }
+
+  // ---- epilogue: dK = scale * dK^T, dV = dV^T (lane = key, regs = d).
+  if (mykey < N) {
+    uint16_t* dkr = dK + head + (size_t)mykey * D;
+    uint16_t* dvr = dV + head + (size_t)mykey * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = dk_acc[db][4 * g + e] * scale;
+          b[e] = dv_acc[db][4 * g + e];
+        }
+        *(bf16x4*)(dkr + 32 * db + 8 * g + 4 * hh) = to_bf16x4(a);
+        *(bf16x4*)(dvr + 32 * db + 8 * g + 4 * hh) = to_bf16x4(b);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Pipelined dQ kernel: one workgroup per (batch, head, 256-row query block),
 // 8 wavefronts of 32 query rows (two per SIMD).  The key axis is walked in
@@ -553,13 +898,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 // stages with one barrier per tile.  Tile loads are raw buffer loads whose
 // descriptor ends at the head's last key: keys past N read as zero.
 constexpr int kDqPBR = 256;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t bwd_rsrc(const uint16_t* p,
-                                                           int bytes) {
-  // 0x00020000: raw 32-bit data format (untyped loads), range-checked.
-  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, bytes,
-                                           0x00020000);
-}
 
 template <bool CAUSAL>
 __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
@@ -823,8 +1161,21 @@ int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     float scale, int causal, hipStream_t stream) {
   if (d != kD) return -3;
   const int n_kblk = (N + kBK - 1) / kBK;
-  const dim3 grid((unsigned)(B * H * n_kblk)), block(kBwdThreads);
   const float c = (float)((double)scale * 1.4426950408889634);
+  // Grids with at least one 128-key workgroup per CU: the pipelined kernel
+  // (4 wavefronts, K/V in registers); smaller ones: 8 wavefronts.
+  if ((long long)B * H * n_kblk >= 256) {
+    const dim3 grid((unsigned)(B * H * n_kblk)), block(256);
+    if (causal) {
+      hipLaunchKernelGGL(bwd_dkdv_pipe_kernel<true>, grid, block, 0, stream,
+                         q, k, v, dO, lse, D, dk, dv, N, n_kblk, c, scale);
+    } else {
+      hipLaunchKernelGGL(bwd_dkdv_pipe_kernel<false>, grid, block, 0, stream,
+                         q, k, v, dO, lse, D, dk, dv, N, n_kblk, c, scale);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+  }
+  const dim3 grid((unsigned)(B * H * n_kblk)), block(kBwdThreads);
   if (causal) {
     hipLaunchKernelGGL(bwd_dkdv_kernel<true>, grid, block, 0, stream, q, k, v,
                        dO, lse, D, dk, dv, N, n_kblk, c, scale);
