@@ -105,9 +105,10 @@ def cpu_baseline(w: S.Workload, inp: dict, target_s: float = 15.0) -> dict:
                        "(BLAS pool + one worker thread per head)")}
 
 
-KERNEL_KEYS = (("bwd_dkdv_kernel", "bwd_dkdv"), ("bwd_dq_kernel", "bwd_dq"),
-               ("bwd_preprocess_kernel", "bwd_preprocess"),
-               ("fwd_bf16_kernel", "fwd"), ("fwd_f32_kernel", "fwd"))
+# rocprofv3 kernel-name fragment -> bench step (all variants of a step)
+KERNEL_KEYS = (("bwd_dkdv_", "bwd_dkdv"), ("bwd_dq_", "bwd_dq"),
+               ("bwd_preprocess_", "bwd_preprocess"),
+               ("fwd_bf16_", "fwd"), ("fwd_f32_", "fwd"))
 
 
 def algorithmic_bytes(w: S.Workload, kernel: str) -> int:
