@@ -548,26 +548,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t bwd_rsrc(const uint16_t* p,
                                            0x00020000);
 }
 
-// dV^T / dK^T accumulation of the pipelined dK/dV kernel: the accumulators
-// live in AGPRs, which only MFMAs touch until the epilogue, while the
-// score MFMAs of the same kernel write VGPRs that the VALU reads.  The
-// compiler assigns one register file to all MFMAs of a kernel, so this one
-// is written out.  Hazards: back-to-back accumulation into the same AGPRs
-// needs no wait states; the AGPR writes of the zero fill before the loop
-// and the reads of the epilogue are separated from these MFMAs by explicit
-// s_nop padding (agpr_hazard_pad).
-__device__ __forceinline__ void mfma_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-               : "+a"(acc)
-               : "v"(a), "v"(b));
-}
-// Wait states between an MFMA that writes AGPRs and an instruction that
-// reads them (or between a VALU write of AGPRs and an MFMA reading them as
-// C), with margin: three s_nop 7 give 24.
-__device__ __forceinline__ void agpr_hazard_pad() {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-}
-
 // ---------------------------------------------------------------------------
 // Pipelined dK/dV kernel: one workgroup per (batch, head, 128-key block), 4
 // wavefronts (one per SIMD) of 32 keys.  The K and V fragments of a

@@ -120,4 +120,24 @@ __device__ __forceinline__ int xcd_remap(int p, int n) {
   return (p % kXcd) * per + p / kXcd;
 }
 
+// MFMA accumulating into AGPRs.  Long-lived accumulators that only MFMAs
+// touch until an epilogue (dK/dV in the backward, O in the 64-row-per-
+// wavefront forward) live in AGPRs, while score MFMAs of the same kernel
+// write VGPRs that the VALU reads; the compiler gives all MFMAs of a kernel
+// one register file, so this one is written out.  Hazards: back-to-back
+// accumulation into the same AGPRs needs no wait states; any other access
+// to these AGPRs (zero fill, rescale, epilogue reads) is separated from the
+// MFMAs by agpr_hazard_pad().
+__device__ __forceinline__ void mfma_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+               : "+a"(acc)
+               : "v"(a), "v"(b));
+}
+// Wait states between an MFMA that writes AGPRs and an instruction that
+// reads them, or between a VALU write of AGPRs and an MFMA reading them as
+// C, with margin: three s_nop 7 give 24.
+__device__ __forceinline__ void agpr_hazard_pad() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
 }  // namespace fa
