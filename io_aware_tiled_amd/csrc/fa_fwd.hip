@@ -911,35 +911,57 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
 // ---------------------------------------------------------------------------
 // Launchers (argument validation happens in the C-ABI layer before these).
 
+namespace {
+
+template <int D, bool CAUSAL, bool KVLEN>
+void fwd_bf16_dispatch(bool pipe, bool two_blocks, dim3 grid, dim3 block,
+                       hipStream_t stream, const uint16_t* q,
+                       const uint16_t* k, const uint16_t* v,
+                       uint16_t* o, float* lse, const int32_t* kv_len, int H,
+                       int N, int n_qblk, float c) {
+  if constexpr (D == 64) {
+    if (pipe && two_blocks) {
+      hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 4, 2, CAUSAL, KVLEN>), grid,
+                         block, 0, stream, q, k, v, o, lse, kv_len, H, N,
+                         n_qblk, c);
+      return;
+    }
+  }
+  if (pipe)
+    hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 8, 1, CAUSAL, KVLEN>), grid,
+                       block, 0, stream, q, k, v, o, lse, kv_len, H, N, n_qblk,
+                       c);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, CAUSAL, KVLEN>), grid, block, 0,
+                       stream, q, k, v, o, lse, kv_len, H, N, n_qblk, c);
+}
+
+}  // namespace
+
 int launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const int32_t* kv_len, uint16_t* o, float* lse, int B,
                     int H, int N, int d, float scale, int causal,
                     hipStream_t stream) {
   // Grids with at least one 256-row workgroup per CU use the pipelined
-  // kernel: head dim 64 with 4 wavefronts of two 32-row blocks (two
-  // workgroups per CU), head dim 128 with 8 wavefronts of one block (its two
-  // blocks would not fit two wavefronts per SIMD).  Smaller grids use the
-  // plain kernel with 128-row workgroups, two per CU.
+  // kernel: head dim 64 with 4 wavefronts of two 32-row blocks when there
+  // are two such workgroups per CU (two resident per CU), else 8 wavefronts
+  // of one block (more wavefronts for a grid that fills the chip once);
+  // head dim 128 with 8 wavefronts of one block (its two blocks would not
+  // fit two wavefronts per SIMD).  Smaller grids use the plain kernel with
+  // 128-row workgroups, two per CU.
   constexpr int kCUs = 256;
   const long long grid256 = (long long)B * H * ((N + 255) / 256);
   const bool pipe = grid256 >= kCUs;
+  const bool two_blocks = d == 64 && grid256 >= 2 * kCUs;
   const int br = pipe ? 256 : 128;
   const int n_qblk = (N + br - 1) / br;
   const dim3 grid((unsigned)(B * H * n_qblk));
-  const dim3 block(pipe && d == 128 ? 512 : 256);
+  const dim3 block(pipe && !two_blocks ? 512 : 256);
   const float c = (float)((double)scale * 1.4426950408889634);
   const bool kv = kv_len != nullptr;
 #define FA_FWD_LAUNCH(DD, CC, KK)                                              \
-  do {                                                                         \
-    if (pipe)                                                                  \
-      hipLaunchKernelGGL((fwd_bf16_pipe_kernel<DD, DD == 64 ? 4 : 8,           \
-                                               DD == 64 ? 2 : 1, CC, KK>),     \
-                         grid, block, 0, stream, q, k, v, o, lse, kv_len, H,   \
-                         N, n_qblk, c);                                        \
-    else                                                                       \
-      hipLaunchKernelGGL((fwd_bf16_kernel<DD, 4, CC, KK>), grid, block, 0,     \
-                         stream, q, k, v, o, lse, kv_len, H, N, n_qblk, c);    \
-  } while (0)
+  fwd_bf16_dispatch<DD, CC, KK>(pipe, two_blocks, grid, block, stream, q, k,   \
+                                v, o, lse, kv_len, H, N, n_qblk, c)
   if (d == 64) {
     if (causal) {
       if (kv) FA_FWD_LAUNCH(64, true, true); else FA_FWD_LAUNCH(64, true, false);
