@@ -591,7 +591,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
 #pragma unroll
     for (int c = 0; c < NB; ++c) {
       asm volatile("" : "+v"(pb[xe][c][0]), "+v"(pb[xe][c][1]), "+v"(tsum[c]));
-      if (__any(tsum[c] > kSumLimit || m_ref[c] == -INFINITY)) {
+      if (__builtin_expect(__any(tsum[c] > kSumLimit || m_ref[c] == -INFINITY), 0)) {
         float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[xe][c][r]);
@@ -618,7 +618,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
     for (int c = 0; c < NB; ++c) {
       const bool need_mask =
           (CAUSAL && k0 + 31 > qlo[c]) || (k0 + 32 > kvlim);
-      if (need_mask) {
+      if (__builtin_expect(need_mask, 0)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 8 * (r / 4) + 4 * hh + (r % 4);
@@ -683,7 +683,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
       __syncthreads();
       load_k(min(j + 2, last));
       load_v(min(j + 1, last));
-      if (j < nt_w) {
+      if (__builtin_expect(j < nt_w, 1)) {
         // step 2j: S of (j, half 1) || P of (j, half 0); O += (j-1, half 1)
         step(std::integral_constant<int, 1>{}, st0, 1, stm, 1);
         settle(0);
