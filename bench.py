@@ -97,8 +97,17 @@ def cpu_baseline(w: S.Workload, inp: dict, target_s: float = 15.0) -> dict:
                     w.backward)
     pairs = visible_pairs(sw, kv)
     flops = pairs * w.d * (4 + (10 if w.backward else 0))
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": flops / t1 / 1e12, "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "blas_threads": cores,
             "sample": (f"fp64 numpy oracle, {'forward+backward' if w.backward else 'forward'}"
                        f" of batch 0, heads 0..{nh - 1} of {w.name} "
                        f"(N={w.N}, d={w.d}); {t1:.2f} s; {cores} threads "
@@ -199,6 +208,56 @@ def write_traffic(w: S.Workload, csvs, command, mib) -> int:
     return 0
 
 
+def summarize_counters(w: S.Workload, csvs, command) -> int:
+    """Per-kernel MFMA busy, executed MFMA FLOP, LDS bank conflicts and L2 hit
+    rate from two rocprofv3 --pmc collections of a bench run."""
+    vals = {}
+    for path in csvs:
+        import csv
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"]
+                key = None
+                for frag, k in KERNEL_KEYS:
+                    if "fa::" in name and frag in name:
+                        key = k
+                if key is None:
+                    continue
+                vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+    pairs = visible_pairs(w, None if w.kv_len_seed is None else
+                          S.make_inputs(w)["kv_len"])
+    alg = {"fwd": 4 * w.d * pairs, "bwd_dkdv": 8 * w.d * pairs,
+           "bwd_dq": 2 * w.d * pairs, "bwd_preprocess": 0}
+    n_xcd, n_simd = 8, 1024
+    md = os.path.join(PROFILES, f"counters_{w.name}.md")
+    with open(md, "w") as f:
+        f.write(f"# Hardware counters: {w.name} (B={w.B} H={w.H} N={w.N} d={w.d}, "
+                f"causal={w.causal})\n\nCommands (repository root, one MI355X):"
+                f"\n\n```\n{command}\n```\n\nPer dispatch (mean over the run's "
+                "dispatches).  Kernel cycles = GRBM_GUI_ACTIVE / 8 XCDs; MFMA busy = "
+                "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x kernel cycles); executed "
+                "MFMA FLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; LDS conflict rate = "
+                "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; L2 hit = TCC_HIT / (TCC_HIT + "
+                "TCC_MISS).\n\n| kernel | kernel cycles | MFMA busy | executed MFMA "
+                "GFLOP | algorithmic GFLOP | LDS bank-conflict cycles / LDS active | "
+                "L2 hit |\n|---|---|---|---|---|---|---|\n")
+        for k in sorted(vals):
+            v = {c: float(np.mean(x)) for c, x in vals[k].items()}
+            cyc = v.get("GRBM_GUI_ACTIVE", float("nan")) / n_xcd
+            busy = v.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (n_simd * cyc)
+            mops = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", float("nan")) * 512 / 1e9
+            lds = (v.get("SQ_LDS_BANK_CONFLICT", float("nan")) /
+                   max(v.get("SQ_LDS_IDX_ACTIVE", float("nan")), 1.0))
+            hit = v.get("TCC_HIT_sum", float("nan"))
+            miss = v.get("TCC_MISS_sum", float("nan"))
+            f.write(f"| {k} | {cyc:.0f} | {busy:.1%} | {mops:.1f} | "
+                    f"{alg.get(k, 0) / 1e9:.1f} | {lds:.3f} | "
+                    f"{hit / (hit + miss):.1%} |\n")
+    print(open(md).read())
+    return 0
+
+
 def summarize_trace(w: S.Workload, path, command) -> int:
     import csv
     with open(path) as f:
@@ -243,11 +302,19 @@ def main(argv=None) -> int:
                     help="no GPU work: write the libfa rows of a rocprofv3 "
                          "--kernel-trace --stats kernel_stats.csv to "
                          "profiles/kernels_<workload>.md")
+    ap.add_argument("--summarize-counters", nargs=2,
+                    metavar=("SQ_CSV", "TCC_CSV"),
+                    help="no GPU work: turn two rocprofv3 --pmc collections "
+                         "(SQ/GRBM counters, then TCC_HIT_sum TCC_MISS_sum) "
+                         "into profiles/counters_<workload>.md")
     ap.add_argument("--command", default="",
                     help="with --traffic-from / --summarize-trace: the "
                          "command that made the CSVs")
     args = ap.parse_args(argv)
 
+    if args.summarize_counters:
+        return summarize_counters(S.WORKLOADS[args.workload],
+                                  args.summarize_counters, args.command)
     if args.summarize_trace:
         return summarize_trace(S.WORKLOADS[args.workload], args.summarize_trace,
                                args.command)
