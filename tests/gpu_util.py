@@ -85,6 +85,14 @@ def oracle_fwd(inp: dict, rows=None, heads=None, workers=8):
                          workers=workers)
 
 
+def rel_err(abs_err: float, ref: np.ndarray) -> float:
+    """The pages' relative error, max|gpu - ref| / max|ref| (finite entries),
+    reported beside the absolute error that the tests gate on."""
+    r = np.asarray(ref, dtype=np.float64)
+    r = np.abs(r[np.isfinite(r)])
+    return abs_err / r.max() if r.size and r.max() > 0 else 0.0
+
+
 def report(name: str, **errs) -> None:
     print(f"[parity] {name}: " + ", ".join(f"{k}={v:.3e}" for k, v in errs.items()),
           flush=True)

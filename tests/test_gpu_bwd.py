@@ -5,7 +5,8 @@ import numpy as np
 import pytest
 
 import synthetic as S
-from gpu_util import (TOL_GRAD, host64, max_err, report, run_fwd, to_dev)
+from gpu_util import (TOL_GRAD, host64, max_err, rel_err, report, run_fwd,
+                      to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -28,10 +29,11 @@ def _check_bwd(name, inp, heads=None):
     ref = attention_bwd(sel(inp["q"]), sel(inp["k"]), sel(inp["v"]),
                         sel(inp["do"]), inp["scale"], inp["causal"],
                         workers=8)
-    errs = {}
+    errs, rels = {}, {}
     for nm, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
         errs[nm] = max_err(sel(host64(g)), r, f"{name} {nm}")
-    report(name, **errs)
+        rels[nm + "_rel"] = rel_err(errs[nm], r)
+    report(name, **errs, **rels)
     for nm, e in errs.items():
         assert e <= TOL_GRAD, (name, nm, e)
     return dq, dk, dv

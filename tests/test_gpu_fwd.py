@@ -10,7 +10,7 @@ import pytest
 
 import synthetic as S
 from gpu_util import (DEV, TOL_BF16_LSE, TOL_BF16_O, TOL_F32, host64,
-                      max_err, oracle_fwd, report, run_fwd)
+                      max_err, oracle_fwd, rel_err, report, run_fwd)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,7 +25,7 @@ def _check(name, inp, rows=None, heads=None):
         og, lg = og[:, :, rows], lg[:, :, rows]
     eo = max_err(og, oo, name + " O")
     el = max_err(lg, lo, name + " LSE")
-    report(name, O=eo, LSE=el)
+    report(name, O=eo, LSE=el, O_rel=rel_err(eo, oo), LSE_rel=rel_err(el, lo))
     if inp["dtype"] == "f32":
         assert eo <= TOL_F32 and el <= TOL_F32, (name, eo, el)
     else:
