@@ -108,18 +108,6 @@ __device__ __forceinline__ float sum_halves(float x) {
          __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
-// Workgroup index remap so that consecutive logical indices stay on one
-// XCD: the hardware deals workgroups round-robin over the 8 XCDs, so
-// physical id p runs on XCD p % 8.  Logical id = (p % 8) * per + p / 8 for
-// the full part of the grid; the remainder maps to itself.
-__device__ __forceinline__ int xcd_remap(int p, int n) {
-  constexpr int kXcd = 8;
-  const int per = n / kXcd;
-  const int full = per * kXcd;
-  if (p >= full) return p;
-  return (p % kXcd) * per + p / kXcd;
-}
-
 // MFMA accumulating into AGPRs.  Long-lived accumulators that only MFMAs
 // touch until an epilogue (dK/dV in the backward, O in the 64-row-per-
 // wavefront forward) live in AGPRs, while score MFMAs of the same kernel

@@ -20,19 +20,20 @@
 // wavefront owns a distinct slice of the query block and shares the K/V
 // tiles, so no reduction crosses wavefronts (item 3; [TW] "Flash Attention 2").
 //
-// gfx950 mapping (one workgroup = 4 or 8 wavefronts, 32 query rows each):
+// gfx950 mapping, shared by both bf16 kernels below (the 128-row kernel for
+// small grids, the software-pipelined 256-row kernel for large ones):
 //   * S^T = K_j Q_i^T on v_mfma_f32_32x32x16_bf16: the accumulator layout
 //     puts one query per lane (two lanes per query, one per half-wave), so
-//     the row max and row sum are in-lane reductions plus one exchange
-//     between half-waves.
+//     the row statistics are in-lane reductions plus one exchange between
+//     half-waves.
 //   * O^T += V_j^T P^T on the same instruction: the probabilities of the
 //     S^T accumulator are already the B operand (same lane, same key
 //     order), and V_j^T is read from the row-major LDS tile with
 //     ds_read_b64_tr_b16.
-//   * K/V tiles of 64 keys stream HBM -> registers -> LDS, double-buffered:
-//     the next tile's global loads are in flight while the current tile is
-//     computed.  LDS row strides are padded so the MFMA operand reads are
-//     free of bank conflicts.
+//   * K/V tiles of 64 keys stream HBM -> registers -> LDS; the next tile's
+//     global loads are in flight while the current tile is computed.  LDS
+//     row strides are padded so the MFMA operand reads are free of bank
+//     conflicts.
 //   * exp is exp2 with scale*log2(e) folded into one FMA per score.
 #include "fa_common.h"
 #include "fa_launch.h"
