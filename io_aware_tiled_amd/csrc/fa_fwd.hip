@@ -30,10 +30,10 @@
 //     S^T accumulator are already the B operand (same lane, same key
 //     order), and V_j^T is read from the row-major LDS tile with
 //     ds_read_b64_tr_b16.
-//   * K/V tiles of 64 keys stream HBM -> registers -> LDS; the next tile's
-//     global loads are in flight while the current tile is computed.  LDS
-//     row strides are padded so the MFMA operand reads are free of bank
-//     conflicts.
+//   * K/V tiles of 64 keys stream HBM -> registers -> LDS (HBM -> LDS by
+//     DMA for head dim 128 in the pipelined kernel); the next tiles' loads
+//     are in flight while the current tile is computed.  LDS row strides
+//     are padded so the MFMA operand reads are free of bank conflicts.
 //   * exp is exp2 with scale*log2(e) folded into one FMA per score.
 #include "fa_common.h"
 #include "fa_launch.h"
@@ -336,7 +336,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
 // through three stages each with one barrier per tile: a stage is
 // overwritten two barriers after its last read.  Tile loads are raw buffer
 // loads whose descriptor ends at the last key of the head, so keys past N
-// read as zero without per-lane selects.
+// read as zero without per-lane selects.  With head dim 128 and one block
+// per wavefront (one workgroup per CU, LDS to spare) the tiles go from HBM
+// straight into LDS by DMA, through four stages: tile j issues K_{j+3} and
+// V_{j+2}, so every transfer has a full tile of compute to land in.
 
 template <int D, int NW, int NB>
 struct PipeTile {
@@ -356,6 +359,35 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* p,
                                            0x00020000);
 }
 
+// s_waitcnt immediate: vmcnt(0) with the LDS and export counters left free.
+constexpr int kWaitVm0 = 0x0F70;
+
+// Byte offset of an LDS location (the 32-bit LDS address).
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One LDS DMA: each lane loads 16 bytes at voffset through the buffer
+// descriptor, and lane i's bytes land at LDS address lds + 16 i (out-of-range
+// lanes load zeros).  Written out rather than through the builtin so that
+// the compiler, which cannot tell the stage being filled from the stages
+// being read, does not wait for the transfer before every LDS read; callers
+// wait for it explicitly (vmcnt) before the barrier that publishes the
+// stage.  M0 carries the LDS base and is saved and restored around it.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs,
+                                          unsigned lds, unsigned voffset) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voffset), "s"(rs)
+      : "memory");
+}
+
 template <int D, int NW, int NB, bool CAUSAL, bool KVLEN>
 __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf16_pipe_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -363,8 +395,14 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
     float* __restrict__ LSE, const int32_t* __restrict__ kv_len, int H,
     int N, int n_qblk, float c_log2) {
   using T = PipeTile<D, NW, NB>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[3][T::KELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[3][T::VELEMS];
+  // Head dim 128 with one block per wavefront stages K and V by DMA
+  // through four LDS stages; the other shapes stage through registers with
+  // three (there the register path measured faster).
+  constexpr bool DMA = D == 128 && NB == 1;
+  constexpr int NS = DMA ? 4 : 3;
+  constexpr int LK = NS - 1, LV = NS - 2;   // DMA lookahead of K and V
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[NS][T::KELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[NS][T::VELEMS];
 
   const int BH = gridDim.x / n_qblk;
   int bh, qb;
@@ -420,6 +458,51 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
   // A zero scale becomes a tiny positive one: every visible weight is then
   // exp2(0) to fp32 precision and masked scores (-inf) still give 0.
   c_log2 = fmaxf(c_log2, 1e-30f);
+  // Q has arrived before any DMA is issued (a wait the compiler can see,
+  // so that it places none of its own inside the tile loop).
+  if constexpr (DMA) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+
+  // ---- DMA tile loads (global -> LDS): instruction u of wavefront w fills
+  // the 1 KB of the (padded) stage at 1024 (w + NW u), 16 bytes per lane;
+  // a lane whose 16 bytes are row padding reads out of range.
+  constexpr int KCR = T::KST / 8, VCR = T::VST / 8;     // 16-B slots per row
+  constexpr int KI = kBC * KCR / 64, VI = kBC * VCR / 64;
+  constexpr int KIW = (KI + NW - 1) / NW, VIW = (VI + NW - 1) / NW;
+  constexpr int kMinBatch = KI / NW + VI / NW;
+  constexpr unsigned kOut = 1u << 30;
+  static_assert(!DMA || (kMinBatch < 16 && T::KELEMS % 512 == 0 &&
+                         T::VELEMS % 512 == 0), "DMA layout");
+  unsigned dk_off[KIW], dv_off[VIW];
+#pragma unroll
+  for (int u = 0; u < KIW; ++u) {
+    const int p = 64 * (w + NW * u) + lane, row = p / KCR, c = p % KCR;
+    dk_off[u] = c < D / 8 ? (unsigned)((row * D + 8 * c) * 2) : kOut;
+  }
+#pragma unroll
+  for (int u = 0; u < VIW; ++u) {
+    const int p = 64 * (w + NW * u) + lane, row = p / VCR, c = p % VCR;
+    dv_off[u] = c < D / 8 ? (unsigned)((row * D + 8 * c) * 2) : kOut;
+  }
+  const unsigned lds_k0 = lds_addr(&lds_k[0][0]);
+  const unsigned lds_v0 = lds_addr(&lds_v[0][0]);
+  auto dma_k = [&](int j, int st) {
+    const int k0 = j * kBC;
+    const auto rs = tile_rsrc(Kh + (size_t)k0 * D, min(N - k0, kBC) * D * 2);
+    const unsigned base = lds_k0 + (unsigned)(st * T::KELEMS * 2);
+#pragma unroll
+    for (int u = 0; u < KIW; ++u)
+      if (KI % NW == 0 || w + NW * u < KI)
+        lds_dma16(rs, base + 1024u * (w + NW * u), dk_off[u]);
+  };
+  auto dma_v = [&](int j, int st) {
+    const int k0 = j * kBC;
+    const auto rs = tile_rsrc(Vh + (size_t)k0 * D, min(N - k0, kBC) * D * 2);
+    const unsigned base = lds_v0 + (unsigned)(st * T::VELEMS * 2);
+#pragma unroll
+    for (int u = 0; u < VIW; ++u)
+      if (VI % NW == 0 || w + NW * u < VI)
+        lds_dma16(rs, base + 1024u * (w + NW * u), dv_off[u]);
+  };
 
   // ---- tile loads: thread chunk r covers row (tid + 256r) / (D/8).
   unsigned voff[T::CPT];
@@ -645,7 +728,65 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
     }
   };
 
-  if (ntiles > 0) {
+  if (DMA && ntiles > 0) {
+    const int last = ntiles - 1;
+    // Stages: K_j and V_j in stage j % NS.  Tile j waits for K_{j+1} and
+    // V_j, then issues K_{j+NS-1} and V_{j+NS-2}.
+    dma_k(0, 0);
+    if (last >= 1) dma_k(1, 1);
+    dma_v(0, 0);
+    for (int e = tid; e < T::VELEMS / 8; e += T::THREADS)
+      *(u32x4*)(&lds_v[NS - 1][8 * e]) = u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int c = 0; c < NB; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) pb[x][c][h] = bf16x8{};
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if constexpr (NS == 4) {
+      if (last >= 2) dma_k(2, 2);
+      if (last >= 1) dma_v(1, 1);
+    }
+    if (nt_w > 0) {
+#pragma unroll
+      for (int c = 0; c < NB; ++c) {
+        s[0][c] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+          s[0][c] = mfma32x16(*(const bf16x8*)(&lds_k[0][lq * T::KST + 8 * hh + 16 * kk]),
+                              qf[c][kk], s[0][c]);
+      }
+      mask_half(0, 0, 0);
+    }
+    // Tile j: wait for K_{j+1} and V_j, barrier, issue the next DMAs.  No
+    // fence: LDS is only read in the loop, and every read of a stage has
+    // returned before its wavefront reaches the barrier after which the
+    // stage is refilled.
+    auto top = [&](int j) {
+      if (NS == 4 && j + 2 <= last)
+        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kMinBatch) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (j + LK <= last) dma_k(j + LK, (j + LK) % NS);
+      if (j + LV <= last) dma_v(j + LV, (j + LV) % NS);
+    };
+    for (int j = 0; j < nt_w; ++j) {
+      top(j);
+      const int st0 = j % NS, st1 = (j + 1) % NS, stm = (j + NS - 1) % NS;
+      step(std::integral_constant<int, 1>{}, st0, 1, stm, 1);
+      settle(0);
+      mask_half(1, j, 1);
+      step(std::integral_constant<int, 0>{}, st1, 0, st0, 0);
+      settle(1);
+      if (j + 1 < nt_w) mask_half(0, j + 1, 0);
+    }
+    if (nt_w > 0) pv_only(1, (nt_w - 1) % NS, 1);
+    for (int j = nt_w; j < ntiles; ++j) top(j);
+  } else if (ntiles > 0) {
     const int last = ntiles - 1;
     // Prologue: K_0 in stage 0, zeros in V stage 2 (the V_{-1} that the
     // first step multiplies by P = 0), S_0 (half 0 of tile 0) and its mask;
