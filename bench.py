@@ -225,6 +225,9 @@ def summarize_counters(w: S.Workload, csvs, command) -> int:
                     continue
                 vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(
                     float(r["Counter_Value"]))
+                if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                    vals[key].setdefault("_ns", []).append(
+                        float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
     pairs = visible_pairs(w, None if w.kv_len_seed is None else
                           S.make_inputs(w)["kv_len"])
     alg = {"fwd": 4 * w.d * pairs, "bwd_dkdv": 8 * w.d * pairs,
@@ -239,9 +242,11 @@ def summarize_counters(w: S.Workload, csvs, command) -> int:
                 "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x kernel cycles); executed "
                 "MFMA FLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; LDS conflict rate = "
                 "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; L2 hit = TCC_HIT / (TCC_HIT + "
-                "TCC_MISS).\n\n| kernel | kernel cycles | MFMA busy | executed MFMA "
+                "TCC_MISS); clock = kernel cycles / dispatch duration (the clock "
+                "the chip held during the kernel).\n\n| kernel | kernel cycles | "
+                "clock | MFMA busy | executed MFMA "
                 "GFLOP | algorithmic GFLOP | LDS bank-conflict cycles / LDS active | "
-                "L2 hit |\n|---|---|---|---|---|---|---|\n")
+                "L2 hit |\n|---|---|---|---|---|---|---|---|\n")
         for k in sorted(vals):
             v = {c: float(np.mean(x)) for c, x in vals[k].items()}
             cyc = v.get("GRBM_GUI_ACTIVE", float("nan")) / n_xcd
@@ -251,9 +256,85 @@ def summarize_counters(w: S.Workload, csvs, command) -> int:
                    max(v.get("SQ_LDS_IDX_ACTIVE", float("nan")), 1.0))
             hit = v.get("TCC_HIT_sum", float("nan"))
             miss = v.get("TCC_MISS_sum", float("nan"))
-            f.write(f"| {k} | {cyc:.0f} | {busy:.1%} | {mops:.1f} | "
+            ghz = cyc / v["_ns"] if "_ns" in v else float("nan")
+            f.write(f"| {k} | {cyc:.0f} | {ghz:.2f} GHz | {busy:.1%} | {mops:.1f} | "
                     f"{alg.get(k, 0) / 1e9:.1f} | {lds:.3f} | "
                     f"{hit / (hit + miss):.1%} |\n")
+    print(open(md).read())
+    return 0
+
+
+def mfma_ceiling(dev, n: int = 8192, iters: int = 20) -> dict:
+    """Sustained bf16 matrix-core rate of a vendor GEMM (torch.matmul, n^3)
+    on iid N(0,1) operands and on constant operands.  The chip's clock under
+    matrix-core load depends on how much the operand bits toggle, so the
+    random-operand rate, not the published peak, is what a kernel on real
+    data can reach; the constant-operand rate shows the published peak's
+    clock."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(0)
+    out = {"gemm": f"torch.matmul bf16 {n}x{n}x{n}", "iters": iters}
+    for kind in ("random", "constant"):
+        if kind == "random":
+            a = torch.randn(n, n, generator=g, device=dev).to(torch.bfloat16)
+            b = torch.randn(n, n, generator=g, device=dev).to(torch.bfloat16)
+        else:
+            a = torch.full((n, n), 1.0, device=dev, dtype=torch.bfloat16)
+            b = torch.full((n, n), 1.0 / 1024, device=dev, dtype=torch.bfloat16)
+        c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+        e0.record()
+        for _ in range(iters):
+            torch.matmul(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        out[f"{kind}_tflops"] = round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+        del a, b, c
+    return out
+
+
+def summarize_ceiling(path, command) -> int:
+    """profiles/mfma_ceiling.md from a rocprofv3 --pmc GRBM_GUI_ACTIVE
+    SQ_VALU_MFMA_BUSY_CYCLES collection of a --ceiling-only run: duration,
+    held clock and matrix-core busy of the GEMM dispatches, random operands
+    (the first half, in dispatch order) versus constant ones."""
+    import csv
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = per.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+            d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    total = {}
+    for d in per.values():
+        total[d["name"]] = total.get(d["name"], 0.0) + d["ns"]
+    gemm = max(total, key=total.get)
+    ids = sorted(i for i, d in per.items() if d["name"] == gemm)
+    half = len(ids) // 2
+    n = 8192
+    md = os.path.join(PROFILES, "mfma_ceiling.md")
+    with open(md, "w") as f:
+        f.write("# Matrix-core rate a kernel can sustain on real data\n\n"
+                "Command (repository root, one MI355X):\n\n```\n"
+                f"{command}\n```\n\nThe vendor bf16 GEMM (torch.matmul, "
+                f"{n}^3, {len(ids)} dispatches of `{gemm[:60]}`) first on iid "
+                "N(0,1) operands, then on constant operands.  Clock = "
+                "GRBM_GUI_ACTIVE / 8 XCDs / dispatch duration; MFMA busy = "
+                "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles).\n\n"
+                "| operands | dispatches | mean duration | TFLOP/s | clock | "
+                "MFMA busy |\n|---|---|---|---|---|---|\n")
+        for label, sel in (("iid N(0,1)", ids[:half]), ("constant", ids[half:])):
+            ns = float(np.mean([per[i]["ns"] for i in sel]))
+            cyc = float(np.mean([per[i]["GRBM_GUI_ACTIVE"] for i in sel])) / 8
+            busy = float(np.mean([per[i]["SQ_VALU_MFMA_BUSY_CYCLES"]
+                                  for i in sel])) / (1024 * cyc)
+            f.write(f"| {label} | {len(sel)} | {ns / 1e3:.1f} us | "
+                    f"{2.0 * n ** 3 / ns / 1e3:.0f} | {cyc / ns:.2f} GHz | "
+                    f"{busy:.1%} |\n")
     print(open(md).read())
     return 0
 
@@ -307,11 +388,22 @@ def main(argv=None) -> int:
                     help="no GPU work: turn two rocprofv3 --pmc collections "
                          "(SQ/GRBM counters, then TCC_HIT_sum TCC_MISS_sum) "
                          "into profiles/counters_<workload>.md")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the vendor-GEMM matrix-core calibration")
+    ap.add_argument("--ceiling-only", action="store_true",
+                    help="run only the vendor-GEMM calibration (random, then "
+                         "constant operands) and print it")
+    ap.add_argument("--summarize-ceiling", metavar="PMC_CSV",
+                    help="no GPU work: write profiles/mfma_ceiling.md from a "
+                         "rocprofv3 --pmc GRBM_GUI_ACTIVE "
+                         "SQ_VALU_MFMA_BUSY_CYCLES run of --ceiling-only")
     ap.add_argument("--command", default="",
                     help="with --traffic-from / --summarize-trace: the "
                          "command that made the CSVs")
     args = ap.parse_args(argv)
 
+    if args.summarize_ceiling:
+        return summarize_ceiling(args.summarize_ceiling, args.command)
     if args.summarize_counters:
         return summarize_counters(S.WORKLOADS[args.workload],
                                   args.summarize_counters, args.command)
@@ -337,6 +429,9 @@ def main(argv=None) -> int:
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         return 1
     dev = torch.device("cuda:0")
+    if args.ceiling_only:
+        print(json.dumps(mfma_ceiling(dev)), flush=True)
+        return 0
     w = S.WORKLOADS[args.workload]
     log(f"[bench] generating {w.name} inputs")
     inp = S.make_inputs(w)
@@ -444,6 +539,12 @@ def main(argv=None) -> int:
         check["grads_finite"] = bool(all(torch.isfinite(t.float()).all()
                                          for t in (dq, dk, dv)))
 
+    ceiling = None
+    if not args.no_ceiling and w.dtype == "bf16":
+        log("[bench] vendor GEMM calibration of the matrix-core rate")
+        ceiling = mfma_ceiling(dev)
+        ceiling["frac_of_random"] = round(achieved / ceiling["random_tflops"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on a sample (cpu_baseline)")
@@ -464,6 +565,7 @@ def main(argv=None) -> int:
         "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},
         "fwd_tflops": round(fwd_flops / (per_kernel["fwd"] * 1e-3) / 1e12, 2),
         "roofline": roofline,
+        "mfma_ceiling": ceiling,
         "cpu_baseline": cpu,
         "sanity": check,
     }
