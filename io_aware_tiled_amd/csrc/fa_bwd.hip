@@ -560,7 +560,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t bwd_rsrc(const uint16_t* p,
 //   phase 1:  A_1(i), B_1(i-1)  ||  V_0(i)
 //   phase 2:  B_0(i), A_0(i+1)  ||  V_1(i)
 // Tile i is read from iteration i-1 to i+1, so query tiles rotate through
-// four LDS stages with one barrier per tile.
+// four LDS stages with one barrier per tile.  Q and dO tiles go from HBM
+// straight into LDS by DMA, issued two tiles ahead; LSE and D (64 floats
+// each, transformed on the way) pass through wavefront 0's registers.
 constexpr int kKvPBK = 128;
 
 template <bool CAUSAL>
@@ -573,7 +575,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
   constexpr int D = kD;
   constexpr int QE = kBQ2 * kRS;                 // elements per tile stage
   constexpr int THREADS = 256;
-  constexpr int CPT = kBQ2 * D / 8 / THREADS;    // 16-byte chunks per thread
   __shared__ __attribute__((aligned(16))) uint16_t lds_q[4][QE];
   __shared__ __attribute__((aligned(16))) uint16_t lds_g[4][QE];   // dO
   __shared__ __attribute__((aligned(16))) float lds_lse[4][kBQ2];
@@ -623,47 +624,59 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
   const int n_qt = (N + kBQ2 - 1) / kBQ2;
   const int it0 = CAUSAL ? kb0 / kBQ2 : 0;
 
-  // ---- query-tile staging (buffer loads: rows past N read as zero).
-  unsigned voff[CPT];
-  int lds_off[CPT];
+  // The K and V fragments have arrived before any DMA is issued (a wait
+  // the compiler can see, so that it places none of its own inside the
+  // tile loop).
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+
+  // ---- query-tile staging.  Q and dO: DMA instruction u of wavefront w
+  // fills the 1 KB of the (padded) stage at 1024 (w + 4u), 16 bytes per
+  // lane; lanes on row padding, and rows past N, read zeros.
+  constexpr int RCH = kRS / 8;                       // 16-B slots per row
+  constexpr int TI = kBQ2 * RCH / 64;                // DMA instructions per tile
+  constexpr int TIW = (TI + 3) / 4;
+  static_assert(QE % 512 == 0, "tile stage must be whole 1 KB blocks");
+  unsigned toff[TIW];
 #pragma unroll
-  for (int r = 0; r < CPT; ++r) {
-    const int cidx = tid + THREADS * r;
-    const int row = cidx / (D / 8);
-    const int col = 8 * (cidx % (D / 8));
-    voff[r] = (unsigned)((row * D + col) * 2);
-    lds_off[r] = row * kRS + col;
+  for (int u = 0; u < TIW; ++u) {
+    const int p = 64 * (w + 4 * u) + lane, row = p / RCH, c = p % RCH;
+    toff[u] = c < D / 8 ? (unsigned)((row * D + 8 * c) * 2) : (1u << 30);
   }
-  u32x4 qreg[CPT], greg[CPT];
-  float lse_r = INFINITY, d_r = 0.f;
-  auto load_tile = [&](int it) {
+  const unsigned lds_q0 = lds_addr(&lds_q[0][0]);
+  const unsigned lds_g0 = lds_addr(&lds_g[0][0]);
+  float lse_r = 0.f, d_r = 0.f;
+  int stats_q = 0;
+  auto dma_tile = [&](int it, int st) {
     const int qt0 = it * kBQ2;
     const int bytes = min(N - qt0, kBQ2) * D * 2;
     const auto rq = bwd_rsrc(Qh + (size_t)qt0 * D, bytes);
     const auto rg = bwd_rsrc(dOh + (size_t)qt0 * D, bytes);
+    const unsigned off = (unsigned)(st * QE * 2);
 #pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      qreg[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, voff[r], 0, 0));
-      greg[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, voff[r], 0, 0));
+    for (int u = 0; u < TIW; ++u)
+      if (TI % 4 == 0 || w + 4 * u < TI) {
+        lds_dma16(rq, lds_q0 + off + 1024u * (w + 4 * u), toff[u]);
+        lds_dma16(rg, lds_g0 + off + 1024u * (w + 4 * u), toff[u]);
+      }
+  };
+  // LSE and D of a tile: loaded raw one iteration ahead, turned into the
+  // per-row exponent offset at the store (so no wait falls mid-tile).
+  auto load_stats = [&](int it) {
+    if (w == 0) {
+      stats_q = it * kBQ2 + lane;
+      const int q = max(min(stats_q, N - 1), 0);
+      lse_r = LSEh[q];
+      d_r = Dh[q];
     }
+  };
+  auto store_stats = [&](int st) {
     if (w == 0) {
       // Rows past N (and rows without any visible key) get +inf, so that
       // exp2(s - lse) = 0 for every key.
-      const int q = qt0 + lane;
-      const float l = q < N ? LSEh[min(q, N - 1)] : INFINITY;
-      lse_r = (l == -INFINITY) ? INFINITY : l * kLog2e;
-      d_r = q < N ? Dh[min(q, N - 1)] : 0.f;
-    }
-  };
-  auto store_tile = [&](int st) {
-#pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      *(u32x4*)(&lds_q[st][lds_off[r]]) = qreg[r];
-      *(u32x4*)(&lds_g[st][lds_off[r]]) = greg[r];
-    }
-    if (w == 0) {
-      lds_lse[st][lane] = lse_r;
-      lds_d[st][lane] = d_r;
+      const bool in = stats_q < N;
+      const float l = in ? lse_r : INFINITY;
+      lds_lse[st][lane] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+      lds_d[st][lane] = in ? d_r : 0.f;
     }
   };
 
@@ -796,17 +809,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
 
   if (it0 < n_qt) {
     const int last = n_qt - 1;
-    // Prologue: tile it0 in stage 0; zeros in stage 3 (the tile before it0,
-    // whose block 1 the first phase multiplies by P = dS = 0); A_0(it0).
-    load_tile(it0);
-    store_tile(0);
-#pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      qreg[r] = u32x4{0, 0, 0, 0};
-      greg[r] = u32x4{0, 0, 0, 0};
+    // Prologue: tile it0 in stage 0, tile it0+1 in stage 1 (its LSE / D in
+    // registers); zeros in stage 3 (the tile before it0, whose block 1 the
+    // first phase multiplies by P = dS = 0); A_0(it0).
+    dma_tile(it0, 0);
+    if (it0 + 1 <= last) dma_tile(it0 + 1, 1);
+    load_stats(it0);
+    store_stats(0);
+    load_stats(min(it0 + 1, last));
+    for (int e = tid; e < QE / 8; e += THREADS) {
+      *(u32x4*)(&lds_q[3][8 * e]) = u32x4{0, 0, 0, 0};
+      *(u32x4*)(&lds_g[3][8 * e]) = u32x4{0, 0, 0, 0};
     }
-    store_tile(3);
-    load_tile(min(it0 + 1, last));
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -814,6 +828,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
         pb[c][h] = bf16x8{};
         dsb[c][h] = bf16x8{};
       }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
@@ -824,13 +839,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
     mask_block(0, it0);
     agpr_hazard_pad();   // zero-filled accumulators -> first MFMA
 
-    // Tile i in stage (i - it0) % 4.  Iteration i stores tile i+1, then
-    // loads tile i+2.
+    // Tile i in stage (i - it0) % 4.  Iteration i publishes tile i+1 (its
+    // DMA has landed, its LSE / D are stored), then issues tile i+2 into the
+    // stage of tile i-2, last read in iteration i-1.
     int sp = 3, s0 = 0, s1 = 1;   // stages of tiles i-1, i, i+1
     for (int it = it0; it < n_qt; ++it) {
-      store_tile(s1);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      store_stats(s1);
       __syncthreads();
-      load_tile(min(it + 2, last));
+      if (it + 2 <= last) dma_tile(it + 2, (s1 + 1) & 3);
+      load_stats(min(it + 2, last));
       // phase 1: A_1(i), B_1(i-1) || V_0(i)
       phase(std::false_type{}, s0, 1, sp, 1, s0, 0);
       mask_block(1, it);

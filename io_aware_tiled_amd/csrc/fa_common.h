@@ -128,4 +128,33 @@ __device__ __forceinline__ void agpr_hazard_pad() {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
+// s_waitcnt immediate: vmcnt(0) with the LDS and export counters left free.
+constexpr int kWaitVm0 = 0x0F70;
+
+// Byte offset of an LDS location (the 32-bit LDS address).
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One LDS DMA: each lane loads 16 bytes at voffset through the buffer
+// descriptor, and lane i's bytes land at LDS address lds + 16 i (out-of-range
+// lanes load zeros).  Written out rather than through the builtin so that
+// the compiler, which cannot tell the stage being filled from the stages
+// being read, does not wait for the transfer before every LDS read; callers
+// wait for it explicitly (vmcnt) before the barrier that publishes the
+// stage.  M0 carries the LDS base and is saved and restored around it.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs,
+                                          unsigned lds, unsigned voffset) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voffset), "s"(rs)
+      : "memory");
+}
+
 }  // namespace fa
