@@ -892,9 +892,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
 //   VALU forms P_t = exp2(c S^T_t - lse) and dS^T_t = P_t (dP^T_t - D),
 //   then dQ^T += K_t^T dS^T_t,
 // with MFMAs and VALU work interleaved one by one in issue order.  K and V
-// tile j are read in tiles j-1 and j, so they rotate through three LDS
-// stages with one barrier per tile.  Tile loads are raw buffer loads whose
-// descriptor ends at the head's last key: keys past N read as zero.
+// tile j are read in tiles j-1 and j; they go from HBM straight into LDS by
+// DMA, issued three tiles ahead into four stages (one barrier per tile).
+// The DMA descriptor ends at the head's last key: keys past N read as zero.
 constexpr int kDqPBR = 256;
 
 template <bool CAUSAL>
@@ -907,9 +907,9 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
   constexpr int D = kD;
   constexpr int TE = kDqBC * kRS;                 // elements per tile stage
   constexpr int THREADS = 512;
-  constexpr int CPT = kDqBC * D / 8 / THREADS;    // 16-byte chunks per thread
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[3][TE];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[3][TE];
+  constexpr int NW = THREADS / 64;
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[4][TE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[4][TE];
 
   const int BH = gridDim.x / n_qblk;
   int bh, qb;
@@ -969,34 +969,39 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
     dd = Dv[(size_t)bh * N + qrow];
   }
 
-  unsigned voff[CPT];
-  int lds_off[CPT];
+  // Every register operand has arrived before any DMA is issued (a wait
+  // the compiler can see, so that it places none of its own inside the
+  // tile loop).
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+
+  // ---- K/V tile DMA: instruction u of wavefront w fills the 1 KB of the
+  // (padded) stage at 1024 (w + NW u), 16 bytes per lane; lanes on row
+  // padding, and keys past N, read zeros.
+  constexpr int RCH = kRS / 8;                       // 16-B slots per row
+  constexpr int TI = kDqBC * RCH / 64;               // DMA instructions per tile
+  constexpr int TIW = (TI + NW - 1) / NW;
+  constexpr int kMinBatch = 2 * (TI / NW);           // fewest a wave issues per tile
+  static_assert(TE % 512 == 0 && kMinBatch < 16, "DMA tile layout");
+  unsigned toff[TIW];
 #pragma unroll
-  for (int r = 0; r < CPT; ++r) {
-    const int cidx = tid + THREADS * r;
-    const int row = cidx / (D / 8);
-    const int col = 8 * (cidx % (D / 8));
-    voff[r] = (unsigned)((row * D + col) * 2);
-    lds_off[r] = row * kRS + col;
+  for (int u = 0; u < TIW; ++u) {
+    const int p = 64 * (w + NW * u) + lane, row = p / RCH, c = p % RCH;
+    toff[u] = c < D / 8 ? (unsigned)((row * D + 8 * c) * 2) : (1u << 30);
   }
-  u32x4 kreg[CPT], vreg[CPT];
-  auto load_kv = [&](int j) {
+  const unsigned lds_k0 = lds_addr(&lds_k[0][0]);
+  const unsigned lds_v0 = lds_addr(&lds_v[0][0]);
+  auto dma_kv = [&](int j, int st) {
     const int k0 = j * kDqBC;
     const int bytes = min(N - k0, kDqBC) * D * 2;
     const auto rk = bwd_rsrc(Kh + (size_t)k0 * D, bytes);
     const auto rv = bwd_rsrc(Vh + (size_t)k0 * D, bytes);
+    const unsigned off = (unsigned)(st * TE * 2);
 #pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      kreg[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff[r], 0, 0));
-      vreg[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[r], 0, 0));
-    }
-  };
-  auto store_kv = [&](int st) {
-#pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      *(u32x4*)(&lds_k[st][lds_off[r]]) = kreg[r];
-      *(u32x4*)(&lds_v[st][lds_off[r]]) = vreg[r];
-    }
+    for (int u = 0; u < TIW; ++u)
+      if (TI % NW == 0 || w + NW * u < TI) {
+        lds_dma16(rk, lds_k0 + off + 1024u * (w + NW * u), toff[u]);
+        lds_dma16(rv, lds_v0 + off + 1024u * (w + NW * u), toff[u]);
+      }
   };
 
   f32x16 dq_acc[D / 32];
@@ -1081,12 +1086,13 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
 
   if (ntiles > 0) {
     const int last = ntiles - 1;
-    // Prologue: K_0, V_0 in stage 0; S^T, dP^T of half-tile (0, 0); K_1, V_1
-    // in registers for tile 0's stores.
-    load_kv(0);
-    store_kv(0);
-    load_kv(min(1, last));
+    // Prologue: K_0, V_0 in stage 0, K_1, V_1 in stage 1, then K_2, V_2
+    // issued; S^T, dP^T of half-tile (0, 0).
+    dma_kv(0, 0);
+    if (last >= 1) dma_kv(1, 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (last >= 2) dma_kv(2, 2);
     if (nt_w > 0) {
       s[0] = f32x16{};
       dp[0] = f32x16{};
@@ -1098,13 +1104,20 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
       }
       mask_half(0, 0, 0);
     }
-    // K_j, V_j in stage j % 3.  Tile j stores K_{j+1}, V_{j+1}, then loads
-    // K_{j+2}, V_{j+2}.
-    int st0 = 0, st1 = 1;
+    // K_j, V_j in stage j % 4.  Tile j waits for K_{j+1}, V_{j+1} (issued
+    // two tiles earlier), then issues K_{j+3}, V_{j+3} into the stage of
+    // tile j-1.  No fence at the barrier: LDS is only read in the loop, and
+    // every read of a stage has returned before its wavefront reaches the
+    // barrier after which the stage is refilled.
     for (int j = 0; j < ntiles; ++j) {
-      store_kv(st1);
-      __syncthreads();
-      load_kv(min(j + 2, last));
+      if (j + 2 <= last)
+        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kMinBatch) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (j + 3 <= last) dma_kv(j + 3, (j + 3) & 3);
+      const int st0 = j & 3, st1 = (j + 1) & 3;
       if (j < nt_w) {
         // step 2j: S^T, dP^T of (j, 1) || dS of (j, 0), dQ += (j, 0)
         step(std::integral_constant<int, 1>{}, st0, 1, st0, 0);
@@ -1113,8 +1126,6 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
         step(std::integral_constant<int, 0>{}, st1, 0, st0, 1);
         if (j + 1 < nt_w) mask_half(0, j + 1, 0);
       }
-      st0 = st1;
-      st1 = st1 == 2 ? 0 : st1 + 1;
     }
   }
 
