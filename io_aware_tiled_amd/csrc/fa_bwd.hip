@@ -676,7 +676,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
       const bool in = stats_q < N;
       const float l = in ? lse_r : INFINITY;
       lds_lse[st][lane] = (l == -INFINITY) ? INFINITY : l * kLog2e;
-      lds_d[st][lane] = in ? d_r : 0.f;
+      lds_d[st][lane] = in ? -d_r : 0.f;   // -D: the dP accumulators start there
     }
   };
 
@@ -719,13 +719,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
     bf16x8 op[kPf];
 #pragma unroll
     for (int i = 0; i < kPf; ++i) op[i] = fetch(i);
-    // LSE / D of the lane's 16 rows of block cv: register r <-> row
-    // 32 cv + 8 (r / 4) + 4 hh + r % 4.
-    f32x4 l4[4], d4[4];
+    // LSE of the lane's 16 rows of block cv, -D of those of block ca:
+    // register r <-> row 32 c + 8 (r / 4) + 4 hh + r % 4.  dP accumulates
+    // onto -D, so the VALU forms dS = P (dP - D) with one product.
+    f32x4 l4[4];
+    f32x16 negd;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       l4[g] = *(const f32x4*)(&lds_lse[stv][32 * cv + 8 * g + 4 * hh]);
-      d4[g] = *(const f32x4*)(&lds_d[stv][32 * cv + 8 * g + 4 * hh]);
+      const f32x4 nd = *(const f32x4*)(&lds_d[sta][32 * ca + 8 * g + 4 * hh]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) negd[4 * g + e] = nd[e];
     }
     // VALU: 16 elements as a three-stage pipeline over the MFMA slots
     // (FMA, then exp2, then dS and, per 8 elements, the bf16 conversions).
@@ -741,7 +745,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
         if (ai % 2 == 0)
           s[ca] = mfma32x16(a, kf[kk], kk == 0 ? f32x16{} : s[ca]);
         else
-          dp[ca] = mfma32x16(a, vf[kk], kk == 0 ? f32x16{} : dp[ca]);
+          dp[ca] = mfma32x16(a, vf[kk], kk == 0 ? negd : dp[ca]);
       } else {
         const int bi = BF ? m : m - kA;
         const int which = bi / (kB / 2);
@@ -755,7 +759,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
       if (m >= 1 && m - 1 < 16) pe[m - 1] = __builtin_amdgcn_exp2f(x[m - 1]);
       if (m >= 2 && m - 2 < 16) {
         const int el = m - 2;
-        dsv[el] = pe[el] * (dp[cv][el] - d4[el / 4][el % 4]);
+        dsv[el] = pe[el] * dp[cv][el];
         if (el % 8 == 7) {
           f32x8 vp, vd;
 #pragma unroll
@@ -830,11 +834,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
       }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
+    f32x16 negd0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 nd = *(const f32x4*)(&lds_d[0][8 * g + 4 * hh]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) negd0[4 * g + e] = nd[e];
+    }
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       const int o = l32 * kRS + 16 * kk + 8 * hh;
       s[0] = mfma32x16(*(const bf16x8*)(&lds_q[0][o]), kf[kk], kk == 0 ? f32x16{} : s[0]);
-      dp[0] = mfma32x16(*(const bf16x8*)(&lds_g[0][o]), vf[kk], kk == 0 ? f32x16{} : dp[0]);
+      dp[0] = mfma32x16(*(const bf16x8*)(&lds_g[0][o]), vf[kk], kk == 0 ? negd0 : dp[0]);
     }
     mask_block(0, it0);
     agpr_hazard_pad();   // zero-filled accumulators -> first MFMA
@@ -968,6 +979,11 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
     lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
     dd = Dv[(size_t)bh * N + qrow];
   }
+  // dP^T accumulates onto -D (one query per lane), so the VALU forms
+  // dS = P (dP - D) with one product.
+  f32x16 negd;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negd[r] = -dd;
 
   // Every register operand has arrived before any DMA is issued (a wait
   // the compiler can see, so that it places none of its own inside the
@@ -1047,7 +1063,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
         s[XS] = mfma32x16(a, qf[m], m == 0 ? f32x16{} : s[XS]);
       } else if (m < 2 * kS) {
         const int kk = m - kS;
-        dp[XS] = mfma32x16(a, gf[kk], kk == 0 ? f32x16{} : dp[XS]);
+        dp[XS] = mfma32x16(a, gf[kk], kk == 0 ? negd : dp[XS]);
       } else {
         // Half 0 of dS^T (converted in slot 9) feeds the first D/32 of
         // these MFMAs, half 1 (converted in slot 17) the last D/32, which
@@ -1059,7 +1075,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
       if (m >= 1 && m - 1 < 16) pe[m - 1] = __builtin_amdgcn_exp2f(x[m - 1]);
       if (m >= 2 && m - 2 < 16) {
         const int el = m - 2;
-        dsv[el] = pe[el] * (dp[XE][el] - dd);
+        dsv[el] = pe[el] * dp[XE][el];
         if (el % 8 == 7) {
           f32x8 v;
 #pragma unroll
@@ -1095,7 +1111,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
     if (last >= 2) dma_kv(2, 2);
     if (nt_w > 0) {
       s[0] = f32x16{};
-      dp[0] = f32x16{};
+      dp[0] = negd;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         const int o = lq * kRS + 8 * hh + 16 * kk;
