@@ -30,6 +30,12 @@ Readings where the pages are silent (each also listed in the design notes):
   * The stored statistic is the natural-log log-sum-exp LSE_i = m_i + ln l_i
     ([TW] "Flash Attention 2": FA2 stores L instead of m and l).
   * A row with no visible key gives O = 0 and LSE = -inf.
+  * Block-sparse attention ([ZN] "Overview": block-sparse FlashAttention
+    skips whole blocks of the score matrix by a fixed block mask; the page
+    gives no further detail) is read as the definition restricted by a
+    boolean block mask M [H, ceil(N/bq), ceil(N/bk)]: key j is also required
+    to satisfy M[h, i // bq, j // bk] for query i of head h, for every batch
+    entry.  bq = 128 query rows and bk = 64 keys unless given.
   * Backward: the pages give no formulas, only that P is recomputed from the
     stored statistics ([MM] "Backward pass: recompute instead of store";
     [TW] "Recomputation").  The oracle is the analytic gradient of
@@ -52,11 +58,13 @@ __all__ = ["attention_fwd", "attention_bwd", "attention_probs",
 
 
 def visible_mask(r0: int, r1: int, n_keys: int, causal: bool,
-                 kv_len_b: int | None, rows: np.ndarray | None = None
-                 ) -> np.ndarray:
+                 kv_len_b: int | None, rows: np.ndarray | None = None,
+                 block_mask: np.ndarray | None = None, bq: int = 128,
+                 bk: int = 64) -> np.ndarray:
     """Boolean [rows, n_keys]: True where key j is visible to query i.
 
-    Query indices are r0..r1-1, or `rows` when given.
+    Query indices are r0..r1-1, or `rows` when given.  block_mask: optional
+    boolean [ceil(N/bq), ceil(N/bk)] of one head.
     """
     i = (np.arange(r0, r1) if rows is None else np.asarray(rows))[:, None]
     j = np.arange(n_keys)[None, :]
@@ -65,6 +73,8 @@ def visible_mask(r0: int, r1: int, n_keys: int, causal: bool,
         vis &= j < int(kv_len_b)
     if causal:
         vis &= j <= i
+    if block_mask is not None:
+        vis &= np.asarray(block_mask, dtype=bool)[i // bq, j // bk]
     return vis
 
 
@@ -83,7 +93,8 @@ def visible_pairs(N: int, causal: bool, kv_len=None, B: int = 1,
     return total
 
 
-def _probs_rows(qh, kh, scale, causal, kv_len_b, r0, r1, rows=None):
+def _probs_rows(qh, kh, scale, causal, kv_len_b, r0, r1, rows=None,
+                bmask=None, bq=128, bk=64):
     """Two-pass softmax of one head's query rows.
 
     Returns (P [rows, N], m [rows], l [rows]); for rows without a visible
@@ -91,7 +102,8 @@ def _probs_rows(qh, kh, scale, causal, kv_len_b, r0, r1, rows=None):
     """
     qr = qh[r0:r1] if rows is None else qh[rows]
     s = scale * (qr @ kh.T)                              # fp64 scores
-    vis = visible_mask(r0, r1, kh.shape[0], causal, kv_len_b, rows)
+    vis = visible_mask(r0, r1, kh.shape[0], causal, kv_len_b, rows,
+                       bmask, bq, bk)
     s = np.where(vis, s, -np.inf)
     m = s.max(axis=1)                                    # pass 1: row max
     empty = ~np.isfinite(m)
@@ -114,13 +126,16 @@ def _run(fn, items, workers):
 
 
 def attention_fwd(q, k, v, scale, causal=False, kv_len=None, rows=None,
-                  row_chunk=512, workers=None):
+                  row_chunk=512, workers=None, block_mask=None,
+                  block_q=128, block_k=64):
     """O and LSE of softmax(scale * Q K^T) V, float64.
 
     q, k, v: [B, H, N, d].  kv_len: None or int [B].  rows: optional 1-D
     array of query indices; then only those rows are computed and the
     outputs have that many rows.  workers: optional thread count over
-    (b, h) heads (numpy releases the GIL in BLAS and exp).
+    (b, h) heads (numpy releases the GIL in BLAS and exp).  block_mask:
+    optional boolean [H, ceil(N/block_q), ceil(N/block_k)], the block-sparse
+    pattern of each head (the same for every batch entry).
 
     Returns (o [B,H,R,d] float64, lse [B,H,R] float64).
     """
@@ -136,14 +151,16 @@ def attention_fwd(q, k, v, scale, causal=False, kv_len=None, rows=None,
     def one(bh):
         b, h = bh
         L = None if kv_len is None else int(kv_len[b])
+        bm = None if block_mask is None else block_mask[h]
         for c0 in range(0, R, row_chunk):
             c1 = min(R, c0 + row_chunk)
             if rows is None:
                 p, m, l = _probs_rows(q[b, h], k[b, h], scale, causal, L,
-                                      c0, c1)
+                                      c0, c1, None, bm, block_q, block_k)
             else:
                 p, m, l = _probs_rows(q[b, h], k[b, h], scale, causal, L,
-                                      0, 0, rows=np.asarray(rows)[c0:c1])
+                                      0, 0, np.asarray(rows)[c0:c1], bm,
+                                      block_q, block_k)
             o[b, h, c0:c1] = p @ v[b, h]
             with np.errstate(divide="ignore"):
                 lse[b, h, c0:c1] = np.where(np.isfinite(m),

@@ -437,10 +437,84 @@ def ORA_brute_vis(N, causal, L):
                if j < L and (not causal or j <= i))
 
 
+def _brute_fwd_vis(q, k, v, scale, vis):
+    """O and LSE of one head by explicit loops over an element mask, with
+    exactly rounded sums (math.fsum) and math.exp."""
+    N, d = q.shape[0], v.shape[1]
+    o = np.zeros((N, d))
+    lse = np.full(N, -np.inf)
+    for i in range(N):
+        js = [j for j in range(k.shape[0]) if vis[i][j]]
+        if not js:
+            continue
+        s = [scale * math.fsum(q[i, c] * k[j, c] for c in range(q.shape[1]))
+             for j in js]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        l = math.fsum(e)
+        for c in range(d):
+            o[i, c] = math.fsum(e[t] * v[js[t], c] for t in range(len(js))) / l
+        lse[i] = m + math.log(l)
+    return o, lse
+
+
+def pin_block_sparse_bruteforce(m):
+    """Block-sparse forward against explicit loops over the element mask
+    built by hand from the block mask (block sizes 2 x 3, so a swapped
+    row/column block index or a transposed mask shows)."""
+    N, d, bq, bk = 7, 3, 2, 3
+    Tq, Tk = -(-N // bq), -(-N // bk)
+    for seed, causal in ((301, False), (302, True)):
+        q, k, v = (_rand(seed + t, 1, 2, N, d) for t in (0, 10, 20))
+        bm = _rng(seed + 30).random((2, Tq, Tk)) < 0.5
+        bm[1, 0, :] = False                      # a block row with no keys
+        o, lse = m.attention_fwd(q, k, v, 0.7, causal, block_mask=bm,
+                                 block_q=bq, block_k=bk)
+        for h in range(2):
+            vis = [[bool(bm[h][i // bq][j // bk]) and (not causal or j <= i)
+                    for j in range(N)] for i in range(N)]
+            wo, wl = _brute_fwd_vis(q[0, h], k[0, h], v[0, h], 0.7, vis)
+            _close(o[0, h], wo, 1e-12, "block-sparse O")
+            _close(lse[0, h], wl, 1e-12, "block-sparse LSE")
+
+
+def pin_block_sparse_reductions(m):
+    """An all-ones block mask is the dense definition; a block-diagonal
+    mask (each 4-row query block sees only its own 4 keys) equals dense
+    attention over each 4-row slice on its own; an empty mask gives O = 0
+    and LSE = -inf."""
+    B, H, N, d = 2, 2, 12, 5
+    q, k, v = (_rand(s, B, H, N, d) for s in (311, 312, 313))
+    for causal in (False, True):
+        full = np.ones((H, 3, 6), dtype=bool)
+        o, lse = m.attention_fwd(q, k, v, 0.4, causal, block_mask=full,
+                                 block_q=4, block_k=2)
+        wo, wl = m.attention_fwd(q, k, v, 0.4, causal)
+        _close(o, wo, 0.0, "all-ones mask O")
+        _close(lse, wl, 0.0, "all-ones mask LSE")
+        diag = np.zeros((H, 3, 6), dtype=bool)
+        for r in range(3):
+            diag[:, r, 2 * r:2 * r + 2] = True
+        o, lse = m.attention_fwd(q, k, v, 0.4, causal, block_mask=diag,
+                                 block_q=4, block_k=2)
+        for r in range(3):
+            sl = slice(4 * r, 4 * r + 4)
+            wo, wl = m.attention_fwd(q[:, :, sl], k[:, :, sl], v[:, :, sl],
+                                     0.4, causal)
+            _close(o[:, :, sl], wo, 1e-13, "block-diagonal O")
+            _close(lse[:, :, sl], wl, 1e-13, "block-diagonal LSE")
+        o, lse = m.attention_fwd(q, k, v, 0.4, causal,
+                                 block_mask=np.zeros((H, 3, 6), dtype=bool),
+                                 block_q=4, block_k=2)
+        _close(o, np.zeros_like(o), 0.0, "empty mask O")
+        assert np.all(lse == -np.inf)
+
+
 PINS = [pin_golden, pin_bruteforce, pin_closed_forms, pin_prob_rows,
         pin_shift, pin_permutation, pin_tiled_recurrence, pin_reductions,
         pin_torch_sdpa, pin_finite_diff, pin_torch_autograd,
-        pin_grad_invariants, pin_visible_pairs]
+        pin_grad_invariants, pin_visible_pairs, pin_block_sparse_bruteforce,
+        pin_block_sparse_reductions]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -482,6 +556,11 @@ MUTANTS = [
      "dq[b, h, c0:c1] = scale * (ds @ v[b, h])"),
     ("dq_transposed_ds", "dq[b, h, c0:c1] = scale * (ds @ k[b, h])",
      "dq[b, h, c0:c1] = scale * (ds.T @ k[b, h])"),
+    ("block_mask_ignored",
+     "vis &= np.asarray(block_mask, dtype=bool)[i // bq, j // bk]", "pass"),
+    ("block_sizes_swapped",
+     "vis &= np.asarray(block_mask, dtype=bool)[i // bq, j // bk]",
+     "vis &= np.asarray(block_mask, dtype=bool)[i // bk, j // bq]"),
 ]
 
 
