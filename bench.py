@@ -53,7 +53,19 @@ def _sources_digest(names):
     return h.hexdigest()[:16]
 
 
-def visible_pairs(w: S.Workload, kv_len) -> int:
+def visible_pairs(w: S.Workload, kv_len, block_mask=None) -> int:
+    if block_mask is not None:
+        # kept 256x64 blocks of each head (every batch entry), causal pairs
+        # counted inside diagonal blocks
+        i = np.arange(w.N)[:, None]
+        j = np.arange(w.N)[None, :]
+        total = 0
+        for h in range(block_mask.shape[0]):
+            vis = block_mask[h].astype(bool)[i // 256, j // 64]
+            if w.causal:
+                vis &= j <= i
+            total += int(vis.sum())
+        return total * w.B
     if w.causal:
         per = w.N * (w.N + 1) // 2
         return per * w.B * w.H
@@ -75,9 +87,11 @@ def cpu_baseline(w: S.Workload, inp: dict, target_s: float = 15.0) -> dict:
     sl = (slice(0, 1), slice(0, nh))
     q, k, v = (inp[n][sl] for n in ("q", "k", "v"))
     kv = None if inp["kv_len"] is None else inp["kv_len"][:1]
+    bm = inp.get("block_mask")
     t0 = time.perf_counter()
     oracle.attention_fwd(q, k, v, inp["scale"], inp["causal"], kv,
-                         workers=cores)
+                         workers=cores,
+                         block_mask=None if bm is None else bm[:nh].astype(bool))
     if w.backward:
         oracle.attention_bwd(q, k, v, inp["do"][sl], inp["scale"],
                              inp["causal"], kv, workers=cores)
@@ -88,14 +102,15 @@ def cpu_baseline(w: S.Workload, inp: dict, target_s: float = 15.0) -> dict:
         q, k, v = (inp[n][sl] for n in ("q", "k", "v"))
         t0 = time.perf_counter()
         oracle.attention_fwd(q, k, v, inp["scale"], inp["causal"], kv,
-                             workers=cores)
+                             workers=cores,
+                             block_mask=None if bm is None else bm[:nh].astype(bool))
         if w.backward:
             oracle.attention_bwd(q, k, v, inp["do"][sl], inp["scale"],
                                  inp["causal"], kv, workers=cores)
         t1 = time.perf_counter() - t0
     sw = S.Workload(w.name, 1, nh, w.N, w.d, w.dtype, w.causal, w.seeds,
                     w.backward)
-    pairs = visible_pairs(sw, kv)
+    pairs = visible_pairs(sw, kv, None if bm is None else bm[:nh])
     flops = pairs * w.d * (4 + (10 if w.backward else 0))
     model = ""
     try:
@@ -228,8 +243,8 @@ def summarize_counters(w: S.Workload, csvs, command) -> int:
                 if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
                     vals[key].setdefault("_ns", []).append(
                         float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
-    pairs = visible_pairs(w, None if w.kv_len_seed is None else
-                          S.make_inputs(w)["kv_len"])
+    ginp = S.make_inputs(w)
+    pairs = visible_pairs(w, ginp["kv_len"], ginp.get("block_mask"))
     alg = {"fwd": 4 * w.d * pairs, "bwd_dkdv": 8 * w.d * pairs,
            "bwd_dq": 2 * w.d * pairs, "bwd_preprocess": 0}
     n_xcd, n_simd = 8, 1024
@@ -445,6 +460,8 @@ def main(argv=None) -> int:
     q, k, v = up("q"), up("k"), up("v")
     do = up("do") if w.backward else None
     kv = None if inp["kv_len"] is None else torch.from_numpy(inp["kv_len"]).to(dev)
+    bmask = (None if inp.get("block_mask") is None
+             else torch.from_numpy(inp["block_mask"]).to(dev))
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     scale, causal = inp["scale"], inp["causal"]
@@ -465,6 +482,8 @@ def main(argv=None) -> int:
         mark(0)
         if w.dtype == "f32":
             fa.fa_fwd_f32(q, k, v, o, lse, scale, causal)
+        elif bmask is not None:
+            fa.fa_fwd_block_sparse(q, k, v, bmask, o, lse, scale, causal)
         else:
             fa.fa_fwd_kvlen(q, k, v, kv, o, lse, scale, causal)
         mark(1)
@@ -503,7 +522,7 @@ def main(argv=None) -> int:
 
     per_kernel = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]))
                   for j, n in enumerate(names)}
-    pairs = visible_pairs(w, inp["kv_len"])
+    pairs = visible_pairs(w, inp["kv_len"], inp.get("block_mask"))
     fwd_flops = 4.0 * w.d * pairs
     bwd_flops = 10.0 * w.d * pairs if w.backward else 0.0
     step_flops = fwd_flops + bwd_flops

@@ -95,6 +95,31 @@ int fa_fwd_kvlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                  int N, int d, float scale, int causal, void* stream);
 
 /*
+ * Block-sparse forward ([ZN] "Overview": block-sparse FlashAttention, which
+ * skips whole blocks of the score matrix by a fixed block mask; the page
+ * gives no detail, so the reading is the definition restricted by the mask).
+ * The block mask has one byte per FA_SPARSE_BQ query rows x FA_SPARSE_BK
+ * keys: key j is visible to query i of head h iff
+ *     block_mask[(h * ceil(N/FA_SPARSE_BQ) + i / FA_SPARSE_BQ)
+ *                * ceil(N/FA_SPARSE_BK) + j / FA_SPARSE_BK] != 0
+ * and (causal == 0 or j <= i); the same mask serves every batch entry.
+ *   block_mask : device uint8 [H, ceil(N/256), ceil(N/64)], read only.
+ *   other arguments as fa_fwd.
+ * A block row is one query workgroup of the kernel and a block column one
+ * key tile; dropped blocks are neither loaded nor computed.  A row with no
+ * visible key gets O = 0 and LSE = -inf.
+ * Errors as fa_fwd, plus FA_ERR_NULL for a NULL block_mask and FA_ERR_SHAPE
+ * when ceil(N/64) exceeds FA_SPARSE_MAX_KEY_BLOCKS (N > 131072).
+ */
+#define FA_SPARSE_BQ 256
+#define FA_SPARSE_BK 64
+#define FA_SPARSE_MAX_KEY_BLOCKS 2048
+int fa_fwd_block_sparse(const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, const uint8_t* block_mask,
+                        uint16_t* o, float* lse, int B, int H, int N, int d,
+                        float scale, int causal, void* stream);
+
+/*
  * Forward, float32 inputs and outputs (no reduced precision anywhere):
  * float32 matrix-core products, float32 softmax.  Same shapes and semantics
  * as fa_fwd.

@@ -41,6 +41,7 @@ _SIGS = {
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_kvlen": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_fwd_block_sparse": (_I, [_P] * 6 + [_I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_workspace_size": (_S, [_I, _I, _I, _I]),
     "fa_bwd": (_I, [_P] * 10 + [_S, _I, _I, _I, _I, _F, _I, _P]),
@@ -146,6 +147,27 @@ def fa_fwd_kvlen(q, k, v, kv_len, o, lse, scale, causal, stream=None):
     _check(st, "fa_fwd_kvlen")
 
 
+SPARSE_BQ, SPARSE_BK = 256, 64   # block-mask granularity (FA_SPARSE_BQ/BK)
+
+
+def fa_fwd_block_sparse(q, k, v, block_mask, o, lse, scale, causal,
+                        stream=None):
+    """C fa_fwd_block_sparse; block_mask is a device uint8 tensor
+    [H, ceil(N/256), ceil(N/64)] (nonzero = block kept)."""
+    import torch
+    B, H, N, d = _bhnd(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _expect(t, torch.bfloat16, (B, H, N, d), n)
+    _expect(lse, torch.float32, (B, H, N), "lse")
+    _expect(block_mask, torch.uint8,
+            (H, -(-N // SPARSE_BQ), -(-N // SPARSE_BK)), "block_mask")
+    st = lib().fa_fwd_block_sparse(_ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(block_mask), _ptr(o), _ptr(lse),
+                                   B, H, N, d, float(scale),
+                                   int(bool(causal)), _stream(q, stream))
+    _check(st, "fa_fwd_block_sparse")
+
+
 def fa_fwd_f32(q, k, v, o, lse, scale, causal, stream=None):
     """C fa_fwd_f32 on float32 tensors [B,H,N,d]."""
     import torch
@@ -216,9 +238,10 @@ def fa_bwd_dq(q, k, v, dO, lse, dq, workspace, scale, causal, stream=None):
 
 # ------------------------------------------------------------- convenience
 
-def forward(q, k, v, *, causal=False, scale=None, kv_len=None, stream=None):
-    """Returns (o, lse).  bf16 inputs use fa_fwd_kvlen, float32 use
-    fa_fwd_f32 (which has no key padding)."""
+def forward(q, k, v, *, causal=False, scale=None, kv_len=None,
+            block_mask=None, stream=None):
+    """Returns (o, lse).  bf16 inputs use fa_fwd_kvlen (fa_fwd_block_sparse
+    with a block mask), float32 use fa_fwd_f32 (no padding, no mask)."""
     import torch
     B, H, N, d = _bhnd(q)
     if scale is None:
@@ -226,9 +249,15 @@ def forward(q, k, v, *, causal=False, scale=None, kv_len=None, stream=None):
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if q.dtype == torch.float32:
-        if kv_len is not None:
-            raise ValueError("fa_fwd_f32 has no key-padding variant")
+        if kv_len is not None or block_mask is not None:
+            raise ValueError("fa_fwd_f32 has no key-padding or block-sparse "
+                             "variant")
         fa_fwd_f32(q, k, v, o, lse, scale, causal, stream)
+    elif block_mask is not None:
+        if kv_len is not None:
+            raise ValueError("fa_fwd_block_sparse has no key padding")
+        fa_fwd_block_sparse(q, k, v, block_mask, o, lse, scale, causal,
+                            stream)
     else:
         fa_fwd_kvlen(q, k, v, kv_len, o, lse, scale, causal, stream)
     return o, lse

@@ -78,8 +78,24 @@ int fa_fwd_kvlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       !aligned16(lse) || ((uintptr_t)kv_len & 3u) != 0)
     return FA_ERR_ALIGN;
-  return fa::launch_fwd_bf16(q, k, v, kv_len, o, lse, B, H, N, d, scale,
-                             causal != 0, (hipStream_t)stream);
+  return fa::launch_fwd_bf16(q, k, v, kv_len, nullptr, o, lse, B, H, N, d,
+                             scale, causal != 0, (hipStream_t)stream);
+}
+
+int fa_fwd_block_sparse(const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, const uint8_t* block_mask,
+                        uint16_t* o, float* lse, int B, int H, int N, int d,
+                        float scale, int causal, void* stream) {
+  if (!q || !k || !v || !block_mask || !o || !lse) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if ((N + FA_SPARSE_BK - 1) / FA_SPARSE_BK > FA_SPARSE_MAX_KEY_BLOCKS)
+    return FA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(lse))
+    return FA_ERR_ALIGN;
+  return fa::launch_fwd_bf16(q, k, v, nullptr, block_mask, o, lse, B, H, N,
+                             d, scale, causal != 0, (hipStream_t)stream);
 }
 
 int fa_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -35,6 +35,7 @@
 //     are in flight while the current tile is computed.  LDS row strides
 //     are padded so the MFMA operand reads are free of bank conflicts.
 //   * exp is exp2 with scale*log2(e) folded into one FMA per score.
+#include "fa.h"
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -55,6 +56,12 @@ constexpr float kRescaleSlack = 8.f;
 // rounding error is smallest (a dominant weight of 2^20 would round with
 // the full 2^-8 relative error of bf16 and show in near one-hot rows).
 constexpr float kSumLimit = 0x1p8f;
+// Block-sparse forward: the block mask has one entry per 256 query rows
+// (one workgroup of the pipelined kernel) x 64 keys (one key tile), and
+// heads have at most 2048 key tiles.
+constexpr int kSparseBQ = FA_SPARSE_BQ;
+constexpr int kSparseMaxTiles = FA_SPARSE_MAX_KEY_BLOCKS;
+static_assert(FA_SPARSE_BK == kBC, "a block-mask column is one key tile");
 
 template <int D, int NW>
 struct FwdTile {
@@ -359,13 +366,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* p,
                                            0x00020000);
 }
 
-template <int D, int NW, int NB, bool CAUSAL, bool KVLEN>
+template <int D, int NW, int NB, bool CAUSAL, bool KVLEN, bool SPARSE>
 __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf16_pipe_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-    float* __restrict__ LSE, const int32_t* __restrict__ kv_len, int H,
-    int N, int n_qblk, float c_log2) {
+    float* __restrict__ LSE, const int32_t* __restrict__ kv_len,
+    const uint8_t* __restrict__ bmask, int H, int N, int n_qblk,
+    float c_log2) {
   using T = PipeTile<D, NW, NB>;
+  static_assert(!SPARSE || T::BR == kSparseBQ,
+                "a workgroup is one block-mask row");
   // Head dim 128 with one block per wavefront stages K and V by DMA
   // through four LDS stages; the other shapes stage through registers with
   // three (there the register path measured faster).
@@ -399,12 +409,54 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
   if (KVLEN) kvlim = min(max(kv_len[b], 0), N);
   int kend = kvlim;
   if (CAUSAL) kend = min(kend, q0 + T::BR);
-  const int ntiles = kend > 0 ? (kend + kBC - 1) / kBC : 0;
+  int ntiles = kend > 0 ? (kend + kBC - 1) / kBC : 0;
   // Tiles this wavefront computes (its block 1 sees the most keys; block 0
   // is masked on the at most two extra tiles).
   int kend_w = kvlim;
   if (CAUSAL) kend_w = min(kend_w, qlo[NB - 1] + 32);
-  const int nt_w = kend_w > 0 ? (kend_w + kBC - 1) / kBC : 0;
+  int nt_w = kend_w > 0 ? (kend_w + kBC - 1) / kBC : 0;
+
+  // ---- block-sparse: the workgroup walks, in order, the key tiles its
+  // block-mask row keeps (a list in LDS); ntiles and nt_w then count list
+  // entries, so dropped tiles are neither loaded nor computed.
+  __shared__ uint32_t tile_list[SPARSE ? kSparseMaxTiles : 1];
+  __shared__ int tile_count;
+  if constexpr (SPARSE) {
+    const int n_mk = (N + kBC - 1) / kBC;
+    const int n_mq = (N + kSparseBQ - 1) / kSparseBQ;
+    const uint8_t* mrow = bmask + ((size_t)(bh % H) * n_mq + qb) * n_mk;
+    if (w == 0) {
+      int cnt = 0;
+      for (int base = 0; base < ntiles; base += 64) {
+        const int j = base + lane;
+        const bool keep = j < ntiles && mrow[j] != 0;
+        const unsigned long long bal = __ballot(keep);
+        const int below = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+        if (keep) tile_list[cnt + below] = (unsigned)j;
+        cnt += __builtin_popcountll(bal);
+      }
+      if (lane == 0) tile_count = cnt;
+    }
+    __syncthreads();
+    const int dense_nt_w = nt_w;
+    ntiles = tile_count;
+    nt_w = 0;
+    for (int base = 0; base < ntiles; base += 64) {
+      const int t = base + lane;
+      const bool in = t < ntiles && (int)tile_list[t] < dense_nt_w;
+      nt_w += __builtin_popcountll(__ballot(in));
+    }
+  }
+  // Key tile of list position t (clamped to the last; the position itself
+  // when dense).  The loops read all the entries a tile needs before its
+  // barrier, so the LDS round trips overlap the wait.
+  auto entry = [&](int t) -> unsigned {
+    if constexpr (SPARSE)
+      return __builtin_amdgcn_readfirstlane(tile_list[max(min(t, ntiles - 1), 0)]);
+    else
+      return (unsigned)t;
+  };
+  auto key_tile = [](unsigned e) -> int { return (int)e; };
 
   const size_t head = (size_t)bh * N * D;
   const uint16_t* Qh = Q + head;
@@ -666,9 +718,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
     }
   };
 
-  // ---- mask half-tile t = 2j + kb (parity x) where needed.
-  auto mask_half = [&](int x, int j, int kb) {
-    const int k0 = j * kBC + 32 * kb;
+  // ---- mask half-tile t = 2j + kb (parity x) where needed; e is the
+  // list entry of tile j.
+  auto mask_half = [&](int x, unsigned e, int kb) {
+    const int k0 = key_tile(e) * kBC + 32 * kb;
 #pragma unroll
     for (int c = 0; c < NB; ++c) {
       const bool need_mask =
@@ -703,9 +756,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
     const int last = ntiles - 1;
     // Stages: K_j and V_j in stage j % NS.  Tile j waits for K_{j+1} and
     // V_j, then issues K_{j+NS-1} and V_{j+NS-2}.
-    dma_k(0, 0);
-    if (last >= 1) dma_k(1, 1);
-    dma_v(0, 0);
+    const unsigned e0 = entry(0), e1 = entry(1), e2 = entry(2);
+    dma_k(key_tile(e0), 0);
+    if (last >= 1) dma_k(key_tile(e1), 1);
+    dma_v(key_tile(e0), 0);
     for (int e = tid; e < T::VELEMS / 8; e += T::THREADS)
       *(u32x4*)(&lds_v[NS - 1][8 * e]) = u32x4{0, 0, 0, 0};
 #pragma unroll
@@ -717,8 +771,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if constexpr (NS == 4) {
-      if (last >= 2) dma_k(2, 2);
-      if (last >= 1) dma_v(1, 1);
+      if (last >= 2) dma_k(key_tile(e2), 2);
+      if (last >= 1) dma_v(key_tile(e1), 1);
     }
     if (nt_w > 0) {
 #pragma unroll
@@ -729,46 +783,48 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
           s[0][c] = mfma32x16(*(const bf16x8*)(&lds_k[0][lq * T::KST + 8 * hh + 16 * kk]),
                               qf[c][kk], s[0][c]);
       }
-      mask_half(0, 0, 0);
+      mask_half(0, e0, 0);
     }
     // Tile j: wait for K_{j+1} and V_j, barrier, issue the next DMAs.  No
     // fence: LDS is only read in the loop, and every read of a stage has
     // returned before its wavefront reaches the barrier after which the
     // stage is refilled.
-    auto top = [&](int j) {
+    auto top = [&](int j, unsigned ek, unsigned ev) {
       if (NS == 4 && j + 2 <= last)
         asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kMinBatch) : "memory");
       else
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      if (j + LK <= last) dma_k(j + LK, (j + LK) % NS);
-      if (j + LV <= last) dma_v(j + LV, (j + LV) % NS);
+      if (j + LK <= last) dma_k(key_tile(ek), (j + LK) % NS);
+      if (j + LV <= last) dma_v(key_tile(ev), (j + LV) % NS);
     };
     for (int j = 0; j < nt_w; ++j) {
-      top(j);
+      const unsigned ej = entry(j), ej1 = entry(j + 1);
+      top(j, entry(j + LK), entry(j + LV));
       const int st0 = j % NS, st1 = (j + 1) % NS, stm = (j + NS - 1) % NS;
       step(std::integral_constant<int, 1>{}, st0, 1, stm, 1);
       settle(0);
-      mask_half(1, j, 1);
+      mask_half(1, ej, 1);
       step(std::integral_constant<int, 0>{}, st1, 0, st0, 0);
       settle(1);
-      if (j + 1 < nt_w) mask_half(0, j + 1, 0);
+      if (j + 1 < nt_w) mask_half(0, ej1, 0);
     }
     if (nt_w > 0) pv_only(1, (nt_w - 1) % NS, 1);
-    for (int j = nt_w; j < ntiles; ++j) top(j);
+    for (int j = nt_w; j < ntiles; ++j) top(j, entry(j + LK), entry(j + LV));
   } else if (ntiles > 0) {
     const int last = ntiles - 1;
     // Prologue: K_0 in stage 0, zeros in V stage 2 (the V_{-1} that the
     // first step multiplies by P = 0), S_0 (half 0 of tile 0) and its mask;
     // K_1, V_0 in registers for tile 0's stores.
-    load_k(0);
+    const unsigned e0 = entry(0), e1 = entry(1);
+    load_k(key_tile(e0));
 #pragma unroll
     for (int r = 0; r < T::CPT; ++r) vreg[r] = u32x4{0, 0, 0, 0};
     store_v(2);
     store_k(0);
-    load_k(min(1, last));
-    load_v(0);
+    load_k(key_tile(e1));
+    load_v(key_tile(e0));
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -785,26 +841,28 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
           s[0][c] = mfma32x16(*(const bf16x8*)(&lds_k[0][lq * T::KST + 8 * hh + 16 * kk]),
                               qf[c][kk], s[0][c]);
       }
-      mask_half(0, 0, 0);
+      mask_half(0, e0, 0);
     }
     // Stages: K_j and V_j in stage j % 3.  Tile j stores K_{j+1} and V_j,
     // then loads K_{j+2} and V_{j+1}.
     int st0 = 0, st1 = 1, stm = 2;   // j % 3, (j+1) % 3, (j-1) % 3
     for (int j = 0; j < ntiles; ++j) {
+      const unsigned ej = entry(j), ej1 = entry(j + 1);
+      const unsigned ek = entry(min(j + 2, last)), ev = entry(min(j + 1, last));
       store_k(st1);
       store_v(st0);
       __syncthreads();
-      load_k(min(j + 2, last));
-      load_v(min(j + 1, last));
+      load_k(key_tile(ek));
+      load_v(key_tile(ev));
       if (__builtin_expect(j < nt_w, 1)) {
         // step 2j: S of (j, half 1) || P of (j, half 0); O += (j-1, half 1)
         step(std::integral_constant<int, 1>{}, st0, 1, stm, 1);
         settle(0);
-        mask_half(1, j, 1);
+        mask_half(1, ej, 1);
         // step 2j+1: S of (j+1, half 0) || P of (j, half 1); O += (j, half 0)
         step(std::integral_constant<int, 0>{}, st1, 0, st0, 0);
         settle(1);
-        if (j + 1 < nt_w) mask_half(0, j + 1, 0);
+        if (j + 1 < nt_w) mask_half(0, ej1, 0);
       } else if (j == nt_w) {
         pv_only(1, stm, 1);
       }
@@ -1026,25 +1084,26 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
 
 namespace {
 
-template <int D, bool CAUSAL, bool KVLEN>
+template <int D, bool CAUSAL, bool KVLEN, bool SPARSE>
 void fwd_bf16_dispatch(bool pipe, bool two_blocks, dim3 grid, dim3 block,
                        hipStream_t stream, const uint16_t* q,
                        const uint16_t* k, const uint16_t* v,
-                       uint16_t* o, float* lse, const int32_t* kv_len, int H,
-                       int N, int n_qblk, float c) {
+                       uint16_t* o, float* lse, const int32_t* kv_len,
+                       const uint8_t* bmask, int H, int N, int n_qblk,
+                       float c) {
   if constexpr (D == 64) {
     if (pipe && two_blocks) {
-      hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 4, 2, CAUSAL, KVLEN>), grid,
-                         block, 0, stream, q, k, v, o, lse, kv_len, H, N,
-                         n_qblk, c);
+      hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 4, 2, CAUSAL, KVLEN, SPARSE>),
+                         grid, block, 0, stream, q, k, v, o, lse, kv_len,
+                         bmask, H, N, n_qblk, c);
       return;
     }
   }
-  if (pipe)
-    hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 8, 1, CAUSAL, KVLEN>), grid,
-                       block, 0, stream, q, k, v, o, lse, kv_len, H, N, n_qblk,
-                       c);
-  else
+  if (pipe || SPARSE)
+    hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 8, 1, CAUSAL, KVLEN, SPARSE>),
+                       grid, block, 0, stream, q, k, v, o, lse, kv_len, bmask,
+                       H, N, n_qblk, c);
+  else if constexpr (!SPARSE)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, CAUSAL, KVLEN>), grid, block, 0,
                        stream, q, k, v, o, lse, kv_len, H, N, n_qblk, c);
 }
@@ -1052,19 +1111,21 @@ void fwd_bf16_dispatch(bool pipe, bool two_blocks, dim3 grid, dim3 block,
 }  // namespace
 
 int launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                    const int32_t* kv_len, uint16_t* o, float* lse, int B,
-                    int H, int N, int d, float scale, int causal,
-                    hipStream_t stream) {
+                    const int32_t* kv_len, const uint8_t* block_mask,
+                    uint16_t* o, float* lse, int B, int H, int N, int d,
+                    float scale, int causal, hipStream_t stream) {
   // Grids with at least one 256-row workgroup per CU use the pipelined
   // kernel: head dim 64 with 4 wavefronts of two 32-row blocks when there
   // are two such workgroups per CU (two resident per CU), else 8 wavefronts
   // of one block (more wavefronts for a grid that fills the chip once);
   // head dim 128 with 8 wavefronts of one block (its two blocks would not
   // fit two wavefronts per SIMD).  Smaller grids use the plain kernel with
-  // 128-row workgroups, two per CU.
+  // 128-row workgroups, two per CU.  Block-sparse calls always take the
+  // pipelined kernel (one 256-row workgroup per block-mask row).
   constexpr int kCUs = 256;
+  const bool sparse = block_mask != nullptr;
   const long long grid256 = (long long)B * H * ((N + 255) / 256);
-  const bool pipe = grid256 >= kCUs;
+  const bool pipe = sparse || grid256 >= kCUs;
   const bool two_blocks = d == 64 && grid256 >= 2 * kCUs;
   const int br = pipe ? 256 : 128;
   const int n_qblk = (N + br - 1) / br;
@@ -1072,20 +1133,27 @@ int launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   const dim3 block(pipe && !two_blocks ? 512 : 256);
   const float c = (float)((double)scale * 1.4426950408889634);
   const bool kv = kv_len != nullptr;
-#define FA_FWD_LAUNCH(DD, CC, KK)                                              \
-  fwd_bf16_dispatch<DD, CC, KK>(pipe, two_blocks, grid, block, stream, q, k,   \
-                                v, o, lse, kv_len, H, N, n_qblk, c)
+#define FA_FWD_LAUNCH(DD, CC, KK, SS)                                          \
+  fwd_bf16_dispatch<DD, CC, KK, SS>(pipe, two_blocks, grid, block, stream, q,  \
+                                    k, v, o, lse, kv_len, block_mask, H, N,    \
+                                    n_qblk, c)
   if (d == 64) {
-    if (causal) {
-      if (kv) FA_FWD_LAUNCH(64, true, true); else FA_FWD_LAUNCH(64, true, false);
+    if (sparse) {
+      if (causal) FA_FWD_LAUNCH(64, true, false, true);
+      else FA_FWD_LAUNCH(64, false, false, true);
+    } else if (causal) {
+      if (kv) FA_FWD_LAUNCH(64, true, true, false); else FA_FWD_LAUNCH(64, true, false, false);
     } else {
-      if (kv) FA_FWD_LAUNCH(64, false, true); else FA_FWD_LAUNCH(64, false, false);
+      if (kv) FA_FWD_LAUNCH(64, false, true, false); else FA_FWD_LAUNCH(64, false, false, false);
     }
   } else {
-    if (causal) {
-      if (kv) FA_FWD_LAUNCH(128, true, true); else FA_FWD_LAUNCH(128, true, false);
+    if (sparse) {
+      if (causal) FA_FWD_LAUNCH(128, true, false, true);
+      else FA_FWD_LAUNCH(128, false, false, true);
+    } else if (causal) {
+      if (kv) FA_FWD_LAUNCH(128, true, true, false); else FA_FWD_LAUNCH(128, true, false, false);
     } else {
-      if (kv) FA_FWD_LAUNCH(128, false, true); else FA_FWD_LAUNCH(128, false, false);
+      if (kv) FA_FWD_LAUNCH(128, false, true, false); else FA_FWD_LAUNCH(128, false, false, false);
     }
   }
 #undef FA_FWD_LAUNCH

@@ -9,10 +9,12 @@
 
 namespace fa {
 
+// kv_len: device int32 [B] or NULL; block_mask: device uint8
+// [H, ceil(N/256), ceil(N/64)] or NULL (never both).
 int launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                    const int32_t* kv_len, uint16_t* o, float* lse, int B,
-                    int H, int N, int d, float scale, int causal,
-                    hipStream_t stream);
+                    const int32_t* kv_len, const uint8_t* block_mask,
+                    uint16_t* o, float* lse, int B, int H, int N, int d,
+                    float scale, int causal, hipStream_t stream);
 
 int launch_fwd_f32(const float* q, const float* k, const float* v, float* o,
                    float* lse, int B, int H, int N, int d, float scale,

@@ -23,7 +23,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "bf16_round_bits", "bf16_bits_to_f32", "normal",
-    "make_inputs", "make_case",
+    "make_inputs", "make_case", "block_mask",
 ]
 
 
@@ -66,6 +66,8 @@ class Workload:
     kv_len_range: tuple = (0, 0)     # inclusive [lo, hi]
     drift_period: float = 0.0        # sinusoidal drift on K (0 = none)
     drift_amp: float = 0.0
+    block_seed: int | None = None    # block-sparse mask drawn from this seed
+    block_density: float = 0.0
     description: str = ""
 
     @property
@@ -89,6 +91,10 @@ WORKLOADS = {
         Workload("causal_fwd_bwd_d128", 4, 16, 4096, 128, "bf16", True,
                  (501, 502, 503, 504), backward=True,
                  description="causal forward + backward, head dim 128"),
+        Workload("blocksparse_d128", 4, 16, 4096, 128, "bf16", False,
+                 (601, 602, 603), block_seed=609, block_density=0.5,
+                 description="block-sparse forward, half of the 256x64 "
+                             "blocks kept per head, head dim 128"),
     ]
 }
 
@@ -133,6 +139,10 @@ def make_inputs(w: Workload | str, heads: slice | None = None) -> dict:
         vals, bits = _finish(a, w.dtype)
         out[name] = vals
         out[name + "_bits"] = bits
+    if w.block_seed is not None:
+        out["block_mask"] = block_mask(w.block_seed, w.H, w.N, w.block_density)
+        if heads is not None:
+            out["block_mask"] = np.ascontiguousarray(out["block_mask"][heads])
     if w.kv_len_seed is not None:
         lo, hi = w.kv_len_range
         out["kv_len"] = np.random.default_rng(w.kv_len_seed).integers(
@@ -140,6 +150,18 @@ def make_inputs(w: Workload | str, heads: slice | None = None) -> dict:
     else:
         out["kv_len"] = None
     return out
+
+
+def block_mask(seed: int, H: int, N: int, density: float,
+               bq: int = 256, bk: int = 64) -> np.ndarray:
+    """Seeded block mask, uint8 [H, ceil(N/bq), ceil(N/bk)]: each block is
+    kept with probability `density`, and the block holding the diagonal of
+    each block row is always kept (so every query row sees some key)."""
+    tq, tk = -(-N // bq), -(-N // bk)
+    m = (np.random.default_rng(seed).random((H, tq, tk)) < density)
+    r = np.arange(tq)
+    m[:, r, np.minimum(r * bq // bk, tk - 1)] = True
+    return m.astype(np.uint8)
 
 
 def make_case(B, H, N, d, dtype="bf16", causal=False, seed=0, kv_len=None,

@@ -32,6 +32,7 @@ def _declared_functions():
 def test_header_declares_expected_calls():
     names = _declared_functions()
     for want in ["fa_fwd", "fa_fwd_kvlen", "fa_fwd_f32", "fa_bwd",
+                 "fa_fwd_block_sparse",
                  "fa_bwd_workspace_size", "fa_status_string", "fa_version",
                  "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq"]:
         assert want in names
@@ -86,6 +87,21 @@ def test_fwd_argument_errors():
     assert L.fa_fwd_f32(A, A, None, A, A, 1, 1, 64, 64, 0.1, 0, None) == NULL
     assert L.fa_fwd_f32(A, A, A, A, MIS, 1, 1, 64, 64, 0.1, 0, None) == ALIGN
     assert L.fa_fwd_f32(A, A, A, A, A, 1, 0, 64, 64, 0.1, 0, None) == SHAPE
+
+
+def test_block_sparse_argument_errors():
+    L = fa.lib()
+
+    def sp(q=A, m=A, o=A, N=64, d=128, B=1):
+        return L.fa_fwd_block_sparse(q, A, A, m, o, A, B, 2, N, d, 0.1, 1,
+                                     None)
+    assert sp(q=None) == NULL
+    assert sp(m=None) == NULL
+    assert sp(o=None) == NULL
+    assert sp(B=0) == SHAPE
+    assert sp(N=64 * 2048 + 1) == SHAPE       # more key blocks than the limit
+    assert sp(d=96) == HEADDIM
+    assert sp(o=MIS) == ALIGN
 
 
 def test_workspace_size():
