@@ -440,11 +440,14 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
     __syncthreads();
     const int dense_nt_w = nt_w;
     ntiles = tile_count;
-    nt_w = 0;
-    for (int base = 0; base < ntiles; base += 64) {
-      const int t = base + lane;
-      const bool in = t < ntiles && (int)tile_list[t] < dense_nt_w;
-      nt_w += __builtin_popcountll(__ballot(in));
+    nt_w = ntiles;
+    if (CAUSAL) {
+      nt_w = 0;
+      for (int base = 0; base < ntiles; base += 64) {
+        const int t = base + lane;
+        const bool in = t < ntiles && (int)tile_list[t] < dense_nt_w;
+        nt_w += __builtin_popcountll(__ballot(in));
+      }
     }
   }
   // Key tile of list position t (clamped to the last; the position itself
@@ -586,13 +589,21 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
   // ---- one step.  xs: parity of S_{t+1} (= parity of P_{t-1}); the
   // exponentials take S_t (parity 1 - xs).  stk/kbs: K stage and 32-key
   // half of S_{t+1}; stv/kbv: V stage and half of P_{t-1}.
-  auto step = [&](auto xs_tag, int stk, int kbs, int stv, int kbv) {
+  // Operand ring.  With one block per wavefront it is carried across steps:
+  // the last slots of a step read the first K operands of the next step
+  // (nstk, nkbs), so a step never starts by waiting for LDS (two blocks per
+  // wavefront leave no registers for it).
+  constexpr bool XP = NB == 1;
+  constexpr int kPf = XP ? 4 : 3;
+  bf16x8 opr[kPf];
+  auto step = [&](auto xs_tag, int stk, int kbs, int stv, int kbv, int nstk,
+                  int nkbs) {
     constexpr int XS = decltype(xs_tag)::value;
     constexpr int XE = 1 - XS;
     constexpr int kS = D / 16;             // S MFMAs per block
     constexpr int kP = 2 * (D / 32);       // PV MFMAs per block
     constexpr int kN = kS + kP;            // operand reads (each used twice)
-    constexpr int kPf = 3;
+    static_assert(!XP || (kN % kPf == 0 && kPf <= kS), "ring alignment");
     auto fetch = [&](int i) -> bf16x8 {
       if (i < kS)
         return *(const bf16x8*)(&lds_k[stk][(32 * kbs + lq) * T::KST + 8 * hh + 16 * i]);
@@ -603,9 +614,14 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
       return join_bf16(lds_read_tr16(&lds_v[stv][key * T::VST + dcol]),
                        lds_read_tr16(&lds_v[stv][(key + 8) * T::VST + dcol]));
     };
-    bf16x8 op[kPf];
+    auto fetch_next = [&](int i) -> bf16x8 {
+      return *(const bf16x8*)(&lds_k[nstk][(32 * nkbs + lq) * T::KST + 8 * hh + 16 * i]);
+    };
+    bf16x8 op[XP ? 1 : kPf];   // the ring of a step when it is not carried
+    if constexpr (!XP) {
 #pragma unroll
-    for (int i = 0; i < kPf; ++i) op[i] = fetch(i);
+      for (int i = 0; i < kPf; ++i) op[i] = fetch(i);
+    }
     // The 16 NB exponentials of the step (16 per block, element el -> block
     // el / 16, half (el / 8) % 2, register el % 8) run as a three-stage
     // pipeline across MFMA slots: slot m takes the FMA of one element group,
@@ -648,8 +664,15 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
     for (int m = 0; m < kM + 2; ++m) {
       if (m < kM) {
         const int i = m / NB, c = m % NB;
-        const bf16x8 a = op[i % kPf];
-        if (c == NB - 1 && i + kPf < kN) op[i % kPf] = fetch(i + kPf);
+        bf16x8 a;
+        if constexpr (XP) {
+          a = opr[i % kPf];
+          if (c == NB - 1)
+            opr[i % kPf] = i + kPf < kN ? fetch(i + kPf) : fetch_next(i + kPf - kN);
+        } else {
+          a = op[i % kPf];
+          if (c == NB - 1 && i + kPf < kN) op[i % kPf] = fetch(i + kPf);
+        }
         if (i < kS) {
           s[XS][c] = mfma32x16(a, qf[c][i], i == 0 ? f32x16{} : s[XS][c]);
         } else {
@@ -785,6 +808,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
       }
       mask_half(0, e0, 0);
     }
+    if constexpr (XP) {
+#pragma unroll
+      for (int i = 0; i < kPf; ++i)
+        opr[i] = *(const bf16x8*)(&lds_k[0][(32 + lq) * T::KST + 8 * hh + 16 * i]);
+    }
     // Tile j: wait for K_{j+1} and V_j, barrier, issue the next DMAs.  No
     // fence: LDS is only read in the loop, and every read of a stage has
     // returned before its wavefront reaches the barrier after which the
@@ -803,10 +831,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
       const unsigned ej = entry(j), ej1 = entry(j + 1);
       top(j, entry(j + LK), entry(j + LV));
       const int st0 = j % NS, st1 = (j + 1) % NS, stm = (j + NS - 1) % NS;
-      step(std::integral_constant<int, 1>{}, st0, 1, stm, 1);
+      step(std::integral_constant<int, 1>{}, st0, 1, stm, 1, st1, 0);
       settle(0);
       mask_half(1, ej, 1);
-      step(std::integral_constant<int, 0>{}, st1, 0, st0, 0);
+      step(std::integral_constant<int, 0>{}, st1, 0, st0, 0, st1, 1);
       settle(1);
       if (j + 1 < nt_w) mask_half(0, ej1, 0);
     }
@@ -843,6 +871,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
       }
       mask_half(0, e0, 0);
     }
+    if constexpr (XP) {
+#pragma unroll
+      for (int i = 0; i < kPf; ++i)
+        opr[i] = *(const bf16x8*)(&lds_k[0][(32 + lq) * T::KST + 8 * hh + 16 * i]);
+    }
     // Stages: K_j and V_j in stage j % 3.  Tile j stores K_{j+1} and V_j,
     // then loads K_{j+2} and V_{j+1}.
     int st0 = 0, st1 = 1, stm = 2;   // j % 3, (j+1) % 3, (j-1) % 3
@@ -856,11 +889,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
       load_v(key_tile(ev));
       if (__builtin_expect(j < nt_w, 1)) {
         // step 2j: S of (j, half 1) || P of (j, half 0); O += (j-1, half 1)
-        step(std::integral_constant<int, 1>{}, st0, 1, stm, 1);
+        step(std::integral_constant<int, 1>{}, st0, 1, stm, 1, st1, 0);
         settle(0);
         mask_half(1, ej, 1);
         // step 2j+1: S of (j+1, half 0) || P of (j, half 1); O += (j, half 0)
-        step(std::integral_constant<int, 0>{}, st1, 0, st0, 0);
+        step(std::integral_constant<int, 0>{}, st1, 0, st0, 0, st1, 1);
         settle(1);
         if (j + 1 < nt_w) mask_half(0, ej1, 0);
       } else if (j == nt_w) {
