@@ -23,7 +23,8 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "bf16_round_bits", "bf16_bits_to_f32", "normal",
-    "make_inputs", "make_case", "block_mask",
+    "make_inputs", "make_case", "block_mask", "rotation_signs",
+    "outlier_channels",
 ]
 
 
@@ -68,6 +69,7 @@ class Workload:
     drift_amp: float = 0.0
     block_seed: int | None = None    # block-sparse mask drawn from this seed
     block_density: float = 0.0
+    sign_seed: int | None = None     # FP8 path: rotation signs from this seed
     description: str = ""
 
     @property
@@ -95,6 +97,11 @@ WORKLOADS = {
                  (601, 602, 603), block_seed=609, block_density=0.5,
                  description="block-sparse forward, half of the 256x64 "
                              "blocks kept per head, head dim 128"),
+        Workload("fp8_causal_d128", 4, 16, 4096, 128, "bf16", True,
+                 (701, 702, 703), sign_seed=709,
+                 description="FP8 causal forward with incoherent processing "
+                             "(bf16 inputs quantised on the GPU), head dim "
+                             "128"),
     ]
 }
 
@@ -143,6 +150,8 @@ def make_inputs(w: Workload | str, heads: slice | None = None) -> dict:
         out["block_mask"] = block_mask(w.block_seed, w.H, w.N, w.block_density)
         if heads is not None:
             out["block_mask"] = np.ascontiguousarray(out["block_mask"][heads])
+    if w.sign_seed is not None:
+        out["signs"] = rotation_signs(w.sign_seed, w.d)
     if w.kv_len_seed is not None:
         lo, hi = w.kv_len_range
         out["kv_len"] = np.random.default_rng(w.kv_len_seed).integers(
@@ -164,12 +173,28 @@ def block_mask(seed: int, H: int, N: int, density: float,
     return m.astype(np.uint8)
 
 
+def rotation_signs(seed: int, d: int) -> np.ndarray:
+    """Seeded random signs (int8, +1 or -1) for the FP8 path's rotation."""
+    return np.where(np.random.default_rng(seed).random(d) < 0.5, -1,
+                    1).astype(np.int8)
+
+
+def outlier_channels(seed: int, d: int, n: int) -> np.ndarray:
+    """Seeded choice of n distinct feature channels (sorted int array)."""
+    return np.sort(np.random.default_rng(seed).choice(d, n, replace=False))
+
+
 def make_case(B, H, N, d, dtype="bf16", causal=False, seed=0, kv_len=None,
-              backward=False, q_scale=1.0, scale=None) -> dict:
+              backward=False, q_scale=1.0, scale=None, outliers=0,
+              outlier_scale=1.0) -> dict:
     """Small seeded case for parity tests; same dict layout as make_inputs.
 
     `q_scale` multiplies Q before rounding (large-magnitude score tests).
     `kv_len` may be None, an int (same for every batch), or a sequence.
+    `outliers` > 0 multiplies that many feature channels (the same ones in
+    Q and K, chosen by `outlier_channels(seed, d, outliers)`) by
+    `outlier_scale` before rounding: outlier features shared by queries and
+    keys.
     """
     shape = (B, H, N, d)
     out = {"causal": causal, "dtype": dtype, "workload": "case"}
@@ -180,6 +205,9 @@ def make_case(B, H, N, d, dtype="bf16", causal=False, seed=0, kv_len=None,
         a = normal(seed * 16 + i, shape)
         if name == "q" and q_scale != 1.0:
             a = (a * np.float32(q_scale)).astype(np.float32)
+        if outliers and name in ("q", "k"):
+            ch = outlier_channels(seed, d, outliers)
+            a[..., ch] *= np.float32(outlier_scale)
         vals, bits = _finish(a, dtype)
         out[name] = vals
         out[name + "_bits"] = bits
