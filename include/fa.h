@@ -129,6 +129,77 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
                int causal, void* stream);
 
 /*
+ * FP8 forward with incoherent processing ([MM] "FA3: Hopper", item 3: the
+ * vectors are rotated at random before block-wise FP8 quantisation, which
+ * spreads outliers over all coordinates and lowers the error of FP8
+ * attention).  Readings of that passage:
+ *   - Rotation: every row of Q and of K is multiplied by R = diag(s) H_d,
+ *     s = signs[0..d-1] (+1, or -1 where signs[c] < 0), H_d the
+ *     Sylvester-Hadamard matrix, applied in float32 by the fast
+ *     Walsh-Hadamard transform, stage t = 0, 1, ... pairing coordinates i
+ *     and i + 2^t (bit t of i clear) into (a + b, a - b).  R R^T = d I, so
+ *     the scores are taken with scale / d.  V is not rotated.  signs = NULL
+ *     skips the rotation (plain FP8) and keeps the scale.
+ *   - Block-wise quantisation: every 32 consecutive values (along d for the
+ *     rows of Q and K, along the keys for each channel of V; keys past N
+ *     are zeros) share a scale 2^e, e the smallest integer with
+ *     max|x| <= 448 * 2^e, clamped to [-127, 127]; each value becomes the
+ *     OCP E4M3 code of x * 2^-e, rounded to nearest even.  The scale byte
+ *     is e + 127 (E8M0).  The matrix cores apply the scales (32-value
+ *     blocks are the hardware's scaled-FP8 block).
+ *   - Softmax weights are rounded to E4M3 (scale 1) before P V; the row sum
+ *     l adds the unrounded float32 weights, so LSE is that of the quantised
+ *     scores.  O and LSE as in fa_fwd (bf16 O, float32 natural-log LSE).
+ * Head dim 64 or 128; causal or not; no key padding or block mask.
+ *
+ * Workspace: the quantised operands, in this layout (Np = N rounded up to
+ * a multiple of 64, RB = FA_FP8_ROW_BYTES(d)):
+ *   Q8 at byte 0:               [B*H][Np][RB]  row n = query n
+ *   K8 at byte B*H*Np*RB:       [B*H][Np][RB]  rows permuted in each 64-key
+ *                               tile: row 64j + 32t + r8 + 4u + r4 (r8 in
+ *                               {0,8,16,24}, u in {0,1}, r4 < 4) holds key
+ *                               64j + 32t + 16u + r8/2 + r4
+ *   V8 at byte 2*B*H*Np*RB:     [B*H][Np/64][d][80]: channel c of key tile
+ *                               j, bytes 0..63 = keys 64j..64j+63, byte 64
+ *                               + u = scale of keys 64j+32u .. +31
+ * A Q8/K8 row holds the d codes (byte c = coordinate c of the rotated row),
+ * then the d/32 scale bytes in the order (u, m) -> byte d + u*(d/64) + m =
+ * scale of coordinates 32(2m+u) .. +31, then zeros.  Rows past N are zero.
+ */
+#define FA_FP8_ROW_BYTES(d) ((d) == 128 ? 144 : 80)
+#define FA_FP8_V_ROW_BYTES 80
+
+/* Bytes of workspace the FP8 forward needs (0 for invalid shapes). */
+size_t fa_fp8_workspace_size(int B, int H, int N, int d);
+
+/*
+ * FP8 step 1: rotate (when signs != NULL) and quantise Q, K and V into the
+ * workspace (layout above).  q, k, v: [B,H,N,d] bf16; signs: device int8
+ * [d] or NULL; workspace: at least fa_fp8_workspace_size() bytes, 256-byte
+ * aligned.  Errors as fa_fwd plus FA_ERR_WORKSPACE.
+ */
+int fa_fp8_quantize(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    const int8_t* signs, void* workspace,
+                    size_t workspace_bytes, int B, int H, int N, int d,
+                    void* stream);
+
+/*
+ * FP8 step 2: attention on quantised operands.  score_scale multiplies the
+ * dequantised products Q8 K8^T (the caller's scale, divided by d when the
+ * operands were rotated).  o: [B,H,N,d] bf16; lse: [B,H,N] float32.
+ */
+int fa_fwd_fp8_quantized(const void* workspace, size_t workspace_bytes,
+                         uint16_t* o, float* lse, int B, int H, int N, int d,
+                         float score_scale, int causal, void* stream);
+
+/* Both steps on one stream: fa_fp8_quantize, then fa_fwd_fp8_quantized
+ * with scale / d (signs != NULL) or scale (signs == NULL). */
+int fa_fwd_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+               const int8_t* signs, uint16_t* o, float* lse, void* workspace,
+               size_t workspace_bytes, int B, int H, int N, int d,
+               float scale, int causal, void* stream);
+
+/*
  * The backward entry points below support head dimension d = 128 only; any
  * other d returns FA_ERR_HEADDIM (and fa_bwd_workspace_size returns 0).
  *

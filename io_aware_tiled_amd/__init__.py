@@ -7,11 +7,13 @@ no CPU path and no fallback: if the library is missing or a tensor is not on
 the GPU, the call raises.
 
 The functions named like the C ABI (``fa_fwd``, ``fa_fwd_kvlen``,
-``fa_fwd_f32``, ``fa_bwd``, ``fa_bwd_preprocess``, ``fa_bwd_dkdv``,
-``fa_bwd_dq``, ``fa_bwd_workspace_size``, ``fa_status_string``,
-``fa_version``) take caller-allocated tensors exactly as the C calls take
-pointers.  ``forward`` and ``backward`` allocate the outputs with
-``torch.empty`` on the inputs' device and call them.
+``fa_fwd_block_sparse``, ``fa_fwd_f32``, ``fa_fp8_quantize``,
+``fa_fwd_fp8_quantized``, ``fa_fwd_fp8``, ``fa_bwd``, ``fa_bwd_preprocess``,
+``fa_bwd_dkdv``, ``fa_bwd_dq``, the workspace-size queries,
+``fa_status_string``, ``fa_version``) take caller-allocated tensors exactly
+as the C calls take pointers.  ``forward``, ``forward_fp8`` and ``backward``
+allocate the outputs with ``torch.empty`` on the inputs' device and call
+them.
 """
 from __future__ import annotations
 
@@ -23,7 +25,9 @@ __all__ = [
     "FAError", "lib", "lib_path", "fa_version", "fa_status_string",
     "fa_fwd", "fa_fwd_kvlen", "fa_fwd_f32", "fa_bwd_workspace_size",
     "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
-    "forward", "backward", "EXPORTED_SYMBOLS",
+    "fa_fwd_block_sparse", "fa_fp8_workspace_size", "fa_fp8_quantize",
+    "fa_fwd_fp8_quantized", "fa_fwd_fp8", "forward", "forward_fp8",
+    "backward", "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -48,6 +52,10 @@ _SIGS = {
     "fa_bwd_preprocess": (_I, [_P, _P, _P, _S, _I, _I, _I, _I, _P]),
     "fa_bwd_dkdv": (_I, [_P] * 8 + [_S, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_dq": (_I, [_P] * 7 + [_S, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_fp8_workspace_size": (_S, [_I, _I, _I, _I]),
+    "fa_fp8_quantize": (_I, [_P] * 5 + [_S, _I, _I, _I, _I, _P]),
+    "fa_fwd_fp8_quantized": (_I, [_P, _S, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_fwd_fp8": (_I, [_P] * 7 + [_S, _I, _I, _I, _I, _F, _I, _P]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -236,6 +244,70 @@ def fa_bwd_dq(q, k, v, dO, lse, dq, workspace, scale, causal, stream=None):
     _check(st, "fa_bwd_dq")
 
 
+FP8_V_ROW_BYTES = 80
+
+
+def fp8_row_bytes(d: int) -> int:
+    """FA_FP8_ROW_BYTES(d): bytes of one quantised Q or K row."""
+    return 144 if d == 128 else 80
+
+
+def fa_fp8_workspace_size(B, H, N, d) -> int:
+    return int(lib().fa_fp8_workspace_size(int(B), int(H), int(N), int(d)))
+
+
+def _signs(signs, d):
+    import torch
+    if signs is None:
+        return None
+    _expect(signs, torch.int8, (d,), "signs")
+    return _ptr(signs)
+
+
+def fa_fp8_quantize(q, k, v, signs, workspace, stream=None):
+    """C fa_fp8_quantize: bf16 q, k, v [B,H,N,d]; signs: device int8 [d] or
+    None (no rotation); workspace: device uint8 tensor."""
+    import torch
+    B, H, N, d = _bhnd(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _expect(t, torch.bfloat16, (B, H, N, d), n)
+    wp, wn = _ws(workspace)
+    st = lib().fa_fp8_quantize(_ptr(q), _ptr(k), _ptr(v), _signs(signs, d),
+                               wp, wn, B, H, N, d, _stream(q, stream))
+    _check(st, "fa_fp8_quantize")
+
+
+def fa_fwd_fp8_quantized(workspace, o, lse, score_scale, causal,
+                         stream=None):
+    """C fa_fwd_fp8_quantized: attention on a quantised workspace; o bf16
+    [B,H,N,d] gives the shape."""
+    import torch
+    B, H, N, d = _bhnd(o)
+    _expect(o, torch.bfloat16, (B, H, N, d), "o")
+    _expect(lse, torch.float32, (B, H, N), "lse")
+    wp, wn = _ws(workspace)
+    st = lib().fa_fwd_fp8_quantized(wp, wn, _ptr(o), _ptr(lse), B, H, N, d,
+                                    float(score_scale), int(bool(causal)),
+                                    _stream(o, stream))
+    _check(st, "fa_fwd_fp8_quantized")
+
+
+def fa_fwd_fp8(q, k, v, signs, o, lse, workspace, scale, causal,
+               stream=None):
+    """C fa_fwd_fp8: quantise (rotating with signs unless None), then
+    attend; the workspace keeps the quantised operands."""
+    import torch
+    B, H, N, d = _bhnd(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _expect(t, torch.bfloat16, (B, H, N, d), n)
+    _expect(lse, torch.float32, (B, H, N), "lse")
+    wp, wn = _ws(workspace)
+    st = lib().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _signs(signs, d),
+                          _ptr(o), _ptr(lse), wp, wn, B, H, N, d,
+                          float(scale), int(bool(causal)), _stream(q, stream))
+    _check(st, "fa_fwd_fp8")
+
+
 # ------------------------------------------------------------- convenience
 
 def forward(q, k, v, *, causal=False, scale=None, kv_len=None,
@@ -261,6 +333,25 @@ def forward(q, k, v, *, causal=False, scale=None, kv_len=None,
     else:
         fa_fwd_kvlen(q, k, v, kv_len, o, lse, scale, causal, stream)
     return o, lse
+
+
+def forward_fp8(q, k, v, signs=None, *, causal=False, scale=None,
+                workspace=None, stream=None):
+    """FP8 forward of bf16 q, k, v; returns (o, lse, workspace).  signs:
+    device int8 [d] (rotation) or None (plain FP8)."""
+    import torch
+    B, H, N, d = _bhnd(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nbytes = fa_fp8_workspace_size(B, H, N, d)
+    if nbytes == 0:
+        raise FAError(-3 if d not in (64, 128) else -2, "fa_fp8_workspace_size")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_fwd_fp8(q, k, v, signs, o, lse, workspace, scale, causal, stream)
+    return o, lse, workspace
 
 
 def backward(q, k, v, o, lse, dO, *, causal=False, scale=None, stream=None,

@@ -41,6 +41,13 @@ size_t ws_bytes(int B, int H, int N) {
   return align256((size_t)B * H * N * sizeof(float));
 }
 
+// FP8 forward workspace: Q8 and K8 rows of FA_FP8_ROW_BYTES(d) bytes for
+// N rounded up to 64 rows, then V8 tiles of d x 80 bytes per 64 keys.
+size_t fp8_ws_bytes(int B, int H, int N, int d) {
+  const size_t bh = (size_t)B * H, np = ((size_t)N + 63) / 64 * 64;
+  return 2 * bh * np * FA_FP8_ROW_BYTES(d) + bh * (np / 64) * d * FA_FP8_V_ROW_BYTES;
+}
+
 int check_workspace(const void* ws, size_t bytes, int B, int H, int N) {
   if (ws == nullptr) return FA_ERR_WORKSPACE;
   if (((uintptr_t)ws & 255u) != 0) return FA_ERR_WORKSPACE;
@@ -116,6 +123,58 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
     return FA_ERR_ALIGN;
   return fa::launch_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal != 0,
                             (hipStream_t)stream);
+}
+
+size_t fa_fp8_workspace_size(int B, int H, int N, int d) {
+  if (check_shape(B, H, N, d) != FA_OK) return 0;
+  return fp8_ws_bytes(B, H, N, d);
+}
+
+int fa_fp8_quantize(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    const int8_t* signs, void* workspace,
+                    size_t workspace_bytes, int B, int H, int N, int d,
+                    void* stream) {
+  if (!q || !k || !v) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return FA_ERR_ALIGN;
+  if (!workspace || ((uintptr_t)workspace & 255u) != 0 ||
+      workspace_bytes < fp8_ws_bytes(B, H, N, d))
+    return FA_ERR_WORKSPACE;
+  return fa::launch_fp8_quantize(q, k, v, signs, (uint8_t*)workspace, B, H,
+                                 N, d, (hipStream_t)stream);
+}
+
+int fa_fwd_fp8_quantized(const void* workspace, size_t workspace_bytes,
+                         uint16_t* o, float* lse, int B, int H, int N, int d,
+                         float score_scale, int causal, void* stream) {
+  if (!o || !lse) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  if (!workspace || ((uintptr_t)workspace & 255u) != 0 ||
+      workspace_bytes < fp8_ws_bytes(B, H, N, d))
+    return FA_ERR_WORKSPACE;
+  return fa::launch_fwd_fp8((const uint8_t*)workspace, o, lse, B, H, N, d,
+                            score_scale, causal != 0, (hipStream_t)stream);
+}
+
+int fa_fwd_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+               const int8_t* signs, uint16_t* o, float* lse, void* workspace,
+               size_t workspace_bytes, int B, int H, int N, int d,
+               float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(lse))
+    return FA_ERR_ALIGN;
+  st = fa_fp8_quantize(q, k, v, signs, workspace, workspace_bytes, B, H, N,
+                       d, stream);
+  if (st != FA_OK) return st;
+  const float score_scale = signs ? scale / (float)d : scale;
+  return fa_fwd_fp8_quantized(workspace, workspace_bytes, o, lse, B, H, N, d,
+                              score_scale, causal, stream);
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {

@@ -33,4 +33,13 @@ int launch_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   uint16_t* dq, int B, int H, int N, int d, float scale,
                   int causal, hipStream_t stream);
 
+// FP8 forward (layouts in include/fa.h).  signs: device int8 [d] or NULL.
+int launch_fp8_quantize(const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, const int8_t* signs, uint8_t* ws,
+                        int B, int H, int N, int d, hipStream_t stream);
+
+int launch_fwd_fp8(const uint8_t* ws, uint16_t* o, float* lse, int B, int H,
+                   int N, int d, float score_scale, int causal,
+                   hipStream_t stream);
+
 }  // namespace fa

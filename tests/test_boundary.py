@@ -32,7 +32,8 @@ def _declared_functions():
 def test_header_declares_expected_calls():
     names = _declared_functions()
     for want in ["fa_fwd", "fa_fwd_kvlen", "fa_fwd_f32", "fa_bwd",
-                 "fa_fwd_block_sparse",
+                 "fa_fwd_block_sparse", "fa_fp8_workspace_size",
+                 "fa_fp8_quantize", "fa_fwd_fp8_quantized", "fa_fwd_fp8",
                  "fa_bwd_workspace_size", "fa_status_string", "fa_version",
                  "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq"]:
         assert want in names
@@ -145,6 +146,48 @@ def test_bwd_argument_errors():
                        1, None) == HEADDIM
     assert L.fa_bwd_dq(A, A, A, A, A, A, W, 0, 1, 1, 64, 128, 0.1,
                        1, None) == WORKSPACE
+
+
+def test_fp8_workspace_size():
+    ws = fa.fa_fp8_workspace_size
+    for B, H, N, d in [(1, 1, 1, 64), (4, 16, 4096, 128), (2, 3, 1000, 128),
+                       (1, 12, 23400, 64)]:
+        Np = -(-N // 64) * 64
+        rb = fa.fp8_row_bytes(d)
+        assert ws(B, H, N, d) == 2 * B * H * Np * rb + B * H * (Np // 64) * d * 80
+        assert ws(B, H, N, d) % 256 == 0
+    assert ws(1, 1, 64, 96) == 0
+    assert ws(0, 1, 64, 128) == 0
+
+
+def test_fp8_argument_errors():
+    L = fa.lib()
+    nbytes = fa.fa_fp8_workspace_size(1, 2, 100, 128)
+    W = 0x100000
+
+    def quant(q=A, k=A, v=A, s=None, ws=W, wsb=nbytes, N=100, d=128):
+        return L.fa_fp8_quantize(q, k, v, s, ws, wsb, 1, 2, N, d, None)
+
+    def attn(ws=W, wsb=nbytes, o=A, lse=A, N=100, d=128):
+        return L.fa_fwd_fp8_quantized(ws, wsb, o, lse, 1, 2, N, d, 0.01, 1,
+                                      None)
+
+    def full(q=A, o=A, ws=W, wsb=nbytes, d=128, N=100):
+        return L.fa_fwd_fp8(q, A, A, A, o, A, ws, wsb, 1, 2, N, d, 0.08, 0,
+                            None)
+    assert quant(q=None) == NULL and quant(v=None) == NULL
+    assert quant(N=0) == SHAPE and quant(d=32) == HEADDIM
+    assert quant(k=MIS) == ALIGN
+    assert quant(ws=None) == WORKSPACE and quant(ws=W + 64) == WORKSPACE
+    assert quant(wsb=nbytes - 1) == WORKSPACE
+    assert attn(o=None) == NULL and attn(lse=None) == NULL
+    assert attn(d=256) == HEADDIM and attn(lse=MIS) == ALIGN
+    assert attn(ws=None) == WORKSPACE and attn(wsb=16) == WORKSPACE
+    assert full(q=None) == NULL and full(o=None) == NULL
+    assert full(d=48) == HEADDIM and full(o=MIS) == ALIGN
+    assert full(wsb=nbytes - 256) == WORKSPACE
+    # The workspace of a larger N does not fit a smaller one's size.
+    assert quant(N=200, wsb=nbytes) == WORKSPACE
 
 
 def test_python_binding_refuses_host_tensors():
