@@ -6,7 +6,10 @@ A step is one pass of the whole hot path over one batch of synthetic input:
 for the default workload (causal, B=4, H=16, N=4096, d=128) that is the
 forward (fa_fwd) and the three backward stages (fa_bwd_preprocess,
 fa_bwd_dkdv, fa_bwd_dq).  Forward-only workloads run fa_fwd (or
-fa_fwd_f32 / fa_fwd_kvlen).  Inputs are resident in HBM before timing starts.
+fa_fwd_f32 / fa_fwd_kvlen / fa_fwd_block_sparse); the FP8 workload runs
+fa_fp8_quantize then fa_fwd_fp8_quantized on the bf16 inputs (its roofline is
+the attention kernel against the fp8 matrix peak).  Inputs are resident in
+HBM before timing starts.
 
 Throughput is algorithmic: 4d FLOP per visible (query, key) pair for the
 forward and 10d for the backward (causal: N(N+1)/2 pairs per head); masked
@@ -40,6 +43,7 @@ METRIC = ("attention fwd(+bwd) TFLOP/s bf16 causal, N=1K-23.4K; "
           "% of MFMA peak")
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix peak (published)
 PEAK_F32_TFLOPS = 157.3         # MI355X fp32 matrix peak (published)
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 matrix peak (published)
 DEFAULT_WORKLOAD = "causal_fwd_bwd_d128"
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
@@ -88,25 +92,27 @@ def cpu_baseline(w: S.Workload, inp: dict, target_s: float = 15.0) -> dict:
     q, k, v = (inp[n][sl] for n in ("q", "k", "v"))
     kv = None if inp["kv_len"] is None else inp["kv_len"][:1]
     bm = inp.get("block_mask")
-    t0 = time.perf_counter()
-    oracle.attention_fwd(q, k, v, inp["scale"], inp["causal"], kv,
-                         workers=cores,
-                         block_mask=None if bm is None else bm[:nh].astype(bool))
-    if w.backward:
-        oracle.attention_bwd(q, k, v, inp["do"][sl], inp["scale"],
-                             inp["causal"], kv, workers=cores)
-    t1 = time.perf_counter() - t0
-    nh = int(max(1, min(w.H, cores, target_s // max(t1, 1e-3))))
-    if nh > 1:
-        sl = (slice(0, 1), slice(0, nh))
-        q, k, v = (inp[n][sl] for n in ("q", "k", "v"))
-        t0 = time.perf_counter()
+    def run(q, k, v, nh, sl):
+        if inp.get("signs") is not None:
+            import oracle.fp8
+            oracle.fp8.fp8_forward(q, k, v, inp["scale"], inp["causal"],
+                                   inp["signs"], workers=cores)
+            return
         oracle.attention_fwd(q, k, v, inp["scale"], inp["causal"], kv,
                              workers=cores,
                              block_mask=None if bm is None else bm[:nh].astype(bool))
         if w.backward:
             oracle.attention_bwd(q, k, v, inp["do"][sl], inp["scale"],
                                  inp["causal"], kv, workers=cores)
+    t0 = time.perf_counter()
+    run(q, k, v, nh, sl)
+    t1 = time.perf_counter() - t0
+    nh = int(max(1, min(w.H, cores, target_s // max(t1, 1e-3))))
+    if nh > 1:
+        sl = (slice(0, 1), slice(0, nh))
+        q, k, v = (inp[n][sl] for n in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        run(q, k, v, nh, sl)
         t1 = time.perf_counter() - t0
     sw = S.Workload(w.name, 1, nh, w.N, w.d, w.dtype, w.causal, w.seeds,
                     w.backward)
@@ -121,9 +127,15 @@ def cpu_baseline(w: S.Workload, inp: dict, target_s: float = 15.0) -> dict:
                     break
     except OSError:
         pass
+    if inp.get("signs") is not None:
+        what = ("fp64 numpy model of the FP8 path (rotation, block "
+                "quantisation, fp64 attention), forward")
+    else:
+        what = ("fp64 numpy oracle, "
+                + ("forward+backward" if w.backward else "forward"))
     return {"value": flops / t1 / 1e12, "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle", "cpu_model": model, "blas_threads": cores,
-            "sample": (f"fp64 numpy oracle, {'forward+backward' if w.backward else 'forward'}"
+            "sample": (what +
                        f" of batch 0, heads 0..{nh - 1} of {w.name} "
                        f"(N={w.N}, d={w.d}); {t1:.2f} s; {cores} threads "
                        "(BLAS pool + one worker thread per head)")}
@@ -132,7 +144,16 @@ def cpu_baseline(w: S.Workload, inp: dict, target_s: float = 15.0) -> dict:
 # rocprofv3 kernel-name fragment -> bench step (all variants of a step)
 KERNEL_KEYS = (("bwd_dkdv_", "bwd_dkdv"), ("bwd_dq_", "bwd_dq"),
                ("bwd_preprocess_", "bwd_preprocess"),
-               ("fwd_bf16_", "fwd"), ("fwd_f32_", "fwd"))
+               ("fwd_bf16_", "fwd"), ("fwd_f32_", "fwd"),
+               ("fwd_fp8_", "fwd_fp8"), ("fp8_quant_", "fp8_quantize"))
+
+
+def fp8_workspace_bytes(w: S.Workload) -> int:
+    """Quantised Q, K (rows of 144 or 80 bytes) and V (80 bytes per channel
+    per 64 keys) of the FP8 path."""
+    np_ = -(-w.N // 64) * 64
+    rb = 144 if w.d == 128 else 80
+    return 2 * w.B * w.H * np_ * rb + w.B * w.H * (np_ // 64) * w.d * 80
 
 
 def algorithmic_bytes(w: S.Workload, kernel: str) -> int:
@@ -141,6 +162,10 @@ def algorithmic_bytes(w: S.Workload, kernel: str) -> int:
     el = 4 if w.dtype == "f32" else 2
     t = w.B * w.H * w.N * w.d * el          # one [B,H,N,d] tensor
     r = w.B * w.H * w.N * 4                 # one float32 [B,H,N] row vector
+    if kernel == "fp8_quantize":                 # Q,K,V -> workspace
+        return 3 * t + fp8_workspace_bytes(w)
+    if kernel == "fwd_fp8":                      # workspace -> O, LSE
+        return fp8_workspace_bytes(w) + t + r
     return {"fwd": 3 * t + t + r,             # Q,K,V -> O, LSE
             "bwd_preprocess": 2 * t + r,      # O, dO -> D
             "bwd_dkdv": 4 * t + 2 * r + 2 * t,  # Q,K,V,dO,LSE,D -> dK,dV
@@ -177,7 +202,9 @@ def write_traffic(w: S.Workload, csvs, command, mib) -> int:
     cal_bytes = mib * (1 << 20)
     f_scale = cal_bytes / (fetch["copy_calibration"][0] * 1024.0)
     w_scale = cal_bytes / (write["copy_calibration"][0] * 1024.0)
-    src = {"fwd": ["fa_fwd.hip", "fa_common.h"]}
+    src = {"fwd": ["fa_fwd.hip", "fa_common.h"],
+           "fwd_fp8": ["fa_fp8.hip", "fa_common.h"],
+           "fp8_quantize": ["fa_fp8.hip", "fa_common.h"]}
     entry = {}
     for k in fetch:
         if k == "copy_calibration" or k not in write:
@@ -465,6 +492,12 @@ def main(argv=None) -> int:
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     scale, causal = inp["scale"], inp["causal"]
+    fp8 = inp.get("signs") is not None
+    if fp8:
+        signs = torch.from_numpy(inp["signs"]).to(dev)
+        ws8 = torch.empty(fa.fa_fp8_workspace_size(w.B, w.H, w.N, w.d),
+                          dtype=torch.uint8, device=dev)
+        score_scale = float(np.float32(scale) / np.float32(w.d))
     if w.backward:
         ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.N, w.d),
                          dtype=torch.uint8, device=dev)
@@ -474,12 +507,20 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream(dev)
     names = ["fwd"] + (["bwd_preprocess", "bwd_dkdv", "bwd_dq"]
                        if w.backward else [])
+    if fp8:
+        names = ["fp8_quantize", "fwd_fp8"]
 
     def step(events=None):
         def mark(i):
             if events is not None:
                 events[i].record(stream)
         mark(0)
+        if fp8:
+            fa.fa_fp8_quantize(q, k, v, signs, ws8)
+            mark(1)
+            fa.fa_fwd_fp8_quantized(ws8, o, lse, score_scale, causal)
+            mark(2)
+            return
         if w.dtype == "f32":
             fa.fa_fwd_f32(q, k, v, o, lse, scale, causal)
         elif bmask is not None:
@@ -527,13 +568,19 @@ def main(argv=None) -> int:
     bwd_flops = 10.0 * w.d * pairs if w.backward else 0.0
     step_flops = fwd_flops + bwd_flops
     value = step_flops / (ms_step * 1e-3) / 1e12
-    peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+    peak = (PEAK_F32_TFLOPS if w.dtype == "f32" else
+            PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS)
 
     if w.backward:
         # fa_bwd_dkdv produces dK and dV: S = Q K^T, dP = dO V^T, dV += P^T dO
         # and dK += dS^T Q, 2d FLOP each per visible pair.
         dom, dom_flops, src = ("bwd_dkdv", 8.0 * w.d * pairs,
                                ["fa_bwd.hip", "fa_common.h"])
+    elif fp8:
+        # the attention kernel on the quantised operands (the quantisation
+        # pass is HBM-bound and reported in kernel_ms)
+        dom, dom_flops, src = ("fwd_fp8", fwd_flops,
+                               ["fa_fp8.hip", "fa_common.h"])
     else:
         dom, dom_flops, src = "fwd", fwd_flops, ["fa_fwd.hip", "fa_common.h"]
     dom_ms = per_kernel[dom]
@@ -559,7 +606,7 @@ def main(argv=None) -> int:
                                          for t in (dq, dk, dv)))
 
     ceiling = None
-    if not args.no_ceiling and w.dtype == "bf16":
+    if not args.no_ceiling and w.dtype == "bf16" and not fp8:
         log("[bench] vendor GEMM calibration of the matrix-core rate")
         ceiling = mfma_ceiling(dev)
         ceiling["frac_of_random"] = round(achieved / ceiling["random_tflops"], 4)
@@ -574,7 +621,7 @@ def main(argv=None) -> int:
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32" if w.dtype == "f32" else "bf16",
+        "dtype": "f32" if w.dtype == "f32" else "fp8_e4m3" if fp8 else "bf16",
         "data": "synthetic (seeded iid N(0,1) inputs of the workload's shape)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal,
@@ -582,12 +629,23 @@ def main(argv=None) -> int:
                    "parallelism": "single GPU"},
         "frac_of_peak": round(value / peak, 4),
         "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},
-        "fwd_tflops": round(fwd_flops / (per_kernel["fwd"] * 1e-3) / 1e12, 2),
+        "fwd_tflops": round(fwd_flops / (per_kernel[dom if fp8 else "fwd"]
+                                         * 1e-3) / 1e12, 2),
         "roofline": roofline,
         "mfma_ceiling": ceiling,
         "cpu_baseline": cpu,
         "sanity": check,
     }
+    if fp8:
+        qb = algorithmic_bytes(w, "fp8_quantize")
+        out["fp8"] = {
+            "quantize_ms": round(per_kernel["fp8_quantize"], 4),
+            "quantize_algorithmic_bytes": qb,
+            "quantize_gb_per_s": round(qb / (per_kernel["fp8_quantize"] * 1e-3) / 1e9, 1),
+            "rotation": "randomised Hadamard (seeded signs)",
+            "blocks": "32 values, E8M0 scale; E4M3 codes"}
+        out["data"] = ("synthetic (seeded iid N(0,1) bf16 inputs of the "
+                       "workload's shape, quantised on the GPU each step)")
     if w.backward:
         bwd_ms = sum(per_kernel[n] for n in names[1:])
         out["bwd_tflops"] = round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2)

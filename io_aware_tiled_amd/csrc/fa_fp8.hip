@@ -9,11 +9,12 @@
 // codes) and the workspace layout are stated in include/fa.h.
 //
 // Two steps:
-//   1. Quantisation (HBM-bound): one pass over Q and K rotates each row with
-//      the fast Walsh-Hadamard transform (float32, sixteen or eight lanes per
-//      row, stages in order) and writes E4M3 codes plus one E8M0 scale byte
-//      per 32 coordinates; one pass over V writes each 64-key tile
-//      transposed (channel-major) with a scale byte per 32 keys.  K rows are
+//   1. Quantisation (HBM-bound, one launch): each row of Q and K is rotated
+//      with the fast Walsh-Hadamard transform (float32, one lane per 32
+//      coordinates, stages in order) and written as E4M3 codes plus one
+//      E8M0 scale byte per 32 coordinates; each 64-key tile of V is staged
+//      through LDS and written transposed (channel-major) with a scale byte
+//      per 32 keys.  K rows are
 //      permuted inside each 64-key tile so that the score accumulator hands
 //      every lane the keys its P operand needs (below).
 //   2. Attention: the online softmax of the bf16 kernels, with both matrix
@@ -33,6 +34,7 @@
 #include "fa_common.h"
 #include "fa_launch.h"
 
+
 namespace fa {
 
 namespace {
@@ -40,7 +42,7 @@ namespace {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kBC = 64;          // keys per tile
-constexpr int kNW = 8;           // wavefronts per attention workgroup
+constexpr int kNW = 4;           // wavefronts per attention workgroup
 constexpr int kBR = 32 * kNW;    // query rows per attention workgroup
 constexpr int kNS = 4;           // LDS stages of the K/V ring
 constexpr int kVRB = FA_FP8_V_ROW_BYTES;
@@ -80,48 +82,52 @@ __device__ __forceinline__ unsigned pack_fp8x4(float a, float b, float c,
 }
 
 // ---------------------------------------------------------------------------
-// Step 1a: rotate and quantise the rows of Q or K.  D/8 lanes per row, eight
-// coordinates per lane (coordinate 8 li + e).  Rows n in [N, Np) are zeros.
+// Step 1: one launch quantises Q, K and V.  Workgroups [0, nrb) take rows of
+// Q, [nrb, 2 nrb) rows of K, the rest 64-key tiles of V.
+constexpr int kQThreads = 256;
+
+// One row of Q or K: D/32 lanes, lane li owning coordinates [32 li, +32)
+// (one scale block).  Walsh-Hadamard stages t = 0..4 inside the lane, then
+// t = 5 (and 6) across lanes: the lower coordinate of a pair becomes a + b,
+// the upper a - b, in float32, in stage order.
 template <int D, bool PERMUTE>
-__global__ __launch_bounds__(256) void fp8_quant_rows_kernel(
-    const uint16_t* __restrict__ src, const int8_t* __restrict__ signs,
-    uint8_t* __restrict__ dst, int N, int Np, long long total_rows) {
-  constexpr int LPR = D / 8;
-  constexpr int RPB = 256 / LPR;
+__device__ __forceinline__ void quant_row(const uint16_t* __restrict__ src,
+                                          const int8_t* __restrict__ signs,
+                                          uint8_t* __restrict__ dst, int N,
+                                          int Np, long long grow, bool live) {
+  constexpr int LPR = D / 32;
   constexpr int RB = FA_FP8_ROW_BYTES(D);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int li = tid % LPR;
-  const long long grow = (long long)blockIdx.x * RPB + tid / LPR;
-  const bool live = grow < total_rows;
+  const int lane = threadIdx.x & 63;
+  const int li = lane % LPR;
   const long long bh = live ? grow / Np : 0;
   const int n = live ? (int)(grow % Np) : 0;
 
-  float x[8];
+  float x[32];
   if (live && n < N) {
-    const u32x4 raw =
-        *(const u32x4*)(src + ((size_t)bh * N + n) * D + 8 * li);
+    const uint16_t* srow = src + ((size_t)bh * N + n) * D + 32 * li;
+    u32x4 raw[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = __uint_as_float(raw[i] << 16);
-      x[2 * i + 1] = __uint_as_float(raw[i] & 0xFFFF0000u);
-    }
+    for (int i = 0; i < 4; ++i) raw[i] = *(const u32x4*)(srow + 8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        x[8 * i + 2 * c] = __uint_as_float(raw[i][c] << 16);
+        x[8 * i + 2 * c + 1] = __uint_as_float(raw[i][c] & 0xFFFF0000u);
+      }
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    for (int e = 0; e < 32; ++e) x[e] = 0.f;
   }
 
   if (signs != nullptr) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (signs[8 * li + e] < 0) x[e] = -x[e];
-    // Walsh-Hadamard stages t = 0, 1, 2 inside the lane (coordinate bit t =
-    // bit t of e), then t = 3 .. log2(D) - 1 across lanes (bit t - 3 of li):
-    // the lower coordinate of a pair becomes a + b, the upper a - b.
+    for (int e = 0; e < 32; ++e)
+      if (signs[32 * li + e] < 0) x[e] = -x[e];
 #pragma unroll
-    for (int h = 1; h < 8; h *= 2) {
+    for (int h = 1; h < 32; h *= 2) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < 32; ++e) {
         if ((e & h) == 0) {
           const float a = x[e], b = x[e + h];
           x[e] = a + b;
@@ -133,37 +139,32 @@ __global__ __launch_bounds__(256) void fp8_quant_rows_kernel(
     for (int lb = 1; lb < LPR; lb *= 2) {
       const bool upper = (li & lb) != 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < 32; ++e) {
         const float p = __shfl_xor(x[e], lb, 64);
         x[e] = upper ? p - x[e] : x[e] + p;
       }
     }
   }
 
-  // Block of 32 coordinates = lanes 4b .. 4b + 3 of the row.
   float am = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(x[e]));
-  am = fmaxf(am, __shfl_xor(am, 1, 64));
-  am = fmaxf(am, __shfl_xor(am, 2, 64));
+  for (int e = 0; e < 32; ++e) am = fmaxf(am, fabsf(x[e]));
   const int ex = block_exponent(am);
   const float inv = pow2_neg(ex);
-  u32x2 codes;
-  codes[0] = pack_fp8x4(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
-  codes[1] = pack_fp8x4(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv);
-
+  u32x4 codes[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    codes[i / 4][i % 4] = pack_fp8x4(x[4 * i] * inv, x[4 * i + 1] * inv,
+                                     x[4 * i + 2] * inv, x[4 * i + 3] * inv);
   // Scale bytes, gathered by the row's first lane: byte u (D/64) + m is the
   // scale of block 2m + u.
   const unsigned sbyte = (unsigned)(ex + 127);
-  const int base = lane - li;
   unsigned tail = 0;
 #pragma unroll
-  for (int blk = 0; blk < D / 32; ++blk) {
-    const unsigned s = (unsigned)__shfl((int)sbyte, base + 4 * blk, 64);
-    const int u = blk % 2, m = blk / 2;
-    tail |= s << (8 * (u * (D / 64) + m));
+  for (int blk = 0; blk < LPR; ++blk) {
+    const unsigned sb = (unsigned)__shfl((int)sbyte, lane - li + blk, 64);
+    tail |= sb << (8 * ((blk % 2) * (D / 64) + blk / 2));
   }
-
   if (!live) return;
   int row = n;
   if (PERMUTE) {
@@ -172,26 +173,59 @@ __global__ __launch_bounds__(256) void fp8_quant_rows_kernel(
     row = (n & ~63) + 32 * t + 8 * (r >> 2) + 4 * u + (r & 3);
   }
   uint8_t* drow = dst + ((size_t)bh * Np + row) * RB;
-  *(u32x2*)(drow + 8 * li) = codes;
+  *(u32x4*)(drow + 32 * li) = codes[0];
+  *(u32x4*)(drow + 32 * li + 16) = codes[1];
   if (li == 0) *(u32x4*)(drow + D) = u32x4{tail, 0u, 0u, 0u};
 }
 
-// Step 1b: quantise V into channel-major 64-key tiles.  Thread (c, u) owns
-// channel c, keys 32u .. 32u + 31 of the tile.
 template <int D>
-__global__ __launch_bounds__(2 * D) void fp8_quant_v_kernel(
-    const uint16_t* __restrict__ V, uint8_t* __restrict__ dst, int N,
-    int ntiles) {
-  const int tile = blockIdx.x % ntiles;
-  const long long bh = blockIdx.x / ntiles;
+__global__ __launch_bounds__(kQThreads) void fp8_quant_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int8_t* __restrict__ signs,
+    uint8_t* __restrict__ q8, uint8_t* __restrict__ k8,
+    uint8_t* __restrict__ v8, int N, int Np, long long rows, int nrb) {
+  constexpr int RPB = kQThreads / (D / 32);     // rows per workgroup
+  constexpr int TPW = kQThreads / (2 * D);      // V tiles per workgroup
+  constexpr int VST = D + 8;                    // LDS row stride (bf16)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[TPW][kBC * VST];
   const int tid = threadIdx.x;
-  const int c = tid >> 1, u = tid & 1;
-  const int k0 = tile * kBC + 32 * u;
-  const uint16_t* vh = V + (size_t)bh * N * D + c;
+  const int wg = blockIdx.x;
+  if (wg < 2 * nrb) {
+    const bool is_k = wg >= nrb;
+    const long long grow = (long long)(is_k ? wg - nrb : wg) * RPB + tid / (D / 32);
+    const bool live = grow < rows;
+    if (is_k) quant_row<D, true>(k, signs, k8, N, Np, grow, live);
+    else quant_row<D, false>(q, signs, q8, N, Np, grow, live);
+    return;
+  }
+  // V: tile (bh, j); coalesced 16-byte loads of the 64 x D bf16 tile into
+  // LDS, then thread (c, u) quantises channel c, keys 32u .. 32u + 31.
+  const int ntiles = Np / kBC;
+  const long long vt = (long long)(wg - 2 * nrb) * TPW + tid / (2 * D);
+  const long long nvt = rows / kBC;
+  const int sub = tid / (2 * D);
+  const int ltid = tid % (2 * D);
+  const bool live = vt < nvt;
+  const long long bh = live ? vt / ntiles : 0;
+  const int j = live ? (int)(vt % ntiles) : 0;
+  const uint16_t* vh = v + (size_t)bh * N * D;
+  constexpr int CPT = kBC * D / 8 / (2 * D);    // 16-byte chunks per thread
+#pragma unroll
+  for (int r = 0; r < CPT; ++r) {
+    const int c = ltid + 2 * D * r;
+    const int row = c / (D / 8), col = 8 * (c % (D / 8));
+    const int key = j * kBC + row;
+    u32x4 val = u32x4{0u, 0u, 0u, 0u};
+    if (live && key < N) val = *(const u32x4*)(vh + (size_t)key * D + col);
+    *(u32x4*)(&tile[sub][row * VST + col]) = val;
+  }
+  __syncthreads();
+  if (!live) return;
+  const int c = ltid >> 1, u = ltid & 1;
   float x[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i)
-    x[i] = k0 + i < N ? bf16_to_f32(vh[(size_t)(k0 + i) * D]) : 0.f;
+    x[i] = bf16_to_f32(tile[sub][(32 * u + i) * VST + c]);
   float am = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(x[i]));
@@ -202,7 +236,7 @@ __global__ __launch_bounds__(2 * D) void fp8_quant_v_kernel(
   for (int i = 0; i < 8; ++i)
     w[i / 4][i % 4] = pack_fp8x4(x[4 * i] * inv, x[4 * i + 1] * inv,
                                  x[4 * i + 2] * inv, x[4 * i + 3] * inv);
-  uint8_t* drow = dst + (((size_t)bh * ntiles + tile) * D + c) * kVRB;
+  uint8_t* drow = v8 + (((size_t)bh * ntiles + j) * D + c) * kVRB;
   *(u32x4*)(drow + 32 * u) = w[0];
   *(u32x4*)(drow + 32 * u + 16) = w[1];
   const unsigned s0 = (unsigned)(ex + 127);
@@ -211,10 +245,14 @@ __global__ __launch_bounds__(2 * D) void fp8_quant_v_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Step 2: attention on the quantised operands.  One workgroup = 8
-// wavefronts = 256 query rows (32 per wavefront, one query per lane pair);
-// K and V tiles go from HBM to LDS by DMA through four stages, tile j
-// issuing tile j + 3, one barrier per tile.
+// Step 2: attention on the quantised operands.  One workgroup = 4
+// wavefronts = 128 query rows (32 per wavefront, one query per lane pair),
+// two workgroups per CU: the two wavefronts on a SIMD belong to different
+// workgroups, so their matrix-core and VALU phases drift apart and overlap
+// (a software pipeline inside each wavefront, as in the bf16 kernels,
+// measured slower here: it needs the score registers of two tiles).  K and
+// V tiles go from HBM to LDS by DMA through four stages, tile j issuing
+// tile j + 3, one barrier per tile.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_rsrc(const uint8_t* p,
                                                             int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, bytes,
@@ -235,7 +273,7 @@ __device__ __forceinline__ i32x8 join8(u32x4 lo, u32x4 hi) {
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * kNW, 1) void fwd_fp8_kernel(
+__global__ __launch_bounds__(64 * kNW, 2) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8,
     const uint8_t* __restrict__ V8, uint16_t* __restrict__ O,
     float* __restrict__ LSE, int N, int Np, int n_qblk, float c_log2) {
@@ -465,30 +503,22 @@ int launch_fp8_quantize(const uint16_t* q, const uint16_t* k,
                         int B, int H, int N, int d, hipStream_t stream) {
   const long long BH = (long long)B * H;
   const int Np = (N + kBC - 1) / kBC * kBC;
-  const int ntiles = Np / kBC;
   const int RB = FA_FP8_ROW_BYTES(d);
   const long long rows = BH * Np;
   uint8_t* q8 = ws;
   uint8_t* k8 = ws + (size_t)rows * RB;
   uint8_t* v8 = ws + 2 * (size_t)rows * RB;
-  const int rpb = 256 / (d / 8);
-  const dim3 grid_rows((unsigned)((rows + rpb - 1) / rpb));
-  const dim3 grid_v((unsigned)(BH * ntiles));
-  if (d == 128) {
-    hipLaunchKernelGGL((fp8_quant_rows_kernel<128, false>), grid_rows, dim3(256), 0,
-                       stream, q, signs, q8, N, Np, rows);
-    hipLaunchKernelGGL((fp8_quant_rows_kernel<128, true>), grid_rows, dim3(256), 0,
-                       stream, k, signs, k8, N, Np, rows);
-    hipLaunchKernelGGL((fp8_quant_v_kernel<128>), grid_v, dim3(256), 0, stream,
-                       v, v8, N, ntiles);
-  } else {
-    hipLaunchKernelGGL((fp8_quant_rows_kernel<64, false>), grid_rows, dim3(256), 0,
-                       stream, q, signs, q8, N, Np, rows);
-    hipLaunchKernelGGL((fp8_quant_rows_kernel<64, true>), grid_rows, dim3(256), 0,
-                       stream, k, signs, k8, N, Np, rows);
-    hipLaunchKernelGGL((fp8_quant_v_kernel<64>), grid_v, dim3(128), 0, stream,
-                       v, v8, N, ntiles);
-  }
+  const int rpb = kQThreads / (d / 32);
+  const int tpw = kQThreads / (2 * d);
+  const int nrb = (int)((rows + rpb - 1) / rpb);
+  const int nvb = (int)((rows / kBC + tpw - 1) / tpw);
+  const dim3 grid((unsigned)(2 * nrb + nvb)), block(kQThreads);
+  if (d == 128)
+    hipLaunchKernelGGL((fp8_quant_kernel<128>), grid, block, 0, stream, q, k,
+                       v, signs, q8, k8, v8, N, Np, rows, nrb);
+  else
+    hipLaunchKernelGGL((fp8_quant_kernel<64>), grid, block, 0, stream, q, k,
+                       v, signs, q8, k8, v8, N, Np, rows, nrb);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
