@@ -1,0 +1,55 @@
+"""fp64 CPU oracle for causal linear attention -- TEST INFRASTRUCTURE ONLY.
+
+Like the rest of this package it is imported only by the tests, the smoke
+check and the benchmark's CPU-baseline leg; it shares no code with the HIP
+library or its binding.
+
+Pages cited:
+  [LA2] "Lightning Attention-2: A Free Lunch for Handling Unlimited Sequence
+        Lengths in Large Language Models" (abstract page): linear attention
+        processed in blocks, with ordinary attention-style computation inside
+        a block and the linear-attention kernel trick between blocks.
+  [GLA] "[Paper review] Gated Linear Attention Transformers with
+        Hardware-Efficient Training" (review page), abstract and "proposed
+        method": linear attention is also an RNN with a matrix-valued hidden
+        state; FLASHLINEARATTENTION combines a recurrence between chunks with
+        parallel computation inside a chunk.
+
+What it computes.  The pages give no formulas.  The reading taken (also in
+the design notes): causal linear attention without softmax, normalisation,
+decay or gates,
+    O_i = scale * sum_{j <= i} (q_i . k_j) v_j,   i.e.  O = scale * tril(Q K^T) V,
+per (batch, head), the form that both the block split of [LA2] and the
+chunkwise/recurrent forms of [GLA] compute exactly.  The oracle is that
+quadratic definition in float64, rows in chunks (each row computed whole).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["linear_attention_fwd", "linear_pairs"]
+
+
+def linear_attention_fwd(q, k, v, scale, row_chunk=1024):
+    """O = scale * tril(Q K^T) V for q, k, v [B, H, N, d]; float64 out."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    scale = float(scale)
+    B, H, N, d = q.shape
+    o = np.zeros((B, H, N, v.shape[-1]), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, N, row_chunk):
+                r1 = min(N, r0 + row_chunk)
+                a = q[b, h, r0:r1] @ k[b, h, :r1].T          # [rows, keys]
+                i = np.arange(r0, r1)[:, None]
+                j = np.arange(r1)[None, :]
+                a = np.where(j <= i, a, 0.0)
+                o[b, h, r0:r1] = scale * (a @ v[b, h, :r1])
+    return o
+
+
+def linear_pairs(N: int, B: int = 1, H: int = 1) -> int:
+    """Visible (query, key) pairs of the causal mask over B*H heads."""
+    return B * H * N * (N + 1) // 2

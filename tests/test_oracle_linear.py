@@ -1,0 +1,160 @@
+"""Pins for the causal linear-attention oracle (oracle/linear.py), CPU only.
+
+Pages: "Lightning Attention-2: A Free Lunch for Handling Unlimited Sequence
+Lengths in Large Language Models" (abstract: intra-block attention-style
+computation, inter-block kernel trick) and "[Paper review] Gated Linear
+Attention Transformers with Hardware-Efficient Training" (abstract: linear
+attention as an RNN with a matrix-valued hidden state; "proposed method":
+chunkwise form, recurrence between chunks, parallel inside a chunk).
+
+The oracle is the quadratic definition O = scale * tril(Q K^T) V.  It is
+pinned by forms computed differently: exactly rounded brute force, the
+recurrent form with a d x d state, the chunkwise intra/inter split with
+ragged chunks, closed forms (N = 1; prefix sums when every score is 1),
+linearity; plus planted mistakes.
+"""
+import math
+import types
+
+import numpy as np
+import pytest
+
+import oracle.linear as OL
+
+
+def _rand(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _close(a, b, tol, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol, (what, err, tol)
+
+
+def pin_bruteforce(m):
+    """Explicit loops with exactly rounded sums (math.fsum)."""
+    for N, d, dv in ((1, 1, 1), (2, 3, 2), (5, 2, 3), (9, 4, 4)):
+        q, k, v = _rand(1, 1, 1, N, d), _rand(2, 1, 1, N, d), _rand(3, 1, 1, N, dv)
+        o = m.linear_attention_fwd(q, k, v, 0.7)
+        ref = np.zeros((N, dv))
+        for i in range(N):
+            for c in range(dv):
+                ref[i, c] = 0.7 * math.fsum(
+                    math.fsum(q[0, 0, i, t] * k[0, 0, j, t] for t in range(d))
+                    * v[0, 0, j, c] for j in range(i + 1))
+        _close(o[0, 0], ref, 1e-12, f"brute N={N}")
+
+
+def pin_recurrent(m):
+    """The RNN form: S_i = S_{i-1} + k_i^T v_i (d x d), o_i = scale q_i S_i."""
+    B, H, N, d = 2, 2, 37, 8
+    q, k, v = _rand(4, B, H, N, d), _rand(5, B, H, N, d), _rand(6, B, H, N, d)
+    o = m.linear_attention_fwd(q, k, v, 0.25)
+    ref = np.zeros_like(o)
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((d, d))
+            for i in range(N):
+                S += np.outer(k[b, h, i], v[b, h, i])
+                ref[b, h, i] = 0.25 * (q[b, h, i] @ S)
+    _close(o, ref, 1e-12, "recurrent")
+
+
+def _chunkwise(q, k, v, scale, C):
+    """Intra-chunk tril(Q_t K_t^T) V_t plus inter-chunk Q_t S_{t-1}."""
+    B, H, N, d = q.shape
+    o = np.zeros((B, H, N, v.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((d, v.shape[-1]))
+            for c0 in range(0, N, C):
+                c1 = min(N, c0 + C)
+                qt, kt, vt = q[b, h, c0:c1], k[b, h, c0:c1], v[b, h, c0:c1]
+                intra = np.tril(qt @ kt.T) @ vt
+                o[b, h, c0:c1] = scale * (intra + qt @ S)
+                S = S + kt.T @ vt
+    return o
+
+
+def pin_chunkwise(m):
+    """The block split of the pages with ragged chunks equals the oracle."""
+    B, H, N, d = 1, 3, 50, 6
+    q, k, v = _rand(7, B, H, N, d), _rand(8, B, H, N, d), _rand(9, B, H, N, d)
+    o = m.linear_attention_fwd(q, k, v, 1.3, row_chunk=16)
+    for C in (1, 3, 7, 16, 64):
+        _close(o, _chunkwise(q, k, v, 1.3, C), 1e-11, f"chunk {C}")
+
+
+def pin_closed_forms(m):
+    """N = 1: o = scale (q . k) v.  Every score 1 (k_j = e_0, q_i0 = 1):
+    o_i = scale * sum_{j <= i} v_j (a prefix sum)."""
+    q, k, v = _rand(10, 1, 1, 1, 5), _rand(11, 1, 1, 1, 5), _rand(12, 1, 1, 1, 3)
+    o = m.linear_attention_fwd(q, k, v, 0.5)
+    _close(o[0, 0, 0], 0.5 * float(q[0, 0, 0] @ k[0, 0, 0]) * v[0, 0, 0], 1e-14)
+    N = 23
+    q = np.zeros((1, 1, N, 4)); q[..., 0] = 1.0
+    k = np.zeros((1, 1, N, 4)); k[..., 0] = 1.0
+    v = _rand(13, 1, 1, N, 3)
+    o = m.linear_attention_fwd(q, k, v, 2.0, row_chunk=5)
+    _close(o[0, 0], 2.0 * np.cumsum(v[0, 0], axis=0), 1e-12, "prefix sums")
+
+
+def pin_linearity(m):
+    """Linear in V and in Q; homogeneous of degree 1 in K."""
+    B, H, N, d = 1, 1, 20, 4
+    q, k = _rand(14, B, H, N, d), _rand(15, B, H, N, d)
+    v1, v2 = _rand(16, B, H, N, d), _rand(17, B, H, N, d)
+    f = lambda q_, k_, v_: m.linear_attention_fwd(q_, k_, v_, 0.9)
+    _close(f(q, k, 2 * v1 - 3 * v2), 2 * f(q, k, v1) - 3 * f(q, k, v2), 1e-12)
+    _close(f(-1.5 * q, k, v1), -1.5 * f(q, k, v1), 1e-12)
+    _close(f(q, 4 * k, v1), 4 * f(q, k, v1), 1e-12)
+
+
+PINS = [pin_bruteforce, pin_recurrent, pin_chunkwise, pin_closed_forms,
+        pin_linearity]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
+def test_linear_oracle_pin(pin):
+    pin(OL)
+
+
+def test_linear_pairs():
+    assert OL.linear_pairs(4096, 4, 16) == 4 * 16 * 4096 * 4097 // 2
+    assert OL.linear_pairs(1) == 1
+
+
+MUTANTS = [
+    ("strict_mask", "a = np.where(j <= i, a, 0.0)", "a = np.where(j < i, a, 0.0)"),
+    ("reversed_mask", "a = np.where(j <= i, a, 0.0)", "a = np.where(j >= i, a, 0.0)"),
+    ("no_mask", "a = np.where(j <= i, a, 0.0)", "a = a"),
+    ("no_scale", "o[b, h, r0:r1] = scale * (a @ v[b, h, :r1])",
+     "o[b, h, r0:r1] = (a @ v[b, h, :r1])"),
+    ("keys_from_q", "a = q[b, h, r0:r1] @ k[b, h, :r1].T",
+     "a = q[b, h, r0:r1] @ q[b, h, :r1].T"),
+    ("chunk_local_keys", "a = q[b, h, r0:r1] @ k[b, h, :r1].T",
+     "a = q[b, h, r0:r1] @ np.concatenate([np.zeros_like(k[b, h, :r0]), k[b, h, r0:r1]]).T"),
+]
+
+
+def _mutant(old, new):
+    with open(OL.__file__) as f:
+        src = f.read()
+    assert src.count(old) >= 1, old
+    mod = types.ModuleType("oracle_linear_mutant")
+    exec(compile(src.replace(old, new), "oracle_linear_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[x[0] for x in MUTANTS])
+def test_planted_mistake_is_caught(name, old, new):
+    mod = _mutant(old, new)
+    for pin in PINS:
+        try:
+            pin(mod)
+        except Exception:
+            return
+    pytest.fail(f"no pin caught the planted mistake {name}")
