@@ -8,8 +8,9 @@ forward (fa_fwd) and the three backward stages (fa_bwd_preprocess,
 fa_bwd_dkdv, fa_bwd_dq).  Forward-only workloads run fa_fwd (or
 fa_fwd_f32 / fa_fwd_kvlen / fa_fwd_block_sparse); the FP8 workload runs
 fa_fp8_quantize then fa_fwd_fp8_quantized on the bf16 inputs (its roofline is
-the attention kernel against the fp8 matrix peak).  Inputs are resident in
-HBM before timing starts.
+the attention kernel against the fp8 matrix peak); the linear-attention
+workload runs fa_linear_fwd (HBM roofline).  Inputs are resident in HBM
+before timing starts.
 
 Throughput is algorithmic: 4d FLOP per visible (query, key) pair for the
 forward and 10d for the backward (causal: N(N+1)/2 pairs per head); masked
@@ -93,6 +94,10 @@ def cpu_baseline(w: S.Workload, inp: dict, target_s: float = 15.0) -> dict:
     kv = None if inp["kv_len"] is None else inp["kv_len"][:1]
     bm = inp.get("block_mask")
     def run(q, k, v, nh, sl):
+        if w.linear:
+            import oracle.linear
+            oracle.linear.linear_attention_fwd(q, k, v, inp["scale"])
+            return
         if inp.get("signs") is not None:
             import oracle.fp8
             oracle.fp8.fp8_forward(q, k, v, inp["scale"], inp["causal"],
@@ -118,6 +123,9 @@ def cpu_baseline(w: S.Workload, inp: dict, target_s: float = 15.0) -> dict:
                     w.backward)
     pairs = visible_pairs(sw, kv, None if bm is None else bm[:nh])
     flops = pairs * w.d * (4 + (10 if w.backward else 0))
+    if w.linear:
+        flops = linear_flops(S.Workload(w.name, 1, nh, w.N, w.d, w.dtype, True,
+                                        w.seeds, linear=True))
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -127,7 +135,9 @@ def cpu_baseline(w: S.Workload, inp: dict, target_s: float = 15.0) -> dict:
                     break
     except OSError:
         pass
-    if inp.get("signs") is not None:
+    if w.linear:
+        what = "fp64 numpy causal linear attention (quadratic definition)"
+    elif inp.get("signs") is not None:
         what = ("fp64 numpy model of the FP8 path (rotation, block "
                 "quantisation, fp64 attention), forward")
     else:
@@ -145,7 +155,19 @@ def cpu_baseline(w: S.Workload, inp: dict, target_s: float = 15.0) -> dict:
 KERNEL_KEYS = (("bwd_dkdv_", "bwd_dkdv"), ("bwd_dq_", "bwd_dq"),
                ("bwd_preprocess_", "bwd_preprocess"),
                ("fwd_bf16_", "fwd"), ("fwd_f32_", "fwd"),
-               ("fwd_fp8_", "fwd_fp8"), ("fp8_quant_", "fp8_quantize"))
+               ("fwd_fp8_", "fwd_fp8"), ("fp8_quant_", "fp8_quantize"),
+               ("linear_fwd_", "linear_fwd"))
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E bandwidth (published)
+LINEAR_CHUNK = 64
+
+
+def linear_flops(w: S.Workload) -> float:
+    """Algorithmic FLOPs of chunkwise causal linear attention: 4d per
+    visible (query, key) pair inside a 64-row chunk (Q K^T and A V), plus
+    2d^2 per row for Q S and 2d^2 per row for the state update K^T V."""
+    full, rem = divmod(w.N, LINEAR_CHUNK)
+    intra = full * LINEAR_CHUNK * (LINEAR_CHUNK + 1) // 2 + rem * (rem + 1) // 2
+    return w.B * w.H * (4.0 * w.d * intra + 4.0 * w.N * w.d * w.d)
 
 
 def fp8_workspace_bytes(w: S.Workload) -> int:
@@ -166,6 +188,8 @@ def algorithmic_bytes(w: S.Workload, kernel: str) -> int:
         return 3 * t + fp8_workspace_bytes(w)
     if kernel == "fwd_fp8":                      # workspace -> O, LSE
         return fp8_workspace_bytes(w) + t + r
+    if kernel == "linear_fwd":                   # Q,K,V -> O
+        return 4 * t
     return {"fwd": 3 * t + t + r,             # Q,K,V -> O, LSE
             "bwd_preprocess": 2 * t + r,      # O, dO -> D
             "bwd_dkdv": 4 * t + 2 * r + 2 * t,  # Q,K,V,dO,LSE,D -> dK,dV
@@ -203,6 +227,7 @@ def write_traffic(w: S.Workload, csvs, command, mib) -> int:
     f_scale = cal_bytes / (fetch["copy_calibration"][0] * 1024.0)
     w_scale = cal_bytes / (write["copy_calibration"][0] * 1024.0)
     src = {"fwd": ["fa_fwd.hip", "fa_common.h"],
+           "linear_fwd": ["fa_linear.hip", "fa_common.h"],
            "fwd_fp8": ["fa_fp8.hip", "fa_common.h"],
            "fp8_quantize": ["fa_fp8.hip", "fa_common.h"]}
     entry = {}
@@ -509,12 +534,18 @@ def main(argv=None) -> int:
                        if w.backward else [])
     if fp8:
         names = ["fp8_quantize", "fwd_fp8"]
+    if w.linear:
+        names = ["linear_fwd"]
 
     def step(events=None):
         def mark(i):
             if events is not None:
                 events[i].record(stream)
         mark(0)
+        if w.linear:
+            fa.fa_linear_fwd(q, k, v, o, scale)
+            mark(1)
+            return
         if fp8:
             fa.fa_fp8_quantize(q, k, v, signs, ws8)
             mark(1)
@@ -564,7 +595,7 @@ def main(argv=None) -> int:
     per_kernel = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]))
                   for j, n in enumerate(names)}
     pairs = visible_pairs(w, inp["kv_len"], inp.get("block_mask"))
-    fwd_flops = 4.0 * w.d * pairs
+    fwd_flops = linear_flops(w) if w.linear else 4.0 * w.d * pairs
     bwd_flops = 10.0 * w.d * pairs if w.backward else 0.0
     step_flops = fwd_flops + bwd_flops
     value = step_flops / (ms_step * 1e-3) / 1e12
@@ -576,6 +607,9 @@ def main(argv=None) -> int:
         # and dK += dS^T Q, 2d FLOP each per visible pair.
         dom, dom_flops, src = ("bwd_dkdv", 8.0 * w.d * pairs,
                                ["fa_bwd.hip", "fa_common.h"])
+    elif w.linear:
+        dom, dom_flops, src = ("linear_fwd", fwd_flops,
+                               ["fa_linear.hip", "fa_common.h"])
     elif fp8:
         # the attention kernel on the quantised operands (the quantisation
         # pass is HBM-bound and reported in kernel_ms)
@@ -597,6 +631,17 @@ def main(argv=None) -> int:
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel": dom, "kernel_ms": round(dom_ms, 4),
                 "algorithmic_flop_per_launch": dom_flops}
+    if w.linear:
+        # ~80 FLOP per compulsory byte at d = 128: HBM, not the matrix
+        # cores, bounds it.
+        nbytes = algorithmic_bytes(w, dom)
+        gbs = nbytes / (dom_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                    "kernel": dom, "kernel_ms": round(dom_ms, 4),
+                    "algorithmic_bytes_per_launch": nbytes,
+                    "algorithmic_flop_per_launch": dom_flops}
 
     # outputs of the timed run must be finite (parity itself is the tests' job)
     check = {"o_finite": bool(torch.isfinite(o.float()).all()),
@@ -606,7 +651,7 @@ def main(argv=None) -> int:
                                          for t in (dq, dk, dv)))
 
     ceiling = None
-    if not args.no_ceiling and w.dtype == "bf16" and not fp8:
+    if not args.no_ceiling and w.dtype == "bf16" and not fp8 and not w.linear:
         log("[bench] vendor GEMM calibration of the matrix-core rate")
         ceiling = mfma_ceiling(dev)
         ceiling["frac_of_random"] = round(achieved / ceiling["random_tflops"], 4)
@@ -625,11 +670,13 @@ def main(argv=None) -> int:
         "data": "synthetic (seeded iid N(0,1) inputs of the workload's shape)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal,
-                   "pass": "forward+backward" if w.backward else "forward",
+                   "pass": ("forward+backward" if w.backward else
+                            "linear attention forward" if w.linear else "forward"),
                    "parallelism": "single GPU"},
         "frac_of_peak": round(value / peak, 4),
         "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},
-        "fwd_tflops": round(fwd_flops / (per_kernel[dom if fp8 else "fwd"]
+        "fwd_tflops": round(fwd_flops / (per_kernel[dom if (fp8 or w.linear)
+                                                    else "fwd"]
                                          * 1e-3) / 1e12, 2),
         "roofline": roofline,
         "mfma_ceiling": ceiling,

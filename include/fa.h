@@ -7,6 +7,7 @@
  *        attention and the sequence-length question" (marketmaker.cc blog)
  *   [TW] "Flash-Attention 2 for performance optimisation" (Medium blog)
  *   [ZN] "Paper summary: FlashAttention" (zenn.dev)
+ *   [LA2], [GLA]: the linear-attention pages, cited at fa_linear_fwd
  *
  * Operation.  O = softmax(scale * Q K^T) V per (batch, head) ([MM] "Why
  * attention is memory-bound"), computed tile by tile with the online-softmax
@@ -198,6 +199,24 @@ int fa_fwd_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                const int8_t* signs, uint16_t* o, float* lse, void* workspace,
                size_t workspace_bytes, int B, int H, int N, int d,
                float scale, int causal, void* stream);
+
+/*
+ * Causal linear attention, forward ([LA2] "Lightning Attention-2: A Free
+ * Lunch for Handling Unlimited Sequence Lengths in Large Language Models",
+ * abstract: blocks with attention-style work inside and the linear-attention
+ * kernel trick between them; [GLA] "[Paper review] Gated Linear Attention
+ * Transformers with Hardware-Efficient Training": the chunkwise form, a
+ * recurrence between chunks with a matrix-valued state).  Reading: no
+ * softmax, normalisation, decay or gate:
+ *     O_i = scale * sum_{j <= i} (q_i . k_j) v_j      (O = scale tril(QK^T) V)
+ * computed per 64-row chunk t as scale (tril(Q_t K_t^T) V_t + Q_t S_{t-1})
+ * with the state S_t = S_{t-1} + K_t^T V_t kept in float32 and used in bf16.
+ *   q, k, v : [B,H,N,d] bf16, read only;  o : [B,H,N,d] bf16, written.
+ * d must be 64 or 128.  Errors as fa_fwd.
+ */
+int fa_linear_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                  uint16_t* o, int B, int H, int N, int d, float scale,
+                  void* stream);
 
 /*
  * The backward entry points below support head dimension d = 128 only; any

@@ -8,10 +8,12 @@ the GPU, the call raises.
 
 The functions named like the C ABI (``fa_fwd``, ``fa_fwd_kvlen``,
 ``fa_fwd_block_sparse``, ``fa_fwd_f32``, ``fa_fp8_quantize``,
-``fa_fwd_fp8_quantized``, ``fa_fwd_fp8``, ``fa_bwd``, ``fa_bwd_preprocess``,
+``fa_fwd_fp8_quantized``, ``fa_fwd_fp8``, ``fa_linear_fwd``, ``fa_bwd``,
+``fa_bwd_preprocess``,
 ``fa_bwd_dkdv``, ``fa_bwd_dq``, the workspace-size queries,
 ``fa_status_string``, ``fa_version``) take caller-allocated tensors exactly
-as the C calls take pointers.  ``forward``, ``forward_fp8`` and ``backward``
+as the C calls take pointers.  ``forward``, ``forward_fp8``,
+``linear_forward`` and ``backward``
 allocate the outputs with ``torch.empty`` on the inputs' device and call
 them.
 """
@@ -26,8 +28,8 @@ __all__ = [
     "fa_fwd", "fa_fwd_kvlen", "fa_fwd_f32", "fa_bwd_workspace_size",
     "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
     "fa_fwd_block_sparse", "fa_fp8_workspace_size", "fa_fp8_quantize",
-    "fa_fwd_fp8_quantized", "fa_fwd_fp8", "forward", "forward_fp8",
-    "backward", "EXPORTED_SYMBOLS",
+    "fa_fwd_fp8_quantized", "fa_fwd_fp8", "fa_linear_fwd", "forward",
+    "forward_fp8", "linear_forward", "backward", "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -56,6 +58,7 @@ _SIGS = {
     "fa_fp8_quantize": (_I, [_P] * 5 + [_S, _I, _I, _I, _I, _P]),
     "fa_fwd_fp8_quantized": (_I, [_P, _S, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_fp8": (_I, [_P] * 7 + [_S, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_linear_fwd": (_I, [_P] * 4 + [_I, _I, _I, _I, _F, _P]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -308,6 +311,17 @@ def fa_fwd_fp8(q, k, v, signs, o, lse, workspace, scale, causal,
     _check(st, "fa_fwd_fp8")
 
 
+def fa_linear_fwd(q, k, v, o, scale, stream=None):
+    """C fa_linear_fwd: causal linear attention on bf16 [B,H,N,d]."""
+    import torch
+    B, H, N, d = _bhnd(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _expect(t, torch.bfloat16, (B, H, N, d), n)
+    st = lib().fa_linear_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d,
+                             float(scale), _stream(q, stream))
+    _check(st, "fa_linear_fwd")
+
+
 # ------------------------------------------------------------- convenience
 
 def forward(q, k, v, *, causal=False, scale=None, kv_len=None,
@@ -352,6 +366,18 @@ def forward_fp8(q, k, v, signs=None, *, causal=False, scale=None,
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     fa_fwd_fp8(q, k, v, signs, o, lse, workspace, scale, causal, stream)
     return o, lse, workspace
+
+
+def linear_forward(q, k, v, *, scale=None, stream=None):
+    """Causal linear attention O = scale tril(Q K^T) V (scale defaults to
+    1/sqrt(d)); returns o."""
+    import torch
+    d = _bhnd(q)[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    fa_linear_fwd(q, k, v, o, scale, stream)
+    return o
 
 
 def backward(q, k, v, o, lse, dO, *, causal=False, scale=None, stream=None,

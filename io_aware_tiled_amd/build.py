@@ -21,7 +21,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
 
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_fp8.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_fp8.hip", "fa_linear.hip",
+           "fa_api.cpp"]
 
 # Per-source flags.  The VALU reads the score MFMAs' results, so MFMA
 # results are kept in VGPRs rather than AGPRs (which the VALU can only reach
@@ -29,7 +30,8 @@ SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_fp8.hip", "fa_api.cpp"]
 # AGPRs explicitly.
 SOURCE_FLAGS = {"fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                 "fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-                "fa_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+                "fa_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "fa_linear.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

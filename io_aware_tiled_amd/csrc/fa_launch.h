@@ -42,4 +42,9 @@ int launch_fwd_fp8(const uint8_t* ws, uint16_t* o, float* lse, int B, int H,
                    int N, int d, float score_scale, int causal,
                    hipStream_t stream);
 
+// Causal linear attention forward (chunkwise).
+int launch_linear_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      uint16_t* o, int B, int H, int N, int d, float scale,
+                      hipStream_t stream);
+
 }  // namespace fa

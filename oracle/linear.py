@@ -30,23 +30,29 @@ import numpy as np
 __all__ = ["linear_attention_fwd", "linear_pairs"]
 
 
-def linear_attention_fwd(q, k, v, scale, row_chunk=1024):
-    """O = scale * tril(Q K^T) V for q, k, v [B, H, N, d]; float64 out."""
+def linear_attention_fwd(q, k, v, scale, row_chunk=1024, rows=None):
+    """O = scale * tril(Q K^T) V for q, k, v [B, H, N, d]; float64 out.
+
+    rows: optional 1-D array of query indices; then only those rows are
+    computed and the output has that many rows."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     scale = float(scale)
     B, H, N, d = q.shape
-    o = np.zeros((B, H, N, v.shape[-1]), dtype=np.float64)
+    idx = np.arange(N) if rows is None else np.asarray(rows)
+    o = np.zeros((B, H, len(idx), v.shape[-1]), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            for r0 in range(0, N, row_chunk):
-                r1 = min(N, r0 + row_chunk)
-                a = q[b, h, r0:r1] @ k[b, h, :r1].T          # [rows, keys]
-                i = np.arange(r0, r1)[:, None]
-                j = np.arange(r1)[None, :]
+            for r0 in range(0, len(idx), row_chunk):
+                r1 = min(len(idx), r0 + row_chunk)
+                rr = idx[r0:r1]
+                n1 = int(rr.max()) + 1
+                a = q[b, h, rr] @ k[b, h, :n1].T             # [rows, keys]
+                i = rr[:, None]
+                j = np.arange(n1)[None, :]
                 a = np.where(j <= i, a, 0.0)
-                o[b, h, r0:r1] = scale * (a @ v[b, h, :r1])
+                o[b, h, r0:r1] = scale * (a @ v[b, h, :n1])
     return o
 
 

@@ -70,6 +70,7 @@ class Workload:
     block_seed: int | None = None    # block-sparse mask drawn from this seed
     block_density: float = 0.0
     sign_seed: int | None = None     # FP8 path: rotation signs from this seed
+    linear: bool = False             # causal linear attention (no softmax)
     description: str = ""
 
     @property
@@ -101,6 +102,10 @@ WORKLOADS = {
                  (701, 702, 703), sign_seed=709,
                  description="FP8 causal forward with incoherent processing "
                              "(bf16 inputs quantised on the GPU), head dim "
+                             "128"),
+        Workload("linear_causal_d128", 4, 16, 4096, 128, "bf16", True,
+                 (801, 802, 803), linear=True,
+                 description="causal linear attention (chunkwise), head dim "
                              "128"),
     ]
 }

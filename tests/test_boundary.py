@@ -34,6 +34,7 @@ def test_header_declares_expected_calls():
     for want in ["fa_fwd", "fa_fwd_kvlen", "fa_fwd_f32", "fa_bwd",
                  "fa_fwd_block_sparse", "fa_fp8_workspace_size",
                  "fa_fp8_quantize", "fa_fwd_fp8_quantized", "fa_fwd_fp8",
+                 "fa_linear_fwd",
                  "fa_bwd_workspace_size", "fa_status_string", "fa_version",
                  "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq"]:
         assert want in names
@@ -188,6 +189,17 @@ def test_fp8_argument_errors():
     assert full(wsb=nbytes - 256) == WORKSPACE
     # The workspace of a larger N does not fit a smaller one's size.
     assert quant(N=200, wsb=nbytes) == WORKSPACE
+
+
+def test_linear_argument_errors():
+    L = fa.lib()
+
+    def lin(q=A, o=A, B=1, N=64, d=128):
+        return L.fa_linear_fwd(q, A, A, o, B, 2, N, d, 0.1, None)
+    assert lin(q=None) == NULL and lin(o=None) == NULL
+    assert lin(B=0) == SHAPE and lin(N=-1) == SHAPE
+    assert lin(d=32) == HEADDIM and lin(d=256) == HEADDIM
+    assert lin(q=MIS) == ALIGN and lin(o=MIS) == ALIGN
 
 
 def test_python_binding_refuses_host_tensors():

@@ -102,6 +102,16 @@ def pin_closed_forms(m):
     _close(o[0, 0], 2.0 * np.cumsum(v[0, 0], axis=0), 1e-12, "prefix sums")
 
 
+def pin_row_subset(m):
+    """Rows computed alone equal the same rows of the full computation."""
+    B, H, N, d = 1, 2, 40, 5
+    q, k, v = _rand(18, B, H, N, d), _rand(19, B, H, N, d), _rand(20, B, H, N, d)
+    full = m.linear_attention_fwd(q, k, v, 0.6)
+    rows = np.array([0, 3, 17, 39])
+    _close(m.linear_attention_fwd(q, k, v, 0.6, rows=rows), full[:, :, rows],
+           1e-12, "row subset")
+
+
 def pin_linearity(m):
     """Linear in V and in Q; homogeneous of degree 1 in K."""
     B, H, N, d = 1, 1, 20, 4
@@ -114,7 +124,7 @@ def pin_linearity(m):
 
 
 PINS = [pin_bruteforce, pin_recurrent, pin_chunkwise, pin_closed_forms,
-        pin_linearity]
+        pin_row_subset, pin_linearity]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -131,12 +141,12 @@ MUTANTS = [
     ("strict_mask", "a = np.where(j <= i, a, 0.0)", "a = np.where(j < i, a, 0.0)"),
     ("reversed_mask", "a = np.where(j <= i, a, 0.0)", "a = np.where(j >= i, a, 0.0)"),
     ("no_mask", "a = np.where(j <= i, a, 0.0)", "a = a"),
-    ("no_scale", "o[b, h, r0:r1] = scale * (a @ v[b, h, :r1])",
-     "o[b, h, r0:r1] = (a @ v[b, h, :r1])"),
-    ("keys_from_q", "a = q[b, h, r0:r1] @ k[b, h, :r1].T",
-     "a = q[b, h, r0:r1] @ q[b, h, :r1].T"),
-    ("chunk_local_keys", "a = q[b, h, r0:r1] @ k[b, h, :r1].T",
-     "a = q[b, h, r0:r1] @ np.concatenate([np.zeros_like(k[b, h, :r0]), k[b, h, r0:r1]]).T"),
+    ("no_scale", "o[b, h, r0:r1] = scale * (a @ v[b, h, :n1])",
+     "o[b, h, r0:r1] = (a @ v[b, h, :n1])"),
+    ("keys_from_q", "a = q[b, h, rr] @ k[b, h, :n1].T",
+     "a = q[b, h, rr] @ q[b, h, :n1].T"),
+    ("chunk_local_keys", "a = q[b, h, rr] @ k[b, h, :n1].T",
+     "a = q[b, h, rr] @ np.concatenate([np.zeros_like(k[b, h, :rr[0]]), k[b, h, rr[0]:n1]]).T"),
 ]
 
 
