@@ -29,11 +29,13 @@
 //   * wavefronts 2 and 3 own the state: S^T += V_t^T K_t in fp32 registers
 //     (the same V_t^T operand; K_t's columns by transposed LDS reads), then
 //     write S_t^T as bf16 to the LDS buffer the next chunk reads.
-// Tiles are loaded one chunk ahead through registers into two LDS buffers;
+// Chunks go from HBM to LDS by DMA two chunks ahead through three stages;
 // one barrier per chunk orders every producer and consumer.
 #include "fa.h"
 #include "fa_common.h"
 #include "fa_launch.h"
+
+#include <type_traits>
 
 namespace fa {
 
@@ -42,6 +44,7 @@ namespace {
 constexpr int kLC = 64;          // rows per chunk
 constexpr int kLThreads = 256;   // four wavefronts
 constexpr int kVB = 32;          // value columns per workgroup
+constexpr int kLS = 3;           // LDS stages of the Q/K/V ring
 
 template <int D>
 struct LinTile {
@@ -49,10 +52,6 @@ struct LinTile {
   static constexpr int VST = kVB;            // V rows of 64 B: transposed
                                              // reads conflict-free
   static constexpr int SST = D + 8;          // S^T rows (row reads)
-  static constexpr int QK_CH = kLC * D / 8;  // 16-B chunks of a Q or K tile
-  static constexpr int V_CH = kLC * kVB / 8; // 16-B chunks of a V slice
-  static constexpr int QK_PT = QK_CH / kLThreads;
-  static_assert(QK_CH % kLThreads == 0 && V_CH == kLThreads, "tile split");
 };
 
 template <int D>
@@ -62,9 +61,9 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
     float scale) {
   using T = LinTile<D>;
   constexpr int NVB = D / kVB;
-  __shared__ __attribute__((aligned(16))) uint16_t lds_q[2][kLC * T::QST];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kLC * T::QST];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kLC * T::VST];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_q[kLS][kLC * T::QST];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kLS][kLC * T::QST];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[kLS][kLC * T::VST];
   __shared__ __attribute__((aligned(16))) uint16_t lds_s[2][kVB * T::SST];
 
   // Workgroup -> (head, value block): workgroups are dispatched round-robin
@@ -89,35 +88,50 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
   const uint16_t* Vh = V + head + kVB * vb;
   const int nchunks = (N + kLC - 1) / kLC;
 
-  // ---- register-staged loads of chunk t (rows >= N read as zero).
-  u32x4 qreg[T::QK_PT], kreg[T::QK_PT], vreg;
-  auto load = [&](int t) __attribute__((always_inline)) {
-    const int r0 = t * kLC;
+  // ---- chunk loads by LDS DMA (buffer loads that write LDS, 16 bytes per
+  // lane): slot p of a stage is 16 bytes of row p / RS; slots that are row
+  // padding, and rows >= N (the descriptors end at the head's last row),
+  // read zero.  Transfer g of a chunk (Q's, then K's, then V's) is issued
+  // by wavefront g % 4.
+  constexpr int QRS = T::QST / 8, VRS = T::VST / 8;     // 16-B slots per row
+  constexpr int QI = kLC * QRS / 64, VI = kLC * VRS / 64;
+  constexpr int NI = 2 * QI + VI;                       // transfers per chunk
+  constexpr int kIW = (NI + 3) / 4;
+  constexpr int kMinBatch = NI / 4;                     // of every wavefront
+  static_assert(kLC * QRS % 64 == 0 && kLC * VRS % 64 == 0 && kMinBatch < 60,
+                "DMA layout");
+  constexpr unsigned kOut = 1u << 30;
+  const unsigned lq0 = lds_addr(&lds_q[0][0]), lk0 = lds_addr(&lds_k[0][0]);
+  const unsigned lv0 = lds_addr(&lds_v[0][0]);
+  auto dma = [&](int t) __attribute__((always_inline)) {
+    const unsigned st = (unsigned)(t % kLS);
+    const int row0 = t * kLC;
+    // descriptors of this chunk's rows (they end at row N - 1)
+    const int bytes = min(N - row0, kLC) * D * 2;
+    const size_t base = (size_t)row0 * D;
+    const auto rq = __builtin_amdgcn_make_buffer_rsrc((void*)(Qh + base), (short)0,
+                                                      bytes, 0x00020000);
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc((void*)(Kh + base), (short)0,
+                                                      bytes, 0x00020000);
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)(Vh + base), (short)0,
+                                                      bytes - kVB * vb * 2, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < T::QK_PT; ++i) {
-      const int c = tid + kLThreads * i;
-      const int row = c / (D / 8), col = 8 * (c % (D / 8));
-      const bool ok = r0 + row < N;
-      const size_t off = (size_t)min(r0 + row, N - 1) * D + col;
-      const u32x4 a = *(const u32x4*)(Qh + off);
-      const u32x4 b = *(const u32x4*)(Kh + off);
-      qreg[i] = ok ? a : u32x4{0u, 0u, 0u, 0u};
-      kreg[i] = ok ? b : u32x4{0u, 0u, 0u, 0u};
+    for (int u = 0; u < kIW; ++u) {
+      const int g = w + 4 * u;
+      if (g < 2 * QI) {
+        const int gi = g % QI;
+        const int p = 64 * gi + lane, row = p / QRS, c = p % QRS;
+        const unsigned off = c < D / 8 ? (unsigned)((row * D + 8 * c) * 2) : kOut;
+        const unsigned lds = (g < QI ? lq0 : lk0) +
+                             st * (unsigned)(kLC * T::QST * 2) + 1024u * gi;
+        lds_dma16(g < QI ? rq : rk, lds, off);
+      } else if (g < NI) {
+        const int gi = g - 2 * QI;
+        const int p = 64 * gi + lane, row = p / VRS, c = p % VRS;
+        const unsigned off = (unsigned)((row * D + 8 * c) * 2);
+        lds_dma16(rv, lv0 + st * (unsigned)(kLC * T::VST * 2) + 1024u * gi, off);
+      }
     }
-    const int row = tid / (kVB / 8), col = 8 * (tid % (kVB / 8));
-    const u32x4 a = *(const u32x4*)(Vh + (size_t)min(r0 + row, N - 1) * D + col);
-    vreg = r0 + row < N ? a : u32x4{0u, 0u, 0u, 0u};
-  };
-  auto store = [&](int b) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < T::QK_PT; ++i) {
-      const int c = tid + kLThreads * i;
-      const int row = c / (D / 8), col = 8 * (c % (D / 8));
-      *(u32x4*)(&lds_q[b][row * T::QST + col]) = qreg[i];
-      *(u32x4*)(&lds_k[b][row * T::QST + col]) = kreg[i];
-    }
-    const int row = tid / (kVB / 8), col = 8 * (tid % (kVB / 8));
-    *(u32x4*)(&lds_v[b][row * T::VST + col]) = vreg;
   };
 
   // V_t^T operand (A: rows = the 32 value columns, contraction = keys) of
@@ -140,79 +154,98 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
   for (int e = tid; e < kVB * T::SST / 8; e += kLThreads)
     *(u32x4*)(&lds_s[1][8 * e]) = u32x4{0u, 0u, 0u, 0u};
 
-  if (nchunks > 0) load(0);
+  // Chunk t waits for its own transfers (issued two chunks earlier), then
+  // the barrier publishes them and the state chunk t - 1 wrote; the stage
+  // refilled after it was last read in chunk t - 1.
+  dma(0);
+  if (nchunks > 1) dma(1);
   for (int t = 0; t < nchunks; ++t) {
-    const int b = t & 1;
-    store(b);
+    const int b = t % kLS;
+    if (t + 1 < nchunks)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kMinBatch) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 1 < nchunks) load(t + 1);
+    if (t + 2 < nchunks) dma(t + 2);
+    const int sb = t & 1;
     const int r0 = t * kLC;
-    if (w < 2) {
-      // ---- query block qb = w: A^T = K Q^T for key blocks kb <= qb.
-      const int qb = w;
-      bf16x8 qf[D / 16];
+    // ---- query block QB (wavefront QB): A^T = K Q^T for key blocks
+    // kb <= QB and the inter-chunk term S_{t-1}^T Q^T, as independent MFMA
+    // chains interleaved (a dependent chain would wait out each MFMA's
+    // latency), then the causal mask, A^T -> bf16 and V_t^T A^T.
+    auto query_block = [&](auto qb_tag) __attribute__((always_inline)) {
+      constexpr int QB = decltype(qb_tag)::value;
+      const int sr = sb ^ 1;
+      f32x16 s[QB + 1], oin = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-        qf[kk] = *(const bf16x8*)(&lds_q[b][(32 * qb + lq) * T::QST + 16 * kk + 8 * hh]);
+      for (int kb = 0; kb <= QB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 qf =
+            *(const bf16x8*)(&lds_q[b][(32 * QB + lq) * T::QST + 16 * kk + 8 * hh]);
+#pragma unroll
+        for (int kb = 0; kb <= QB; ++kb)
+          s[kb] = mfma32x16(
+              *(const bf16x8*)(&lds_k[b][(32 * kb + lq) * T::QST + 16 * kk + 8 * hh]),
+              qf, s[kb]);
+        oin = mfma32x16(*(const bf16x8*)(&lds_s[sr][lq * T::SST + 16 * kk + 8 * hh]),
+                        qf, oin);
+      }
+      // causal mask inside the diagonal block: key 8(r/4) + 4hh + r%4
+      // against query lq.
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r / 4) + 4 * hh + (r % 4) > lq) s[QB][r] = 0.f;
       f32x16 oacc = f32x16{};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (kb > qb) break;
-        f32x16 s = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-          s = mfma32x16(*(const bf16x8*)(&lds_k[b][(32 * kb + lq) * T::QST + 16 * kk + 8 * hh]),
-                        qf[kk], s);
-        if (kb == qb) {
-          // causal mask inside the diagonal block: key 8(r/4) + 4hh + r%4
-          // against query lq.
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (8 * (r / 4) + 4 * hh + (r % 4) > lq) s[r] = 0.f;
-        }
+      for (int kb = 0; kb <= QB; ++kb)
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           f32x8 p;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) p[e] = s[8 * c + e];
+          for (int e = 0; e < 8; ++e) p[e] = s[kb][8 * c + e];
           oacc = mfma32x16(vt_frag(b, kb, c), to_bf16x8(p), oacc);
         }
-      }
-      // ---- inter-chunk term: O^T += S_{t-1}^T Q^T.
-      const int sr = b ^ 1;
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-        oacc = mfma32x16(*(const bf16x8*)(&lds_s[sr][lq * T::SST + 16 * kk + 8 * hh]),
-                         qf[kk], oacc);
-      // ---- store O rows r0 + 32qb + lq, columns 32vb + 8g + 4hh + 0..3.
-      const int row = r0 + 32 * qb + lq;
+      // ---- store O rows r0 + 32QB + lq, columns 32vb + 8g + 4hh + 0..3.
+      const int row = r0 + 32 * QB + lq;
       if (row < N) {
         uint16_t* orow = O + head + (size_t)row * D + kVB * vb;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           f32x4 x;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = oacc[4 * g + e] * scale;
+          for (int e = 0; e < 4; ++e)
+            x[e] = (oacc[4 * g + e] + oin[4 * g + e]) * scale;
           *(bf16x4*)(orow + 8 * g + 4 * hh) = to_bf16x4(x);
         }
       }
+    };
+    if (w == 0) {
+      query_block(std::integral_constant<int, 0>{});
+    } else if (w == 1) {
+      query_block(std::integral_constant<int, 1>{});
     } else {
-      // ---- state: S^T += V_t^T K_t for d-blocks dt of this wavefront,
-      // then S_t^T -> bf16 into the buffer chunk t + 1 reads.
+      // ---- state: S^T += V_t^T K_t for the d-blocks of this wavefront
+      // (their chains interleaved), then S_t^T -> bf16 into the buffer
+      // chunk t + 1 reads.
 #pragma unroll
-      for (int i = 0; i < NDT; ++i) {
-        const int dt = (w - 2) * NDT + i;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int c = 0; c < 2; ++c) {
+          const bf16x8 vt = vt_frag(b, kb, c);
+          const int key = 32 * kb + 16 * c + 4 * hh + (r16 >> 2);
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const int key = 32 * kb + 16 * c + 4 * hh + (r16 >> 2);
-            const int col = 32 * dt + 16 * dsub + 4 * (r16 & 3);
+          for (int i = 0; i < NDT; ++i) {
+            const int col = 32 * ((w - 2) * NDT + i) + 16 * dsub + 4 * (r16 & 3);
             const bf16x8 kc =
                 join_bf16(lds_read_tr16(&lds_k[b][key * T::QST + col]),
                           lds_read_tr16(&lds_k[b][(key + 8) * T::QST + col]));
-            sacc[i] = mfma32x16(vt_frag(b, kb, c), kc, sacc[i]);
+            sacc[i] = mfma32x16(vt, kc, sacc[i]);
           }
+        }
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) {
+        const int dt = (w - 2) * NDT + i;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           f32x4 x;
@@ -222,7 +255,7 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
           const i16x4 yi = __builtin_bit_cast(i16x4, y);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            lds_s[b][(8 * g + 4 * hh + e) * T::SST + 32 * dt + lq] = (uint16_t)yi[e];
+            lds_s[sb][(8 * g + 4 * hh + e) * T::SST + 32 * dt + lq] = (uint16_t)yi[e];
         }
       }
     }
