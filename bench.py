@@ -518,6 +518,9 @@ def main(argv=None) -> int:
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     scale, causal = inp["scale"], inp["causal"]
     fp8 = inp.get("signs") is not None
+    if w.linear:
+        nl = fa.fa_linear_workspace_size(w.B, w.H, w.N, w.d)
+        wsl = torch.empty(nl, dtype=torch.uint8, device=dev) if nl else None
     if fp8:
         signs = torch.from_numpy(inp["signs"]).to(dev)
         ws8 = torch.empty(fa.fa_fp8_workspace_size(w.B, w.H, w.N, w.d),
@@ -543,7 +546,7 @@ def main(argv=None) -> int:
                 events[i].record(stream)
         mark(0)
         if w.linear:
-            fa.fa_linear_fwd(q, k, v, o, scale)
+            fa.fa_linear_fwd(q, k, v, o, scale, wsl)
             mark(1)
             return
         if fp8:

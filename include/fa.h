@@ -212,11 +212,23 @@ int fa_fwd_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * computed per 64-row chunk t as scale (tril(Q_t K_t^T) V_t + Q_t S_{t-1})
  * with the state S_t = S_{t-1} + K_t^T V_t kept in float32 and used in bf16.
  *   q, k, v : [B,H,N,d] bf16, read only;  o : [B,H,N,d] bf16, written.
- * d must be 64 or 128.  Errors as fa_fwd.
+ *   workspace: see fa_linear_workspace_size.
+ * d must be 64 or 128.  Errors as fa_fwd, plus FA_ERR_WORKSPACE when a
+ * needed workspace is NULL, too small or not 256-byte aligned.
  */
 int fa_linear_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                  uint16_t* o, int B, int H, int N, int d, float scale,
-                  void* stream);
+                  uint16_t* o, void* workspace, size_t workspace_bytes, int B,
+                  int H, int N, int d, float scale, void* stream);
+
+/*
+ * Bytes of workspace fa_linear_fwd needs (0 for invalid shapes, and 0 when
+ * the sequence is not split: then workspace may be NULL).  When B*H*d/32
+ * workgroups would leave CUs idle, the chunks of each head are split into
+ * segments; the workspace holds each segment's float32 K^T V state
+ * [B*H][d/32][segments][32][d], written by a first pass.  256-byte aligned,
+ * owned by the caller, contents on entry irrelevant.
+ */
+size_t fa_linear_workspace_size(int B, int H, int N, int d);
 
 /*
  * The backward entry points below support head dimension d = 128 only; any

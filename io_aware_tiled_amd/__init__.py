@@ -28,7 +28,8 @@ __all__ = [
     "fa_fwd", "fa_fwd_kvlen", "fa_fwd_f32", "fa_bwd_workspace_size",
     "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
     "fa_fwd_block_sparse", "fa_fp8_workspace_size", "fa_fp8_quantize",
-    "fa_fwd_fp8_quantized", "fa_fwd_fp8", "fa_linear_fwd", "forward",
+    "fa_fwd_fp8_quantized", "fa_fwd_fp8", "fa_linear_fwd",
+    "fa_linear_workspace_size", "forward",
     "forward_fp8", "linear_forward", "backward", "EXPORTED_SYMBOLS",
 ]
 
@@ -58,7 +59,8 @@ _SIGS = {
     "fa_fp8_quantize": (_I, [_P] * 5 + [_S, _I, _I, _I, _I, _P]),
     "fa_fwd_fp8_quantized": (_I, [_P, _S, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_fp8": (_I, [_P] * 7 + [_S, _I, _I, _I, _I, _F, _I, _P]),
-    "fa_linear_fwd": (_I, [_P] * 4 + [_I, _I, _I, _I, _F, _P]),
+    "fa_linear_fwd": (_I, [_P] * 5 + [_S, _I, _I, _I, _I, _F, _P]),
+    "fa_linear_workspace_size": (_S, [_I, _I, _I, _I]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -311,14 +313,21 @@ def fa_fwd_fp8(q, k, v, signs, o, lse, workspace, scale, causal,
     _check(st, "fa_fwd_fp8")
 
 
-def fa_linear_fwd(q, k, v, o, scale, stream=None):
-    """C fa_linear_fwd: causal linear attention on bf16 [B,H,N,d]."""
+def fa_linear_workspace_size(B, H, N, d) -> int:
+    return int(lib().fa_linear_workspace_size(int(B), int(H), int(N), int(d)))
+
+
+def fa_linear_fwd(q, k, v, o, scale, workspace=None, stream=None):
+    """C fa_linear_fwd: causal linear attention on bf16 [B,H,N,d];
+    workspace: device uint8 tensor of fa_linear_workspace_size bytes, or
+    None when that size is 0."""
     import torch
     B, H, N, d = _bhnd(q)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
         _expect(t, torch.bfloat16, (B, H, N, d), n)
-    st = lib().fa_linear_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d,
-                             float(scale), _stream(q, stream))
+    wp, wn = (None, 0) if workspace is None else _ws(workspace)
+    st = lib().fa_linear_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), wp, wn, B, H,
+                             N, d, float(scale), _stream(q, stream))
     _check(st, "fa_linear_fwd")
 
 
@@ -372,11 +381,13 @@ def linear_forward(q, k, v, *, scale=None, stream=None):
     """Causal linear attention O = scale tril(Q K^T) V (scale defaults to
     1/sqrt(d)); returns o."""
     import torch
-    d = _bhnd(q)[3]
+    B, H, N, d = _bhnd(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q)
-    fa_linear_fwd(q, k, v, o, scale, stream)
+    n = fa_linear_workspace_size(B, H, N, d)
+    ws = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+    fa_linear_fwd(q, k, v, o, scale, ws, stream)
     return o
 
 

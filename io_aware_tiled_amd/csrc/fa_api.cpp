@@ -177,16 +177,25 @@ int fa_fwd_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               score_scale, causal, stream);
 }
 
+size_t fa_linear_workspace_size(int B, int H, int N, int d) {
+  if (check_shape(B, H, N, d) != FA_OK) return 0;
+  return fa::linear_workspace_bytes(B, H, N, d);
+}
+
 int fa_linear_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                  uint16_t* o, int B, int H, int N, int d, float scale,
-                  void* stream) {
+                  uint16_t* o, void* workspace, size_t workspace_bytes, int B,
+                  int H, int N, int d, float scale, void* stream) {
   if (!q || !k || !v || !o) return FA_ERR_NULL;
   int st = check_shape(B, H, N, d);
   if (st != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return FA_ERR_ALIGN;
-  return fa::launch_linear_fwd(q, k, v, o, B, H, N, d, scale,
-                               (hipStream_t)stream);
+  const size_t need = fa::linear_workspace_bytes(B, H, N, d);
+  if (need > 0 && (!workspace || ((uintptr_t)workspace & 255u) != 0 ||
+                   workspace_bytes < need))
+    return FA_ERR_WORKSPACE;
+  return fa::launch_linear_fwd(q, k, v, o, (float*)workspace, B, H, N, d,
+                               scale, (hipStream_t)stream);
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {

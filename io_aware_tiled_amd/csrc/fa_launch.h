@@ -42,9 +42,11 @@ int launch_fwd_fp8(const uint8_t* ws, uint16_t* o, float* lse, int B, int H,
                    int N, int d, float score_scale, int causal,
                    hipStream_t stream);
 
-// Causal linear attention forward (chunkwise).
+// Causal linear attention forward (chunkwise).  ws: fp32 segment states
+// of linear_workspace_bytes() bytes (NULL when that is 0).
+size_t linear_workspace_bytes(int B, int H, int N, int d);
 int launch_linear_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                      uint16_t* o, int B, int H, int N, int d, float scale,
-                      hipStream_t stream);
+                      uint16_t* o, float* ws, int B, int H, int N, int d,
+                      float scale, hipStream_t stream);
 
 }  // namespace fa

@@ -30,11 +30,16 @@
 //     (the same V_t^T operand; K_t's columns by transposed LDS reads), then
 //     write S_t^T as bf16 to the LDS buffer the next chunk reads.
 // Chunks go from HBM to LDS by DMA two chunks ahead through three stages;
-// one barrier per chunk orders every producer and consumer.
+// one barrier per chunk orders every producer and consumer.  When heads and
+// value blocks leave CUs idle (few heads, long sequences), the chunks of a
+// head are split into segments: a first pass writes each segment's
+// K^T V sum (fp32) to a workspace, and each segment's workgroup then starts
+// from the sum of the states before it.
 #include "fa.h"
 #include "fa_common.h"
 #include "fa_launch.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace fa {
@@ -54,10 +59,16 @@ struct LinTile {
   static constexpr int SST = D + 8;          // S^T rows (row reads)
 };
 
-template <int D>
+// STATE_ONLY: the first pass of a split sequence -- each workgroup sums
+// K_t^T V_t over its segment and writes that fp32 state to the workspace
+// (no Q, no O).  Otherwise the workgroup produces O for its segment,
+// starting from the sum of the previous segments' states (zero for the
+// first segment or an unsplit sequence).
+template <int D, bool STATE_ONLY>
 __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, int BH, int N,
+    const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+    float* __restrict__ seg_state, int BH, int N, int nseg, int seg_chunks,
     float scale) {
   using T = LinTile<D>;
   constexpr int NVB = D / kVB;
@@ -66,14 +77,16 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[kLS][kLC * T::VST];
   __shared__ __attribute__((aligned(16))) uint16_t lds_s[2][kVB * T::SST];
 
-  // Workgroup -> (head, value block): workgroups are dispatched round-robin
-  // over the 8 XCDs, so id % 8 picks the XCD and every value block of a
-  // head gets the same one.
+  // Workgroup -> (head, value block, segment): workgroups are dispatched
+  // round-robin over the 8 XCDs, so id % 8 picks the XCD and every value
+  // block of a head gets the same one.
   const int id = blockIdx.x;
   const int xcd = id & 7, rest = id >> 3;
   const int vb = rest % NVB;
-  const int bh = (rest / NVB) * 8 + xcd;
+  const int seg = (rest / NVB) % nseg;
+  const int bh = (rest / NVB / nseg) * 8 + xcd;
   if (bh >= BH) return;
+  if (STATE_ONLY && seg == nseg - 1) return;   // no later segment needs it
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -86,7 +99,10 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
   const uint16_t* Qh = Q + head;
   const uint16_t* Kh = K + head;
   const uint16_t* Vh = V + head + kVB * vb;
-  const int nchunks = (N + kLC - 1) / kLC;
+  const int nchunks_all = (N + kLC - 1) / kLC;
+  const int c_begin = seg * seg_chunks;
+  const int nchunks = min(seg_chunks, nchunks_all - c_begin);   // this segment
+  float* const st_base = seg_state + (size_t)(bh * NVB + vb) * nseg * kVB * D;
 
   // ---- chunk loads by LDS DMA (buffer loads that write LDS, 16 bytes per
   // lane): slot p of a stage is 16 bytes of row p / RS; slots that are row
@@ -97,15 +113,15 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
   constexpr int QI = kLC * QRS / 64, VI = kLC * VRS / 64;
   constexpr int NI = 2 * QI + VI;                       // transfers per chunk
   constexpr int kIW = (NI + 3) / 4;
-  constexpr int kMinBatch = NI / 4;                     // of every wavefront
+  constexpr int kMinBatch = (STATE_ONLY ? NI - QI : NI) / 4;   // per wavefront
   static_assert(kLC * QRS % 64 == 0 && kLC * VRS % 64 == 0 && kMinBatch < 60,
                 "DMA layout");
   constexpr unsigned kOut = 1u << 30;
   const unsigned lq0 = lds_addr(&lds_q[0][0]), lk0 = lds_addr(&lds_k[0][0]);
   const unsigned lv0 = lds_addr(&lds_v[0][0]);
-  auto dma = [&](int t) __attribute__((always_inline)) {
-    const unsigned st = (unsigned)(t % kLS);
-    const int row0 = t * kLC;
+  auto dma = [&](int u) __attribute__((always_inline)) {
+    const unsigned st = (unsigned)(u % kLS);
+    const int row0 = (c_begin + u) * kLC;
     // descriptors of this chunk's rows (they end at row N - 1)
     const int bytes = min(N - row0, kLC) * D * 2;
     const size_t base = (size_t)row0 * D;
@@ -119,6 +135,7 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
     for (int u = 0; u < kIW; ++u) {
       const int g = w + 4 * u;
       if (g < 2 * QI) {
+        if (STATE_ONLY && g < QI) continue;         // no Q in the state pass
         const int gi = g % QI;
         const int p = 64 * gi + lane, row = p / QRS, c = p % QRS;
         const unsigned off = c < D / 8 ? (unsigned)((row * D + 8 * c) * 2) : kOut;
@@ -150,25 +167,50 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
   f32x16 sacc[NDT];
 #pragma unroll
   for (int i = 0; i < NDT; ++i) sacc[i] = f32x16{};
-  // S_{-1} = 0 in the buffer the first chunk reads.
+  // The state entering the segment: zero, or the sum of the previous
+  // segments' states (state wavefronts, fp32); as bf16 in the buffer the
+  // first chunk reads.
   for (int e = tid; e < kVB * T::SST / 8; e += kLThreads)
     *(u32x4*)(&lds_s[1][8 * e]) = u32x4{0u, 0u, 0u, 0u};
+  if (!STATE_ONLY && seg > 0 && w >= 2) {
+#pragma unroll
+    for (int i = 0; i < NDT; ++i) {
+      const int dt = (w - 2) * NDT + i;
+      for (int sp = 0; sp < seg; ++sp) {
+        const float* src = st_base + (size_t)sp * kVB * D;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sacc[i][r] += src[(8 * (r / 4) + 4 * hh + (r % 4)) * D + 32 * dt + lq];
+      }
+    }
+  }
+  __syncthreads();
+  if (!STATE_ONLY && seg > 0 && w >= 2) {
+#pragma unroll
+    for (int i = 0; i < NDT; ++i) {
+      const int dt = (w - 2) * NDT + i;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        lds_s[1][(8 * (r / 4) + 4 * hh + (r % 4)) * T::SST + 32 * dt + lq] =
+            __builtin_bit_cast(uint16_t, (__bf16)sacc[i][r]);
+    }
+  }
 
   // Chunk t waits for its own transfers (issued two chunks earlier), then
   // the barrier publishes them and the state chunk t - 1 wrote; the stage
   // refilled after it was last read in chunk t - 1.
   dma(0);
   if (nchunks > 1) dma(1);
-  for (int t = 0; t < nchunks; ++t) {
-    const int b = t % kLS;
-    if (t + 1 < nchunks)
+  for (int u = 0; u < nchunks; ++u) {
+    const int b = u % kLS;
+    if (u + 1 < nchunks)
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kMinBatch) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 2 < nchunks) dma(t + 2);
-    const int sb = t & 1;
-    const int r0 = t * kLC;
+    if (u + 2 < nchunks) dma(u + 2);
+    const int sb = u & 1;
+    const int r0 = (c_begin + u) * kLC;
     // ---- query block QB (wavefront QB): A^T = K Q^T for key blocks
     // kb <= QB and the inter-chunk term S_{t-1}^T Q^T, as independent MFMA
     // chains interleaved (a dependent chain would wait out each MFMA's
@@ -220,7 +262,9 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
         }
       }
     };
-    if (w == 0) {
+    if (STATE_ONLY && w < 2) {
+      // the state pass computes no output
+    } else if (w == 0) {
       query_block(std::integral_constant<int, 0>{});
     } else if (w == 1) {
       query_block(std::integral_constant<int, 1>{});
@@ -260,22 +304,61 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
       }
     }
   }
+  if (STATE_ONLY && w >= 2) {
+    float* dst = st_base + (size_t)seg * kVB * D;
+#pragma unroll
+    for (int i = 0; i < NDT; ++i) {
+      const int dt = (w - 2) * NDT + i;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        dst[(8 * (r / 4) + 4 * hh + (r % 4)) * D + 32 * dt + lq] = sacc[i][r];
+    }
+  }
 }
 
 }  // namespace
 
+// Split of a head's chunks into segments (one workgroup each) when the
+// heads and value blocks alone leave the chip's CUs idle.
+void linear_split(int B, int H, int N, int d, int& nseg, int& seg_chunks) {
+  constexpr int kCUs = 256, kMinSegChunks = 4;
+  const long long wgs = (long long)B * H * (d / kVB);
+  const int nchunks = (N + kLC - 1) / kLC;
+  nseg = 1;
+  if (wgs < kCUs)
+    nseg = (int)std::min<long long>((kCUs + wgs - 1) / wgs,
+                                    std::max(1, nchunks / kMinSegChunks));
+  seg_chunks = (nchunks + nseg - 1) / nseg;
+  nseg = (nchunks + seg_chunks - 1) / seg_chunks;
+}
+
+size_t linear_workspace_bytes(int B, int H, int N, int d) {
+  int nseg, seg_chunks;
+  linear_split(B, H, N, d, nseg, seg_chunks);
+  if (nseg == 1) return 0;
+  const size_t bytes = (size_t)B * H * (d / kVB) * nseg * kVB * d * 4;
+  return (bytes + 255) & ~(size_t)255;
+}
+
 int launch_linear_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                      uint16_t* o, int B, int H, int N, int d, float scale,
-                      hipStream_t stream) {
+                      uint16_t* o, float* ws, int B, int H, int N, int d,
+                      float scale, hipStream_t stream) {
   const int BH = B * H;
   const int nvb = d / kVB;
-  const dim3 grid((unsigned)(((BH + 7) / 8) * 8 * nvb)), block(kLThreads);
-  if (d == 128)
-    hipLaunchKernelGGL((linear_fwd_kernel<128>), grid, block, 0, stream, q, k,
-                       v, o, BH, N, scale);
-  else
-    hipLaunchKernelGGL((linear_fwd_kernel<64>), grid, block, 0, stream, q, k,
-                       v, o, BH, N, scale);
+  int nseg, seg_chunks;
+  linear_split(B, H, N, d, nseg, seg_chunks);
+  const dim3 grid((unsigned)(((BH + 7) / 8) * 8 * nvb * nseg)), block(kLThreads);
+#define FA_LIN_LAUNCH(DD, SO)                                                \
+  hipLaunchKernelGGL((linear_fwd_kernel<DD, SO>), grid, block, 0, stream, q, \
+                     k, v, o, ws, BH, N, nseg, seg_chunks, scale)
+  if (d == 128) {
+    if (nseg > 1) FA_LIN_LAUNCH(128, true);
+    FA_LIN_LAUNCH(128, false);
+  } else {
+    if (nseg > 1) FA_LIN_LAUNCH(64, true);
+    FA_LIN_LAUNCH(64, false);
+  }
+#undef FA_LIN_LAUNCH
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

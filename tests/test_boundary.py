@@ -34,7 +34,7 @@ def test_header_declares_expected_calls():
     for want in ["fa_fwd", "fa_fwd_kvlen", "fa_fwd_f32", "fa_bwd",
                  "fa_fwd_block_sparse", "fa_fp8_workspace_size",
                  "fa_fp8_quantize", "fa_fwd_fp8_quantized", "fa_fwd_fp8",
-                 "fa_linear_fwd",
+                 "fa_linear_fwd", "fa_linear_workspace_size",
                  "fa_bwd_workspace_size", "fa_status_string", "fa_version",
                  "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq"]:
         assert want in names
@@ -194,12 +194,22 @@ def test_fp8_argument_errors():
 def test_linear_argument_errors():
     L = fa.lib()
 
-    def lin(q=A, o=A, B=1, N=64, d=128):
-        return L.fa_linear_fwd(q, A, A, o, B, 2, N, d, 0.1, None)
+    W = 0x100000
+
+    def lin(q=A, o=A, B=1, N=64, d=128, ws=None, wsb=0):
+        return L.fa_linear_fwd(q, A, A, o, ws, wsb, B, 2, N, d, 0.1, None)
     assert lin(q=None) == NULL and lin(o=None) == NULL
     assert lin(B=0) == SHAPE and lin(N=-1) == SHAPE
     assert lin(d=32) == HEADDIM and lin(d=256) == HEADDIM
     assert lin(q=MIS) == ALIGN and lin(o=MIS) == ALIGN
+    # a long sequence with few heads is split and needs the workspace
+    n = fa.fa_linear_workspace_size(1, 2, 20000, 128)
+    assert n > 0 and n % 256 == 0
+    assert lin(N=20000) == WORKSPACE
+    assert lin(N=20000, ws=W, wsb=n - 1) == WORKSPACE
+    assert lin(N=20000, ws=W + 16, wsb=n) == WORKSPACE
+    assert fa.fa_linear_workspace_size(4, 16, 4096, 128) == 0
+    assert fa.fa_linear_workspace_size(1, 1, 64, 96) == 0
 
 
 def test_python_binding_refuses_host_tensors():

@@ -33,7 +33,9 @@ def _run(inp):
     import io_aware_tiled_amd as fa
     q, k, v = (to_dev(inp, n) for n in ("q", "k", "v"))
     o = torch.full_like(q, float("nan"))
-    fa.fa_linear_fwd(q, k, v, o, inp["scale"])
+    n = fa.fa_linear_workspace_size(*q.shape)
+    ws = torch.full((n,), 0x7F, dtype=torch.uint8, device=DEV) if n else None
+    fa.fa_linear_fwd(q, k, v, o, inp["scale"], ws)
     torch.cuda.synchronize()
     return o
 
@@ -84,8 +86,12 @@ def _check(name, inp, rows=None, heads=None):
     report(name, O_max=worst, O_over_bound=worst_ratio)
 
 
+# Few heads split each sequence into segments (a first pass writes the
+# segments' states): (1,1,1000,64), (1,2,2000,128), (1,3,1100,64) and the
+# N = 23400 case below; the others run unsplit.
 CASES = [(1, 1, 1, 64), (1, 2, 64, 128), (2, 3, 100, 128), (1, 2, 300, 64),
-         (3, 4, 513, 64), (2, 5, 1000, 128), (1, 9, 130, 128)]
+         (3, 4, 513, 64), (2, 5, 1000, 128), (1, 9, 130, 128), (1, 1, 1000, 64),
+         (1, 2, 2000, 128), (1, 3, 1100, 64)]
 
 
 @pytest.mark.parametrize("B,H,N,d", CASES)
@@ -112,6 +118,17 @@ def test_linear_long_sequence():
     rows = np.unique(np.concatenate([np.arange(0, 70), np.arange(23330, 23400),
                                      np.random.default_rng(2).integers(0, 23400, 100)]))
     _check("linear N=23400", inp, rows=rows)
+
+
+def test_linear_split_matches_definition_boundaries():
+    """Rows on both sides of every segment boundary of a split sequence."""
+    import io_aware_tiled_amd as fa
+    N = 3000
+    assert fa.fa_linear_workspace_size(1, 1, N, 128) > 0
+    inp = S.make_case(1, 1, N, 128, causal=True, seed=80)
+    rows = np.unique(np.clip(np.concatenate(
+        [np.arange(c - 2, c + 2) for c in range(0, N + 64, 64)]), 0, N - 1))
+    _check("linear split boundaries", inp, rows=rows)
 
 
 def test_linear_workload_sampled():
