@@ -76,7 +76,7 @@ def visible_pairs(w: S.Workload, kv_len, block_mask=None) -> int:
         return per * w.B * w.H
     if kv_len is None:
         return w.N * w.N * w.B * w.H
-    return int(sum(w.N * int(L) for L in kv_len)) * w.H
+    return int(sum(w.N * min(max(int(L), 0), w.N) for L in kv_len)) * w.H
 
 
 def log(msg):
@@ -93,13 +93,14 @@ def cpu_baseline(w: S.Workload, inp: dict, target_s: float = 15.0) -> dict:
     q, k, v = (inp[n][sl] for n in ("q", "k", "v"))
     kv = None if inp["kv_len"] is None else inp["kv_len"][:1]
     bm = inp.get("block_mask")
+    import oracle.fp8
+    import oracle.linear
+
     def run(q, k, v, nh, sl):
         if w.linear:
-            import oracle.linear
             oracle.linear.linear_attention_fwd(q, k, v, inp["scale"])
             return
         if inp.get("signs") is not None:
-            import oracle.fp8
             oracle.fp8.fp8_forward(q, k, v, inp["scale"], inp["causal"],
                                    inp["signs"], workers=cores)
             return
@@ -108,7 +109,9 @@ def cpu_baseline(w: S.Workload, inp: dict, target_s: float = 15.0) -> dict:
                              block_mask=None if bm is None else bm[:nh].astype(bool))
         if w.backward:
             oracle.attention_bwd(q, k, v, inp["do"][sl], inp["scale"],
-                                 inp["causal"], kv, workers=cores)
+                                 inp["causal"], kv, workers=cores,
+                                 block_mask=None if bm is None
+                                 else bm[:nh].astype(bool))
     t0 = time.perf_counter()
     run(q, k, v, nh, sl)
     t1 = time.perf_counter() - t0
@@ -565,9 +568,17 @@ def main(argv=None) -> int:
         if w.backward:
             fa.fa_bwd_preprocess(o, do, ws)
             mark(2)
-            fa.fa_bwd_dkdv(q, k, v, do, lse, dk, dv, ws, scale, causal)
+            if bmask is not None:
+                fa.fa_bwd_dkdv_block_sparse(q, k, v, do, lse, bmask, dk, dv,
+                                            ws, scale, causal)
+            else:
+                fa.fa_bwd_dkdv(q, k, v, do, lse, dk, dv, ws, scale, causal)
             mark(3)
-            fa.fa_bwd_dq(q, k, v, do, lse, dq, ws, scale, causal)
+            if bmask is not None:
+                fa.fa_bwd_dq_block_sparse(q, k, v, do, lse, bmask, dq, ws,
+                                          scale, causal)
+            else:
+                fa.fa_bwd_dq(q, k, v, do, lse, dq, ws, scale, causal)
             mark(4)
 
     log(f"[bench] warmup {args.warmup} steps")

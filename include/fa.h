@@ -281,6 +281,40 @@ int fa_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
               const void* workspace, size_t workspace_bytes, int B, int H,
               int N, int d, float scale, int causal, void* stream);
 
+/*
+ * Backward of the block-sparse forward (fa_fwd_block_sparse; [ZN]
+ * "Overview"): the same gradients as fa_bwd with P taken over the block
+ * mask's visible keys only.
+ * dK/dV workgroups visit only the 64-row query tiles whose block-mask row
+ * keeps one of their two 64-key columns; dQ workgroups (one per 256-row
+ * block-mask row) visit only the kept key tiles.  Arguments as fa_bwd plus
+ * block_mask as in fa_fwd_block_sparse; lse must come from
+ * fa_fwd_block_sparse with the same mask.  d = 128.  Errors as fa_bwd, plus
+ * FA_ERR_NULL for a NULL block_mask and FA_ERR_SHAPE for N > 131072.
+ */
+int fa_bwd_block_sparse(const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, const uint16_t* o,
+                        const uint16_t* dO, const float* lse,
+                        const uint8_t* block_mask, uint16_t* dq, uint16_t* dk,
+                        uint16_t* dv, void* workspace, size_t workspace_bytes,
+                        int B, int H, int N, int d, float scale, int causal,
+                        void* stream);
+
+/* Its stages 2 and 3 (after fa_bwd_preprocess), as fa_bwd_dkdv and
+ * fa_bwd_dq with the block mask. */
+int fa_bwd_dkdv_block_sparse(const uint16_t* q, const uint16_t* k,
+                             const uint16_t* v, const uint16_t* dO,
+                             const float* lse, const uint8_t* block_mask,
+                             uint16_t* dk, uint16_t* dv, const void* workspace,
+                             size_t workspace_bytes, int B, int H, int N, int d,
+                             float scale, int causal, void* stream);
+int fa_bwd_dq_block_sparse(const uint16_t* q, const uint16_t* k,
+                           const uint16_t* v, const uint16_t* dO,
+                           const float* lse, const uint8_t* block_mask,
+                           uint16_t* dq, const void* workspace,
+                           size_t workspace_bytes, int B, int H, int N, int d,
+                           float scale, int causal, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

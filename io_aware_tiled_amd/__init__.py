@@ -27,7 +27,9 @@ __all__ = [
     "FAError", "lib", "lib_path", "fa_version", "fa_status_string",
     "fa_fwd", "fa_fwd_kvlen", "fa_fwd_f32", "fa_bwd_workspace_size",
     "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
-    "fa_fwd_block_sparse", "fa_fp8_workspace_size", "fa_fp8_quantize",
+    "fa_fwd_block_sparse", "fa_bwd_block_sparse", "fa_bwd_dkdv_block_sparse",
+    "fa_bwd_dq_block_sparse", "fa_fp8_workspace_size",
+    "fa_fp8_quantize",
     "fa_fwd_fp8_quantized", "fa_fwd_fp8", "fa_linear_fwd",
     "fa_linear_workspace_size", "forward",
     "forward_fp8", "linear_forward", "backward", "EXPORTED_SYMBOLS",
@@ -61,6 +63,9 @@ _SIGS = {
     "fa_fwd_fp8": (_I, [_P] * 7 + [_S, _I, _I, _I, _I, _F, _I, _P]),
     "fa_linear_fwd": (_I, [_P] * 5 + [_S, _I, _I, _I, _I, _F, _P]),
     "fa_linear_workspace_size": (_S, [_I, _I, _I, _I]),
+    "fa_bwd_block_sparse": (_I, [_P] * 11 + [_S, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_bwd_dkdv_block_sparse": (_I, [_P] * 9 + [_S, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_bwd_dq_block_sparse": (_I, [_P] * 8 + [_S, _I, _I, _I, _I, _F, _I, _P]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -220,6 +225,49 @@ def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, workspace, scale, causal,
                       _ptr(dq), _ptr(dk), _ptr(dv), wp, wn, B, H, N, d,
                       float(scale), int(bool(causal)), _stream(q, stream))
     _check(st, "fa_bwd")
+
+
+def fa_bwd_block_sparse(q, k, v, o, dO, lse, block_mask, dq, dk, dv,
+                        workspace, scale, causal, stream=None):
+    """C fa_bwd_block_sparse: backward of fa_fwd_block_sparse with the same
+    uint8 block mask [H, ceil(N/256), ceil(N/64)]."""
+    import torch
+    B, H, N, d = _bhnd(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO"),
+                 (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _expect(t, torch.bfloat16, (B, H, N, d), n)
+    _expect(lse, torch.float32, (B, H, N), "lse")
+    _expect(block_mask, torch.uint8,
+            (H, -(-N // SPARSE_BQ), -(-N // SPARSE_BK)), "block_mask")
+    wp, wn = _ws(workspace)
+    st = lib().fa_bwd_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                   _ptr(dO), _ptr(lse), _ptr(block_mask),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), wp, wn, B, H,
+                                   N, d, float(scale), int(bool(causal)),
+                                   _stream(q, stream))
+    _check(st, "fa_bwd_block_sparse")
+
+
+def fa_bwd_dkdv_block_sparse(q, k, v, dO, lse, block_mask, dk, dv,
+                             workspace, scale, causal, stream=None):
+    B, H, N, d = _bhnd(q)
+    wp, wn = _ws(workspace)
+    st = lib().fa_bwd_dkdv_block_sparse(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(block_mask),
+        _ptr(dk), _ptr(dv), wp, wn, B, H, N, d, float(scale),
+        int(bool(causal)), _stream(q, stream))
+    _check(st, "fa_bwd_dkdv_block_sparse")
+
+
+def fa_bwd_dq_block_sparse(q, k, v, dO, lse, block_mask, dq, workspace,
+                           scale, causal, stream=None):
+    B, H, N, d = _bhnd(q)
+    wp, wn = _ws(workspace)
+    st = lib().fa_bwd_dq_block_sparse(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(block_mask),
+        _ptr(dq), wp, wn, B, H, N, d, float(scale), int(bool(causal)),
+        _stream(q, stream))
+    _check(st, "fa_bwd_dq_block_sparse")
 
 
 def fa_bwd_preprocess(o, dO, workspace, stream=None):
@@ -392,8 +440,9 @@ def linear_forward(q, k, v, *, scale=None, stream=None):
 
 
 def backward(q, k, v, o, lse, dO, *, causal=False, scale=None, stream=None,
-             workspace=None):
-    """Returns (dq, dk, dv) for the bf16 forward."""
+             workspace=None, block_mask=None):
+    """Returns (dq, dk, dv) for the bf16 forward (fa_bwd_block_sparse when a
+    block mask is given)."""
     import torch
     B, H, N, d = _bhnd(q)
     if scale is None:
@@ -406,5 +455,10 @@ def backward(q, k, v, o, lse, dO, *, causal=False, scale=None, stream=None,
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, workspace, scale, causal, stream)
+    if block_mask is not None:
+        fa_bwd_block_sparse(q, k, v, o, dO, lse, block_mask, dq, dk, dv,
+                            workspace, scale, causal, stream)
+    else:
+        fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, workspace, scale, causal,
+               stream)
     return dq, dk, dv

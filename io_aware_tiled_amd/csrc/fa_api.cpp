@@ -229,8 +229,8 @@ int fa_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     return FA_ERR_ALIGN;
   st = check_workspace(workspace, workspace_bytes, B, H, N);
   if (st != FA_OK) return st;
-  return fa::launch_bwd_dkdv(q, k, v, dO, lse, (const float*)workspace, dk,
-                             dv, B, H, N, d, scale, causal != 0,
+  return fa::launch_bwd_dkdv(q, k, v, dO, lse, (const float*)workspace,
+                             nullptr, dk, dv, B, H, N, d, scale, causal != 0,
                              (hipStream_t)stream);
 }
 
@@ -246,8 +246,9 @@ int fa_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     return FA_ERR_ALIGN;
   st = check_workspace(workspace, workspace_bytes, B, H, N);
   if (st != FA_OK) return st;
-  return fa::launch_bwd_dq(q, k, v, dO, lse, (const float*)workspace, dq, B,
-                           H, N, d, scale, causal != 0, (hipStream_t)stream);
+  return fa::launch_bwd_dq(q, k, v, dO, lse, (const float*)workspace, nullptr,
+                           dq, B, H, N, d, scale, causal != 0,
+                           (hipStream_t)stream);
 }
 
 int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -272,6 +273,79 @@ int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   if (st != FA_OK) return st;
   return fa_bwd_dq(q, k, v, dO, lse, dq, workspace, workspace_bytes, B, H, N,
                    d, scale, causal, stream);
+}
+
+int fa_bwd_dkdv_block_sparse(const uint16_t* q, const uint16_t* k,
+                             const uint16_t* v, const uint16_t* dO,
+                             const float* lse, const uint8_t* block_mask,
+                             uint16_t* dk, uint16_t* dv, const void* workspace,
+                             size_t workspace_bytes, int B, int H, int N, int d,
+                             float scale, int causal, void* stream) {
+  if (!q || !k || !v || !dO || !lse || !block_mask || !dk || !dv)
+    return FA_ERR_NULL;
+  int st = check_shape_bwd(B, H, N, d);
+  if (st != FA_OK) return st;
+  if ((N + FA_SPARSE_BK - 1) / FA_SPARSE_BK > FA_SPARSE_MAX_KEY_BLOCKS)
+    return FA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) ||
+      !aligned16(lse) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_ALIGN;
+  st = check_workspace(workspace, workspace_bytes, B, H, N);
+  if (st != FA_OK) return st;
+  return fa::launch_bwd_dkdv(q, k, v, dO, lse, (const float*)workspace,
+                             block_mask, dk, dv, B, H, N, d, scale,
+                             causal != 0, (hipStream_t)stream);
+}
+
+int fa_bwd_dq_block_sparse(const uint16_t* q, const uint16_t* k,
+                           const uint16_t* v, const uint16_t* dO,
+                           const float* lse, const uint8_t* block_mask,
+                           uint16_t* dq, const void* workspace,
+                           size_t workspace_bytes, int B, int H, int N, int d,
+                           float scale, int causal, void* stream) {
+  if (!q || !k || !v || !dO || !lse || !block_mask || !dq) return FA_ERR_NULL;
+  int st = check_shape_bwd(B, H, N, d);
+  if (st != FA_OK) return st;
+  if ((N + FA_SPARSE_BK - 1) / FA_SPARSE_BK > FA_SPARSE_MAX_KEY_BLOCKS)
+    return FA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) ||
+      !aligned16(lse) || !aligned16(dq))
+    return FA_ERR_ALIGN;
+  st = check_workspace(workspace, workspace_bytes, B, H, N);
+  if (st != FA_OK) return st;
+  return fa::launch_bwd_dq(q, k, v, dO, lse, (const float*)workspace,
+                           block_mask, dq, B, H, N, d, scale, causal != 0,
+                           (hipStream_t)stream);
+}
+
+int fa_bwd_block_sparse(const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, const uint16_t* o,
+                        const uint16_t* dO, const float* lse,
+                        const uint8_t* block_mask, uint16_t* dq, uint16_t* dk,
+                        uint16_t* dv, void* workspace, size_t workspace_bytes,
+                        int B, int H, int N, int d, float scale, int causal,
+                        void* stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !block_mask || !dq || !dk || !dv)
+    return FA_ERR_NULL;
+  int st = check_shape_bwd(B, H, N, d);
+  if (st != FA_OK) return st;
+  if ((N + FA_SPARSE_BK - 1) / FA_SPARSE_BK > FA_SPARSE_MAX_KEY_BLOCKS)
+    return FA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(dO) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv))
+    return FA_ERR_ALIGN;
+  st = check_workspace(workspace, workspace_bytes, B, H, N);
+  if (st != FA_OK) return st;
+  st = fa_bwd_preprocess(o, dO, workspace, workspace_bytes, B, H, N, d, stream);
+  if (st != FA_OK) return st;
+  st = fa_bwd_dkdv_block_sparse(q, k, v, dO, lse, block_mask, dk, dv,
+                                workspace, workspace_bytes, B, H, N, d, scale,
+                                causal, stream);
+  if (st != FA_OK) return st;
+  return fa_bwd_dq_block_sparse(q, k, v, dO, lse, block_mask, dq, workspace,
+                                workspace_bytes, B, H, N, d, scale, causal,
+                                stream);
 }
 
 }  // extern "C"

@@ -44,6 +44,7 @@
 //     operand of dQ^T += K_j^T dS^T with K_j^T read transposed from LDS.
 //   * LDS rows are padded to 304 bytes: conflict-free 16-byte row reads and
 //     at most 2-way transposed reads.
+#include "fa.h"
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -55,6 +56,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBK = 128;   // keys per workgroup (32 per wavefront)
+// Block-sparse backward: query and key tiles of one head are listed in LDS
+// as 16-bit entries, at most this many (64-row tiles up to N = 131072).
+constexpr int kSparseMaxTiles = FA_SPARSE_MAX_KEY_BLOCKS;
 constexpr int kD = 128;    // head dimension of the backward kernel
 
 // ---------------------------------------------------------------------------
@@ -169,6 +173,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
 
   const int n_qt = (N + kBQ2 - 1) / kBQ2;
   const int it0 = CAUSAL ? kb0 / kBQ2 : 0;
+
 
   // Query-tile staging: 2 chunks of Q and 2 of dO per thread, plus LSE / D.
   // Rows past N load row N-1 (in bounds) and are replaced by zeros with a
@@ -565,12 +570,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t bwd_rsrc(const uint16_t* p,
 // each, transformed on the way) pass through wavefront 0's registers.
 constexpr int kKvPBK = 128;
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dv,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kblk,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+    const uint8_t* __restrict__ bmask, int H, int N, int n_kblk,
     float c_log2, float scale) {
   constexpr int D = kD;
   constexpr int QE = kBQ2 * kRS;                 // elements per tile stage
@@ -623,6 +629,48 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
 
   const int n_qt = (N + kBQ2 - 1) / kBQ2;
   const int it0 = CAUSAL ? kb0 / kBQ2 : 0;
+
+  // ---- query tiles to visit, as entries: tile index | keep bits << 12,
+  // bit w/2 telling whether wavefront w's 64-key block column is kept for
+  // the tile's block-mask row.  Dense: tiles it0 .. n_qt - 1, all kept.
+  // Block-sparse: the tiles whose row keeps either of the workgroup's two
+  // key columns, compacted into an LDS list; a wavefront whose column is
+  // dropped masks the whole tile.
+  __shared__ uint16_t qt_list[SPARSE ? kSparseMaxTiles : 1];
+  __shared__ int qt_count;
+  int n_vis = n_qt - it0;
+  if constexpr (SPARSE) {
+    const int n_mk = (N + FA_SPARSE_BK - 1) / FA_SPARSE_BK;
+    const int n_mq = (N + FA_SPARSE_BQ - 1) / FA_SPARSE_BQ;
+    const uint8_t* mh = bmask + (size_t)(bh % H) * n_mq * n_mk;
+    const int c0 = kb0 / FA_SPARSE_BK;
+    if (w == 0) {
+      int cnt = 0;
+      for (int base = it0; base < n_qt; base += 64) {
+        const int q = base + lane;
+        unsigned bits = 0;
+        if (q < n_qt) {
+          const uint8_t* mr = mh + (size_t)(q * kBQ2 / FA_SPARSE_BQ) * n_mk;
+          bits = (mr[c0] != 0 ? 1u : 0u) |
+                 ((c0 + 1 < n_mk && mr[c0 + 1] != 0) ? 2u : 0u);
+        }
+        const unsigned long long bal = __ballot(bits != 0);
+        const int below = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+        if (bits != 0) qt_list[cnt + below] = (uint16_t)((unsigned)q | (bits << 12));
+        cnt += __builtin_popcountll(bal);
+      }
+      if (lane == 0) qt_count = cnt;
+    }
+    __syncthreads();
+    n_vis = qt_count;
+  }
+  auto entry = [&](int p) -> unsigned {
+    if constexpr (SPARSE)
+      return __builtin_amdgcn_readfirstlane((unsigned)qt_list[max(min(p, n_vis - 1), 0)]);
+    else
+      return (unsigned)(it0 + p) | (3u << 12);
+  };
+  auto qtile = [](unsigned e) -> int { return (int)(e & 0xFFFu); };
 
   // The K and V fragments have arrived before any DMA is issued (a wait
   // the compiler can see, so that it places none of its own inside the
@@ -779,10 +827,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
                  "+v"(dsb[cv][1]));
   };
 
-  // ---- mask block c of query tile it where needed (causal diagonal, keys
-  // past N; rows past N already have P = 0 through LSE = +inf).
-  auto mask_block = [&](int c, int it) {
-    const int qb0 = it * kBQ2 + 32 * c;
+  // ---- mask block c of the query tile of entry e where needed (causal
+  // diagonal, keys past N, a dropped block of the mask; rows past N already
+  // have P = 0 through LSE = +inf).
+  auto mask_block = [&](int c, unsigned e) {
+    const int qb0 = qtile(e) * kBQ2 + 32 * c;
+    const bool dropped = SPARSE && ((e >> (12 + (w >> 1))) & 1u) == 0;
+    if (dropped) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[c][r] = -INFINITY;
+      return;
+    }
     const bool need_mask = (CAUSAL && wk0 + 31 > qb0) || (wk0 + 32 > N);
     if (need_mask) {
 #pragma unroll
@@ -811,16 +866,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
     }
   };
 
-  if (it0 < n_qt) {
-    const int last = n_qt - 1;
-    // Prologue: tile it0 in stage 0, tile it0+1 in stage 1 (its LSE / D in
-    // registers); zeros in stage 3 (the tile before it0, whose block 1 the
-    // first phase multiplies by P = dS = 0); A_0(it0).
-    dma_tile(it0, 0);
-    if (it0 + 1 <= last) dma_tile(it0 + 1, 1);
-    load_stats(it0);
+  if (n_vis > 0) {
+    const int last = n_vis - 1;      // list positions
+    // Prologue: the first tile in stage 0, the second in stage 1 (its LSE /
+    // D in registers); zeros in stage 3 (the tile before the first, whose
+    // block 1 the first phase multiplies by P = dS = 0); A_0 of the first.
+    const unsigned e0 = entry(0);
+    dma_tile(qtile(e0), 0);
+    if (last >= 1) dma_tile(qtile(entry(1)), 1);
+    load_stats(qtile(e0));
     store_stats(0);
-    load_stats(min(it0 + 1, last));
+    load_stats(qtile(entry(min(1, last))));
     for (int e = tid; e < QE / 8; e += THREADS) {
       *(u32x4*)(&lds_q[3][8 * e]) = u32x4{0, 0, 0, 0};
       *(u32x4*)(&lds_g[3][8 * e]) = u32x4{0, 0, 0, 0};
@@ -847,25 +903,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
       s[0] = mfma32x16(*(const bf16x8*)(&lds_q[0][o]), kf[kk], kk == 0 ? f32x16{} : s[0]);
       dp[0] = mfma32x16(*(const bf16x8*)(&lds_g[0][o]), vf[kk], kk == 0 ? negd0 : dp[0]);
     }
-    mask_block(0, it0);
+    mask_block(0, e0);
     agpr_hazard_pad();   // zero-filled accumulators -> first MFMA
 
-    // Tile i in stage (i - it0) % 4.  Iteration i publishes tile i+1 (its
-    // DMA has landed, its LSE / D are stored), then issues tile i+2 into the
-    // stage of tile i-2, last read in iteration i-1.
+    // Visited tile i (list position) in stage i % 4.  Iteration i publishes
+    // tile i+1 (its DMA has landed, its LSE / D are stored), then issues
+    // tile i+2 into the stage of tile i-2, last read in iteration i-1.
     int sp = 3, s0 = 0, s1 = 1;   // stages of tiles i-1, i, i+1
-    for (int it = it0; it < n_qt; ++it) {
+    for (int i = 0; i < n_vis; ++i) {
+      const unsigned ei = entry(i), ei1 = entry(i + 1);
+      const unsigned ei2 = entry(min(i + 2, last));
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       store_stats(s1);
       __syncthreads();
-      if (it + 2 <= last) dma_tile(it + 2, (s1 + 1) & 3);
-      load_stats(min(it + 2, last));
+      if (i + 2 <= last) dma_tile(qtile(ei2), (s1 + 1) & 3);
+      load_stats(qtile(ei2));
       // phase 1: A_1(i), B_1(i-1) || V_0(i)
       phase(std::false_type{}, s0, 1, sp, 1, s0, 0);
-      mask_block(1, it);
+      mask_block(1, ei);
       // phase 2: B_0(i), A_0(i+1) || V_1(i)
       phase(std::true_type{}, s1, 0, s0, 0, s0, 1);
-      if (it + 1 < n_qt) mask_block(0, it + 1);
+      if (i + 1 < n_vis) mask_block(0, ei1);
       sp = s0;
       s0 = s1;
       s1 = (s1 + 1) & 3;
@@ -908,13 +966,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
 // The DMA descriptor ends at the head's last key: keys past N read as zero.
 constexpr int kDqPBR = 256;
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dv,
-    uint16_t* __restrict__ dQ, int N, int n_qblk, float c_log2,
-    float scale) {
+    uint16_t* __restrict__ dQ, const uint8_t* __restrict__ bmask, int H,
+    int N, int n_qblk, float c_log2, float scale) {
+  static_assert(!SPARSE || kDqPBR == FA_SPARSE_BQ, "a workgroup is a mask row");
   constexpr int D = kD;
   constexpr int TE = kDqBC * kRS;                 // elements per tile stage
   constexpr int THREADS = 512;
@@ -944,10 +1003,51 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
 
   int kend = N;
   if (CAUSAL) kend = min(kend, q0 + kDqPBR);
-  const int ntiles = (kend + kDqBC - 1) / kDqBC;
+  int ntiles = (kend + kDqBC - 1) / kDqBC;
   int kend_w = N;
   if (CAUSAL) kend_w = min(kend_w, qlo + 32);
-  const int nt_w = (kend_w + kDqBC - 1) / kDqBC;
+  int nt_w = (kend_w + kDqBC - 1) / kDqBC;
+
+  // ---- block-sparse: the key tiles this workgroup's block-mask row keeps,
+  // in order, as a list in LDS; ntiles and nt_w then count list entries.
+  __shared__ uint16_t tile_list[SPARSE ? kSparseMaxTiles : 1];
+  __shared__ int tile_count;
+  if constexpr (SPARSE) {
+    const int n_mk = (N + kDqBC - 1) / kDqBC;
+    const int n_mq = (N + kDqPBR - 1) / kDqPBR;
+    const uint8_t* mrow = bmask + ((size_t)(bh % H) * n_mq + qb) * n_mk;
+    if (w == 0) {
+      int cnt = 0;
+      for (int base = 0; base < ntiles; base += 64) {
+        const int j = base + lane;
+        const bool keep = j < ntiles && mrow[j] != 0;
+        const unsigned long long bal = __ballot(keep);
+        const int below = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+        if (keep) tile_list[cnt + below] = (uint16_t)j;
+        cnt += __builtin_popcountll(bal);
+      }
+      if (lane == 0) tile_count = cnt;
+    }
+    __syncthreads();
+    const int dense_nt_w = nt_w;
+    ntiles = tile_count;
+    nt_w = ntiles;
+    if (CAUSAL) {
+      nt_w = 0;
+      for (int base = 0; base < ntiles; base += 64) {
+        const int t = base + lane;
+        nt_w += __builtin_popcountll(
+            __ballot(t < ntiles && (int)tile_list[t] < dense_nt_w));
+      }
+    }
+  }
+  // Key tile of list position t (clamped; the position itself when dense).
+  auto ktile = [&](int t) -> int {
+    if constexpr (SPARSE)
+      return (int)__builtin_amdgcn_readfirstlane((unsigned)tile_list[max(min(t, ntiles - 1), 0)]);
+    else
+      return t;
+  };
 
   const size_t head = (size_t)bh * N * D;
   const uint16_t* Qh = Q + head;
@@ -1104,11 +1204,11 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
     const int last = ntiles - 1;
     // Prologue: K_0, V_0 in stage 0, K_1, V_1 in stage 1, then K_2, V_2
     // issued; S^T, dP^T of half-tile (0, 0).
-    dma_kv(0, 0);
-    if (last >= 1) dma_kv(1, 1);
+    dma_kv(ktile(0), 0);
+    if (last >= 1) dma_kv(ktile(1), 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (last >= 2) dma_kv(2, 2);
+    if (last >= 2) dma_kv(ktile(2), 2);
     if (nt_w > 0) {
       s[0] = f32x16{};
       dp[0] = negd;
@@ -1118,7 +1218,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
         s[0] = mfma32x16(*(const bf16x8*)(&lds_k[0][o]), qf[kk], s[0]);
         dp[0] = mfma32x16(*(const bf16x8*)(&lds_v[0][o]), gf[kk], dp[0]);
       }
-      mask_half(0, 0, 0);
+      mask_half(0, ktile(0), 0);
     }
     // K_j, V_j in stage j % 4.  Tile j waits for K_{j+1}, V_{j+1} (issued
     // two tiles earlier), then issues K_{j+3}, V_{j+3} into the stage of
@@ -1126,21 +1226,22 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
     // every read of a stage has returned before its wavefront reaches the
     // barrier after which the stage is refilled.
     for (int j = 0; j < ntiles; ++j) {
+      const int kj = ktile(j), kj1 = ktile(j + 1), kj3 = ktile(j + 3);
       if (j + 2 <= last)
         asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kMinBatch) : "memory");
       else
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      if (j + 3 <= last) dma_kv(j + 3, (j + 3) & 3);
+      if (j + 3 <= last) dma_kv(kj3, (j + 3) & 3);
       const int st0 = j & 3, st1 = (j + 1) & 3;
       if (j < nt_w) {
         // step 2j: S^T, dP^T of (j, 1) || dS of (j, 0), dQ += (j, 0)
         step(std::integral_constant<int, 1>{}, st0, 1, st0, 0);
-        mask_half(1, j, 1);
+        mask_half(1, kj, 1);
         // step 2j+1: S^T, dP^T of (j+1, 0) || dS of (j, 1), dQ += (j, 1)
         step(std::integral_constant<int, 0>{}, st1, 0, st0, 1);
-        if (j + 1 < nt_w) mask_half(0, j + 1, 0);
+        if (j + 1 < nt_w) mask_half(0, kj1, 0);
       }
     }
   }
@@ -1182,22 +1283,27 @@ int launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, float* D,
 
 int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const uint16_t* dO, const float* lse, const float* D,
-                    uint16_t* dk, uint16_t* dv, int B, int H, int N, int d,
-                    float scale, int causal, hipStream_t stream) {
+                    const uint8_t* block_mask, uint16_t* dk, uint16_t* dv,
+                    int B, int H, int N, int d, float scale, int causal,
+                    hipStream_t stream) {
   if (d != kD) return -3;
   const int n_kblk = (N + kBK - 1) / kBK;
   const float c = (float)((double)scale * 1.4426950408889634);
-  // Grids with at least one 128-key workgroup per CU: the pipelined kernel
-  // (4 wavefronts, K/V in registers); smaller ones: 8 wavefronts.
-  if ((long long)B * H * n_kblk >= 256) {
+  // Grids with at least one 128-key workgroup per CU, and every
+  // block-sparse call: the pipelined kernel (4 wavefronts, K/V in
+  // registers); smaller dense ones: 8 wavefronts.
+  if ((long long)B * H * n_kblk >= 256 || block_mask != nullptr) {
     const dim3 grid((unsigned)(B * H * n_kblk)), block(256);
-    if (causal) {
-      hipLaunchKernelGGL(bwd_dkdv_pipe_kernel<true>, grid, block, 0, stream,
-                         q, k, v, dO, lse, D, dk, dv, N, n_kblk, c, scale);
+#define FA_DKDV_LAUNCH(CC, SS)                                                  \
+  hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<CC, SS>), grid, block, 0, stream, q, \
+                     k, v, dO, lse, D, dk, dv, block_mask, H, N, n_kblk, c,     \
+                     scale)
+    if (block_mask) {
+      if (causal) FA_DKDV_LAUNCH(true, true); else FA_DKDV_LAUNCH(false, true);
     } else {
-      hipLaunchKernelGGL(bwd_dkdv_pipe_kernel<false>, grid, block, 0, stream,
-                         q, k, v, dO, lse, D, dk, dv, N, n_kblk, c, scale);
+      if (causal) FA_DKDV_LAUNCH(true, false); else FA_DKDV_LAUNCH(false, false);
     }
+#undef FA_DKDV_LAUNCH
     return hipGetLastError() == hipSuccess ? 0 : -6;
   }
   const dim3 grid((unsigned)(B * H * n_kblk)), block(kBwdThreads);
@@ -1213,23 +1319,26 @@ int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 
 int launch_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   const uint16_t* dO, const float* lse, const float* D,
-                  uint16_t* dq, int B, int H, int N, int d, float scale,
-                  int causal, hipStream_t stream) {
+                  const uint8_t* block_mask, uint16_t* dq, int B, int H, int N,
+                  int d, float scale, int causal, hipStream_t stream) {
   if (d != kD) return -3;
   const float c = (float)((double)scale * 1.4426950408889634);
-  // Grids with at least one 256-row workgroup per CU: the pipelined kernel;
-  // smaller ones: 128-row workgroups, two per CU.
+  // Grids with at least one 256-row workgroup per CU, and every
+  // block-sparse call (a workgroup is one block-mask row): the pipelined
+  // kernel; smaller dense ones: 128-row workgroups, two per CU.
   const long long grid256 = (long long)B * H * ((N + kDqPBR - 1) / kDqPBR);
-  if (grid256 >= 256) {
+  if (grid256 >= 256 || block_mask != nullptr) {
     const int n_qblk = (N + kDqPBR - 1) / kDqPBR;
     const dim3 grid((unsigned)(B * H * n_qblk)), block(512);
-    if (causal) {
-      hipLaunchKernelGGL(bwd_dq_pipe_kernel<true>, grid, block, 0, stream, q,
-                         k, v, dO, lse, D, dq, N, n_qblk, c, scale);
+#define FA_DQ_LAUNCH(CC, SS)                                                  \
+  hipLaunchKernelGGL((bwd_dq_pipe_kernel<CC, SS>), grid, block, 0, stream, q, \
+                     k, v, dO, lse, D, dq, block_mask, H, N, n_qblk, c, scale)
+    if (block_mask) {
+      if (causal) FA_DQ_LAUNCH(true, true); else FA_DQ_LAUNCH(false, true);
     } else {
-      hipLaunchKernelGGL(bwd_dq_pipe_kernel<false>, grid, block, 0, stream, q,
-                         k, v, dO, lse, D, dq, N, n_qblk, c, scale);
+      if (causal) FA_DQ_LAUNCH(true, false); else FA_DQ_LAUNCH(false, false);
     }
+#undef FA_DQ_LAUNCH
     return hipGetLastError() == hipSuccess ? 0 : -6;
   }
   const int n_qblk = (N + kDqBR - 1) / kDqBR;

@@ -23,15 +23,17 @@ int launch_fwd_f32(const float* q, const float* k, const float* v, float* o,
 int launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, float* D,
                           int B, int H, int N, int d, hipStream_t stream);
 
+// block_mask: device uint8 [H, ceil(N/256), ceil(N/64)] or NULL (dense).
 int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const uint16_t* dO, const float* lse, const float* D,
-                    uint16_t* dk, uint16_t* dv, int B, int H, int N, int d,
-                    float scale, int causal, hipStream_t stream);
+                    const uint8_t* block_mask, uint16_t* dk, uint16_t* dv,
+                    int B, int H, int N, int d, float scale, int causal,
+                    hipStream_t stream);
 
 int launch_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   const uint16_t* dO, const float* lse, const float* D,
-                  uint16_t* dq, int B, int H, int N, int d, float scale,
-                  int causal, hipStream_t stream);
+                  const uint8_t* block_mask, uint16_t* dq, int B, int H, int N,
+                  int d, float scale, int causal, hipStream_t stream);
 
 // FP8 forward (layouts in include/fa.h).  signs: device int8 [d] or NULL.
 int launch_fp8_quantize(const uint16_t* q, const uint16_t* k,

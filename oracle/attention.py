@@ -186,11 +186,13 @@ def attention_probs(q, k, scale, causal=False, kv_len=None):
 
 
 def attention_bwd(q, k, v, do, scale, causal=False, kv_len=None,
-                  row_chunk=512, workers=None):
+                  row_chunk=512, workers=None, block_mask=None, block_q=256,
+                  block_k=64):
     """Analytic gradients (dQ, dK, dV) of <dO, O>, float64, [B,H,N,d] each.
 
-    P is recomputed from Q and K by the forward's definition; D_i is the
-    row sum of P * dP (equal to dO_i . O_i).
+    P is recomputed from Q and K by the forward's definition (with the same
+    optional block mask as attention_fwd); D_i is the row sum of P * dP
+    (equal to dO_i . O_i).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -205,9 +207,11 @@ def attention_bwd(q, k, v, do, scale, causal=False, kv_len=None,
     def one(bh):
         b, h = bh
         L = None if kv_len is None else int(kv_len[b])
+        bm = None if block_mask is None else block_mask[h]
         for c0 in range(0, N, row_chunk):
             c1 = min(N, c0 + row_chunk)
-            p, _, _ = _probs_rows(q[b, h], k[b, h], scale, causal, L, c0, c1)
+            p, _, _ = _probs_rows(q[b, h], k[b, h], scale, causal, L, c0, c1,
+                                  None, bm, block_q, block_k)
             dor = do[b, h, c0:c1]
             dv[b, h] += p.T @ dor
             dp = dor @ v[b, h].T

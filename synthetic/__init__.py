@@ -98,6 +98,11 @@ WORKLOADS = {
                  (601, 602, 603), block_seed=609, block_density=0.5,
                  description="block-sparse forward, half of the 256x64 "
                              "blocks kept per head, head dim 128"),
+        Workload("blocksparse_fwd_bwd_d128", 4, 16, 4096, 128, "bf16", False,
+                 (601, 602, 603, 604), backward=True, block_seed=609,
+                 block_density=0.5,
+                 description="block-sparse forward + backward, the blocks "
+                             "of blocksparse_d128"),
         Workload("fp8_causal_d128", 4, 16, 4096, 128, "bf16", True,
                  (701, 702, 703), sign_seed=709,
                  description="FP8 causal forward with incoherent processing "

@@ -35,6 +35,8 @@ def test_header_declares_expected_calls():
                  "fa_fwd_block_sparse", "fa_fp8_workspace_size",
                  "fa_fp8_quantize", "fa_fwd_fp8_quantized", "fa_fwd_fp8",
                  "fa_linear_fwd", "fa_linear_workspace_size",
+                 "fa_bwd_block_sparse", "fa_bwd_dkdv_block_sparse",
+                 "fa_bwd_dq_block_sparse",
                  "fa_bwd_workspace_size", "fa_status_string", "fa_version",
                  "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq"]:
         assert want in names
@@ -104,6 +106,32 @@ def test_block_sparse_argument_errors():
     assert sp(N=64 * 2048 + 1) == SHAPE       # more key blocks than the limit
     assert sp(d=96) == HEADDIM
     assert sp(o=MIS) == ALIGN
+
+
+def test_block_sparse_bwd_argument_errors():
+    L = fa.lib()
+    nbytes = fa.fa_bwd_workspace_size(1, 2, 64, 128)
+    W = 0x100000
+
+    def sb(ptrs=None, N=64, d=128, ws=W, wsb=nbytes):
+        p = ptrs or [A] * 10
+        return L.fa_bwd_block_sparse(*p, ws, wsb, 1, 2, N, d, 0.1, 1, None)
+    for i in range(10):
+        p = [A] * 10
+        p[i] = None
+        assert sb(p) == NULL, i
+    assert sb(d=64) == HEADDIM
+    assert sb(N=64 * 2048 + 1, wsb=1 << 40) == SHAPE
+    assert sb(ws=None) == WORKSPACE
+    p = [A] * 10
+    p[7] = MIS
+    assert sb(p) == ALIGN
+    assert L.fa_bwd_dkdv_block_sparse(A, A, A, A, A, None, A, A, W, nbytes,
+                                      1, 2, 64, 128, 0.1, 1, None) == NULL
+    assert L.fa_bwd_dq_block_sparse(A, A, A, A, A, A, A, W, 0, 1, 2, 64, 128,
+                                    0.1, 1, None) == WORKSPACE
+    assert L.fa_bwd_dq_block_sparse(A, A, A, A, A, A, A, W, nbytes, 1, 2, 64,
+                                    64, 0.1, 1, None) == HEADDIM
 
 
 def test_workspace_size():

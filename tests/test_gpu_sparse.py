@@ -112,3 +112,92 @@ def test_sparse_workload_sampled_rows():
                                    [0, 255, 256, 4095]]))
     _check("blocksparse_d128 sampled", inp, inp["block_mask"], rows=rows,
            heads=[0, 7, 15])
+
+
+# ---------------------------------------------------------------- backward
+
+def _check_bwd(name, inp, mask, heads=None):
+    """fa_fwd_block_sparse then fa_bwd_block_sparse against the oracle's
+    gradients under the same block mask (max abs error <= 5e-2)."""
+    import torch
+    import io_aware_tiled_amd as fa
+    from oracle import attention_bwd
+    from gpu_util import TOL_GRAD
+    q, k, v, do = (to_dev(inp, n) for n in ("q", "k", "v", "do"))
+    m = torch.from_numpy(np.ascontiguousarray(mask, dtype=np.uint8)).to(DEV)
+    o, lse = fa.forward(q, k, v, causal=inp["causal"], scale=inp["scale"],
+                        block_mask=m)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=inp["causal"],
+                             scale=inp["scale"], block_mask=m)
+    torch.cuda.synchronize()
+    sel = (lambda a: a) if heads is None else (lambda a: a[:, heads])
+    bm = mask.astype(bool) if heads is None else mask.astype(bool)[heads]
+    ref = attention_bwd(sel(inp["q"]), sel(inp["k"]), sel(inp["v"]),
+                        sel(inp["do"]), inp["scale"], inp["causal"],
+                        workers=8, block_mask=bm)
+    errs = {}
+    for nm, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        errs[nm] = max_err(sel(host64(g)), r, f"{name} {nm}")
+    report(name, **errs)
+    for nm, e in errs.items():
+        assert e <= TOL_GRAD, (name, nm, e)
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [64, 300, 1000])
+def test_sparse_bwd_small(causal, N):
+    inp = S.make_case(2, 3, N, 128, "bf16", causal, seed=60 + N,
+                      backward=True)
+    _check_bwd(f"sparse bwd causal={causal} N={N}", inp,
+               _mask(N + 7, 3, N, 0.4))
+
+
+def test_sparse_bwd_single_columns():
+    """Masks that keep exactly one of a dK/dV workgroup's two 64-key columns
+    (the other wavefront pair must see the tile as masked)."""
+    N, H = 640, 2
+    tq, tk = -(-N // 256), -(-N // 64)
+    m = np.zeros((H, tq, tk), dtype=np.uint8)
+    m[0, :, 0::2] = 1          # even key columns only
+    m[1, :, 1::2] = 1          # odd key columns only
+    inp = S.make_case(1, H, N, 128, "bf16", False, seed=61, backward=True)
+    _check_bwd("sparse bwd single columns", inp, m)
+
+
+def test_sparse_bwd_all_ones_equals_dense_bitwise():
+    """With every block kept the block-sparse backward must return the
+    dense backward's bits; the grid (4 x 64 heads, N = 300) makes the dense
+    call take the same pipelined kernels that every block-sparse call
+    takes."""
+    import torch
+    import io_aware_tiled_amd as fa
+    inp = S.make_case(4, 64, 300, 128, "bf16", True, seed=62, backward=True)
+    q, k, v, do = (to_dev(inp, n) for n in ("q", "k", "v", "do"))
+    o, lse = fa.forward(q, k, v, causal=True, scale=inp["scale"])
+    ones = torch.ones((64, 2, 5), dtype=torch.uint8, device=DEV)
+    g_sparse = fa.backward(q, k, v, o, lse, do, causal=True,
+                           scale=inp["scale"], block_mask=ones)
+    g_dense = fa.backward(q, k, v, o, lse, do, causal=True, scale=inp["scale"])
+    torch.cuda.synchronize()
+    for a, b in zip(g_sparse, g_dense):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_sparse_bwd_empty_rows():
+    """A block row with no kept block: its queries get dQ = 0 and add
+    nothing to dK, dV."""
+    inp = S.make_case(1, 3, 512, 128, "bf16", True, seed=63, backward=True)
+    m = _mask(64, 3, 512, 0.5)           # row 1 of head 0 emptied
+    dq, _, _ = _check_bwd("sparse bwd empty row", inp, m)
+    assert float(dq[0, 0, 256:512].float().abs().max()) == 0.0
+
+
+def test_sparse_bwd_workload_heads():
+    """The block-sparse workload's shape (4 x 16 x 4096, half the blocks):
+    two heads of batch 0 against the full oracle."""
+    w = S.WORKLOADS["blocksparse_d128"]
+    inp = S.make_case(1, w.H, w.N, w.d, "bf16", False, seed=64, backward=True)
+    mask = S.block_mask(w.block_seed, w.H, w.N, w.block_density)
+    _check_bwd("blocksparse_d128 shape bwd heads 0,11", inp, mask,
+               heads=np.array([0, 11]))

@@ -510,11 +510,42 @@ def pin_block_sparse_reductions(m):
         assert np.all(lse == -np.inf)
 
 
+def pin_block_sparse_grad(m):
+    """Gradients with a block mask: central finite differences of <dO, O>
+    under the same mask, and an all-ones mask equals the dense gradients."""
+    N, d = 9, 3
+    bm = np.array([[[1, 0, 1], [0, 1, 1], [1, 1, 0]]], dtype=bool)   # bq 3, bk 3
+    q, k, v = _rand(91, 1, 1, N, d), _rand(92, 1, 1, N, d), _rand(93, 1, 1, N, d)
+    do = _rand(94, 1, 1, N, d)
+    grads = m.attention_bwd(q, k, v, do, 0.7, False, block_mask=bm,
+                            block_q=3, block_k=3)
+
+    def loss(*a):
+        o, _ = m.attention_fwd(*a, 0.7, False, block_mask=bm, block_q=3,
+                               block_k=3)
+        return float(np.sum(o * do))
+    h = 1e-6
+    for which, g in zip(range(3), grads):
+        num = np.zeros_like(g)
+        for idx in np.ndindex(*g.shape):
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][idx] += h
+            lp = loss(*args)
+            args[which][idx] -= 2 * h
+            num[idx] = (lp - loss(*args)) / (2 * h)
+        _close(g, num, 1e-6 * max(1.0, np.abs(num).max()), f"sparse fd {which}")
+    ones = np.ones((1, 3, 3), dtype=bool)
+    for a, b in zip(m.attention_bwd(q, k, v, do, 0.7, True, block_mask=ones,
+                                    block_q=3, block_k=3),
+                    m.attention_bwd(q, k, v, do, 0.7, True)):
+        _close(a, b, 1e-13, "all-ones mask gradients")
+
+
 PINS = [pin_golden, pin_bruteforce, pin_closed_forms, pin_prob_rows,
         pin_shift, pin_permutation, pin_tiled_recurrence, pin_reductions,
         pin_torch_sdpa, pin_finite_diff, pin_torch_autograd,
         pin_grad_invariants, pin_visible_pairs, pin_block_sparse_bruteforce,
-        pin_block_sparse_reductions]
+        pin_block_sparse_reductions, pin_block_sparse_grad]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
