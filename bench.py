@@ -60,13 +60,13 @@ def _sources_digest(names):
 
 def visible_pairs(w: S.Workload, kv_len, block_mask=None) -> int:
     if block_mask is not None:
-        # kept 256x64 blocks of each head (every batch entry), causal pairs
+        # kept 256x128 blocks of each head (every batch entry), causal pairs
         # counted inside diagonal blocks
         i = np.arange(w.N)[:, None]
         j = np.arange(w.N)[None, :]
         total = 0
         for h in range(block_mask.shape[0]):
-            vis = block_mask[h].astype(bool)[i // 256, j // 64]
+            vis = block_mask[h].astype(bool)[i // 256, j // 128]
             if w.causal:
                 vis &= j <= i
             total += int(vis.sum())

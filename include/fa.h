@@ -104,17 +104,18 @@ int fa_fwd_kvlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  *     block_mask[(h * ceil(N/FA_SPARSE_BQ) + i / FA_SPARSE_BQ)
  *                * ceil(N/FA_SPARSE_BK) + j / FA_SPARSE_BK] != 0
  * and (causal == 0 or j <= i); the same mask serves every batch entry.
- *   block_mask : device uint8 [H, ceil(N/256), ceil(N/64)], read only.
+ *   block_mask : device uint8 [H, ceil(N/256), ceil(N/128)], read only.
  *   other arguments as fa_fwd.
- * A block row is one query workgroup of the kernel and a block column one
- * key tile; dropped blocks are neither loaded nor computed.  A row with no
+ * A block row is one query workgroup of the forward and dQ kernels and a
+ * block column one dK/dV workgroup (two key tiles of the forward); dropped
+ * blocks are neither loaded nor computed.  A row with no
  * visible key gets O = 0 and LSE = -inf.
  * Errors as fa_fwd, plus FA_ERR_NULL for a NULL block_mask and FA_ERR_SHAPE
- * when ceil(N/64) exceeds FA_SPARSE_MAX_KEY_BLOCKS (N > 131072).
+ * when ceil(N/128) exceeds FA_SPARSE_MAX_KEY_BLOCKS (N > 131072).
  */
 #define FA_SPARSE_BQ 256
-#define FA_SPARSE_BK 64
-#define FA_SPARSE_MAX_KEY_BLOCKS 2048
+#define FA_SPARSE_BK 128
+#define FA_SPARSE_MAX_KEY_BLOCKS 1024
 int fa_fwd_block_sparse(const uint16_t* q, const uint16_t* k,
                         const uint16_t* v, const uint8_t* block_mask,
                         uint16_t* o, float* lse, int B, int H, int N, int d,
@@ -285,9 +286,9 @@ int fa_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * Backward of the block-sparse forward (fa_fwd_block_sparse; [ZN]
  * "Overview"): the same gradients as fa_bwd with P taken over the block
  * mask's visible keys only.
- * dK/dV workgroups visit only the 64-row query tiles whose block-mask row
- * keeps one of their two 64-key columns; dQ workgroups (one per 256-row
- * block-mask row) visit only the kept key tiles.  Arguments as fa_bwd plus
+ * dK/dV workgroups (one per 128-key block-mask column) visit only the
+ * 64-row query tiles whose block-mask row keeps their column; dQ workgroups
+ * (one per 256-row block-mask row) visit only the kept key tiles.  Arguments as fa_bwd plus
  * block_mask as in fa_fwd_block_sparse; lse must come from
  * fa_fwd_block_sparse with the same mask.  d = 128.  Errors as fa_bwd, plus
  * FA_ERR_NULL for a NULL block_mask and FA_ERR_SHAPE for N > 131072.

@@ -165,13 +165,13 @@ def fa_fwd_kvlen(q, k, v, kv_len, o, lse, scale, causal, stream=None):
     _check(st, "fa_fwd_kvlen")
 
 
-SPARSE_BQ, SPARSE_BK = 256, 64   # block-mask granularity (FA_SPARSE_BQ/BK)
+SPARSE_BQ, SPARSE_BK = 256, 128   # block-mask granularity (FA_SPARSE_BQ/BK)
 
 
 def fa_fwd_block_sparse(q, k, v, block_mask, o, lse, scale, causal,
                         stream=None):
     """C fa_fwd_block_sparse; block_mask is a device uint8 tensor
-    [H, ceil(N/256), ceil(N/64)] (nonzero = block kept)."""
+    [H, ceil(N/256), ceil(N/128)] (nonzero = block kept)."""
     import torch
     B, H, N, d = _bhnd(q)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
@@ -230,7 +230,7 @@ def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, workspace, scale, causal,
 def fa_bwd_block_sparse(q, k, v, o, dO, lse, block_mask, dq, dk, dv,
                         workspace, scale, causal, stream=None):
     """C fa_bwd_block_sparse: backward of fa_fwd_block_sparse with the same
-    uint8 block mask [H, ceil(N/256), ceil(N/64)]."""
+    uint8 block mask [H, ceil(N/256), ceil(N/128)]."""
     import torch
     B, H, N, d = _bhnd(q)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO"),

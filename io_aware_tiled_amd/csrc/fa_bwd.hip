@@ -58,7 +58,8 @@ constexpr int kThreads = 256;
 constexpr int kBK = 128;   // keys per workgroup (32 per wavefront)
 // Block-sparse backward: query and key tiles of one head are listed in LDS
 // as 16-bit entries, at most this many (64-row tiles up to N = 131072).
-constexpr int kSparseMaxTiles = FA_SPARSE_MAX_KEY_BLOCKS;
+constexpr int kSparseMaxTiles = 2 * FA_SPARSE_MAX_KEY_BLOCKS;
+static_assert(FA_SPARSE_BK == kBK, "a block-mask column is one dK/dV workgroup");
 constexpr int kD = 128;    // head dimension of the backward kernel
 
 // ---------------------------------------------------------------------------
@@ -630,33 +631,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
   const int n_qt = (N + kBQ2 - 1) / kBQ2;
   const int it0 = CAUSAL ? kb0 / kBQ2 : 0;
 
-  // ---- query tiles to visit, as entries: tile index | keep bits << 12,
-  // bit w/2 telling whether wavefront w's 64-key block column is kept for
-  // the tile's block-mask row.  Dense: tiles it0 .. n_qt - 1, all kept.
-  // Block-sparse: the tiles whose row keeps either of the workgroup's two
-  // key columns, compacted into an LDS list; a wavefront whose column is
-  // dropped masks the whole tile.
+  // ---- query tiles to visit.  Dense: it0 .. n_qt - 1.  Block-sparse: the
+  // workgroup's 128 keys are one block-mask column; the 64-row query tiles
+  // whose block row keeps it are compacted into an LDS list.
   __shared__ uint16_t qt_list[SPARSE ? kSparseMaxTiles : 1];
   __shared__ int qt_count;
   int n_vis = n_qt - it0;
   if constexpr (SPARSE) {
     const int n_mk = (N + FA_SPARSE_BK - 1) / FA_SPARSE_BK;
     const int n_mq = (N + FA_SPARSE_BQ - 1) / FA_SPARSE_BQ;
-    const uint8_t* mh = bmask + (size_t)(bh % H) * n_mq * n_mk;
-    const int c0 = kb0 / FA_SPARSE_BK;
+    const uint8_t* mcol = bmask + (size_t)(bh % H) * n_mq * n_mk + jb;
     if (w == 0) {
       int cnt = 0;
       for (int base = it0; base < n_qt; base += 64) {
         const int q = base + lane;
-        unsigned bits = 0;
-        if (q < n_qt) {
-          const uint8_t* mr = mh + (size_t)(q * kBQ2 / FA_SPARSE_BQ) * n_mk;
-          bits = (mr[c0] != 0 ? 1u : 0u) |
-                 ((c0 + 1 < n_mk && mr[c0 + 1] != 0) ? 2u : 0u);
-        }
-        const unsigned long long bal = __ballot(bits != 0);
+        const bool keep =
+            q < n_qt && mcol[(size_t)(q * kBQ2 / FA_SPARSE_BQ) * n_mk] != 0;
+        const unsigned long long bal = __ballot(keep);
         const int below = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
-        if (bits != 0) qt_list[cnt + below] = (uint16_t)((unsigned)q | (bits << 12));
+        if (keep) qt_list[cnt + below] = (uint16_t)q;
         cnt += __builtin_popcountll(bal);
       }
       if (lane == 0) qt_count = cnt;
@@ -664,13 +657,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
     __syncthreads();
     n_vis = qt_count;
   }
-  auto entry = [&](int p) -> unsigned {
+  // Query tile of visit i (clamped; it0 + i when dense).
+  auto qtile = [&](int i) -> int {
     if constexpr (SPARSE)
-      return __builtin_amdgcn_readfirstlane((unsigned)qt_list[max(min(p, n_vis - 1), 0)]);
+      return (int)__builtin_amdgcn_readfirstlane((unsigned)qt_list[max(min(i, n_vis - 1), 0)]);
     else
-      return (unsigned)(it0 + p) | (3u << 12);
+      return it0 + i;
   };
-  auto qtile = [](unsigned e) -> int { return (int)(e & 0xFFFu); };
 
   // The K and V fragments have arrived before any DMA is issued (a wait
   // the compiler can see, so that it places none of its own inside the
@@ -827,17 +820,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
                  "+v"(dsb[cv][1]));
   };
 
-  // ---- mask block c of the query tile of entry e where needed (causal
-  // diagonal, keys past N, a dropped block of the mask; rows past N already
-  // have P = 0 through LSE = +inf).
-  auto mask_block = [&](int c, unsigned e) {
-    const int qb0 = qtile(e) * kBQ2 + 32 * c;
-    const bool dropped = SPARSE && ((e >> (12 + (w >> 1))) & 1u) == 0;
-    if (dropped) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[c][r] = -INFINITY;
-      return;
-    }
+  // ---- mask block c of query tile qt where needed (causal diagonal, keys
+  // past N; rows past N already have P = 0 through LSE = +inf).
+  auto mask_block = [&](int c, int qt) {
+    const int qb0 = qt * kBQ2 + 32 * c;
     const bool need_mask = (CAUSAL && wk0 + 31 > qb0) || (wk0 + 32 > N);
     if (need_mask) {
 #pragma unroll
@@ -871,12 +857,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
     // Prologue: the first tile in stage 0, the second in stage 1 (its LSE /
     // D in registers); zeros in stage 3 (the tile before the first, whose
     // block 1 the first phase multiplies by P = dS = 0); A_0 of the first.
-    const unsigned e0 = entry(0);
-    dma_tile(qtile(e0), 0);
-    if (last >= 1) dma_tile(qtile(entry(1)), 1);
-    load_stats(qtile(e0));
+    const int e0 = qtile(0);
+    dma_tile(e0, 0);
+    if (last >= 1) dma_tile(qtile(1), 1);
+    load_stats(e0);
     store_stats(0);
-    load_stats(qtile(entry(min(1, last))));
+    load_stats(qtile(min(1, last)));
     for (int e = tid; e < QE / 8; e += THREADS) {
       *(u32x4*)(&lds_q[3][8 * e]) = u32x4{0, 0, 0, 0};
       *(u32x4*)(&lds_g[3][8 * e]) = u32x4{0, 0, 0, 0};
@@ -911,13 +897,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
     // tile i+2 into the stage of tile i-2, last read in iteration i-1.
     int sp = 3, s0 = 0, s1 = 1;   // stages of tiles i-1, i, i+1
     for (int i = 0; i < n_vis; ++i) {
-      const unsigned ei = entry(i), ei1 = entry(i + 1);
-      const unsigned ei2 = entry(min(i + 2, last));
+      const int ei = qtile(i), ei1 = qtile(i + 1), ei2 = qtile(min(i + 2, last));
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       store_stats(s1);
       __syncthreads();
-      if (i + 2 <= last) dma_tile(qtile(ei2), (s1 + 1) & 3);
-      load_stats(qtile(ei2));
+      if (i + 2 <= last) dma_tile(ei2, (s1 + 1) & 3);
+      load_stats(ei2);
       // phase 1: A_1(i), B_1(i-1) || V_0(i)
       phase(std::false_type{}, s0, 1, sp, 1, s0, 0);
       mask_block(1, ei);
@@ -1013,14 +998,14 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
   __shared__ uint16_t tile_list[SPARSE ? kSparseMaxTiles : 1];
   __shared__ int tile_count;
   if constexpr (SPARSE) {
-    const int n_mk = (N + kDqBC - 1) / kDqBC;
+    const int n_mk = (N + FA_SPARSE_BK - 1) / FA_SPARSE_BK;
     const int n_mq = (N + kDqPBR - 1) / kDqPBR;
     const uint8_t* mrow = bmask + ((size_t)(bh % H) * n_mq + qb) * n_mk;
     if (w == 0) {
       int cnt = 0;
       for (int base = 0; base < ntiles; base += 64) {
-        const int j = base + lane;
-        const bool keep = j < ntiles && mrow[j] != 0;
+        const int j = base + lane;      // key tile j lies in mask column j/2
+        const bool keep = j < ntiles && mrow[j >> 1] != 0;
         const unsigned long long bal = __ballot(keep);
         const int below = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
         if (keep) tile_list[cnt + below] = (uint16_t)j;

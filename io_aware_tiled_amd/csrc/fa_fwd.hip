@@ -60,8 +60,8 @@ constexpr float kSumLimit = 0x1p8f;
 // (one workgroup of the pipelined kernel) x 64 keys (one key tile), and
 // heads have at most 2048 key tiles.
 constexpr int kSparseBQ = FA_SPARSE_BQ;
-constexpr int kSparseMaxTiles = FA_SPARSE_MAX_KEY_BLOCKS;
-static_assert(FA_SPARSE_BK == kBC, "a block-mask column is one key tile");
+constexpr int kSparseMaxTiles = 2 * FA_SPARSE_MAX_KEY_BLOCKS;
+static_assert(FA_SPARSE_BK == 2 * kBC, "a block-mask column is two key tiles");
 
 template <int D, int NW>
 struct FwdTile {
@@ -422,14 +422,14 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
   __shared__ uint32_t tile_list[SPARSE ? kSparseMaxTiles : 1];
   __shared__ int tile_count;
   if constexpr (SPARSE) {
-    const int n_mk = (N + kBC - 1) / kBC;
+    const int n_mk = (N + FA_SPARSE_BK - 1) / FA_SPARSE_BK;
     const int n_mq = (N + kSparseBQ - 1) / kSparseBQ;
     const uint8_t* mrow = bmask + ((size_t)(bh % H) * n_mq + qb) * n_mk;
     if (w == 0) {
       int cnt = 0;
       for (int base = 0; base < ntiles; base += 64) {
-        const int j = base + lane;
-        const bool keep = j < ntiles && mrow[j] != 0;
+        const int j = base + lane;      // key tile j lies in mask column j/2
+        const bool keep = j < ntiles && mrow[j >> 1] != 0;
         const unsigned long long bal = __ballot(keep);
         const int below = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
         if (keep) tile_list[cnt + below] = (unsigned)j;

@@ -10,7 +10,7 @@
 namespace fa {
 
 // kv_len: device int32 [B] or NULL; block_mask: device uint8
-// [H, ceil(N/256), ceil(N/64)] or NULL (never both).
+// [H, ceil(N/256), ceil(N/128)] or NULL (never both).
 int launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const int32_t* kv_len, const uint8_t* block_mask,
                     uint16_t* o, float* lse, int B, int H, int N, int d,
@@ -23,7 +23,7 @@ int launch_fwd_f32(const float* q, const float* k, const float* v, float* o,
 int launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, float* D,
                           int B, int H, int N, int d, hipStream_t stream);
 
-// block_mask: device uint8 [H, ceil(N/256), ceil(N/64)] or NULL (dense).
+// block_mask: device uint8 [H, ceil(N/256), ceil(N/128)] or NULL (dense).
 int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const uint16_t* dO, const float* lse, const float* D,
                     const uint8_t* block_mask, uint16_t* dk, uint16_t* dv,

@@ -35,7 +35,7 @@ Readings where the pages are silent (each also listed in the design notes):
     gives no further detail) is read as the definition restricted by a
     boolean block mask M [H, ceil(N/bq), ceil(N/bk)]: key j is also required
     to satisfy M[h, i // bq, j // bk] for query i of head h, for every batch
-    entry.  bq = 256 query rows and bk = 64 keys unless given.
+    entry.  bq = 256 query rows and bk = 128 keys unless given.
   * Backward: the pages give no formulas, only that P is recomputed from the
     stored statistics ([MM] "Backward pass: recompute instead of store";
     [TW] "Recomputation").  The oracle is the analytic gradient of
@@ -60,7 +60,7 @@ __all__ = ["attention_fwd", "attention_bwd", "attention_probs",
 def visible_mask(r0: int, r1: int, n_keys: int, causal: bool,
                  kv_len_b: int | None, rows: np.ndarray | None = None,
                  block_mask: np.ndarray | None = None, bq: int = 256,
-                 bk: int = 64) -> np.ndarray:
+                 bk: int = 128) -> np.ndarray:
     """Boolean [rows, n_keys]: True where key j is visible to query i.
 
     Query indices are r0..r1-1, or `rows` when given.  block_mask: optional
@@ -94,7 +94,7 @@ def visible_pairs(N: int, causal: bool, kv_len=None, B: int = 1,
 
 
 def _probs_rows(qh, kh, scale, causal, kv_len_b, r0, r1, rows=None,
-                bmask=None, bq=256, bk=64):
+                bmask=None, bq=256, bk=128):
     """Two-pass softmax of one head's query rows.
 
     Returns (P [rows, N], m [rows], l [rows]); for rows without a visible
@@ -127,7 +127,7 @@ def _run(fn, items, workers):
 
 def attention_fwd(q, k, v, scale, causal=False, kv_len=None, rows=None,
                   row_chunk=512, workers=None, block_mask=None,
-                  block_q=256, block_k=64):
+                  block_q=256, block_k=128):
     """O and LSE of softmax(scale * Q K^T) V, float64.
 
     q, k, v: [B, H, N, d].  kv_len: None or int [B].  rows: optional 1-D
@@ -187,7 +187,7 @@ def attention_probs(q, k, scale, causal=False, kv_len=None):
 
 def attention_bwd(q, k, v, do, scale, causal=False, kv_len=None,
                   row_chunk=512, workers=None, block_mask=None, block_q=256,
-                  block_k=64):
+                  block_k=128):
     """Analytic gradients (dQ, dK, dV) of <dO, O>, float64, [B,H,N,d] each.
 
     P is recomputed from Q and K by the forward's definition (with the same

@@ -96,7 +96,7 @@ WORKLOADS = {
                  description="causal forward + backward, head dim 128"),
         Workload("blocksparse_d128", 4, 16, 4096, 128, "bf16", False,
                  (601, 602, 603), block_seed=609, block_density=0.5,
-                 description="block-sparse forward, half of the 256x64 "
+                 description="block-sparse forward, half of the 256x128 "
                              "blocks kept per head, head dim 128"),
         Workload("blocksparse_fwd_bwd_d128", 4, 16, 4096, 128, "bf16", False,
                  (601, 602, 603, 604), backward=True, block_seed=609,
@@ -172,7 +172,7 @@ def make_inputs(w: Workload | str, heads: slice | None = None) -> dict:
 
 
 def block_mask(seed: int, H: int, N: int, density: float,
-               bq: int = 256, bk: int = 64) -> np.ndarray:
+               bq: int = 256, bk: int = 128) -> np.ndarray:
     """Seeded block mask, uint8 [H, ceil(N/bq), ceil(N/bk)]: each block is
     kept with probability `density`, and the block holding the diagonal of
     each block row is always kept (so every query row sees some key)."""

@@ -1,7 +1,7 @@
 """GPU parity of the block-sparse forward (fa_fwd_block_sparse) against the
 fp64 oracle restricted by the same block mask.
 
-Block mask: one byte per 256 query rows x 64 keys and head; the oracle
+Block mask: one byte per 256 query rows x 128 keys and head; the oracle
 expands it to an element mask.  Tolerances as the dense bf16 forward:
 max abs error O 2e-2, LSE 1e-3.
 """
@@ -88,7 +88,7 @@ def test_sparse_all_ones_equals_dense_bitwise():
     from gpu_util import run_fwd
     for d in (64, 128):
         inp = S.make_case(2, 64, 600, d, "bf16", True, seed=12 + d)
-        ones = np.ones((64, 3, 10), dtype=np.uint8)
+        ones = np.ones((64, 3, 5), dtype=np.uint8)
         o, lse = _run_sparse(inp, ones)
         od, lsed = run_fwd(inp)
         assert torch.equal(o.view(torch.int16), od.view(torch.int16)), d
@@ -98,7 +98,7 @@ def test_sparse_all_ones_equals_dense_bitwise():
 def test_sparse_empty_mask():
     import torch
     inp = S.make_case(1, 2, 200, 64, "bf16", True, seed=13)
-    o, lse = _run_sparse(inp, np.zeros((2, 1, 4), dtype=np.uint8))
+    o, lse = _run_sparse(inp, np.zeros((2, 1, 2), dtype=np.uint8))
     assert torch.all(o.float() == 0)
     assert torch.all(lse == -float("inf"))
 
@@ -153,16 +153,18 @@ def test_sparse_bwd_small(causal, N):
                _mask(N + 7, 3, N, 0.4))
 
 
-def test_sparse_bwd_single_columns():
-    """Masks that keep exactly one of a dK/dV workgroup's two 64-key columns
-    (the other wavefront pair must see the tile as masked)."""
+def test_sparse_bwd_alternate_columns():
+    """Masks that keep every other 128-key column (every other dK/dV
+    workgroup sees no query at all and must write dK = dV = 0)."""
     N, H = 640, 2
-    tq, tk = -(-N // 256), -(-N // 64)
+    tq, tk = -(-N // 256), -(-N // 128)
     m = np.zeros((H, tq, tk), dtype=np.uint8)
     m[0, :, 0::2] = 1          # even key columns only
     m[1, :, 1::2] = 1          # odd key columns only
     inp = S.make_case(1, H, N, 128, "bf16", False, seed=61, backward=True)
-    _check_bwd("sparse bwd single columns", inp, m)
+    dq, dk, dv = _check_bwd("sparse bwd alternate columns", inp, m)
+    assert float(dk[0, 0, 128:256].float().abs().max()) == 0.0
+    assert float(dv[0, 1, 0:128].float().abs().max()) == 0.0
 
 
 def test_sparse_bwd_all_ones_equals_dense_bitwise():
@@ -175,7 +177,7 @@ def test_sparse_bwd_all_ones_equals_dense_bitwise():
     inp = S.make_case(4, 64, 300, 128, "bf16", True, seed=62, backward=True)
     q, k, v, do = (to_dev(inp, n) for n in ("q", "k", "v", "do"))
     o, lse = fa.forward(q, k, v, causal=True, scale=inp["scale"])
-    ones = torch.ones((64, 2, 5), dtype=torch.uint8, device=DEV)
+    ones = torch.ones((64, 2, 3), dtype=torch.uint8, device=DEV)
     g_sparse = fa.backward(q, k, v, o, lse, do, causal=True,
                            scale=inp["scale"], block_mask=ones)
     g_dense = fa.backward(q, k, v, o, lse, do, causal=True, scale=inp["scale"])
