@@ -93,10 +93,22 @@ def cpu_baseline(w: S.Workload, inp: dict, target_s: float = 15.0) -> dict:
     q, k, v = (inp[n][sl] for n in ("q", "k", "v"))
     kv = None if inp["kv_len"] is None else inp["kv_len"][:1]
     bm = inp.get("block_mask")
+    import oracle.dropout
     import oracle.fp8
     import oracle.linear
+    dr = inp.get("dropout")
 
     def run(q, k, v, nh, sl):
+        if dr is not None:
+            p8 = oracle.dropout.threshold(dr["p"])
+            oracle.dropout.attention_dropout_fwd(q, k, v, inp["scale"],
+                                                 inp["causal"], p8, dr["seed"],
+                                                 dr["offset"])
+            if w.backward:
+                oracle.dropout.attention_dropout_bwd(
+                    q, k, v, inp["do"][sl], inp["scale"], inp["causal"], p8,
+                    dr["seed"], dr["offset"])
+            return
         if w.linear:
             oracle.linear.linear_attention_fwd(q, k, v, inp["scale"])
             return
@@ -143,6 +155,9 @@ def cpu_baseline(w: S.Workload, inp: dict, target_s: float = 15.0) -> dict:
     elif inp.get("signs") is not None:
         what = ("fp64 numpy model of the FP8 path (rotation, block "
                 "quantisation, fp64 attention), forward")
+    elif dr is not None:
+        what = ("fp64 numpy oracle with dropout (Philox keep mask), "
+                + ("forward+backward" if w.backward else "forward"))
     else:
         what = ("fp64 numpy oracle, "
                 + ("forward+backward" if w.backward else "forward"))
@@ -151,7 +166,8 @@ def cpu_baseline(w: S.Workload, inp: dict, target_s: float = 15.0) -> dict:
             "sample": (what +
                        f" of batch 0, heads 0..{nh - 1} of {w.name} "
                        f"(N={w.N}, d={w.d}); {t1:.2f} s; {cores} threads "
-                       "(BLAS pool + one worker thread per head)")}
+                       + ("(BLAS pool; heads in sequence)" if dr is not None
+                          else "(BLAS pool + one worker thread per head)"))}
 
 
 # rocprofv3 kernel-name fragment -> bench step (all variants of a step)
@@ -521,6 +537,7 @@ def main(argv=None) -> int:
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     scale, causal = inp["scale"], inp["causal"]
     fp8 = inp.get("signs") is not None
+    dr = inp.get("dropout")
     if w.linear:
         nl = fa.fa_linear_workspace_size(w.B, w.H, w.N, w.d)
         wsl = torch.empty(nl, dtype=torch.uint8, device=dev) if nl else None
@@ -560,6 +577,9 @@ def main(argv=None) -> int:
             return
         if w.dtype == "f32":
             fa.fa_fwd_f32(q, k, v, o, lse, scale, causal)
+        elif dr is not None:
+            fa.fa_fwd_dropout(q, k, v, o, lse, scale, causal, dr["p"],
+                              dr["seed"], dr["offset"])
         elif bmask is not None:
             fa.fa_fwd_block_sparse(q, k, v, bmask, o, lse, scale, causal)
         else:
@@ -568,13 +588,19 @@ def main(argv=None) -> int:
         if w.backward:
             fa.fa_bwd_preprocess(o, do, ws)
             mark(2)
-            if bmask is not None:
+            if dr is not None:
+                fa.fa_bwd_dkdv_dropout(q, k, v, do, lse, dk, dv, ws, scale,
+                                       causal, dr["p"], dr["seed"], dr["offset"])
+            elif bmask is not None:
                 fa.fa_bwd_dkdv_block_sparse(q, k, v, do, lse, bmask, dk, dv,
                                             ws, scale, causal)
             else:
                 fa.fa_bwd_dkdv(q, k, v, do, lse, dk, dv, ws, scale, causal)
             mark(3)
-            if bmask is not None:
+            if dr is not None:
+                fa.fa_bwd_dq_dropout(q, k, v, do, lse, dq, ws, scale, causal,
+                                     dr["p"], dr["seed"], dr["offset"])
+            elif bmask is not None:
                 fa.fa_bwd_dq_block_sparse(q, k, v, do, lse, bmask, dq, ws,
                                           scale, causal)
             else:
@@ -697,6 +723,11 @@ def main(argv=None) -> int:
         "cpu_baseline": cpu,
         "sanity": check,
     }
+    if dr is not None:
+        out["dropout"] = {"p": dr["p"], "seed": dr["seed"],
+                          "offset": dr["offset"],
+                          "generator": "Philox4x32-10, one byte per pair",
+                          "flops": "algorithmic (generator work not counted)"}
     if fp8:
         qb = algorithmic_bytes(w, "fp8_quantize")
         out["fp8"] = {

@@ -64,7 +64,8 @@ enum fa_status {
   FA_ERR_HEADDIM = -3,   /* d is not 64 or 128 (backward: not 128)         */
   FA_ERR_ALIGN = -4,     /* a tensor pointer is not 16-byte aligned        */
   FA_ERR_WORKSPACE = -5, /* workspace NULL, too small or not 256-B aligned */
-  FA_ERR_HIP = -6        /* the HIP runtime reported a launch error        */
+  FA_ERR_HIP = -6,       /* the HIP runtime reported a launch error        */
+  FA_ERR_DROPOUT = -7    /* drop probability outside [0, 255.5/256)       */
 };
 
 /* Library version, as 10000*major + 100*minor + patch. */
@@ -315,6 +316,64 @@ int fa_bwd_dq_block_sparse(const uint16_t* q, const uint16_t* k,
                            uint16_t* dq, const void* workspace,
                            size_t workspace_bytes, int B, int H, int N, int d,
                            float scale, int causal, void* stream);
+
+/*
+ * Attention with dropout on the weights ([MM] "Integration": the framework
+ * call takes a dropout probability next to q, k, v and the causal flag; the
+ * pages give nothing more).  O = (P o Z / keep) V with P the softmax of
+ * fa_fwd, Z a 0/1 keep mask and keep the keep probability; lse is that of
+ * the undropped scores (as fa_fwd), which the backward needs.
+ *
+ * Random numbers: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
+ * random numbers: as easy as 1, 2, 3", SC 2011).  Element (b, h, i, j) reads
+ * byte j % 4 (least significant first) of word i % 4 of the generator
+ * output for counter (j / 4, i / 4, b*H + h, offset) and key
+ * (seed & 0xFFFFFFFF, seed >> 32); it is kept iff that byte is >= p8, where
+ * p8 = round(256 * p_drop) (the drop probability is applied in steps of
+ * 1/256), and kept weights are scaled by 256 / (256 - p8).  The mask is a
+ * pure function of (seed, offset, p_drop, b, h, i, j): the same arguments
+ * give the same mask in the forward and in the backward, on any launch
+ * configuration.
+ *
+ * Arguments as fa_fwd plus p_drop in [0, 255.5/256), seed and offset
+ * (callers advance offset, or the seed, between calls that need different
+ * masks).  Dense heads only (no key padding or block mask).  Errors as
+ * fa_fwd, plus FA_ERR_DROPOUT for p_drop outside that range (or NaN).
+ */
+int fa_fwd_dropout(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                   uint16_t* o, float* lse, int B, int H, int N, int d,
+                   float scale, int causal, float p_drop, uint64_t seed,
+                   uint32_t offset, void* stream);
+
+/*
+ * Gradients of fa_fwd_dropout for the same mask: dV = (P o Z / keep)^T dO,
+ * dP = (dO V^T) o Z / keep, D_i = dO_i . O_i, dS = P o (dP - D),
+ * dQ = scale dS K, dK = scale dS^T Q.  Arguments as fa_bwd plus p_drop,
+ * seed and offset, which must be those of the forward call that produced o
+ * and lse.  d = 128.  Errors as fa_bwd plus FA_ERR_DROPOUT.
+ */
+int fa_bwd_dropout(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                   const uint16_t* o, const uint16_t* dO, const float* lse,
+                   uint16_t* dq, uint16_t* dk, uint16_t* dv, void* workspace,
+                   size_t workspace_bytes, int B, int H, int N, int d,
+                   float scale, int causal, float p_drop, uint64_t seed,
+                   uint32_t offset, void* stream);
+
+/* Its stages 2 and 3 (after fa_bwd_preprocess), as fa_bwd_dkdv and
+ * fa_bwd_dq with dropout. */
+int fa_bwd_dkdv_dropout(const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, const uint16_t* dO,
+                        const float* lse, uint16_t* dk, uint16_t* dv,
+                        const void* workspace, size_t workspace_bytes, int B,
+                        int H, int N, int d, float scale, int causal,
+                        float p_drop, uint64_t seed, uint32_t offset,
+                        void* stream);
+int fa_bwd_dq_dropout(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const uint16_t* dO, const float* lse, uint16_t* dq,
+                      const void* workspace, size_t workspace_bytes, int B,
+                      int H, int N, int d, float scale, int causal,
+                      float p_drop, uint64_t seed, uint32_t offset,
+                      void* stream);
 
 #ifdef __cplusplus
 }

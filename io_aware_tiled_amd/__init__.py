@@ -31,7 +31,9 @@ __all__ = [
     "fa_bwd_dq_block_sparse", "fa_fp8_workspace_size",
     "fa_fp8_quantize",
     "fa_fwd_fp8_quantized", "fa_fwd_fp8", "fa_linear_fwd",
-    "fa_linear_workspace_size", "forward",
+    "fa_linear_workspace_size", "fa_fwd_dropout", "fa_bwd_dropout",
+    "fa_bwd_dkdv_dropout", "fa_bwd_dq_dropout", "dropout_threshold",
+    "forward",
     "forward_fp8", "linear_forward", "backward", "EXPORTED_SYMBOLS",
 ]
 
@@ -43,6 +45,8 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
 _S = ctypes.c_size_t
+_U64 = ctypes.c_uint64
+_U32 = ctypes.c_uint32
 
 # name -> (restype, argtypes); mirrors include/fa.h
 _SIGS = {
@@ -66,6 +70,13 @@ _SIGS = {
     "fa_bwd_block_sparse": (_I, [_P] * 11 + [_S, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_dkdv_block_sparse": (_I, [_P] * 9 + [_S, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_dq_block_sparse": (_I, [_P] * 8 + [_S, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_fwd_dropout": (_I, [_P] * 5 + [_I, _I, _I, _I, _F, _I, _F, _U64, _U32, _P]),
+    "fa_bwd_dropout": (_I, [_P] * 10 + [_S, _I, _I, _I, _I, _F, _I, _F, _U64,
+                                        _U32, _P]),
+    "fa_bwd_dkdv_dropout": (_I, [_P] * 8 + [_S, _I, _I, _I, _I, _F, _I, _F,
+                                            _U64, _U32, _P]),
+    "fa_bwd_dq_dropout": (_I, [_P] * 7 + [_S, _I, _I, _I, _I, _F, _I, _F, _U64,
+                                          _U32, _P]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -298,6 +309,82 @@ def fa_bwd_dq(q, k, v, dO, lse, dq, workspace, scale, causal, stream=None):
 
 
 FP8_V_ROW_BYTES = 80
+
+
+# ------------------------------------------------------------- dropout
+
+def dropout_threshold(p_drop: float) -> int:
+    """The byte threshold p8 = round(256 p) the library applies (keep
+    probability (256 - p8) / 256)."""
+    x = 256.0 * float(ctypes.c_float(p_drop).value)
+    p8 = int(math.floor(x))
+    frac = x - p8
+    if frac > 0.5 or (frac == 0.5 and p8 % 2 == 1):
+        p8 += 1
+    return p8
+
+
+def _seed(seed):
+    seed = int(seed)
+    if not 0 <= seed < 1 << 64:
+        raise ValueError("seed must fit in 64 unsigned bits")
+    return seed
+
+
+def fa_fwd_dropout(q, k, v, o, lse, scale, causal, p_drop, seed, offset=0,
+                   stream=None):
+    """C fa_fwd_dropout: attention with dropout on the weights (Philox
+    mask of (seed, offset), see include/fa.h)."""
+    import torch
+    B, H, N, d = _bhnd(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _expect(t, torch.bfloat16, (B, H, N, d), n)
+    _expect(lse, torch.float32, (B, H, N), "lse")
+    st = lib().fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                              B, H, N, d, float(scale), int(bool(causal)),
+                              float(p_drop), _seed(seed), int(offset),
+                              _stream(q, stream))
+    _check(st, "fa_fwd_dropout")
+
+
+def fa_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, workspace, scale, causal,
+                   p_drop, seed, offset=0, stream=None):
+    """C fa_bwd_dropout: gradients of fa_fwd_dropout for the same mask."""
+    import torch
+    B, H, N, d = _bhnd(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO"),
+                 (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _expect(t, torch.bfloat16, (B, H, N, d), n)
+    _expect(lse, torch.float32, (B, H, N), "lse")
+    wp, wn = _ws(workspace)
+    st = lib().fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO),
+                              _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), wp, wn,
+                              B, H, N, d, float(scale), int(bool(causal)),
+                              float(p_drop), _seed(seed), int(offset),
+                              _stream(q, stream))
+    _check(st, "fa_bwd_dropout")
+
+
+def fa_bwd_dkdv_dropout(q, k, v, dO, lse, dk, dv, workspace, scale, causal,
+                        p_drop, seed, offset=0, stream=None):
+    B, H, N, d = _bhnd(q)
+    wp, wn = _ws(workspace)
+    st = lib().fa_bwd_dkdv_dropout(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(dk), _ptr(dv),
+        wp, wn, B, H, N, d, float(scale), int(bool(causal)), float(p_drop),
+        _seed(seed), int(offset), _stream(q, stream))
+    _check(st, "fa_bwd_dkdv_dropout")
+
+
+def fa_bwd_dq_dropout(q, k, v, dO, lse, dq, workspace, scale, causal, p_drop,
+                      seed, offset=0, stream=None):
+    B, H, N, d = _bhnd(q)
+    wp, wn = _ws(workspace)
+    st = lib().fa_bwd_dq_dropout(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(dq), wp, wn, B,
+        H, N, d, float(scale), int(bool(causal)), float(p_drop), _seed(seed),
+        int(offset), _stream(q, stream))
+    _check(st, "fa_bwd_dq_dropout")
 
 
 def fp8_row_bytes(d: int) -> int:

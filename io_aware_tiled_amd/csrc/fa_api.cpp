@@ -48,6 +48,22 @@ size_t fp8_ws_bytes(int B, int H, int N, int d) {
   return 2 * bh * np * FA_FP8_ROW_BYTES(d) + bh * (np / 64) * d * FA_FP8_V_ROW_BYTES;
 }
 
+// Dropout parameters: p8 = round(256 p) must lie in 0..255.
+int make_dropout(float p_drop, uint64_t seed, uint32_t offset,
+                 fa::Dropout* out) {
+  if (!(p_drop >= 0.f && p_drop < 255.5f / 256.f)) return FA_ERR_DROPOUT;
+  const float x = 256.f * p_drop;
+  int p8 = (int)x;
+  const float frac = x - (float)p8;
+  if (frac > 0.5f || (frac == 0.5f && (p8 & 1))) ++p8;   // ties to even
+  if (p8 > 255) return FA_ERR_DROPOUT;
+  out->k0 = (uint32_t)(seed & 0xFFFFFFFFu);
+  out->k1 = (uint32_t)(seed >> 32);
+  out->offset = offset;
+  out->p8 = p8;
+  return FA_OK;
+}
+
 int check_workspace(const void* ws, size_t bytes, int B, int H, int N) {
   if (ws == nullptr) return FA_ERR_WORKSPACE;
   if (((uintptr_t)ws & 255u) != 0) return FA_ERR_WORKSPACE;
@@ -72,6 +88,8 @@ const char* fa_status_string(int status) {
     case FA_ERR_WORKSPACE:
       return "FA_ERR_WORKSPACE: workspace is NULL, not 256-byte aligned or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported a launch error";
+    case FA_ERR_DROPOUT:
+      return "FA_ERR_DROPOUT: drop probability must lie in [0, 255.5/256)";
     default: return "unknown fa status code";
   }
 }
@@ -86,7 +104,7 @@ int fa_fwd_kvlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
       !aligned16(lse) || ((uintptr_t)kv_len & 3u) != 0)
     return FA_ERR_ALIGN;
   return fa::launch_fwd_bf16(q, k, v, kv_len, nullptr, o, lse, B, H, N, d,
-                             scale, causal != 0, (hipStream_t)stream);
+                             scale, causal != 0, nullptr, (hipStream_t)stream);
 }
 
 int fa_fwd_block_sparse(const uint16_t* q, const uint16_t* k,
@@ -102,7 +120,7 @@ int fa_fwd_block_sparse(const uint16_t* q, const uint16_t* k,
       !aligned16(lse))
     return FA_ERR_ALIGN;
   return fa::launch_fwd_bf16(q, k, v, nullptr, block_mask, o, lse, B, H, N,
-                             d, scale, causal != 0, (hipStream_t)stream);
+                             d, scale, causal != 0, nullptr, (hipStream_t)stream);
 }
 
 int fa_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -231,7 +249,7 @@ int fa_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   if (st != FA_OK) return st;
   return fa::launch_bwd_dkdv(q, k, v, dO, lse, (const float*)workspace,
                              nullptr, dk, dv, B, H, N, d, scale, causal != 0,
-                             (hipStream_t)stream);
+                             nullptr, (hipStream_t)stream);
 }
 
 int fa_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -247,7 +265,7 @@ int fa_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   st = check_workspace(workspace, workspace_bytes, B, H, N);
   if (st != FA_OK) return st;
   return fa::launch_bwd_dq(q, k, v, dO, lse, (const float*)workspace, nullptr,
-                           dq, B, H, N, d, scale, causal != 0,
+                           dq, B, H, N, d, scale, causal != 0, nullptr,
                            (hipStream_t)stream);
 }
 
@@ -294,7 +312,7 @@ int fa_bwd_dkdv_block_sparse(const uint16_t* q, const uint16_t* k,
   if (st != FA_OK) return st;
   return fa::launch_bwd_dkdv(q, k, v, dO, lse, (const float*)workspace,
                              block_mask, dk, dv, B, H, N, d, scale,
-                             causal != 0, (hipStream_t)stream);
+                             causal != 0, nullptr, (hipStream_t)stream);
 }
 
 int fa_bwd_dq_block_sparse(const uint16_t* q, const uint16_t* k,
@@ -315,7 +333,7 @@ int fa_bwd_dq_block_sparse(const uint16_t* q, const uint16_t* k,
   if (st != FA_OK) return st;
   return fa::launch_bwd_dq(q, k, v, dO, lse, (const float*)workspace,
                            block_mask, dq, B, H, N, d, scale, causal != 0,
-                           (hipStream_t)stream);
+                           nullptr, (hipStream_t)stream);
 }
 
 int fa_bwd_block_sparse(const uint16_t* q, const uint16_t* k,
@@ -346,6 +364,98 @@ int fa_bwd_block_sparse(const uint16_t* q, const uint16_t* k,
   return fa_bwd_dq_block_sparse(q, k, v, dO, lse, block_mask, dq, workspace,
                                 workspace_bytes, B, H, N, d, scale, causal,
                                 stream);
+}
+
+int fa_fwd_dropout(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                   uint16_t* o, float* lse, int B, int H, int N, int d,
+                   float scale, int causal, float p_drop, uint64_t seed,
+                   uint32_t offset, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  fa::Dropout drop;
+  st = make_dropout(p_drop, seed, offset, &drop);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(lse))
+    return FA_ERR_ALIGN;
+  return fa::launch_fwd_bf16(q, k, v, nullptr, nullptr, o, lse, B, H, N, d,
+                             scale, causal != 0, &drop, (hipStream_t)stream);
+}
+
+int fa_bwd_dkdv_dropout(const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, const uint16_t* dO,
+                        const float* lse, uint16_t* dk, uint16_t* dv,
+                        const void* workspace, size_t workspace_bytes, int B,
+                        int H, int N, int d, float scale, int causal,
+                        float p_drop, uint64_t seed, uint32_t offset,
+                        void* stream) {
+  if (!q || !k || !v || !dO || !lse || !dk || !dv) return FA_ERR_NULL;
+  int st = check_shape_bwd(B, H, N, d);
+  if (st != FA_OK) return st;
+  fa::Dropout drop;
+  st = make_dropout(p_drop, seed, offset, &drop);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) ||
+      !aligned16(lse) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_ALIGN;
+  st = check_workspace(workspace, workspace_bytes, B, H, N);
+  if (st != FA_OK) return st;
+  return fa::launch_bwd_dkdv(q, k, v, dO, lse, (const float*)workspace,
+                             nullptr, dk, dv, B, H, N, d, scale, causal != 0,
+                             &drop, (hipStream_t)stream);
+}
+
+int fa_bwd_dq_dropout(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const uint16_t* dO, const float* lse, uint16_t* dq,
+                      const void* workspace, size_t workspace_bytes, int B,
+                      int H, int N, int d, float scale, int causal,
+                      float p_drop, uint64_t seed, uint32_t offset,
+                      void* stream) {
+  if (!q || !k || !v || !dO || !lse || !dq) return FA_ERR_NULL;
+  int st = check_shape_bwd(B, H, N, d);
+  if (st != FA_OK) return st;
+  fa::Dropout drop;
+  st = make_dropout(p_drop, seed, offset, &drop);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) ||
+      !aligned16(lse) || !aligned16(dq))
+    return FA_ERR_ALIGN;
+  st = check_workspace(workspace, workspace_bytes, B, H, N);
+  if (st != FA_OK) return st;
+  return fa::launch_bwd_dq(q, k, v, dO, lse, (const float*)workspace, nullptr,
+                           dq, B, H, N, d, scale, causal != 0, &drop,
+                           (hipStream_t)stream);
+}
+
+int fa_bwd_dropout(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                   const uint16_t* o, const uint16_t* dO, const float* lse,
+                   uint16_t* dq, uint16_t* dk, uint16_t* dv, void* workspace,
+                   size_t workspace_bytes, int B, int H, int N, int d,
+                   float scale, int causal, float p_drop, uint64_t seed,
+                   uint32_t offset, void* stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv)
+    return FA_ERR_NULL;
+  int st = check_shape_bwd(B, H, N, d);
+  if (st != FA_OK) return st;
+  fa::Dropout drop;
+  st = make_dropout(p_drop, seed, offset, &drop);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(dO) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv))
+    return FA_ERR_ALIGN;
+  st = check_workspace(workspace, workspace_bytes, B, H, N);
+  if (st != FA_OK) return st;
+  st = fa_bwd_preprocess(o, dO, workspace, workspace_bytes, B, H, N, d, stream);
+  if (st != FA_OK) return st;
+  st = fa_bwd_dkdv_dropout(q, k, v, dO, lse, dk, dv, workspace,
+                           workspace_bytes, B, H, N, d, scale, causal, p_drop,
+                           seed, offset, stream);
+  if (st != FA_OK) return st;
+  return fa_bwd_dq_dropout(q, k, v, dO, lse, dq, workspace, workspace_bytes,
+                           B, H, N, d, scale, causal, p_drop, seed, offset,
+                           stream);
 }
 
 }  // extern "C"

@@ -571,14 +571,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t bwd_rsrc(const uint16_t* p,
 // each, transformed on the way) pass through wavefront 0's registers.
 constexpr int kKvPBK = 128;
 
-template <bool CAUSAL, bool SPARSE>
+template <bool CAUSAL, bool SPARSE, bool DROP = false>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dv,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
     const uint8_t* __restrict__ bmask, int H, int N, int n_kblk,
-    float c_log2, float scale) {
+    float c_log2, float scale, Dropout drop) {
   constexpr int D = kD;
   constexpr int QE = kBQ2 * kRS;                 // elements per tile stage
   constexpr int THREADS = 256;
@@ -710,6 +710,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
       d_r = Dh[q];
     }
   };
+  // With dropout the dP accumulators start at -D times the keep
+  // probability (see the phase).
+  const float kp = DROP ? (float)(256 - drop.p8) * (1.f / 256.f) : 1.f;
   auto store_stats = [&](int st) {
     if (w == 0) {
       // Rows past N (and rows without any visible key) get +inf, so that
@@ -717,7 +720,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
       const bool in = stats_q < N;
       const float l = in ? lse_r : INFINITY;
       lds_lse[st][lane] = (l == -INFINITY) ? INFINITY : l * kLog2e;
-      lds_d[st][lane] = in ? -d_r : 0.f;   // -D: the dP accumulators start there
+      lds_d[st][lane] = in ? -d_r * kp : 0.f;   // -D: the dP accumulators start there
     }
   };
 
@@ -730,11 +733,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
   f32x16 s[2], dp[2];          // S, dP of each block (lane = key)
   bf16x8 pb[2][2], dsb[2][2];  // P, dS of each block in bf16, 16-row halves
 
+  // ---- dropout bytes.  kz[m]: keep bytes of the VALU block's rows
+  // 8m + 4hh + a (byte a) for this lane's key, i.e. register 4m + a.  Quad
+  // lane w (keys 4kb .. 4kb+3) makes the generator call of row group w,
+  // transposes its bytes so that word b holds key 4kb + b, and the quad
+  // exchange hands each lane its key's word of every call.  A phase
+  // computes the bytes of the next phase's VALU block (kzn) in the MFMA
+  // slots after its own VALU work, and takes them over at its start.
+  uint32_t kz[4], kzn[4];
+  auto gen_begin = [&](int qt, int c) __attribute__((always_inline)) {
+    kzn[0] = (uint32_t)(mykey >> 2);
+    kzn[1] = (uint32_t)(qt * (kBQ2 / 4) + 8 * c + 2 * (l32 & 3) + hh);
+    kzn[2] = (uint32_t)bh;
+    kzn[3] = drop.offset;
+  };
+  auto gen_end = [&]() __attribute__((always_inline)) {
+    byte_transpose(kzn);
+    quad_gather(kzn);
+  };
+
   // ---- one phase.  A: S, dP of block ca from stage sta.  B: dV, dK of
   // block cb from stage stb.  VALU: P, dS of block cv with LSE / D from
   // stage stv.  B_FIRST orders the B products before the A ones.
   auto phase = [&](auto b_first, int sta, int ca, int stb, int cb,
-                   int stv, int cv) {
+                   int stv, int cv, int qtn, int cvn) {
     constexpr bool BF = decltype(b_first)::value;
     constexpr int kA = 2 * (D / 16);       // S and dP MFMAs
     constexpr int kB = 4 * (D / 32);       // dV and dK MFMAs
@@ -764,13 +786,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
     // register r <-> row 32 c + 8 (r / 4) + 4 hh + r % 4.  dP accumulates
     // onto -D, so the VALU forms dS = P (dP - D) with one product.
     f32x4 l4[4];
-    f32x16 negd;
+    f32x16 negd, negd_v;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       l4[g] = *(const f32x4*)(&lds_lse[stv][32 * cv + 8 * g + 4 * hh]);
       const f32x4 nd = *(const f32x4*)(&lds_d[sta][32 * ca + 8 * g + 4 * hh]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) negd[4 * g + e] = nd[e];
+      if constexpr (DROP) {
+        const f32x4 nv = *(const f32x4*)(&lds_d[stv][32 * cv + 8 * g + 4 * hh]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) negd_v[4 * g + e] = nv[e];
+      }
+    }
+    // Dropout: with Z the keep mask and k the keep probability,
+    // dS = P (Z dP'/k - D) = (P/k) (Z ? dP' - k D : -k D), where dP' =
+    // dO V^T and the accumulator holds dP' - k D; dV takes P Z.  The 1/k
+    // of both is applied at the end.
+    if constexpr (DROP) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) kz[m] = kzn[m];
+      gen_begin(qtn, cvn);
     }
     // VALU: 16 elements as a three-stage pipeline over the MFMA slots
     // (FMA, then exp2, then dS and, per 8 elements, the bf16 conversions).
@@ -800,7 +836,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
       if (m >= 1 && m - 1 < 16) pe[m - 1] = __builtin_amdgcn_exp2f(x[m - 1]);
       if (m >= 2 && m - 2 < 16) {
         const int el = m - 2;
-        dsv[el] = pe[el] * dp[cv][el];
+        if constexpr (DROP) {
+          const bool kept = drop_keep(kz[el / 4], el % 4, drop.p8);
+          dsv[el] = pe[el] * (kept ? dp[cv][el] : negd_v[el]);
+          if (!kept) pe[el] = 0.f;
+        } else {
+          dsv[el] = pe[el] * dp[cv][el];
+        }
         if (el % 8 == 7) {
           f32x8 vp, vd;
 #pragma unroll
@@ -811,6 +853,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
           pb[cv][el / 8] = to_bf16x8(vp);
           dsb[cv][el / 8] = to_bf16x8(vd);
         }
+      }
+      if constexpr (DROP) {
+        static_assert(kN >= 29, "generator rounds fit after the VALU work");
+        if (m >= 18 && m < 28) philox_round(kzn, drop.k0, drop.k1, m - 18);
+        if (m == 28) gen_end();
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -890,6 +937,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
       dp[0] = mfma32x16(*(const bf16x8*)(&lds_g[0][o]), vf[kk], kk == 0 ? negd0 : dp[0]);
     }
     mask_block(0, e0);
+    if constexpr (DROP) {
+      gen_begin(e0, 0);
+#pragma unroll
+      for (int r = 0; r < 10; ++r) philox_round(kzn, drop.k0, drop.k1, r);
+      gen_end();
+    }
     agpr_hazard_pad();   // zero-filled accumulators -> first MFMA
 
     // Visited tile i (list position) in stage i % 4.  Iteration i publishes
@@ -904,10 +957,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
       if (i + 2 <= last) dma_tile(ei2, (s1 + 1) & 3);
       load_stats(ei2);
       // phase 1: A_1(i), B_1(i-1) || V_0(i)
-      phase(std::false_type{}, s0, 1, sp, 1, s0, 0);
+      phase(std::false_type{}, s0, 1, sp, 1, s0, 0, ei, 1);
       mask_block(1, ei);
       // phase 2: B_0(i), A_0(i+1) || V_1(i)
-      phase(std::true_type{}, s1, 0, s0, 0, s0, 1);
+      phase(std::true_type{}, s1, 0, s0, 0, s0, 1, ei1, 0);
       if (i + 1 < n_vis) mask_block(0, ei1);
       sp = s0;
       s0 = s1;
@@ -917,7 +970,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
     agpr_hazard_pad();   // last MFMA -> epilogue reads
   }
 
-  // ---- epilogue: dK = scale * dK^T, dV = dV^T (lane = key, regs = d).
+  // ---- epilogue: dK = scale * dK^T, dV = dV^T (lane = key, regs = d);
+  // with dropout both are divided by the keep probability.
+  const float sk = DROP ? scale / kp : scale, sv = DROP ? 1.f / kp : 1.f;
   if (mykey < N) {
     uint16_t* dkr = dK + head + (size_t)mykey * D;
     uint16_t* dvr = dV + head + (size_t)mykey * D;
@@ -928,8 +983,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
         f32x4 a, b;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          a[e] = dk_acc[db][4 * g + e] * scale;
-          b[e] = dv_acc[db][4 * g + e];
+          a[e] = dk_acc[db][4 * g + e] * sk;
+          b[e] = dv_acc[db][4 * g + e] * sv;
         }
         *(bf16x4*)(dkr + 32 * db + 8 * g + 4 * hh) = to_bf16x4(a);
         *(bf16x4*)(dvr + 32 * db + 8 * g + 4 * hh) = to_bf16x4(b);
@@ -951,13 +1006,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
 // The DMA descriptor ends at the head's last key: keys past N read as zero.
 constexpr int kDqPBR = 256;
 
-template <bool CAUSAL, bool SPARSE>
+template <bool CAUSAL, bool SPARSE, bool DROP = false>
 __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dv,
     uint16_t* __restrict__ dQ, const uint8_t* __restrict__ bmask, int H,
-    int N, int n_qblk, float c_log2, float scale) {
+    int N, int n_qblk, float c_log2, float scale, Dropout drop) {
   static_assert(!SPARSE || kDqPBR == FA_SPARSE_BQ, "a workgroup is a mask row");
   constexpr int D = kD;
   constexpr int TE = kDqBC * kRS;                 // elements per tile stage
@@ -1065,10 +1120,14 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
     dd = Dv[(size_t)bh * N + qrow];
   }
   // dP^T accumulates onto -D (one query per lane), so the VALU forms
-  // dS = P (dP - D) with one product.
+  // dS = P (dP - D) with one product.  Dropout (Z the keep mask, k the
+  // keep probability): dS = P (Z dP'/k - D) = (P/k) (Z ? dP' - k D : -k D)
+  // with dP' = dO V^T; the accumulator starts at -k D and the 1/k is
+  // applied at the end.
+  const float kp = DROP ? (float)(256 - drop.p8) * (1.f / 256.f) : 1.f;
   f32x16 negd;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) negd[r] = -dd;
+  for (int r = 0; r < 16; ++r) negd[r] = -dd * kp;
 
   // Every register operand has arrived before any DMA is issued (a wait
   // the compiler can see, so that it places none of its own inside the
@@ -1111,10 +1170,24 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
   f32x16 s[2], dp[2];        // S^T, dP^T of a half-tile, by parity
   bf16x8 dsb[2];             // dS^T in bf16, 16-key halves
 
+  // ---- dropout bytes.  kz[m]: keep bytes of the VALU half-tile, key group
+  // m (keys k0 + 8m + 4hh + b, byte b) for this lane's query, i.e.
+  // register 4m + b.  Quad lane w makes the generator call of key group w
+  // for the quad's four queries; a step computes the bytes of the next
+  // step's half-tile in its last MFMA slots, after its own VALU work (one
+  // set of registers: the kernel has none to spare).
+  uint32_t kz[4];
+  auto gen_begin = [&](int k0) __attribute__((always_inline)) {
+    kz[0] = (uint32_t)(k0 / 4 + 2 * (lq & 3) + hh);
+    kz[1] = (uint32_t)(qrow >> 2);
+    kz[2] = (uint32_t)bh;
+    kz[3] = drop.offset;
+  };
+
   // ---- one step.  XS: parity receiving S^T, dP^T of the next half-tile
   // (stage stn, 32-key half kbn); the VALU and dQ take the current one
   // (parity 1 - XS, K stage stc, half kbc).
-  auto step = [&](auto xs_tag, int stn, int kbn, int stc, int kbc) {
+  auto step = [&](auto xs_tag, int stn, int kbn, int stc, int kbc, int k0n) {
     constexpr int XS = decltype(xs_tag)::value;
     constexpr int XE = 1 - XS;
     constexpr int kS = D / 16;           // MFMAs for S^T (and for dP^T)
@@ -1160,13 +1233,27 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
       if (m >= 1 && m - 1 < 16) pe[m - 1] = __builtin_amdgcn_exp2f(x[m - 1]);
       if (m >= 2 && m - 2 < 16) {
         const int el = m - 2;
-        dsv[el] = pe[el] * dp[XE][el];
+        if constexpr (DROP)
+          dsv[el] = pe[el] * (drop_keep(kz[el / 4], el % 4, drop.p8) ? dp[XE][el]
+                                                                    : negd[el]);
+        else
+          dsv[el] = pe[el] * dp[XE][el];
         if (el % 8 == 7) {
           f32x8 v;
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = dsv[el - 7 + e];
           dsb[el / 8] = to_bf16x8(v);
         }
+      }
+      if constexpr (DROP) {
+        // Slots 18 .. 22: two generator rounds each; slot 23: exchange.
+        static_assert(kN == 24, "generator slots");
+        if (m == 18) gen_begin(k0n);
+        if (m >= 18 && m < 23) {
+          philox_round(kz, drop.k0, drop.k1, 2 * (m - 18));
+          philox_round(kz, drop.k0, drop.k1, 2 * (m - 18) + 1);
+        }
+        if (m == 23) quad_gather(kz);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1205,6 +1292,12 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
       }
       mask_half(0, ktile(0), 0);
     }
+    if constexpr (DROP) {
+      gen_begin(ktile(0) * kDqBC);
+#pragma unroll
+      for (int r = 0; r < 10; ++r) philox_round(kz, drop.k0, drop.k1, r);
+      quad_gather(kz);
+    }
     // K_j, V_j in stage j % 4.  Tile j waits for K_{j+1}, V_{j+1} (issued
     // two tiles earlier), then issues K_{j+3}, V_{j+3} into the stage of
     // tile j-1.  No fence at the barrier: LDS is only read in the loop, and
@@ -1222,16 +1315,18 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
       const int st0 = j & 3, st1 = (j + 1) & 3;
       if (j < nt_w) {
         // step 2j: S^T, dP^T of (j, 1) || dS of (j, 0), dQ += (j, 0)
-        step(std::integral_constant<int, 1>{}, st0, 1, st0, 0);
+        step(std::integral_constant<int, 1>{}, st0, 1, st0, 0, kj * kDqBC + 32);
         mask_half(1, kj, 1);
         // step 2j+1: S^T, dP^T of (j+1, 0) || dS of (j, 1), dQ += (j, 1)
-        step(std::integral_constant<int, 0>{}, st1, 0, st0, 1);
+        step(std::integral_constant<int, 0>{}, st1, 0, st0, 1, kj1 * kDqBC);
         if (j + 1 < nt_w) mask_half(0, kj1, 0);
       }
     }
   }
 
-  // ---- epilogue: dQ = scale * dQ^T (lane = query, regs = d).
+  // ---- epilogue: dQ = scale * dQ^T (lane = query, regs = d); with
+  // dropout divided by the keep probability.
+  const float sq = DROP ? scale / kp : scale;
   if (qrow < N) {
     uint16_t* out = dQ + head + (size_t)qrow * D;
 #pragma unroll
@@ -1240,7 +1335,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
       for (int g = 0; g < 4; ++g) {
         f32x4 xo;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) xo[e] = dq_acc[db][4 * g + e] * scale;
+        for (int e = 0; e < 4; ++e) xo[e] = dq_acc[db][4 * g + e] * sq;
         *(bf16x4*)(out + 32 * db + 8 * g + 4 * hh) = to_bf16x4(xo);
       }
     }
@@ -1270,25 +1365,32 @@ int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const uint16_t* dO, const float* lse, const float* D,
                     const uint8_t* block_mask, uint16_t* dk, uint16_t* dv,
                     int B, int H, int N, int d, float scale, int causal,
-                    hipStream_t stream) {
+                    const Dropout* drop, hipStream_t stream) {
   if (d != kD) return -3;
   const int n_kblk = (N + kBK - 1) / kBK;
   const float c = (float)((double)scale * 1.4426950408889634);
   // Grids with at least one 128-key workgroup per CU, and every
-  // block-sparse call: the pipelined kernel (4 wavefronts, K/V in
-  // registers); smaller dense ones: 8 wavefronts.
-  if ((long long)B * H * n_kblk >= 256 || block_mask != nullptr) {
+  // block-sparse or dropout call: the pipelined kernel (4 wavefronts, K/V
+  // in registers); smaller dense ones: 8 wavefronts.
+  if ((long long)B * H * n_kblk >= 256 || block_mask != nullptr || drop != nullptr) {
     const dim3 grid((unsigned)(B * H * n_kblk)), block(256);
 #define FA_DKDV_LAUNCH(CC, SS)                                                  \
   hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<CC, SS>), grid, block, 0, stream, q, \
                      k, v, dO, lse, D, dk, dv, block_mask, H, N, n_kblk, c,     \
-                     scale)
-    if (block_mask) {
+                     scale, Dropout{})
+#define FA_DKDV_DROP(CC)                                                       \
+  hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<CC, false, true>), grid, block, 0,  \
+                     stream, q, k, v, dO, lse, D, dk, dv, nullptr, H, N,       \
+                     n_kblk, c, scale, *drop)
+    if (drop) {
+      if (causal) FA_DKDV_DROP(true); else FA_DKDV_DROP(false);
+    } else if (block_mask) {
       if (causal) FA_DKDV_LAUNCH(true, true); else FA_DKDV_LAUNCH(false, true);
     } else {
       if (causal) FA_DKDV_LAUNCH(true, false); else FA_DKDV_LAUNCH(false, false);
     }
 #undef FA_DKDV_LAUNCH
+#undef FA_DKDV_DROP
     return hipGetLastError() == hipSuccess ? 0 : -6;
   }
   const dim3 grid((unsigned)(B * H * n_kblk)), block(kBwdThreads);
@@ -1305,25 +1407,34 @@ int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 int launch_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   const uint16_t* dO, const float* lse, const float* D,
                   const uint8_t* block_mask, uint16_t* dq, int B, int H, int N,
-                  int d, float scale, int causal, hipStream_t stream) {
+                  int d, float scale, int causal, const Dropout* drop,
+                  hipStream_t stream) {
   if (d != kD) return -3;
   const float c = (float)((double)scale * 1.4426950408889634);
   // Grids with at least one 256-row workgroup per CU, and every
-  // block-sparse call (a workgroup is one block-mask row): the pipelined
-  // kernel; smaller dense ones: 128-row workgroups, two per CU.
+  // block-sparse call (a workgroup is one block-mask row) or dropout call:
+  // the pipelined kernel; smaller dense ones: 128-row workgroups, two per CU.
   const long long grid256 = (long long)B * H * ((N + kDqPBR - 1) / kDqPBR);
-  if (grid256 >= 256 || block_mask != nullptr) {
+  if (grid256 >= 256 || block_mask != nullptr || drop != nullptr) {
     const int n_qblk = (N + kDqPBR - 1) / kDqPBR;
     const dim3 grid((unsigned)(B * H * n_qblk)), block(512);
 #define FA_DQ_LAUNCH(CC, SS)                                                  \
   hipLaunchKernelGGL((bwd_dq_pipe_kernel<CC, SS>), grid, block, 0, stream, q, \
-                     k, v, dO, lse, D, dq, block_mask, H, N, n_qblk, c, scale)
-    if (block_mask) {
+                     k, v, dO, lse, D, dq, block_mask, H, N, n_qblk, c, scale, \
+                     Dropout{})
+#define FA_DQ_DROP(CC)                                                        \
+  hipLaunchKernelGGL((bwd_dq_pipe_kernel<CC, false, true>), grid, block, 0,   \
+                     stream, q, k, v, dO, lse, D, dq, nullptr, H, N, n_qblk,  \
+                     c, scale, *drop)
+    if (drop) {
+      if (causal) FA_DQ_DROP(true); else FA_DQ_DROP(false);
+    } else if (block_mask) {
       if (causal) FA_DQ_LAUNCH(true, true); else FA_DQ_LAUNCH(false, true);
     } else {
       if (causal) FA_DQ_LAUNCH(true, false); else FA_DQ_LAUNCH(false, false);
     }
 #undef FA_DQ_LAUNCH
+#undef FA_DQ_DROP
     return hipGetLastError() == hipSuccess ? 0 : -6;
   }
   const int n_qblk = (N + kDqBR - 1) / kDqBR;

@@ -157,4 +157,72 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs,
       : "memory");
 }
 
+// ---------------------------------------------------------------------------
+// Attention dropout.  Random bytes come from Philox4x32-10, the counter-based
+// generator of Salmon, Moraes, Dror and Shaw ("Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): ten rounds map a 128-bit counter and a 64-bit
+// key to four 32-bit words.  Element (b, h, i, j) uses the call with counter
+// (j / 4, i / 4, b H + h, offset) and key (seed low, seed high) and reads
+// byte j % 4 (least significant first) of word i % 4; it is kept iff that
+// byte is >= p8 (= round(256 p)), and kept weights are scaled by
+// 256 / (256 - p8).  One call thus serves a 4 x 4 block of (query, key)
+// pairs.  The parameters travel as struct Dropout (fa_launch.h).
+
+// Round r of Philox4x32 on counter x with the round key (k0, k1) advanced r
+// times by the Weyl increments.
+__device__ __forceinline__ void philox_round(uint32_t (&x)[4], uint32_t k0,
+                                             uint32_t k1, int r) {
+  const uint32_t r0 = k0 + 0x9E3779B9u * (uint32_t)r;
+  const uint32_t r1 = k1 + 0xBB67AE85u * (uint32_t)r;
+  const uint64_t p0 = (uint64_t)0xD2511F53u * x[0];
+  const uint64_t p1 = (uint64_t)0xCD9E8D57u * x[2];
+  const uint32_t n0 = (uint32_t)(p1 >> 32) ^ x[1] ^ r0;
+  const uint32_t n2 = (uint32_t)(p0 >> 32) ^ x[3] ^ r1;
+  x[0] = n0;
+  x[1] = (uint32_t)p1;
+  x[2] = n2;
+  x[3] = (uint32_t)p0;
+}
+
+// Quad exchange.  Each lane of a group of four lanes (lane & 3 = w) holds
+// the four words x of "its" generator call; on return x[m] holds word w of
+// the call of quad lane m.  The lane first rotates its words so that the
+// word lane w ^ r needs sits in slot r, the quad-permute moves bring slot r
+// from lane w ^ r, and a second rotation puts them in call order.
+template <int CTRL>
+__device__ __forceinline__ uint32_t quad_perm(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ void quad_gather(uint32_t (&x)[4]) {
+  const bool b0 = threadIdx.x & 1, b1 = threadIdx.x & 2;
+  uint32_t t[4], a[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) t[r] = b0 ? x[r ^ 1] : x[r];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) a[r] = b1 ? t[r ^ 2] : t[r];
+  a[1] = quad_perm<0xB1>(a[1]);   // lanes (1, 0, 3, 2)
+  a[2] = quad_perm<0x4E>(a[2]);   // lanes (2, 3, 0, 1)
+  a[3] = quad_perm<0x1B>(a[3]);   // lanes (3, 2, 1, 0)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) t[r] = b0 ? a[r ^ 1] : a[r];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) x[r] = b1 ? t[r ^ 2] : t[r];
+}
+
+// 4 x 4 byte transpose: byte a of y[b] = byte b of x[a].
+__device__ __forceinline__ void byte_transpose(uint32_t (&x)[4]) {
+  uint32_t y[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    y[b] = ((x[0] >> (8 * b)) & 0xFFu) | (((x[1] >> (8 * b)) & 0xFFu) << 8) |
+           (((x[2] >> (8 * b)) & 0xFFu) << 16) | (((x[3] >> (8 * b)) & 0xFFu) << 24);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) x[b] = y[b];
+}
+
+// Keep decision of byte b of word z.
+__device__ __forceinline__ bool drop_keep(uint32_t z, int b, int p8) {
+  return (int)((z >> (8 * b)) & 0xFFu) >= p8;
+}
+
 }  // namespace fa

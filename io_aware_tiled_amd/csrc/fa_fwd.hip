@@ -366,13 +366,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* p,
                                            0x00020000);
 }
 
-template <int D, int NW, int NB, bool CAUSAL, bool KVLEN, bool SPARSE>
+template <int D, int NW, int NB, bool CAUSAL, bool KVLEN, bool SPARSE,
+          bool DROP = false>
 __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf16_pipe_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
     float* __restrict__ LSE, const int32_t* __restrict__ kv_len,
     const uint8_t* __restrict__ bmask, int H, int N, int n_qblk,
-    float c_log2) {
+    float c_log2, Dropout drop) {
   using T = PipeTile<D, NW, NB>;
   static_assert(!SPARSE || T::BR == kSparseBQ,
                 "a workgroup is one block-mask row");
@@ -596,8 +597,38 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
   constexpr bool XP = NB == 1;
   constexpr int kPf = XP ? 4 : 3;
   bf16x8 opr[kPf];
+
+  // ---- dropout bytes.  kz[c][m]: for block c, the keep bytes of the
+  // exponentials' half-tile, key group m (keys k0 + 8m + 4hh + b, byte b),
+  // i.e. register 4m + b of the score accumulator.  Quad lane w makes the
+  // generator call of key group w for the quad's four queries; a step
+  // computes the bytes of the next step's half-tile (kzn) in its MFMA
+  // slots, and takes them over at its start.
+  constexpr int kDB = DROP ? NB : 1;
+  uint32_t kz[kDB][4], kzn[kDB][4];
+  auto gen_begin = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < kDB; ++c) {
+      kzn[c][0] = (uint32_t)(k0 / 4 + 2 * (lq & 3) + hh);
+      kzn[c][1] = (uint32_t)(qrow[c] >> 2);
+      kzn[c][2] = (uint32_t)bh;
+      kzn[c][3] = drop.offset;
+    }
+  };
+  auto gen_round = [&](int r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < kDB; ++c) philox_round(kzn[c], drop.k0, drop.k1, r);
+  };
+  auto gen_end = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < kDB; ++c) quad_gather(kzn[c]);
+  };
+  auto keep = [&](int c, int r) __attribute__((always_inline)) -> bool {
+    return drop_keep(kz[c][r / 4], r % 4, drop.p8);
+  };
+
   auto step = [&](auto xs_tag, int stk, int kbs, int stv, int kbv, int nstk,
-                  int nkbs) {
+                  int nkbs, int k0n) {
     constexpr int XS = decltype(xs_tag)::value;
     constexpr int XE = 1 - XS;
     constexpr int kS = D / 16;             // S MFMAs per block
@@ -655,11 +686,23 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
         if (el % 8 == 7) {
           f32x8 v;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = pe[el - 7 + e];
+          for (int e = 0; e < 8; ++e) {
+            v[e] = pe[el - 7 + e];
+            if constexpr (DROP) {
+              if (!keep(ce, (el - 7 + e) % 16)) v[e] = 0.f;
+            }
+          }
           pb[XE][ce][(el / 8) % 2] = to_bf16x8(v);
         }
       }
     };
+    if constexpr (DROP) {
+#pragma unroll
+      for (int c = 0; c < kDB; ++c)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) kz[c][m] = kzn[c][m];
+      gen_begin(k0n);
+    }
 #pragma unroll
     for (int m = 0; m < kM + 2; ++m) {
       if (m < kM) {
@@ -683,6 +726,14 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
       if (m < kSlots) el_fma(m);
       if (m >= 1 && m - 1 < kSlots) el_exp(m - 1);
       if (m >= 2 && m - 2 < kSlots) el_sum(m - 2);
+      if constexpr (DROP) {
+        // The ten generator rounds spread over the slots, the exchange last.
+        constexpr int kIt = kM + 2;
+#pragma unroll
+        for (int r = 0; r < 10; ++r)
+          if (m == r * (kIt - 1) / 10) gen_round(r);
+        if (m == kIt - 1) gen_end();
+      }
       // Without a use here the compiler moves the adds to the step's end.
 #pragma unroll
       for (int c = 0; c < NB; ++c) asm volatile("" : "+v"(t[c][0]), "+v"(t[c][1]));
@@ -693,7 +744,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
   };
 
   // ---- P_t of block c recomputed against the current reference.
-  auto probs = [&](int xe, int c) {
+  auto probs = [&](int xe, int c) __attribute__((always_inline)) {
     float t = 0.f;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -703,6 +754,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
         p[e] = __builtin_amdgcn_exp2f(
             __builtin_fmaf(s[xe][c][8 * h + e], c_log2, -m_use[c]));
         t += p[e];
+        if constexpr (DROP) {
+          if (!keep(c, 8 * h + e)) p[e] = 0.f;
+        }
       }
       pb[xe][c][h] = to_bf16x8(p);
     }
@@ -717,7 +771,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
   // m_ref = -inf) the reference moves to the true running max, O and l are
   // rescaled by exp2(m_ref_old - m_ref_new) as in the online-softmax
   // recurrence, and the step's weights are recomputed.
-  auto settle = [&](int xe) {
+  auto settle = [&](int xe) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < NB; ++c) {
       asm volatile("" : "+v"(pb[xe][c][0]), "+v"(pb[xe][c][1]), "+v"(tsum[c]));
@@ -808,6 +862,12 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
       }
       mask_half(0, e0, 0);
     }
+    if constexpr (DROP) {
+      gen_begin(key_tile(e0) * kBC);
+#pragma unroll
+      for (int r = 0; r < 10; ++r) gen_round(r);
+      gen_end();
+    }
     if constexpr (XP) {
 #pragma unroll
       for (int i = 0; i < kPf; ++i)
@@ -831,10 +891,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
       const unsigned ej = entry(j), ej1 = entry(j + 1);
       top(j, entry(j + LK), entry(j + LV));
       const int st0 = j % NS, st1 = (j + 1) % NS, stm = (j + NS - 1) % NS;
-      step(std::integral_constant<int, 1>{}, st0, 1, stm, 1, st1, 0);
+      const int kj = key_tile(ej) * kBC, kj1 = key_tile(ej1) * kBC;
+      step(std::integral_constant<int, 1>{}, st0, 1, stm, 1, st1, 0, kj + 32);
       settle(0);
       mask_half(1, ej, 1);
-      step(std::integral_constant<int, 0>{}, st1, 0, st0, 0, st1, 1);
+      step(std::integral_constant<int, 0>{}, st1, 0, st0, 0, st1, 1, kj1);
       settle(1);
       if (j + 1 < nt_w) mask_half(0, ej1, 0);
     }
@@ -871,6 +932,12 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
       }
       mask_half(0, e0, 0);
     }
+    if constexpr (DROP) {
+      gen_begin(key_tile(e0) * kBC);
+#pragma unroll
+      for (int r = 0; r < 10; ++r) gen_round(r);
+      gen_end();
+    }
     if constexpr (XP) {
 #pragma unroll
       for (int i = 0; i < kPf; ++i)
@@ -888,12 +955,13 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
       load_k(key_tile(ek));
       load_v(key_tile(ev));
       if (__builtin_expect(j < nt_w, 1)) {
+        const int kj = key_tile(ej) * kBC, kj1 = key_tile(ej1) * kBC;
         // step 2j: S of (j, half 1) || P of (j, half 0); O += (j-1, half 1)
-        step(std::integral_constant<int, 1>{}, st0, 1, stm, 1, st1, 0);
+        step(std::integral_constant<int, 1>{}, st0, 1, stm, 1, st1, 0, kj + 32);
         settle(0);
         mask_half(1, ej, 1);
         // step 2j+1: S of (j+1, half 0) || P of (j, half 1); O += (j, half 0)
-        step(std::integral_constant<int, 0>{}, st1, 0, st0, 0, st1, 1);
+        step(std::integral_constant<int, 0>{}, st1, 0, st0, 0, st1, 1, kj1);
         settle(1);
         if (j + 1 < nt_w) mask_half(0, ej1, 0);
       } else if (j == nt_w) {
@@ -911,7 +979,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
 #pragma unroll
   for (int c = 0; c < NB; ++c) {
     const float l_tot = sum_halves(l_run[c]);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    // Dropout: kept weights are divided by the keep probability.
+    if constexpr (DROP) inv *= 256.f / (float)(256 - drop.p8);
     if (qrow[c] < N) {
       uint16_t* orow = O + head + (size_t)qrow[c] * D;
 #pragma unroll
@@ -1117,26 +1187,27 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
 
 namespace {
 
-template <int D, bool CAUSAL, bool KVLEN, bool SPARSE>
+template <int D, bool CAUSAL, bool KVLEN, bool SPARSE, bool DROP = false>
 void fwd_bf16_dispatch(bool pipe, bool two_blocks, dim3 grid, dim3 block,
                        hipStream_t stream, const uint16_t* q,
                        const uint16_t* k, const uint16_t* v,
                        uint16_t* o, float* lse, const int32_t* kv_len,
                        const uint8_t* bmask, int H, int N, int n_qblk,
-                       float c) {
-  if constexpr (D == 64) {
+                       float c, Dropout drop) {
+  // (Dropout keeps one block per wavefront: two would not fit the registers.)
+  if constexpr (D == 64 && !DROP) {
     if (pipe && two_blocks) {
-      hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 4, 2, CAUSAL, KVLEN, SPARSE>),
+      hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 4, 2, CAUSAL, KVLEN, SPARSE, DROP>),
                          grid, block, 0, stream, q, k, v, o, lse, kv_len,
-                         bmask, H, N, n_qblk, c);
+                         bmask, H, N, n_qblk, c, drop);
       return;
     }
   }
-  if (pipe || SPARSE)
-    hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 8, 1, CAUSAL, KVLEN, SPARSE>),
+  if (pipe || SPARSE || DROP)
+    hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 8, 1, CAUSAL, KVLEN, SPARSE, DROP>),
                        grid, block, 0, stream, q, k, v, o, lse, kv_len, bmask,
-                       H, N, n_qblk, c);
-  else if constexpr (!SPARSE)
+                       H, N, n_qblk, c, drop);
+  else if constexpr (!SPARSE && !DROP)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, CAUSAL, KVLEN>), grid, block, 0,
                        stream, q, k, v, o, lse, kv_len, H, N, n_qblk, c);
 }
@@ -1146,7 +1217,8 @@ void fwd_bf16_dispatch(bool pipe, bool two_blocks, dim3 grid, dim3 block,
 int launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const int32_t* kv_len, const uint8_t* block_mask,
                     uint16_t* o, float* lse, int B, int H, int N, int d,
-                    float scale, int causal, hipStream_t stream) {
+                    float scale, int causal, const Dropout* drop,
+                    hipStream_t stream) {
   // Grids with at least one 256-row workgroup per CU use the pipelined
   // kernel: head dim 64 with 4 wavefronts of two 32-row blocks when there
   // are two such workgroups per CU (two resident per CU), else 8 wavefronts
@@ -1154,11 +1226,12 @@ int launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   // head dim 128 with 8 wavefronts of one block (its two blocks would not
   // fit two wavefronts per SIMD).  Smaller grids use the plain kernel with
   // 128-row workgroups, two per CU.  Block-sparse calls always take the
-  // pipelined kernel (one 256-row workgroup per block-mask row).
+  // pipelined kernel (one 256-row workgroup per block-mask row), and so do
+  // calls with dropout.
   constexpr int kCUs = 256;
   const bool sparse = block_mask != nullptr;
   const long long grid256 = (long long)B * H * ((N + 255) / 256);
-  const bool pipe = sparse || grid256 >= kCUs;
+  const bool pipe = sparse || drop != nullptr || grid256 >= kCUs;
   const bool two_blocks = d == 64 && grid256 >= 2 * kCUs;
   const int br = pipe ? 256 : 128;
   const int n_qblk = (N + br - 1) / br;
@@ -1169,8 +1242,19 @@ int launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 #define FA_FWD_LAUNCH(DD, CC, KK, SS)                                          \
   fwd_bf16_dispatch<DD, CC, KK, SS>(pipe, two_blocks, grid, block, stream, q,  \
                                     k, v, o, lse, kv_len, block_mask, H, N,    \
-                                    n_qblk, c)
-  if (d == 64) {
+                                    n_qblk, c, Dropout{})
+#define FA_FWD_DROP(DD, CC)                                                    \
+  fwd_bf16_dispatch<DD, CC, false, false, true>(                               \
+      pipe, two_blocks, grid, block, stream, q, k, v, o, lse, nullptr,         \
+      nullptr, H, N, n_qblk, c, *drop)
+  // Dropout: dense heads without key padding (the C layer checks).
+  if (drop) {
+    if (d == 64) {
+      if (causal) FA_FWD_DROP(64, true); else FA_FWD_DROP(64, false);
+    } else {
+      if (causal) FA_FWD_DROP(128, true); else FA_FWD_DROP(128, false);
+    }
+  } else if (d == 64) {
     if (sparse) {
       if (causal) FA_FWD_LAUNCH(64, true, false, true);
       else FA_FWD_LAUNCH(64, false, false, true);
@@ -1190,6 +1274,7 @@ int launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     }
   }
 #undef FA_FWD_LAUNCH
+#undef FA_FWD_DROP
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

@@ -9,12 +9,24 @@
 
 namespace fa {
 
+// Attention-dropout parameters (kernel argument).  Element (b, h, i, j)
+// reads byte j % 4 of word i % 4 of Philox4x32-10 at counter
+// (j / 4, i / 4, b H + h, offset) with key (k0, k1), and is kept iff that
+// byte is >= p8.
+struct Dropout {
+  uint32_t k0, k1;    // key: the seed's low and high words
+  uint32_t offset;    // fourth counter word
+  int p8;             // byte threshold, 0..255
+};
+
 // kv_len: device int32 [B] or NULL; block_mask: device uint8
-// [H, ceil(N/256), ceil(N/128)] or NULL (never both).
+// [H, ceil(N/256), ceil(N/128)] or NULL; drop: dropout parameters or NULL
+// (at most one of the three).
 int launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const int32_t* kv_len, const uint8_t* block_mask,
                     uint16_t* o, float* lse, int B, int H, int N, int d,
-                    float scale, int causal, hipStream_t stream);
+                    float scale, int causal, const Dropout* drop,
+                    hipStream_t stream);
 
 int launch_fwd_f32(const float* q, const float* k, const float* v, float* o,
                    float* lse, int B, int H, int N, int d, float scale,
@@ -23,17 +35,19 @@ int launch_fwd_f32(const float* q, const float* k, const float* v, float* o,
 int launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, float* D,
                           int B, int H, int N, int d, hipStream_t stream);
 
-// block_mask: device uint8 [H, ceil(N/256), ceil(N/128)] or NULL (dense).
+// block_mask: device uint8 [H, ceil(N/256), ceil(N/128)] or NULL (dense);
+// drop: dropout parameters or NULL (not both).
 int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const uint16_t* dO, const float* lse, const float* D,
                     const uint8_t* block_mask, uint16_t* dk, uint16_t* dv,
                     int B, int H, int N, int d, float scale, int causal,
-                    hipStream_t stream);
+                    const Dropout* drop, hipStream_t stream);
 
 int launch_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   const uint16_t* dO, const float* lse, const float* D,
                   const uint8_t* block_mask, uint16_t* dq, int B, int H, int N,
-                  int d, float scale, int causal, hipStream_t stream);
+                  int d, float scale, int causal, const Dropout* drop,
+                  hipStream_t stream);
 
 // FP8 forward (layouts in include/fa.h).  signs: device int8 [d] or NULL.
 int launch_fp8_quantize(const uint16_t* q, const uint16_t* k,

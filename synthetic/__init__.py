@@ -71,6 +71,8 @@ class Workload:
     block_density: float = 0.0
     sign_seed: int | None = None     # FP8 path: rotation signs from this seed
     linear: bool = False             # causal linear attention (no softmax)
+    drop_p: float = 0.0              # attention dropout probability
+    drop_seed: int | None = None     # 64-bit generator key of the dropout mask
     description: str = ""
 
     @property
@@ -112,6 +114,11 @@ WORKLOADS = {
                  (801, 802, 803), linear=True,
                  description="causal linear attention (chunkwise), head dim "
                              "128"),
+        Workload("dropout_causal_fwd_bwd_d128", 4, 16, 4096, 128, "bf16", True,
+                 (901, 902, 903, 904), backward=True, drop_p=0.1,
+                 drop_seed=0x243F6A8885A308D3,
+                 description="causal forward + backward with attention "
+                             "dropout p = 0.1, head dim 128"),
     ]
 }
 
@@ -162,6 +169,8 @@ def make_inputs(w: Workload | str, heads: slice | None = None) -> dict:
             out["block_mask"] = np.ascontiguousarray(out["block_mask"][heads])
     if w.sign_seed is not None:
         out["signs"] = rotation_signs(w.sign_seed, w.d)
+    if w.drop_seed is not None:
+        out["dropout"] = {"p": w.drop_p, "seed": w.drop_seed, "offset": 0}
     if w.kv_len_seed is not None:
         lo, hi = w.kv_len_range
         out["kv_len"] = np.random.default_rng(w.kv_len_seed).integers(

@@ -15,7 +15,7 @@ import io_aware_tiled_amd as fa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
 
-OK, NULL, SHAPE, HEADDIM, ALIGN, WORKSPACE, HIP = 0, -1, -2, -3, -4, -5, -6
+OK, NULL, SHAPE, HEADDIM, ALIGN, WORKSPACE, HIP, DROPOUT = 0, -1, -2, -3, -4, -5, -6, -7
 
 pytestmark = pytest.mark.skipif(not os.path.exists(fa.lib_path()),
                                 reason="libfa.so not built")
@@ -36,7 +36,8 @@ def test_header_declares_expected_calls():
                  "fa_fp8_quantize", "fa_fwd_fp8_quantized", "fa_fwd_fp8",
                  "fa_linear_fwd", "fa_linear_workspace_size",
                  "fa_bwd_block_sparse", "fa_bwd_dkdv_block_sparse",
-                 "fa_bwd_dq_block_sparse",
+                 "fa_bwd_dq_block_sparse", "fa_fwd_dropout",
+                 "fa_bwd_dropout", "fa_bwd_dkdv_dropout", "fa_bwd_dq_dropout",
                  "fa_bwd_workspace_size", "fa_status_string", "fa_version",
                  "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq"]:
         assert want in names
@@ -52,11 +53,11 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_status_strings():
     assert fa.fa_version() == 10000
     seen = set()
-    for code in (OK, NULL, SHAPE, HEADDIM, ALIGN, WORKSPACE, HIP):
+    for code in (OK, NULL, SHAPE, HEADDIM, ALIGN, WORKSPACE, HIP, DROPOUT):
         s = fa.fa_status_string(code)
         assert s.startswith("FA_"), s
         seen.add(s)
-    assert len(seen) == 7
+    assert len(seen) == 8
     assert "unknown" in fa.fa_status_string(12345)
 
 
@@ -245,3 +246,52 @@ def test_python_binding_refuses_host_tensors():
     q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.forward(q, q, q)
+
+
+def test_dropout_argument_errors():
+    """Drop probability outside [0, 255.5/256) (or NaN) is rejected before
+    any launch, and so are the usual pointer, shape and workspace errors."""
+    L = fa.lib()
+
+    def fw(p=0.1, q=A, o=A, d=64, N=64):
+        return L.fa_fwd_dropout(q, A, A, o, A, 1, 2, N, d, 0.1, 1, p, 7, 0,
+                                None)
+    assert fw(p=-0.01) == DROPOUT
+    assert fw(p=1.0) == DROPOUT
+    assert fw(p=255.5 / 256) == DROPOUT      # rounds to 256
+    assert fw(p=float("nan")) == DROPOUT
+    assert fw(q=None) == NULL
+    assert fw(d=96) == HEADDIM
+    assert fw(N=0) == SHAPE
+    assert fw(o=MIS) == ALIGN
+    nbytes = fa.fa_bwd_workspace_size(1, 2, 64, 128)
+    W = 0x100000
+
+    def bw(p=0.1, ptrs=None, d=128, ws=W, wsb=nbytes):
+        pp = ptrs or [A] * 9
+        return L.fa_bwd_dropout(*pp, ws, wsb, 1, 2, 64, d, 0.1, 1, p, 7, 0,
+                                None)
+    assert bw(p=1.5) == DROPOUT
+    assert bw(p=-1.0) == DROPOUT
+    for i in range(9):
+        pp = [A] * 9
+        pp[i] = None
+        assert bw(ptrs=pp) == NULL, i
+    assert bw(d=64) == HEADDIM
+    assert bw(ws=None) == WORKSPACE
+    assert bw(wsb=nbytes - 1) == WORKSPACE
+    assert L.fa_bwd_dkdv_dropout(A, A, A, A, A, A, A, W, nbytes, 1, 2, 64, 128,
+                                 0.1, 1, 2.0, 7, 0, None) == DROPOUT
+    assert L.fa_bwd_dq_dropout(A, A, A, A, A, None, W, nbytes, 1, 2, 64, 128,
+                               0.1, 1, 0.1, 7, 0, None) == NULL
+
+
+def test_dropout_threshold_rounding():
+    """p8 = round(256 p) in float32, ties to even; agrees with the oracle's."""
+    import numpy as np
+    import oracle.dropout as OD
+    for p in (0.0, 0.1, 0.25, 0.5, 0.3, 1.5 / 256, 2.5 / 256, 0.99, 254.5 / 256):
+        assert fa.dropout_threshold(p) == OD.threshold(p), p
+    assert fa.dropout_threshold(1.5 / 256) == 2
+    assert fa.dropout_threshold(2.5 / 256) == 2
+    assert fa.dropout_threshold(0.5) == 128
