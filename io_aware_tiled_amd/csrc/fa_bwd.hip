@@ -1125,9 +1125,10 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
   // with dP' = dO V^T; the accumulator starts at -k D and the 1/k is
   // applied at the end.
   const float kp = DROP ? (float)(256 - drop.p8) * (1.f / 256.f) : 1.f;
+  const float negd_s = -dd * kp;
   f32x16 negd;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) negd[r] = -dd * kp;
+  for (int r = 0; r < 16; ++r) negd[r] = negd_s;
 
   // Every register operand has arrived before any DMA is issued (a wait
   // the compiler can see, so that it places none of its own inside the
@@ -1221,7 +1222,22 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
         s[XS] = mfma32x16(a, qf[m], m == 0 ? f32x16{} : s[XS]);
       } else if (m < 2 * kS) {
         const int kk = m - kS;
-        dp[XS] = mfma32x16(a, gf[kk], kk == 0 ? negd : dp[XS]);
+        if constexpr (DROP) {
+          // The splat of -k D is rebuilt per step from one register (the
+          // dropout variant has no registers to keep all sixteen live).
+          if (kk == 0) {
+            float nd = negd_s;
+            asm volatile("" : "+v"(nd));
+            f32x16 c0;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) c0[r] = nd;
+            dp[XS] = mfma32x16(a, gf[kk], c0);
+          } else {
+            dp[XS] = mfma32x16(a, gf[kk], dp[XS]);
+          }
+        } else {
+          dp[XS] = mfma32x16(a, gf[kk], kk == 0 ? negd : dp[XS]);
+        }
       } else {
         // Half 0 of dS^T (converted in slot 9) feeds the first D/32 of
         // these MFMAs, half 1 (converted in slot 17) the last D/32, which
@@ -1235,7 +1251,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
         const int el = m - 2;
         if constexpr (DROP)
           dsv[el] = pe[el] * (drop_keep(kz[el / 4], el % 4, drop.p8) ? dp[XE][el]
-                                                                    : negd[el]);
+                                                                    : negd_s);
         else
           dsv[el] = pe[el] * dp[XE][el];
         if (el % 8 == 7) {
