@@ -83,13 +83,20 @@ struct FwdTile {
 // query blocks (largest index) first so the tail holds the short ones.
 __device__ __forceinline__ void fwd_schedule(int wg, int n_qblk, int BH,
                                              bool causal, int& bh, int& qb) {
-  if (causal) {
-    qb = n_qblk - 1 - wg / BH;
-    bh = wg % BH;
-  } else {
-    bh = wg / n_qblk;
-    qb = wg % n_qblk;
-  }
+  // Workgroups are dealt to the 8 XCDs round robin (wg % 8), each with its
+  // own L2.  Consecutive ids take consecutive heads, so with BH a multiple
+  // of 8 every block of a head runs on one XCD and reads K and V from one
+  // L2.  Otherwise each head is split into P = 8 / gcd(BH, 8) parts
+  // (alternate query blocks) so that BH P is a multiple of 8 and a head
+  // spans P XCDs (when n_qblk is a multiple of P).  Causal: longest query
+  // blocks first.
+  int P = 8 / min(BH & -BH, 8);
+  if (n_qblk % P != 0) P = 1;
+  const int VH = BH * P;
+  const int v = wg % VH;
+  const int t = (wg / VH) * P + v % P;
+  bh = v / P;
+  qb = causal ? n_qblk - 1 - t : t;
 }
 
 template <int D, int NW, bool CAUSAL, bool KVLEN>
