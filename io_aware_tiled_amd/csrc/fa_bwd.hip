@@ -385,13 +385,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
   const int BH = gridDim.x / n_qblk;
   int bh, qb;
-  if (CAUSAL) {
-    qb = n_qblk - 1 - (int)blockIdx.x / BH;
-    bh = blockIdx.x % BH;
-  } else {
-    bh = blockIdx.x / n_qblk;
-    qb = blockIdx.x % n_qblk;
-  }
+  block_schedule((int)blockIdx.x, n_qblk, BH, CAUSAL, bh, qb);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = wave_id();
@@ -1023,13 +1017,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
 
   const int BH = gridDim.x / n_qblk;
   int bh, qb;
-  if (CAUSAL) {
-    qb = n_qblk - 1 - (int)blockIdx.x / BH;
-    bh = blockIdx.x % BH;
-  } else {
-    bh = blockIdx.x / n_qblk;
-    qb = blockIdx.x % n_qblk;
-  }
+  block_schedule((int)blockIdx.x, n_qblk, BH, CAUSAL, bh, qb);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = wave_id();

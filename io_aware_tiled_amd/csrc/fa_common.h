@@ -157,6 +157,26 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs,
       : "memory");
 }
 
+// Workgroup id -> (batch-head bh, query block qb) for grids of BH heads
+// times n_qblk query blocks.
+__device__ __forceinline__ void block_schedule(int wg, int n_qblk, int BH,
+                                               bool causal, int& bh, int& qb) {
+  // Workgroups are dealt to the 8 XCDs round robin (wg % 8), each with its
+  // own L2.  Consecutive ids take consecutive heads, so with BH a multiple
+  // of 8 every block of a head runs on one XCD and reads K and V from one
+  // L2.  Otherwise each head is split into P = 8 / gcd(BH, 8) parts
+  // (alternate query blocks) so that BH P is a multiple of 8 and a head
+  // spans P XCDs (when n_qblk is a multiple of P).  Causal: longest query
+  // blocks first.
+  int P = 8 / min(BH & -BH, 8);
+  if (n_qblk % P != 0) P = 1;
+  const int VH = BH * P;
+  const int v = wg % VH;
+  const int t = (wg / VH) * P + v % P;
+  bh = v / P;
+  qb = causal ? n_qblk - 1 - t : t;
+}
+
 // ---------------------------------------------------------------------------
 // Attention dropout.  Random bytes come from Philox4x32-10, the counter-based
 // generator of Salmon, Moraes, Dror and Shaw ("Parallel random numbers: as

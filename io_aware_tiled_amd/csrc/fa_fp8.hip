@@ -291,13 +291,7 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_fp8_kernel(
 
   const int BH = gridDim.x / n_qblk;
   int bh, qb;
-  if (CAUSAL) {
-    qb = n_qblk - 1 - (int)blockIdx.x / BH;
-    bh = (int)blockIdx.x % BH;
-  } else {
-    bh = (int)blockIdx.x / n_qblk;
-    qb = (int)blockIdx.x % n_qblk;
-  }
+  block_schedule((int)blockIdx.x, n_qblk, BH, CAUSAL, bh, qb);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = wave_id();

@@ -81,23 +81,6 @@ struct FwdTile {
 
 // Map a workgroup index to (bh, query block): causal grids run the longest
 // query blocks (largest index) first so the tail holds the short ones.
-__device__ __forceinline__ void fwd_schedule(int wg, int n_qblk, int BH,
-                                             bool causal, int& bh, int& qb) {
-  // Workgroups are dealt to the 8 XCDs round robin (wg % 8), each with its
-  // own L2.  Consecutive ids take consecutive heads, so with BH a multiple
-  // of 8 every block of a head runs on one XCD and reads K and V from one
-  // L2.  Otherwise each head is split into P = 8 / gcd(BH, 8) parts
-  // (alternate query blocks) so that BH P is a multiple of 8 and a head
-  // spans P XCDs (when n_qblk is a multiple of P).  Causal: longest query
-  // blocks first.
-  int P = 8 / min(BH & -BH, 8);
-  if (n_qblk % P != 0) P = 1;
-  const int VH = BH * P;
-  const int v = wg % VH;
-  const int t = (wg / VH) * P + v % P;
-  bh = v / P;
-  qb = causal ? n_qblk - 1 - t : t;
-}
 
 template <int D, int NW, bool CAUSAL, bool KVLEN>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
@@ -111,7 +94,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
 
   const int BH = gridDim.x / n_qblk;
   int bh, qb;
-  fwd_schedule(blockIdx.x, n_qblk, BH, CAUSAL, bh, qb);
+  block_schedule(blockIdx.x, n_qblk, BH, CAUSAL, bh, qb);
   const int b = bh / H;
 
   const int tid = threadIdx.x;
@@ -395,7 +378,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
 
   const int BH = gridDim.x / n_qblk;
   int bh, qb;
-  fwd_schedule(blockIdx.x, n_qblk, BH, CAUSAL, bh, qb);
+  block_schedule(blockIdx.x, n_qblk, BH, CAUSAL, bh, qb);
   const int b = bh / H;
 
   const int tid = threadIdx.x;
@@ -1037,7 +1020,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
 
   const int BH = gridDim.x / n_qblk;
   int bh, qb;
-  fwd_schedule(blockIdx.x, n_qblk, BH, CAUSAL, bh, qb);
+  block_schedule(blockIdx.x, n_qblk, BH, CAUSAL, bh, qb);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
