@@ -61,7 +61,7 @@ enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = -1,      /* a required pointer is NULL                     */
   FA_ERR_SHAPE = -2,     /* B, H or N <= 0, or B*H*N > 2^31-1              */
-  FA_ERR_HEADDIM = -3,   /* d is not 64 or 128 (backward: not 128)         */
+  FA_ERR_HEADDIM = -3,   /* d is not 64 or 128 (sparse/dropout bwd: 128)   */
   FA_ERR_ALIGN = -4,     /* a tensor pointer is not 16-byte aligned        */
   FA_ERR_WORKSPACE = -5, /* workspace NULL, too small or not 256-B aligned */
   FA_ERR_HIP = -6,       /* the HIP runtime reported a launch error        */
@@ -233,8 +233,11 @@ int fa_linear_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 size_t fa_linear_workspace_size(int B, int H, int N, int d);
 
 /*
- * The backward entry points below support head dimension d = 128 only; any
- * other d returns FA_ERR_HEADDIM (and fa_bwd_workspace_size returns 0).
+ * The dense backward entry points below take head dimension d = 64 or 128
+ * (any other d returns FA_ERR_HEADDIM and fa_bwd_workspace_size returns 0);
+ * d = 128 runs the pipelined kernels on grids that fill the chip, d = 64 the
+ * 8-wavefront dK/dV and 4-wavefront dQ kernels.  The block-sparse and
+ * dropout backward entry points take d = 128 only.
  *
  * Bytes of device workspace the backward needs: D [B,H,N] float32 (the row
  * dot products dO_i . O_i), rounded up to 256 bytes.  Returns 0 for invalid

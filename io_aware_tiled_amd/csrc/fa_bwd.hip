@@ -60,7 +60,7 @@ constexpr int kBK = 128;   // keys per workgroup (32 per wavefront)
 // as 16-bit entries, at most this many (64-row tiles up to N = 131072).
 constexpr int kSparseMaxTiles = 2 * FA_SPARSE_MAX_KEY_BLOCKS;
 static_assert(FA_SPARSE_BK == kBK, "a block-mask column is one dK/dV workgroup");
-constexpr int kD = 128;    // head dimension of the backward kernel
+constexpr int kD = 128;    // head dimension of the pipelined backward kernels
 
 // ---------------------------------------------------------------------------
 template <int D>
@@ -97,14 +97,14 @@ constexpr int kBQ2 = 64;   // query rows per tile
 // plus an immediate offset.
 constexpr int kRS = 152;   // K, V, Q, dO row stride
 
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dv,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kblk,
     float c_log2, float scale) {
-  constexpr int D = kD;
+  static_assert(D == 64 || D == 128, "head dimension");
   constexpr int KB = kBK * kRS;        // elements of the K (or V) block
   constexpr int QB = kBQ2 * kRS;       // elements of a Q (or dO) tile
   // K | V | Q0 | dO0 | Q1 | dO1 (bf16), then LSE and D (float), the query
@@ -176,17 +176,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   const int it0 = CAUSAL ? kb0 / kBQ2 : 0;
 
 
-  // Query-tile staging: 2 chunks of Q and 2 of dO per thread, plus LSE / D.
-  // Rows past N load row N-1 (in bounds) and are replaced by zeros with a
-  // select, so the loads need no branch.
-  u32x4 qreg[2], doreg[2];
+  // Query-tile staging: QCH 16-byte chunks of Q and of dO per thread, plus
+  // LSE / D.  Rows past N load row N-1 (in bounds) and are replaced by zeros
+  // with a select, so the loads need no branch.
+  constexpr int QCH = kBQ2 * D / 8 / kBwdThreads;
+  static_assert(QCH * 8 * kBwdThreads == kBQ2 * D, "tile staging");
+  u32x4 qreg[QCH], doreg[QCH];
   float lse_r = 0.f, d_r = 0.f;
   auto load_qtile = [&](int it) {
     const int qt0 = it * kBQ2;
     const uint16_t* qb = Qh + (size_t)qt0 * D;      // wave-uniform bases
     const uint16_t* gb = dOh + (size_t)qt0 * D;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < QCH; ++r) {
       const int c = tid + kBwdThreads * r;
       const int row = c / (D / 8);
       const int col = 8 * (c % (D / 8));
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     uint16_t* lq_ = lds_q0 + (buf ? qbuf : 0);
     uint16_t* ld_ = lq_ + dooff;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < QCH; ++r) {
       const int c = tid + kBwdThreads * r;
       const int row = c / (D / 8);
       const int col = 8 * (c % (D / 8));
@@ -368,14 +370,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
 constexpr int kDqBR = 128;
 constexpr int kDqBC = 64;
 
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dv,
     uint16_t* __restrict__ dQ, int N, int n_qblk, float c_log2,
     float scale) {
-  constexpr int D = kD;
+  static_assert(D == 64 || D == 128, "head dimension");
   constexpr int TE = kDqBC * kRS;      // elements per K (or V) tile buffer
   constexpr int CPT = kDqBC * D / 8 / kThreads;   // 16-byte chunks per thread
   __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TE];
@@ -1370,13 +1372,15 @@ int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const uint8_t* block_mask, uint16_t* dk, uint16_t* dv,
                     int B, int H, int N, int d, float scale, int causal,
                     const Dropout* drop, hipStream_t stream) {
-  if (d != kD) return -3;
+  if (d != kD && d != 64) return -3;
+  if (d != kD && (block_mask != nullptr || drop != nullptr)) return -3;
   const int n_kblk = (N + kBK - 1) / kBK;
   const float c = (float)((double)scale * 1.4426950408889634);
-  // Grids with at least one 128-key workgroup per CU, and every
-  // block-sparse or dropout call: the pipelined kernel (4 wavefronts, K/V
-  // in registers); smaller dense ones: 8 wavefronts.
-  if ((long long)B * H * n_kblk >= 256 || block_mask != nullptr || drop != nullptr) {
+  // Head dim 128 on grids with at least one 128-key workgroup per CU, and
+  // every block-sparse or dropout call: the pipelined kernel (4 wavefronts,
+  // K/V in registers); the rest (and head dim 64): 8 wavefronts.
+  if (d == kD && ((long long)B * H * n_kblk >= 256 || block_mask != nullptr ||
+                  drop != nullptr)) {
     const dim3 grid((unsigned)(B * H * n_kblk)), block(256);
 #define FA_DKDV_LAUNCH(CC, SS)                                                  \
   hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<CC, SS>), grid, block, 0, stream, q, \
@@ -1398,13 +1402,15 @@ int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     return hipGetLastError() == hipSuccess ? 0 : -6;
   }
   const dim3 grid((unsigned)(B * H * n_kblk)), block(kBwdThreads);
-  if (causal) {
-    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, grid, block, 0, stream, q, k, v,
-                       dO, lse, D, dk, dv, N, n_kblk, c, scale);
+#define FA_DKDV_PLAIN(DD, CC)                                                  \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<DD, CC>), grid, block, 0, stream, q, k,   \
+                     v, dO, lse, D, dk, dv, N, n_kblk, c, scale)
+  if (d == 64) {
+    if (causal) FA_DKDV_PLAIN(64, true); else FA_DKDV_PLAIN(64, false);
   } else {
-    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, grid, block, 0, stream, q, k,
-                       v, dO, lse, D, dk, dv, N, n_kblk, c, scale);
+    if (causal) FA_DKDV_PLAIN(128, true); else FA_DKDV_PLAIN(128, false);
   }
+#undef FA_DKDV_PLAIN
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
@@ -1413,13 +1419,15 @@ int launch_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   const uint8_t* block_mask, uint16_t* dq, int B, int H, int N,
                   int d, float scale, int causal, const Dropout* drop,
                   hipStream_t stream) {
-  if (d != kD) return -3;
+  if (d != kD && d != 64) return -3;
+  if (d != kD && (block_mask != nullptr || drop != nullptr)) return -3;
   const float c = (float)((double)scale * 1.4426950408889634);
-  // Grids with at least one 256-row workgroup per CU, and every
-  // block-sparse call (a workgroup is one block-mask row) or dropout call:
-  // the pipelined kernel; smaller dense ones: 128-row workgroups, two per CU.
+  // Head dim 128 on grids with at least one 256-row workgroup per CU, and
+  // every block-sparse call (a workgroup is one block-mask row) or dropout
+  // call: the pipelined kernel; the rest (and head dim 64): 128-row
+  // workgroups, two per CU.
   const long long grid256 = (long long)B * H * ((N + kDqPBR - 1) / kDqPBR);
-  if (grid256 >= 256 || block_mask != nullptr || drop != nullptr) {
+  if (d == kD && (grid256 >= 256 || block_mask != nullptr || drop != nullptr)) {
     const int n_qblk = (N + kDqPBR - 1) / kDqPBR;
     const dim3 grid((unsigned)(B * H * n_qblk)), block(512);
 #define FA_DQ_LAUNCH(CC, SS)                                                  \
@@ -1443,13 +1451,15 @@ int launch_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   }
   const int n_qblk = (N + kDqBR - 1) / kDqBR;
   const dim3 grid((unsigned)(B * H * n_qblk)), block(kThreads);
-  if (causal) {
-    hipLaunchKernelGGL(bwd_dq_kernel<true>, grid, block, 0, stream, q, k, v,
-                       dO, lse, D, dq, N, n_qblk, c, scale);
+#define FA_DQ_PLAIN(DD, CC)                                                    \
+  hipLaunchKernelGGL((bwd_dq_kernel<DD, CC>), grid, block, 0, stream, q, k, v,  \
+                     dO, lse, D, dq, N, n_qblk, c, scale)
+  if (d == 64) {
+    if (causal) FA_DQ_PLAIN(64, true); else FA_DQ_PLAIN(64, false);
   } else {
-    hipLaunchKernelGGL(bwd_dq_kernel<false>, grid, block, 0, stream, q, k, v,
-                       dO, lse, D, dq, N, n_qblk, c, scale);
+    if (causal) FA_DQ_PLAIN(128, true); else FA_DQ_PLAIN(128, false);
   }
+#undef FA_DQ_PLAIN
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

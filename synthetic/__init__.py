@@ -87,6 +87,10 @@ WORKLOADS = {
                  description="tiny fp32 non-causal forward"),
         Workload("gpt2_causal", 8, 12, 1024, 64, "bf16", True, (201, 202, 203),
                  description="GPT-2-small-shaped causal forward"),
+        Workload("gpt2_causal_fwd_bwd", 8, 12, 1024, 64, "bf16", True,
+                 (201, 202, 203, 204), backward=True,
+                 description="GPT-2-small-shaped causal forward + backward "
+                             "(a training step's attention)"),
         Workload("bert_keypad", 16, 16, 512, 64, "bf16", False, (301, 302, 303),
                  kv_len_seed=309, kv_len_range=(256, 512),
                  description="BERT-large-shaped forward with key padding"),

@@ -141,7 +141,8 @@ def test_workspace_size():
         return (x + 255) // 256 * 256
     for B, H, N in [(1, 1, 1), (4, 16, 4096), (2, 3, 1000)]:
         assert ws(B, H, N, 128) == a256(B * H * N * 4)
-    assert ws(1, 1, 64, 64) == 0          # backward: head dim 128 only
+    assert ws(1, 1, 64, 64) == a256(64 * 4)   # head dim 64 or 128
+    assert ws(1, 1, 64, 96) == 0
     assert ws(0, 1, 64, 128) == 0
     assert ws(1, 1, -5, 128) == 0
 
@@ -158,7 +159,7 @@ def test_bwd_argument_errors():
         p = [A] * 9
         p[i] = None
         assert bwd(p) == NULL, i
-    assert bwd(d=64) == HEADDIM
+    assert bwd(d=96) == HEADDIM
     assert bwd(N=0) == SHAPE
     assert bwd(ws=None) == WORKSPACE
     assert bwd(ws=W + 16) == WORKSPACE    # not 256-byte aligned
@@ -172,7 +173,7 @@ def test_bwd_argument_errors():
                          0.1, 1, None) == NULL
     assert L.fa_bwd_dq(A, A, A, A, A, None, W, nbytes, 1, 1, 64, 128, 0.1,
                        1, None) == NULL
-    assert L.fa_bwd_dq(A, A, A, A, A, A, W, nbytes, 1, 1, 64, 64, 0.1,
+    assert L.fa_bwd_dq(A, A, A, A, A, A, W, nbytes, 1, 1, 64, 32, 0.1,
                        1, None) == HEADDIM
     assert L.fa_bwd_dq(A, A, A, A, A, A, W, 0, 1, 1, 64, 128, 0.1,
                        1, None) == WORKSPACE

@@ -78,13 +78,47 @@ def test_bwd_bitwise_repeatable():
         assert torch.equal(dq, dq0)
 
 
-def test_bwd_rejects_head_dim_64():
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 33, 64, 300, 1000])
+def test_bwd_head_dim_64(causal, N):
+    """Head dimension 64 (the 8-wavefront dK/dV and 4-wavefront dQ kernels)."""
+    B, H = (1, 3) if N <= 300 else (2, 2)
+    inp = S.make_case(B, H, N, 64, "bf16", causal, seed=500 + N + causal,
+                      backward=True)
+    _check_bwd(f"bwd d64 causal={causal} N={N}", inp)
+
+
+def test_bwd_gpt2_shape_d64():
+    """GPT-2-small-shaped training step (8 x 12 x 1024 x 64, causal): two
+    heads against the oracle, every head against the gradient invariants."""
+    inp = S.make_case(8, 12, 1024, 64, "bf16", True, seed=31, backward=True)
+    dq, dk, dv = _check_bwd("bwd gpt2 shape heads 0,7", inp,
+                            heads=np.array([0, 7]))
+    tol = 3 * TOL_GRAD * np.sqrt(1024)
+    e1 = float(np.abs(dk.float().sum(dim=2).cpu().numpy()).max())
+    e2 = float(np.abs(dv.float().sum(dim=2).cpu().numpy()
+                      - inp["do"].astype(np.float64).sum(axis=2)).max())
+    report("gpt2 invariants", sum_dK=e1, sum_dV_minus_sum_dO=e2)
+    assert e1 <= tol and e2 <= tol
+
+
+def test_bwd_rejects_unsupported_head_dims():
+    """d = 96 has no kernel; the block-sparse and dropout backward take
+    d = 128 only.  Rejected before any launch."""
     import torch
     import io_aware_tiled_amd as fa
-    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16, device="cuda:0")
+    q = torch.zeros(1, 1, 64, 96, dtype=torch.bfloat16, device="cuda:0")
     lse = torch.zeros(1, 1, 64, dtype=torch.float32, device="cuda:0")
     with pytest.raises(fa.FAError):
         fa.backward(q, q, q, q, lse, q)
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16, device="cuda:0")
+    m = torch.ones(1, 1, 1, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(fa.FAError):
+        fa.backward(q, q, q, q, lse, q, block_mask=m)
+    ws = torch.empty(fa.fa_bwd_workspace_size(1, 1, 64, 64), dtype=torch.uint8,
+                     device="cuda:0")
+    with pytest.raises(fa.FAError):
+        fa.fa_bwd_dropout(q, q, q, q, q, lse, q, q, q, ws, 0.125, True, 0.1, 1)
 
 
 def test_workload_d128_fwd_bwd():
