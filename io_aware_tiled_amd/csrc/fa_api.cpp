@@ -30,7 +30,7 @@ int check_shape(int B, int H, int N, int d) {
 // The dense backward takes head dimension 64 or 128 (as the forward).
 int check_shape_bwd(int B, int H, int N, int d) { return check_shape(B, H, N, d); }
 
-// The block-sparse and dropout backward kernels exist for head dimension 128.
+// The block-sparse backward kernels exist for head dimension 128.
 int check_shape_bwd128(int B, int H, int N, int d) {
   const int st = check_shape(B, H, N, d);
   if (st != FA_OK) return st;
@@ -394,7 +394,7 @@ int fa_bwd_dkdv_dropout(const uint16_t* q, const uint16_t* k,
                         float p_drop, uint64_t seed, uint32_t offset,
                         void* stream) {
   if (!q || !k || !v || !dO || !lse || !dk || !dv) return FA_ERR_NULL;
-  int st = check_shape_bwd128(B, H, N, d);
+  int st = check_shape_bwd(B, H, N, d);
   if (st != FA_OK) return st;
   fa::Dropout drop;
   st = make_dropout(p_drop, seed, offset, &drop);
@@ -416,7 +416,7 @@ int fa_bwd_dq_dropout(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       float p_drop, uint64_t seed, uint32_t offset,
                       void* stream) {
   if (!q || !k || !v || !dO || !lse || !dq) return FA_ERR_NULL;
-  int st = check_shape_bwd128(B, H, N, d);
+  int st = check_shape_bwd(B, H, N, d);
   if (st != FA_OK) return st;
   fa::Dropout drop;
   st = make_dropout(p_drop, seed, offset, &drop);
@@ -439,7 +439,7 @@ int fa_bwd_dropout(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                    uint32_t offset, void* stream) {
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv)
     return FA_ERR_NULL;
-  int st = check_shape_bwd128(B, H, N, d);
+  int st = check_shape_bwd(B, H, N, d);
   if (st != FA_OK) return st;
   fa::Dropout drop;
   st = make_dropout(p_drop, seed, offset, &drop);

@@ -97,13 +97,13 @@ constexpr int kBQ2 = 64;   // query rows per tile
 // plus an immediate offset.
 constexpr int kRS = 152;   // K, V, Q, dO row stride
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP = false>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dv,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kblk,
-    float c_log2, float scale) {
+    float c_log2, float scale, Dropout drop) {
   static_assert(D == 64 || D == 128, "head dimension");
   constexpr int KB = kBK * kRS;        // elements of the K (or V) block
   constexpr int QB = kBQ2 * kRS;       // elements of a Q (or dO) tile
@@ -261,6 +261,24 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     // ---- P = exp2(s*c - lse2), dS = P (dP - D).  Register r holds query
     // qw0 + 8(r/4) + 4hh + r%4 of this lane's key.
     const bool need_mask = (CAUSAL && wk0 + 31 > qw0) || (wk0 + 32 > N);
+    // Dropout: kz[g] holds the keep bytes of rows qw0 + 8g + 4hh + e (byte
+    // e) for this lane's key: quad lane w makes the generator call of row
+    // group w, transposes its bytes to key-major order, and the quad
+    // exchange hands each lane its key's word of every call.  With Z the
+    // mask and k the keep probability, dV takes P Z (1/k at the end) and
+    // dS = P (Z dP / k - D).
+    uint32_t kz[4];
+    const float ik = DROP ? 256.f / (float)(256 - drop.p8) : 1.f;
+    if constexpr (DROP) {
+      kz[0] = (uint32_t)(mykey >> 2);
+      kz[1] = (uint32_t)((qw0 >> 2) + 2 * (l32 & 3) + hh);
+      kz[2] = (uint32_t)bh;
+      kz[3] = drop.offset;
+#pragma unroll
+      for (int r = 0; r < 10; ++r) philox_round(kz, drop.k0, drop.k1, r);
+      byte_transpose(kz);
+      quad_gather(kz);
+    }
     bf16x8 pb[2], dsb[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -278,8 +296,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
             const int q = qw0 + 8 * g + 4 * hh + e;
             if ((CAUSAL && mykey > q) || mykey >= N) p = 0.f;
           }
-          pv[4 * g2 + e] = p;
-          dsv[4 * g2 + e] = p * (dp[r] - d4[e]);
+          if constexpr (DROP) {
+            const bool kept = drop_keep(kz[g], e, drop.p8);
+            pv[4 * g2 + e] = kept ? p : 0.f;
+            dsv[4 * g2 + e] = p * ((kept ? dp[r] * ik : 0.f) - d4[e]);
+          } else {
+            pv[4 * g2 + e] = p;
+            dsv[4 * g2 + e] = p * (dp[r] - d4[e]);
+          }
         }
       }
       pb[c] = to_bf16x8(pv);
@@ -350,7 +374,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           a[e] = (dk_acc[db][4 * g + e] + red[red_idx(db, 4 * g + e)]) * scale;
-          b[e] = dv_acc[db][4 * g + e];
+          b[e] = DROP ? dv_acc[db][4 * g + e] * (256.f / (float)(256 - drop.p8))
+                      : dv_acc[db][4 * g + e];
         }
         *(bf16x4*)(dkr + 32 * db + 8 * g + 4 * hh) = to_bf16x4(a);
         *(bf16x4*)(dvr + 32 * db + 8 * g + 4 * hh) = to_bf16x4(b);
@@ -370,13 +395,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
 constexpr int kDqBR = 128;
 constexpr int kDqBC = 64;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP = false>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dv,
     uint16_t* __restrict__ dQ, int N, int n_qblk, float c_log2,
-    float scale) {
+    float scale, Dropout drop) {
   static_assert(D == 64 || D == 128, "head dimension");
   constexpr int TE = kDqBC * kRS;      // elements per K (or V) tile buffer
   constexpr int CPT = kDqBC * D / 8 / kThreads;   // 16-byte chunks per thread
@@ -491,8 +516,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     // k0 + 32kb + 8(r/4) + 4hh + r%4 for this lane's query.
     const bool need_mask = (CAUSAL && k0 + kDqBC - 1 > qw0) || (k0 + kDqBC > N);
     bf16x8 dsb[2][2];
+    const float ik = DROP ? 256.f / (float)(256 - drop.p8) : 1.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      // Dropout: kz[m] holds the keep bytes of keys k0 + 32kb + 8m + 4hh + b
+      // (byte b) for this lane's query; quad lane w makes the generator
+      // call of key group w.  dS = P (Z dP / k - D).
+      uint32_t kz[4];
+      if constexpr (DROP) {
+        kz[0] = (uint32_t)((k0 + 32 * kb) / 4 + 2 * (lq & 3) + hh);
+        kz[1] = (uint32_t)(qrow >> 2);
+        kz[2] = (uint32_t)bh;
+        kz[3] = drop.offset;
+#pragma unroll
+        for (int r = 0; r < 10; ++r) philox_round(kz, drop.k0, drop.k1, r);
+        quad_gather(kz);
+      }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         f32x8 x;
@@ -504,7 +543,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
             const int key = k0 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
             if ((CAUSAL && key > qrow) || key >= N) p = 0.f;
           }
-          x[e] = p * (dp[kb][r] - dd);
+          if constexpr (DROP)
+            x[e] = p * ((drop_keep(kz[r / 4], r % 4, drop.p8) ? dp[kb][r] * ik : 0.f) - dd);
+          else
+            x[e] = p * (dp[kb][r] - dd);
         }
         dsb[kb][c] = to_bf16x8(x);
       }
@@ -1373,12 +1415,13 @@ int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     int B, int H, int N, int d, float scale, int causal,
                     const Dropout* drop, hipStream_t stream) {
   if (d != kD && d != 64) return -3;
-  if (d != kD && (block_mask != nullptr || drop != nullptr)) return -3;
+  if (d != kD && block_mask != nullptr) return -3;
   const int n_kblk = (N + kBK - 1) / kBK;
   const float c = (float)((double)scale * 1.4426950408889634);
   // Head dim 128 on grids with at least one 128-key workgroup per CU, and
   // every block-sparse or dropout call: the pipelined kernel (4 wavefronts,
-  // K/V in registers); the rest (and head dim 64): 8 wavefronts.
+  // K/V in registers); the rest (and head dim 64, with or without dropout):
+  // 8 wavefronts.
   if (d == kD && ((long long)B * H * n_kblk >= 256 || block_mask != nullptr ||
                   drop != nullptr)) {
     const dim3 grid((unsigned)(B * H * n_kblk)), block(256);
@@ -1404,8 +1447,17 @@ int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   const dim3 grid((unsigned)(B * H * n_kblk)), block(kBwdThreads);
 #define FA_DKDV_PLAIN(DD, CC)                                                  \
   hipLaunchKernelGGL((bwd_dkdv_kernel<DD, CC>), grid, block, 0, stream, q, k,   \
-                     v, dO, lse, D, dk, dv, N, n_kblk, c, scale)
-  if (d == 64) {
+                     v, dO, lse, D, dk, dv, N, n_kblk, c, scale, Dropout{})
+  if (d == 64 && drop != nullptr) {
+    if (causal)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<64, true, true>), grid, block, 0,
+                         stream, q, k, v, dO, lse, D, dk, dv, N, n_kblk, c,
+                         scale, *drop);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<64, false, true>), grid, block, 0,
+                         stream, q, k, v, dO, lse, D, dk, dv, N, n_kblk, c,
+                         scale, *drop);
+  } else if (d == 64) {
     if (causal) FA_DKDV_PLAIN(64, true); else FA_DKDV_PLAIN(64, false);
   } else {
     if (causal) FA_DKDV_PLAIN(128, true); else FA_DKDV_PLAIN(128, false);
@@ -1420,12 +1472,12 @@ int launch_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   int d, float scale, int causal, const Dropout* drop,
                   hipStream_t stream) {
   if (d != kD && d != 64) return -3;
-  if (d != kD && (block_mask != nullptr || drop != nullptr)) return -3;
+  if (d != kD && block_mask != nullptr) return -3;
   const float c = (float)((double)scale * 1.4426950408889634);
   // Head dim 128 on grids with at least one 256-row workgroup per CU, and
   // every block-sparse call (a workgroup is one block-mask row) or dropout
-  // call: the pipelined kernel; the rest (and head dim 64): 128-row
-  // workgroups, two per CU.
+  // call: the pipelined kernel; the rest (and head dim 64, with or without
+  // dropout): 128-row workgroups, two per CU.
   const long long grid256 = (long long)B * H * ((N + kDqPBR - 1) / kDqPBR);
   if (d == kD && (grid256 >= 256 || block_mask != nullptr || drop != nullptr)) {
     const int n_qblk = (N + kDqPBR - 1) / kDqPBR;
@@ -1453,8 +1505,17 @@ int launch_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   const dim3 grid((unsigned)(B * H * n_qblk)), block(kThreads);
 #define FA_DQ_PLAIN(DD, CC)                                                    \
   hipLaunchKernelGGL((bwd_dq_kernel<DD, CC>), grid, block, 0, stream, q, k, v,  \
-                     dO, lse, D, dq, N, n_qblk, c, scale)
-  if (d == 64) {
+                     dO, lse, D, dq, N, n_qblk, c, scale, Dropout{})
+  if (d == 64 && drop != nullptr) {
+    if (causal)
+      hipLaunchKernelGGL((bwd_dq_kernel<64, true, true>), grid, block, 0,
+                         stream, q, k, v, dO, lse, D, dq, N, n_qblk, c, scale,
+                         *drop);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<64, false, true>), grid, block, 0,
+                         stream, q, k, v, dO, lse, D, dq, N, n_qblk, c, scale,
+                         *drop);
+  } else if (d == 64) {
     if (causal) FA_DQ_PLAIN(64, true); else FA_DQ_PLAIN(64, false);
   } else {
     if (causal) FA_DQ_PLAIN(128, true); else FA_DQ_PLAIN(128, false);

@@ -278,7 +278,7 @@ def test_dropout_argument_errors():
         pp = [A] * 9
         pp[i] = None
         assert bw(ptrs=pp) == NULL, i
-    assert bw(d=64) == HEADDIM
+    assert bw(d=96) == HEADDIM
     assert bw(ws=None) == WORKSPACE
     assert bw(wsb=nbytes - 1) == WORKSPACE
     assert L.fa_bwd_dkdv_dropout(A, A, A, A, A, A, A, W, nbytes, 1, 2, 64, 128,

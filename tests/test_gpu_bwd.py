@@ -103,8 +103,8 @@ def test_bwd_gpt2_shape_d64():
 
 
 def test_bwd_rejects_unsupported_head_dims():
-    """d = 96 has no kernel; the block-sparse and dropout backward take
-    d = 128 only.  Rejected before any launch."""
+    """d = 96 has no kernel; the block-sparse backward takes d = 128 only.
+    Rejected before any launch."""
     import torch
     import io_aware_tiled_amd as fa
     q = torch.zeros(1, 1, 64, 96, dtype=torch.bfloat16, device="cuda:0")
@@ -117,8 +117,10 @@ def test_bwd_rejects_unsupported_head_dims():
         fa.backward(q, q, q, q, lse, q, block_mask=m)
     ws = torch.empty(fa.fa_bwd_workspace_size(1, 1, 64, 64), dtype=torch.uint8,
                      device="cuda:0")
+    q96 = torch.zeros(1, 1, 64, 96, dtype=torch.bfloat16, device="cuda:0")
     with pytest.raises(fa.FAError):
-        fa.fa_bwd_dropout(q, q, q, q, q, lse, q, q, q, ws, 0.125, True, 0.1, 1)
+        fa.fa_bwd_dropout(q96, q96, q96, q96, q96, lse, q96, q96, q96, ws,
+                          0.125, True, 0.1, 1)
 
 
 def test_workload_d128_fwd_bwd():

@@ -116,12 +116,15 @@ def _bwd(inp, o, lse, p, seed, offset):
     return dq, dk, dv
 
 
-@pytest.mark.parametrize("B,H,N,causal,p", [
-    (1, 2, 300, True, 0.1), (1, 2, 300, False, 0.2), (2, 2, 129, True, 0.5),
-    (1, 3, 64, False, 0.3), (1, 1, 1, True, 0.5), (1, 2, 700, True, 0.75)])
-def test_dropout_bwd_parity(B, H, N, causal, p):
+@pytest.mark.parametrize("B,H,N,d,causal,p", [
+    (1, 2, 300, 128, True, 0.1), (1, 2, 300, 128, False, 0.2),
+    (2, 2, 129, 128, True, 0.5), (1, 3, 64, 128, False, 0.3),
+    (1, 1, 1, 128, True, 0.5), (1, 2, 700, 128, True, 0.75),
+    (1, 2, 300, 64, True, 0.1), (2, 3, 257, 64, False, 0.5),
+    (1, 2, 1000, 64, True, 0.2)])
+def test_dropout_bwd_parity(B, H, N, d, causal, p):
     seed, offset = 31337 + N, 5
-    inp = S.make_case(B, H, N, 128, "bf16", causal, seed=720 + N, backward=True)
+    inp = S.make_case(B, H, N, d, "bf16", causal, seed=720 + N + d, backward=True)
     o, lse = _fwd(inp, p, seed, offset)
     dq, dk, dv = _bwd(inp, o, lse, p, seed, offset)
     ref = OD.attention_dropout_bwd(inp["q"], inp["k"], inp["v"], inp["do"],
@@ -129,7 +132,7 @@ def test_dropout_bwd_parity(B, H, N, causal, p):
     _, tol = _tols(p)
     errs = {nm: max_err(host64(g), r, nm)
             for nm, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref)}
-    report(f"dropout bwd B{B} H{H} N{N} causal={causal} p={p}", **errs)
+    report(f"dropout bwd B{B} H{H} N{N} d{d} causal={causal} p={p}", **errs)
     for nm, e in errs.items():
         assert e <= tol, (nm, e, tol)
 
