@@ -154,6 +154,20 @@ def test_dropout_zero_matches_dense_bitwise():
         assert torch.equal(a, b)
 
 
+def test_dropout_zero_matches_dense_bitwise_d64():
+    """The same at head dim 64 (the 8-wavefront dK/dV and 4-wavefront dQ
+    kernels take the dropout path)."""
+    import torch
+    import io_aware_tiled_amd as fa
+    inp = S.make_case(2, 4, 600, 64, "bf16", True, seed=10, backward=True)
+    q, k, v, do = (to_dev(inp, n) for n in ("q", "k", "v", "do"))
+    o0, l0 = fa.forward(q, k, v, causal=True, scale=inp["scale"])
+    g0 = fa.backward(q, k, v, o0, l0, do, causal=True, scale=inp["scale"])
+    g1 = _bwd(inp, o0, l0, 0.0, 1, 0)
+    for a, b in zip(g0, g1):
+        assert torch.equal(a, b)
+
+
 def test_dropout_repeatable_and_seeded():
     """Same (seed, offset): bit-identical outputs; another offset or seed:
     a different mask."""
