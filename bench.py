@@ -28,6 +28,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -350,6 +351,67 @@ def summarize_counters(w: S.Workload, csvs, command) -> int:
     return 0
 
 
+def sweep(dev) -> int:
+    """Forward and the dK/dV and dQ backward stages over N = 1K..32K
+    with B*H*N = 2^18 tokens (seeded N(0,1) bf16 inputs), HIP events on the
+    launch stream, median of 5 runs of 10 launches; prints a markdown
+    table of algorithmic TFLOP/s and the fraction of the 2.5 PF bf16 peak."""
+    import torch
+    import io_aware_tiled_amd as fa
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, reps=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / reps)
+        return sorted(ts)[2]
+
+    print("| d | causal | B x H x N | forward ms | forward TFLOP/s | % of peak "
+          "| dK/dV ms | dQ ms | backward TFLOP/s | % of peak |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    tokens = 1 << 18
+    for d in (64, 128):
+        for causal in (True, False):
+            for N in (1024, 2048, 4096, 8192, 16384, 32768):
+                bh = tokens // N
+                B, H = (bh // 16, 16) if bh >= 16 else (1, bh)
+                g = torch.Generator(device=dev).manual_seed(N + d)
+                q, k, v, do = (torch.randn(B, H, N, d, device=dev, generator=g)
+                               .to(torch.bfloat16) for _ in range(4))
+                o = torch.empty_like(q)
+                lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+                sc = 1.0 / math.sqrt(d)
+                pairs = B * H * (N * (N + 1) // 2 if causal else N * N)
+                tf = timed(lambda: fa.fa_fwd(q, k, v, o, lse, sc, causal))
+                row = (f"| {d} | {causal} | {B} x {H} x {N} | {tf:.3f} | "
+                       f"{4 * d * pairs / tf / 1e9:.0f} | "
+                       f"{4 * d * pairs / tf / 1e9 / PEAK_BF16_TFLOPS:.1%} |")
+                ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d),
+                                 dtype=torch.uint8, device=dev)
+                dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+                fa.fa_bwd_preprocess(o, do, ws)
+                tk = timed(lambda: fa.fa_bwd_dkdv(q, k, v, do, lse, dk, dv, ws,
+                                                  sc, causal))
+                tq = timed(lambda: fa.fa_bwd_dq(q, k, v, do, lse, dq, ws, sc,
+                                                causal))
+                tb = 10 * d * pairs / (tk + tq) / 1e9
+                row += (f" {tk:.3f} | {tq:.3f} | {tb:.0f} | "
+                        f"{tb / PEAK_BF16_TFLOPS:.1%} |")
+                print(row, flush=True)
+                del q, k, v, do, o, lse, ws, dq, dk, dv
+    return 0
+
+
 def mfma_ceiling(dev, n: int = 8192, iters: int = 20) -> dict:
     """Sustained bf16 matrix-core rate of a vendor GEMM (torch.matmul, n^3)
     on iid N(0,1) operands and on constant operands.  The chip's clock under
@@ -483,6 +545,10 @@ def main(argv=None) -> int:
                     help="no GPU work: write profiles/mfma_ceiling.md from a "
                          "rocprofv3 --pmc GRBM_GUI_ACTIVE "
                          "SQ_VALU_MFMA_BUSY_CYCLES run of --ceiling-only")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the bf16 forward and backward kernels over "
+                         "sequence lengths 1K..32K at a fixed token count "
+                         "and print a markdown table")
     ap.add_argument("--command", default="",
                     help="with --traffic-from / --summarize-trace: the "
                          "command that made the CSVs")
@@ -518,6 +584,8 @@ def main(argv=None) -> int:
     if args.ceiling_only:
         print(json.dumps(mfma_ceiling(dev)), flush=True)
         return 0
+    if args.sweep:
+        return sweep(dev)
     w = S.WORKLOADS[args.workload]
     log(f"[bench] generating {w.name} inputs")
     inp = S.make_inputs(w)
