@@ -220,3 +220,28 @@ def test_dropout_workload_sampled():
         for nm, e in errs.items():
             assert e <= TOL_GRAD, (nm, e)
     assert torch.isfinite(dq).all() and torch.isfinite(dk).all()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("scale", [-0.08, 0.0])
+def test_dropout_scales(d, scale):
+    """Negative and zero scales (the sign is folded into Q or K inside the
+    kernels) with dropout, forward and backward."""
+    seed, offset = 4242, 9
+    inp = S.make_case(1, 2, 200, d, "bf16", True, seed=730 + d, backward=True,
+                      scale=scale)
+    o, lse = _fwd(inp, 0.25, seed, offset)
+    p8 = _p8(0.25)
+    ref_o, ref_l = OD.attention_dropout_fwd(inp["q"], inp["k"], inp["v"],
+                                            inp["scale"], True, p8, seed, offset)
+    eo = max_err(host64(o), ref_o, "O")
+    el = max_err(host64(lse), ref_l, "LSE")
+    dq, dk, dv = _bwd(inp, o, lse, 0.25, seed, offset)
+    ref = OD.attention_dropout_bwd(inp["q"], inp["k"], inp["v"], inp["do"],
+                                   inp["scale"], True, p8, seed, offset)
+    errs = {nm: max_err(host64(g), r, nm)
+            for nm, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref)}
+    report(f"dropout scale={scale} d{d}", O=eo, LSE=el, **errs)
+    assert eo <= TOL_BF16_O and el <= TOL_BF16_LSE
+    for nm, e in errs.items():
+        assert e <= TOL_GRAD, (nm, e)
