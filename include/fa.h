@@ -61,7 +61,7 @@ enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = -1,      /* a required pointer is NULL                     */
   FA_ERR_SHAPE = -2,     /* B, H or N <= 0, or B*H*N > 2^31-1              */
-  FA_ERR_HEADDIM = -3,   /* d is not 64 or 128 (block-sparse bwd: 128)     */
+  FA_ERR_HEADDIM = -3,   /* d is not 64 or 128                             */
   FA_ERR_ALIGN = -4,     /* a tensor pointer is not 16-byte aligned        */
   FA_ERR_WORKSPACE = -5, /* workspace NULL, too small or not 256-B aligned */
   FA_ERR_HIP = -6,       /* the HIP runtime reported a launch error        */
@@ -236,8 +236,8 @@ size_t fa_linear_workspace_size(int B, int H, int N, int d);
  * The dense backward entry points below take head dimension d = 64 or 128
  * (any other d returns FA_ERR_HEADDIM and fa_bwd_workspace_size returns 0);
  * d = 128 runs the pipelined kernels on grids that fill the chip, d = 64 the
- * 8-wavefront dK/dV and 4-wavefront dQ kernels.  The block-sparse backward
- * entry points take d = 128 only.
+ * 8-wavefront dK/dV and 4-wavefront dQ kernels (so do the block-sparse and
+ * dropout variants).
  *
  * Bytes of device workspace the backward needs: D [B,H,N] float32 (the row
  * dot products dO_i . O_i), rounded up to 256 bytes.  Returns 0 for invalid
@@ -294,7 +294,7 @@ int fa_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * 64-row query tiles whose block-mask row keeps their column; dQ workgroups
  * (one per 256-row block-mask row) visit only the kept key tiles.  Arguments as fa_bwd plus
  * block_mask as in fa_fwd_block_sparse; lse must come from
- * fa_fwd_block_sparse with the same mask.  d = 128.  Errors as fa_bwd, plus
+ * fa_fwd_block_sparse with the same mask.  d = 64 or 128.  Errors as fa_bwd, plus
  * FA_ERR_NULL for a NULL block_mask and FA_ERR_SHAPE for N > 131072.
  */
 int fa_bwd_block_sparse(const uint16_t* q, const uint16_t* k,

@@ -30,12 +30,6 @@ int check_shape(int B, int H, int N, int d) {
 // The dense backward takes head dimension 64 or 128 (as the forward).
 int check_shape_bwd(int B, int H, int N, int d) { return check_shape(B, H, N, d); }
 
-// The block-sparse backward kernels exist for head dimension 128.
-int check_shape_bwd128(int B, int H, int N, int d) {
-  const int st = check_shape(B, H, N, d);
-  if (st != FA_OK) return st;
-  return d == 128 ? FA_OK : FA_ERR_HEADDIM;
-}
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -304,7 +298,7 @@ int fa_bwd_dkdv_block_sparse(const uint16_t* q, const uint16_t* k,
                              float scale, int causal, void* stream) {
   if (!q || !k || !v || !dO || !lse || !block_mask || !dk || !dv)
     return FA_ERR_NULL;
-  int st = check_shape_bwd128(B, H, N, d);
+  int st = check_shape_bwd(B, H, N, d);
   if (st != FA_OK) return st;
   if ((N + FA_SPARSE_BK - 1) / FA_SPARSE_BK > FA_SPARSE_MAX_KEY_BLOCKS)
     return FA_ERR_SHAPE;
@@ -325,7 +319,7 @@ int fa_bwd_dq_block_sparse(const uint16_t* q, const uint16_t* k,
                            size_t workspace_bytes, int B, int H, int N, int d,
                            float scale, int causal, void* stream) {
   if (!q || !k || !v || !dO || !lse || !block_mask || !dq) return FA_ERR_NULL;
-  int st = check_shape_bwd128(B, H, N, d);
+  int st = check_shape_bwd(B, H, N, d);
   if (st != FA_OK) return st;
   if ((N + FA_SPARSE_BK - 1) / FA_SPARSE_BK > FA_SPARSE_MAX_KEY_BLOCKS)
     return FA_ERR_SHAPE;
@@ -348,7 +342,7 @@ int fa_bwd_block_sparse(const uint16_t* q, const uint16_t* k,
                         void* stream) {
   if (!q || !k || !v || !o || !dO || !lse || !block_mask || !dq || !dk || !dv)
     return FA_ERR_NULL;
-  int st = check_shape_bwd128(B, H, N, d);
+  int st = check_shape_bwd(B, H, N, d);
   if (st != FA_OK) return st;
   if ((N + FA_SPARSE_BK - 1) / FA_SPARSE_BK > FA_SPARSE_MAX_KEY_BLOCKS)
     return FA_ERR_SHAPE;

@@ -97,13 +97,14 @@ constexpr int kBQ2 = 64;   // query rows per tile
 // plus an immediate offset.
 constexpr int kRS = 152;   // K, V, Q, dO row stride
 
-template <int D, bool CAUSAL, bool DROP = false>
+template <int D, bool CAUSAL, bool DROP = false, bool SPARSE = false>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dv,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kblk,
-    float c_log2, float scale, Dropout drop) {
+    float c_log2, float scale, Dropout drop, const uint8_t* __restrict__ bmask,
+    int H) {
   static_assert(D == 64 || D == 128, "head dimension");
   constexpr int KB = kBK * kRS;        // elements of the K (or V) block
   constexpr int QB = kBQ2 * kRS;       // elements of a Q (or dO) tile
@@ -175,6 +176,39 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   const int n_qt = (N + kBQ2 - 1) / kBQ2;
   const int it0 = CAUSAL ? kb0 / kBQ2 : 0;
 
+  // Query tiles to visit: it0 .. n_qt - 1, or (block-sparse: the 128 keys
+  // are one block-mask column) the 64-row tiles whose block row keeps the
+  // column, listed in LDS.
+  __shared__ uint16_t qt_list[SPARSE ? kSparseMaxTiles : 1];
+  __shared__ int qt_count;
+  int n_vis = n_qt - it0;
+  if constexpr (SPARSE) {
+    const int n_mk = (N + FA_SPARSE_BK - 1) / FA_SPARSE_BK;
+    const int n_mq = (N + FA_SPARSE_BQ - 1) / FA_SPARSE_BQ;
+    const uint8_t* mcol = bmask + (size_t)(bh % H) * n_mq * n_mk + jb;
+    if (w == 0) {
+      int cnt = 0;
+      for (int base = it0; base < n_qt; base += 64) {
+        const int q = base + lane;
+        const bool keep =
+            q < n_qt && mcol[(size_t)(q * kBQ2 / FA_SPARSE_BQ) * n_mk] != 0;
+        const unsigned long long bal = __ballot(keep);
+        const int below = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+        if (keep) qt_list[cnt + below] = (uint16_t)q;
+        cnt += __builtin_popcountll(bal);
+      }
+      if (lane == 0) qt_count = cnt;
+    }
+    __syncthreads();
+    n_vis = qt_count;
+  }
+  auto qtile = [&](int i) -> int {
+    if constexpr (SPARSE)
+      return (int)__builtin_amdgcn_readfirstlane((unsigned)qt_list[i]);
+    else
+      return it0 + i;
+  };
+
 
   // Query-tile staging: QCH 16-byte chunks of Q and of dO per thread, plus
   // LSE / D.  Rows past N load row N-1 (in bounds) and are replaced by zeros
@@ -227,14 +261,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     }
   };
 
-  if (it0 < n_qt) load_qtile(it0);
-  for (int it = it0; it < n_qt; ++it) {
-    const int buf = (it - it0) & 1;
+  if (n_vis > 0) load_qtile(qtile(0));
+  for (int i = 0; i < n_vis; ++i) {
+    const int it = qtile(i);
+    const int buf = i & 1;
     store_qtile(buf);
     // Q_i, dO_i, LSE, D (and K, V) ready; also every wavefront has finished
     // reading the other buffer, which the next iteration overwrites.
     __syncthreads();
-    if (it + 1 < n_qt) load_qtile(it + 1);
+    if (i + 1 < n_vis) load_qtile(qtile(i + 1));
     const uint16_t* lds_q = lds_q0 + (buf ? qbuf : 0);
     const uint16_t* lds_do = lds_q + dooff;
     const float* lse_t = lds_lse[buf];
@@ -393,15 +428,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
 // dQ^T += K^T dS^T with K^T read transposed from LDS.  No atomics: dQ is
 // written once, deterministically.
 constexpr int kDqBR = 128;
+static_assert(FA_SPARSE_BQ % kDqBR == 0, "a dQ block lies in one block-mask row");
 constexpr int kDqBC = 64;
 
-template <int D, bool CAUSAL, bool DROP = false>
+template <int D, bool CAUSAL, bool DROP = false, bool SPARSE = false>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dv,
     uint16_t* __restrict__ dQ, int N, int n_qblk, float c_log2,
-    float scale, Dropout drop) {
+    float scale, Dropout drop, const uint8_t* __restrict__ bmask, int H) {
   static_assert(D == 64 || D == 128, "head dimension");
   constexpr int TE = kDqBC * kRS;      // elements per K (or V) tile buffer
   constexpr int CPT = kDqBC * D / 8 / kThreads;   // 16-byte chunks per thread
@@ -433,7 +469,43 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
   int kend = N;
   if (CAUSAL) kend = min(kend, q0 + kDqBR);
-  const int ntiles = (kend + kDqBC - 1) / kDqBC;
+  const int ntiles_dense = (kend + kDqBC - 1) / kDqBC;
+
+  // Key tiles to visit: 0 .. ntiles_dense - 1, or (block-sparse: the
+  // 128-row block lies in one 256-row block-mask row) the two 64-key tiles
+  // of each kept 128-key mask column, the columns listed in LDS; a tile
+  // past ntiles_dense is loaded clamped and not computed.
+  __shared__ uint16_t col_list[SPARSE ? FA_SPARSE_MAX_KEY_BLOCKS : 1];
+  __shared__ int col_count;
+  int ntiles = ntiles_dense;
+  if constexpr (SPARSE) {
+    const int n_mk = (N + FA_SPARSE_BK - 1) / FA_SPARSE_BK;
+    const int n_mq = (N + FA_SPARSE_BQ - 1) / FA_SPARSE_BQ;
+    const int n_cols = (ntiles_dense + 1) / 2;
+    const uint8_t* mrow =
+        bmask + ((size_t)(bh % H) * n_mq + q0 / FA_SPARSE_BQ) * n_mk;
+    if (w == 0) {
+      int cnt = 0;
+      for (int base = 0; base < n_cols; base += 64) {
+        const int cidx = base + lane;
+        const bool keep = cidx < n_cols && mrow[cidx] != 0;
+        const unsigned long long bal = __ballot(keep);
+        const int below = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+        if (keep) col_list[cnt + below] = (uint16_t)cidx;
+        cnt += __builtin_popcountll(bal);
+      }
+      if (lane == 0) col_count = cnt;
+    }
+    __syncthreads();
+    ntiles = 2 * col_count;
+  }
+  // Key tile of position t (possibly >= ntiles_dense when sparse).
+  auto ktile = [&](int t) -> int {
+    if constexpr (SPARSE)
+      return 2 * (int)__builtin_amdgcn_readfirstlane((unsigned)col_list[t >> 1]) + (t & 1);
+    else
+      return t;
+  };
 
   // Q and dO fragments of this lane's query (B operands), LSE and D.
   bf16x8 qf[D / 16], gf[D / 16];
@@ -488,12 +560,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) dq_acc[i] = f32x16{};
 
-  if (ntiles > 0) load_tile(0);
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
+  if (ntiles > 0) load_tile(min(ktile(0), ntiles_dense - 1));
+  for (int t = 0; t < ntiles; ++t) {
+    const int j = ktile(t);
+    const int buf = t & 1;
     store_tile(buf);
     __syncthreads();
-    if (j + 1 < ntiles) load_tile(j + 1);
+    if (t + 1 < ntiles) load_tile(min(ktile(t + 1), ntiles_dense - 1));
+    if (SPARSE && j >= ntiles_dense) continue;   // second tile past the end
     const int k0 = j * kDqBC;
     if (CAUSAL && k0 > qw1) continue;     // tile wholly in this wave's future
     const uint16_t* kt = smem + (buf ? buf1 : 0);
@@ -1415,7 +1489,7 @@ int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     int B, int H, int N, int d, float scale, int causal,
                     const Dropout* drop, hipStream_t stream) {
   if (d != kD && d != 64) return -3;
-  if (d != kD && block_mask != nullptr) return -3;
+  if (d != kD && block_mask != nullptr && drop != nullptr) return -3;
   const int n_kblk = (N + kBK - 1) / kBK;
   const float c = (float)((double)scale * 1.4426950408889634);
   // Head dim 128 on grids with at least one 128-key workgroup per CU, and
@@ -1447,16 +1521,26 @@ int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   const dim3 grid((unsigned)(B * H * n_kblk)), block(kBwdThreads);
 #define FA_DKDV_PLAIN(DD, CC)                                                  \
   hipLaunchKernelGGL((bwd_dkdv_kernel<DD, CC>), grid, block, 0, stream, q, k,   \
-                     v, dO, lse, D, dk, dv, N, n_kblk, c, scale, Dropout{})
+                     v, dO, lse, D, dk, dv, N, n_kblk, c, scale, Dropout{},     \
+                     nullptr, H)
   if (d == 64 && drop != nullptr) {
     if (causal)
       hipLaunchKernelGGL((bwd_dkdv_kernel<64, true, true>), grid, block, 0,
                          stream, q, k, v, dO, lse, D, dk, dv, N, n_kblk, c,
-                         scale, *drop);
+                         scale, *drop, nullptr, H);
     else
       hipLaunchKernelGGL((bwd_dkdv_kernel<64, false, true>), grid, block, 0,
                          stream, q, k, v, dO, lse, D, dk, dv, N, n_kblk, c,
-                         scale, *drop);
+                         scale, *drop, nullptr, H);
+  } else if (d == 64 && block_mask != nullptr) {
+    if (causal)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<64, true, false, true>), grid, block,
+                         0, stream, q, k, v, dO, lse, D, dk, dv, N, n_kblk, c,
+                         scale, Dropout{}, block_mask, H);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<64, false, false, true>), grid,
+                         block, 0, stream, q, k, v, dO, lse, D, dk, dv, N,
+                         n_kblk, c, scale, Dropout{}, block_mask, H);
   } else if (d == 64) {
     if (causal) FA_DKDV_PLAIN(64, true); else FA_DKDV_PLAIN(64, false);
   } else {
@@ -1472,7 +1556,7 @@ int launch_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   int d, float scale, int causal, const Dropout* drop,
                   hipStream_t stream) {
   if (d != kD && d != 64) return -3;
-  if (d != kD && block_mask != nullptr) return -3;
+  if (d != kD && block_mask != nullptr && drop != nullptr) return -3;
   const float c = (float)((double)scale * 1.4426950408889634);
   // Head dim 128 on grids with at least one 256-row workgroup per CU, and
   // every block-sparse call (a workgroup is one block-mask row) or dropout
@@ -1505,16 +1589,25 @@ int launch_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   const dim3 grid((unsigned)(B * H * n_qblk)), block(kThreads);
 #define FA_DQ_PLAIN(DD, CC)                                                    \
   hipLaunchKernelGGL((bwd_dq_kernel<DD, CC>), grid, block, 0, stream, q, k, v,  \
-                     dO, lse, D, dq, N, n_qblk, c, scale, Dropout{})
+                     dO, lse, D, dq, N, n_qblk, c, scale, Dropout{}, nullptr, H)
   if (d == 64 && drop != nullptr) {
     if (causal)
       hipLaunchKernelGGL((bwd_dq_kernel<64, true, true>), grid, block, 0,
                          stream, q, k, v, dO, lse, D, dq, N, n_qblk, c, scale,
-                         *drop);
+                         *drop, nullptr, H);
     else
       hipLaunchKernelGGL((bwd_dq_kernel<64, false, true>), grid, block, 0,
                          stream, q, k, v, dO, lse, D, dq, N, n_qblk, c, scale,
-                         *drop);
+                         *drop, nullptr, H);
+  } else if (d == 64 && block_mask != nullptr) {
+    if (causal)
+      hipLaunchKernelGGL((bwd_dq_kernel<64, true, false, true>), grid, block, 0,
+                         stream, q, k, v, dO, lse, D, dq, N, n_qblk, c, scale,
+                         Dropout{}, block_mask, H);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<64, false, false, true>), grid, block,
+                         0, stream, q, k, v, dO, lse, D, dq, N, n_qblk, c,
+                         scale, Dropout{}, block_mask, H);
   } else if (d == 64) {
     if (causal) FA_DQ_PLAIN(64, true); else FA_DQ_PLAIN(64, false);
   } else {

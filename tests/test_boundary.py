@@ -121,7 +121,7 @@ def test_block_sparse_bwd_argument_errors():
         p = [A] * 10
         p[i] = None
         assert sb(p) == NULL, i
-    assert sb(d=64) == HEADDIM
+    assert sb(d=96) == HEADDIM
     assert sb(N=64 * 2048 + 1, wsb=1 << 40) == SHAPE
     assert sb(ws=None) == WORKSPACE
     p = [A] * 10
@@ -132,7 +132,7 @@ def test_block_sparse_bwd_argument_errors():
     assert L.fa_bwd_dq_block_sparse(A, A, A, A, A, A, A, W, 0, 1, 2, 64, 128,
                                     0.1, 1, None) == WORKSPACE
     assert L.fa_bwd_dq_block_sparse(A, A, A, A, A, A, A, W, nbytes, 1, 2, 64,
-                                    64, 0.1, 1, None) == HEADDIM
+                                    96, 0.1, 1, None) == HEADDIM
 
 
 def test_workspace_size():

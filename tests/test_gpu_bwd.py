@@ -103,15 +103,14 @@ def test_bwd_gpt2_shape_d64():
 
 
 def test_bwd_rejects_unsupported_head_dims():
-    """d = 96 has no kernel; the block-sparse backward takes d = 128 only.
-    Rejected before any launch."""
+    """d = 96 has no kernel, dense, block-sparse or with dropout: rejected
+    before any launch."""
     import torch
     import io_aware_tiled_amd as fa
     q = torch.zeros(1, 1, 64, 96, dtype=torch.bfloat16, device="cuda:0")
     lse = torch.zeros(1, 1, 64, dtype=torch.float32, device="cuda:0")
     with pytest.raises(fa.FAError):
         fa.backward(q, q, q, q, lse, q)
-    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16, device="cuda:0")
     m = torch.ones(1, 1, 1, dtype=torch.uint8, device="cuda:0")
     with pytest.raises(fa.FAError):
         fa.backward(q, q, q, q, lse, q, block_mask=m)

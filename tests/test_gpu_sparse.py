@@ -144,13 +144,47 @@ def _check_bwd(name, inp, mask, heads=None):
     return dq, dk, dv
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [64, 300, 1000])
-def test_sparse_bwd_small(causal, N):
-    inp = S.make_case(2, 3, N, 128, "bf16", causal, seed=60 + N,
+def test_sparse_bwd_small(d, causal, N):
+    inp = S.make_case(2, 3, N, d, "bf16", causal, seed=60 + N + d,
                       backward=True)
-    _check_bwd(f"sparse bwd causal={causal} N={N}", inp,
+    _check_bwd(f"sparse bwd d{d} causal={causal} N={N}", inp,
                _mask(N + 7, 3, N, 0.4))
+
+
+def test_sparse_bwd_d64_alternate_columns_and_empty_rows():
+    """Head dim 64 (the 8-wavefront dK/dV and 4-wavefront dQ kernels with
+    tile lists): a key column no query keeps gets dK = dV = 0, a block row
+    with no kept block dQ = 0."""
+    N, H = 640, 2
+    tq, tk = -(-N // 256), -(-N // 128)
+    m = np.zeros((H, tq, tk), dtype=np.uint8)
+    m[0, :, 0::2] = 1
+    m[1, :, 1::2] = 1
+    m[1, 1, :] = 0
+    inp = S.make_case(1, H, N, 64, "bf16", True, seed=64, backward=True)
+    dq, dk, dv = _check_bwd("sparse bwd d64 columns/rows", inp, m)
+    assert float(dk[0, 0, 128:256].float().abs().max()) == 0.0
+    assert float(dv[0, 1, 0:128].float().abs().max()) == 0.0
+    assert float(dq[0, 1, 256:512].float().abs().max()) == 0.0
+
+
+def test_sparse_bwd_d64_all_ones_equals_dense_bitwise():
+    """At head dim 64 both calls take the same non-pipelined kernels."""
+    import torch
+    import io_aware_tiled_amd as fa
+    inp = S.make_case(2, 4, 700, 64, "bf16", True, seed=65, backward=True)
+    q, k, v, do = (to_dev(inp, n) for n in ("q", "k", "v", "do"))
+    o, lse = fa.forward(q, k, v, causal=True, scale=inp["scale"])
+    ones = torch.ones((4, 3, 6), dtype=torch.uint8, device=DEV)
+    g_sparse = fa.backward(q, k, v, o, lse, do, causal=True,
+                           scale=inp["scale"], block_mask=ones)
+    g_dense = fa.backward(q, k, v, o, lse, do, causal=True, scale=inp["scale"])
+    torch.cuda.synchronize()
+    for a, b in zip(g_sparse, g_dense):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 def test_sparse_bwd_alternate_columns():
