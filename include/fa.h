@@ -266,6 +266,21 @@ int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
            size_t workspace_bytes, int B, int H, int N, int d, float scale,
            int causal, void* stream);
 
+/*
+ * Backward of fa_fwd_kvlen (key padding, the BERT-shaped workload): the
+ * gradients of fa_bwd with key j of batch entry b visible only while
+ * j < kv_len[b] (kv_len device int32 [B], values clamped to [0, N]; NULL
+ * means N).  Keys at or past kv_len get dK = dV = 0; a query row with no
+ * visible key gets dQ = 0.  o and lse must come from fa_fwd_kvlen with the
+ * same kv_len.  Arguments otherwise as fa_bwd; errors as fa_bwd, plus
+ * FA_ERR_ALIGN for a kv_len pointer that is not 4-byte aligned.
+ */
+int fa_bwd_kvlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                 const uint16_t* o, const uint16_t* dO, const float* lse,
+                 const int32_t* kv_len, uint16_t* dq, uint16_t* dk,
+                 uint16_t* dv, void* workspace, size_t workspace_bytes, int B,
+                 int H, int N, int d, float scale, int causal, void* stream);
+
 /* Backward stage 1: D_i = dO_i . O_i (float32) into the workspace. */
 int fa_bwd_preprocess(const uint16_t* o, const uint16_t* dO, void* workspace,
                       size_t workspace_bytes, int B, int H, int N, int d,

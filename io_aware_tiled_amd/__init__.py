@@ -26,7 +26,7 @@ import os
 __all__ = [
     "FAError", "lib", "lib_path", "fa_version", "fa_status_string",
     "fa_fwd", "fa_fwd_kvlen", "fa_fwd_f32", "fa_bwd_workspace_size",
-    "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
+    "fa_bwd", "fa_bwd_kvlen", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
     "fa_fwd_block_sparse", "fa_bwd_block_sparse", "fa_bwd_dkdv_block_sparse",
     "fa_bwd_dq_block_sparse", "fa_fp8_workspace_size",
     "fa_fp8_quantize",
@@ -58,6 +58,7 @@ _SIGS = {
     "fa_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_workspace_size": (_S, [_I, _I, _I, _I]),
     "fa_bwd": (_I, [_P] * 10 + [_S, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_bwd_kvlen": (_I, [_P] * 11 + [_S, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_preprocess": (_I, [_P, _P, _P, _S, _I, _I, _I, _I, _P]),
     "fa_bwd_dkdv": (_I, [_P] * 8 + [_S, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_dq": (_I, [_P] * 7 + [_S, _I, _I, _I, _I, _F, _I, _P]),
@@ -236,6 +237,28 @@ def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, workspace, scale, causal,
                       _ptr(dq), _ptr(dk), _ptr(dv), wp, wn, B, H, N, d,
                       float(scale), int(bool(causal)), _stream(q, stream))
     _check(st, "fa_bwd")
+
+
+def fa_bwd_kvlen(q, k, v, o, dO, lse, kv_len, dq, dk, dv, workspace, scale,
+                 causal, stream=None):
+    """C fa_bwd_kvlen: backward of fa_fwd_kvlen (kv_len: device int32 [B]
+    or None)."""
+    import torch
+    B, H, N, d = _bhnd(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO"),
+                 (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _expect(t, torch.bfloat16, (B, H, N, d), n)
+    _expect(lse, torch.float32, (B, H, N), "lse")
+    kp = None
+    if kv_len is not None:
+        _expect(kv_len, torch.int32, (B,), "kv_len")
+        kp = _ptr(kv_len)
+    wp, wn = _ws(workspace)
+    st = lib().fa_bwd_kvlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO),
+                            _ptr(lse), kp, _ptr(dq), _ptr(dk), _ptr(dv), wp, wn,
+                            B, H, N, d, float(scale), int(bool(causal)),
+                            _stream(q, stream))
+    _check(st, "fa_bwd_kvlen")
 
 
 def fa_bwd_block_sparse(q, k, v, o, dO, lse, block_mask, dq, dk, dv,
@@ -527,9 +550,9 @@ def linear_forward(q, k, v, *, scale=None, stream=None):
 
 
 def backward(q, k, v, o, lse, dO, *, causal=False, scale=None, stream=None,
-             workspace=None, block_mask=None):
+             workspace=None, block_mask=None, kv_len=None):
     """Returns (dq, dk, dv) for the bf16 forward (fa_bwd_block_sparse when a
-    block mask is given)."""
+    block mask is given, fa_bwd_kvlen with key lengths)."""
     import torch
     B, H, N, d = _bhnd(q)
     if scale is None:
@@ -543,8 +566,13 @@ def backward(q, k, v, o, lse, dO, *, causal=False, scale=None, stream=None,
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     if block_mask is not None:
+        if kv_len is not None:
+            raise ValueError("fa_bwd_block_sparse has no key padding")
         fa_bwd_block_sparse(q, k, v, o, dO, lse, block_mask, dq, dk, dv,
                             workspace, scale, causal, stream)
+    elif kv_len is not None:
+        fa_bwd_kvlen(q, k, v, o, dO, lse, kv_len, dq, dk, dv, workspace,
+                     scale, causal, stream)
     else:
         fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, workspace, scale, causal,
                stream)

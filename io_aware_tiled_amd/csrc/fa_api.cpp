@@ -246,7 +246,7 @@ int fa_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   if (st != FA_OK) return st;
   return fa::launch_bwd_dkdv(q, k, v, dO, lse, (const float*)workspace,
                              nullptr, dk, dv, B, H, N, d, scale, causal != 0,
-                             nullptr, (hipStream_t)stream);
+                             nullptr, nullptr, (hipStream_t)stream);
 }
 
 int fa_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -263,7 +263,7 @@ int fa_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   if (st != FA_OK) return st;
   return fa::launch_bwd_dq(q, k, v, dO, lse, (const float*)workspace, nullptr,
                            dq, B, H, N, d, scale, causal != 0, nullptr,
-                           (hipStream_t)stream);
+                           nullptr, (hipStream_t)stream);
 }
 
 int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -290,6 +290,33 @@ int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                    d, scale, causal, stream);
 }
 
+int fa_bwd_kvlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                 const uint16_t* o, const uint16_t* dO, const float* lse,
+                 const int32_t* kv_len, uint16_t* dq, uint16_t* dk,
+                 uint16_t* dv, void* workspace, size_t workspace_bytes, int B,
+                 int H, int N, int d, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv)
+    return FA_ERR_NULL;
+  int st = check_shape_bwd(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(dO) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv) || ((uintptr_t)kv_len & 3u) != 0)
+    return FA_ERR_ALIGN;
+  st = check_workspace(workspace, workspace_bytes, B, H, N);
+  if (st != FA_OK) return st;
+  st = fa_bwd_preprocess(o, dO, workspace, workspace_bytes, B, H, N, d, stream);
+  if (st != FA_OK) return st;
+  st = fa::launch_bwd_dkdv(q, k, v, dO, lse, (const float*)workspace, nullptr,
+                           dk, dv, B, H, N, d, scale, causal != 0, nullptr,
+                           kv_len, (hipStream_t)stream);
+  if (st != FA_OK) return FA_ERR_HIP;
+  st = fa::launch_bwd_dq(q, k, v, dO, lse, (const float*)workspace, nullptr,
+                         dq, B, H, N, d, scale, causal != 0, nullptr, kv_len,
+                         (hipStream_t)stream);
+  return st == 0 ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_bwd_dkdv_block_sparse(const uint16_t* q, const uint16_t* k,
                              const uint16_t* v, const uint16_t* dO,
                              const float* lse, const uint8_t* block_mask,
@@ -309,7 +336,7 @@ int fa_bwd_dkdv_block_sparse(const uint16_t* q, const uint16_t* k,
   if (st != FA_OK) return st;
   return fa::launch_bwd_dkdv(q, k, v, dO, lse, (const float*)workspace,
                              block_mask, dk, dv, B, H, N, d, scale,
-                             causal != 0, nullptr, (hipStream_t)stream);
+                             causal != 0, nullptr, nullptr, (hipStream_t)stream);
 }
 
 int fa_bwd_dq_block_sparse(const uint16_t* q, const uint16_t* k,
@@ -330,7 +357,7 @@ int fa_bwd_dq_block_sparse(const uint16_t* q, const uint16_t* k,
   if (st != FA_OK) return st;
   return fa::launch_bwd_dq(q, k, v, dO, lse, (const float*)workspace,
                            block_mask, dq, B, H, N, d, scale, causal != 0,
-                           nullptr, (hipStream_t)stream);
+                           nullptr, nullptr, (hipStream_t)stream);
 }
 
 int fa_bwd_block_sparse(const uint16_t* q, const uint16_t* k,
@@ -400,7 +427,7 @@ int fa_bwd_dkdv_dropout(const uint16_t* q, const uint16_t* k,
   if (st != FA_OK) return st;
   return fa::launch_bwd_dkdv(q, k, v, dO, lse, (const float*)workspace,
                              nullptr, dk, dv, B, H, N, d, scale, causal != 0,
-                             &drop, (hipStream_t)stream);
+                             &drop, nullptr, (hipStream_t)stream);
 }
 
 int fa_bwd_dq_dropout(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -422,7 +449,7 @@ int fa_bwd_dq_dropout(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   if (st != FA_OK) return st;
   return fa::launch_bwd_dq(q, k, v, dO, lse, (const float*)workspace, nullptr,
                            dq, B, H, N, d, scale, causal != 0, &drop,
-                           (hipStream_t)stream);
+                           nullptr, (hipStream_t)stream);
 }
 
 int fa_bwd_dropout(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const float* __restrict__ LSE, const float* __restrict__ Dv,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kblk,
     float c_log2, float scale, Dropout drop, const uint8_t* __restrict__ bmask,
-    int H) {
+    int H, const int32_t* __restrict__ kv_len = nullptr) {
   static_assert(D == 64 || D == 128, "head dimension");
   constexpr int KB = kBK * kRS;        // elements of the K (or V) block
   constexpr int QB = kBQ2 * kRS;       // elements of a Q (or dO) tile
@@ -174,6 +174,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   }
 
   const int n_qt = (N + kBQ2 - 1) / kBQ2;
+  // Key padding: keys >= kv_len[b] are masked (a block wholly past it
+  // visits no query tile and writes dK = dV = 0).
+  const int kvlim = kv_len ? min(max(kv_len[bh / H], 0), N) : N;
   const int it0 = CAUSAL ? kb0 / kBQ2 : 0;
 
   // Query tiles to visit: it0 .. n_qt - 1, or (block-sparse: the 128 keys
@@ -202,6 +205,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     __syncthreads();
     n_vis = qt_count;
   }
+  if (kb0 >= kvlim) n_vis = 0;
   auto qtile = [&](int i) -> int {
     if constexpr (SPARSE)
       return (int)__builtin_amdgcn_readfirstlane((unsigned)qt_list[i]);
@@ -295,7 +299,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     }
     // ---- P = exp2(s*c - lse2), dS = P (dP - D).  Register r holds query
     // qw0 + 8(r/4) + 4hh + r%4 of this lane's key.
-    const bool need_mask = (CAUSAL && wk0 + 31 > qw0) || (wk0 + 32 > N);
+    const bool need_mask = (CAUSAL && wk0 + 31 > qw0) || (wk0 + 32 > kvlim);
     // Dropout: kz[g] holds the keep bytes of rows qw0 + 8g + 4hh + e (byte
     // e) for this lane's key: quad lane w makes the generator call of row
     // group w, transposes its bytes to key-major order, and the quad
@@ -329,7 +333,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
           float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l4[e]));
           if (need_mask) {
             const int q = qw0 + 8 * g + 4 * hh + e;
-            if ((CAUSAL && mykey > q) || mykey >= N) p = 0.f;
+            if ((CAUSAL && mykey > q) || mykey >= kvlim) p = 0.f;
           }
           if constexpr (DROP) {
             const bool kept = drop_keep(kz[g], e, drop.p8);
@@ -437,7 +441,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dv,
     uint16_t* __restrict__ dQ, int N, int n_qblk, float c_log2,
-    float scale, Dropout drop, const uint8_t* __restrict__ bmask, int H) {
+    float scale, Dropout drop, const uint8_t* __restrict__ bmask, int H,
+    const int32_t* __restrict__ kv_len = nullptr) {
   static_assert(D == 64 || D == 128, "head dimension");
   constexpr int TE = kDqBC * kRS;      // elements per K (or V) tile buffer
   constexpr int CPT = kDqBC * D / 8 / kThreads;   // 16-byte chunks per thread
@@ -467,7 +472,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const uint16_t* Vh = V + head;
   const uint16_t* dOh = dO + head;
 
-  int kend = N;
+  // Key padding: keys >= kv_len[b] are masked and not loaded past.
+  const int kvlim = kv_len ? min(max(kv_len[bh / H], 0), N) : N;
+  int kend = kvlim;
   if (CAUSAL) kend = min(kend, q0 + kDqBR);
   const int ntiles_dense = (kend + kDqBC - 1) / kDqBC;
 
@@ -588,7 +595,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     }
     // ---- P^T and dS^T in-lane; register r of block kb holds key
     // k0 + 32kb + 8(r/4) + 4hh + r%4 for this lane's query.
-    const bool need_mask = (CAUSAL && k0 + kDqBC - 1 > qw0) || (k0 + kDqBC > N);
+    const bool need_mask = (CAUSAL && k0 + kDqBC - 1 > qw0) || (k0 + kDqBC > kvlim);
     bf16x8 dsb[2][2];
     const float ik = DROP ? 256.f / (float)(256 - drop.p8) : 1.f;
 #pragma unroll
@@ -615,7 +622,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
           float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c_log2, -lse2));
           if (need_mask) {
             const int key = k0 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
-            if ((CAUSAL && key > qrow) || key >= N) p = 0.f;
+            if ((CAUSAL && key > qrow) || key >= kvlim) p = 0.f;
           }
           if constexpr (DROP)
             x[e] = p * ((drop_keep(kz[r / 4], r % 4, drop.p8) ? dp[kb][r] * ik : 0.f) - dd);
@@ -690,7 +697,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
     const float* __restrict__ LSE, const float* __restrict__ Dv,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
     const uint8_t* __restrict__ bmask, int H, int N, int n_kblk,
-    float c_log2, float scale, Dropout drop) {
+    float c_log2, float scale, Dropout drop,
+    const int32_t* __restrict__ kv_len = nullptr) {
   constexpr int D = kD;
   constexpr int QE = kBQ2 * kRS;                 // elements per tile stage
   constexpr int THREADS = 256;
@@ -741,6 +749,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
   c_log2 = fmaxf(c_log2, 1e-30f);
 
   const int n_qt = (N + kBQ2 - 1) / kBQ2;
+  // Key padding: keys >= kv_len[b] are masked (a block wholly past it
+  // visits no query tile and writes dK = dV = 0).
+  const int kvlim = kv_len ? min(max(kv_len[bh / H], 0), N) : N;
   const int it0 = CAUSAL ? kb0 / kBQ2 : 0;
 
   // ---- query tiles to visit.  Dense: it0 .. n_qt - 1.  Block-sparse: the
@@ -769,6 +780,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
     __syncthreads();
     n_vis = qt_count;
   }
+  if (kb0 >= kvlim) n_vis = 0;
   // Query tile of visit i (clamped; it0 + i when dense).
   auto qtile = [&](int i) -> int {
     if constexpr (SPARSE)
@@ -983,12 +995,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
   // past N; rows past N already have P = 0 through LSE = +inf).
   auto mask_block = [&](int c, int qt) {
     const int qb0 = qt * kBQ2 + 32 * c;
-    const bool need_mask = (CAUSAL && wk0 + 31 > qb0) || (wk0 + 32 > N);
+    const bool need_mask = (CAUSAL && wk0 + 31 > qb0) || (wk0 + 32 > kvlim);
     if (need_mask) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int q = qb0 + 8 * (r / 4) + 4 * hh + (r % 4);
-        if ((CAUSAL && mykey > q) || mykey >= N) s[c][r] = -INFINITY;
+        if ((CAUSAL && mykey > q) || mykey >= kvlim) s[c][r] = -INFINITY;
       }
     }
   };
@@ -1124,7 +1136,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dv,
     uint16_t* __restrict__ dQ, const uint8_t* __restrict__ bmask, int H,
-    int N, int n_qblk, float c_log2, float scale, Dropout drop) {
+    int N, int n_qblk, float c_log2, float scale, Dropout drop,
+    const int32_t* __restrict__ kv_len = nullptr) {
   static_assert(!SPARSE || kDqPBR == FA_SPARSE_BQ, "a workgroup is a mask row");
   constexpr int D = kD;
   constexpr int TE = kDqBC * kRS;                 // elements per tile stage
@@ -1147,10 +1160,12 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
   const int qlo = q0 + 32 * w;
   const int qrow = qlo + lq;
 
-  int kend = N;
+  // Key padding: keys >= kv_len[b] are masked and not loaded past.
+  const int kvlim = kv_len ? min(max(kv_len[bh / H], 0), N) : N;
+  int kend = kvlim;
   if (CAUSAL) kend = min(kend, q0 + kDqPBR);
   int ntiles = (kend + kDqBC - 1) / kDqBC;
-  int kend_w = N;
+  int kend_w = kvlim;
   if (CAUSAL) kend_w = min(kend_w, qlo + 32);
   int nt_w = (kend_w + kDqBC - 1) / kDqBC;
 
@@ -1384,12 +1399,12 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
   // ---- mask the half-tile (j, kb) held in parity x where needed.
   auto mask_half = [&](int x, int j, int kb) {
     const int k0 = j * kDqBC + 32 * kb;
-    const bool need_mask = (CAUSAL && k0 + 31 > qlo) || (k0 + 32 > N);
+    const bool need_mask = (CAUSAL && k0 + 31 > qlo) || (k0 + 32 > kvlim);
     if (need_mask) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + 8 * (r / 4) + 4 * hh + (r % 4);
-        if ((CAUSAL && key > qrow) || key >= N) s[x][r] = -INFINITY;
+        if ((CAUSAL && key > qrow) || key >= kvlim) s[x][r] = -INFINITY;
       }
     }
   };
@@ -1487,7 +1502,8 @@ int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const uint16_t* dO, const float* lse, const float* D,
                     const uint8_t* block_mask, uint16_t* dk, uint16_t* dv,
                     int B, int H, int N, int d, float scale, int causal,
-                    const Dropout* drop, hipStream_t stream) {
+                    const Dropout* drop, const int32_t* kv_len,
+                    hipStream_t stream) {
   if (d != kD && d != 64) return -3;
   if (d != kD && block_mask != nullptr && drop != nullptr) return -3;
   const int n_kblk = (N + kBK - 1) / kBK;
@@ -1502,7 +1518,7 @@ int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 #define FA_DKDV_LAUNCH(CC, SS)                                                  \
   hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<CC, SS>), grid, block, 0, stream, q, \
                      k, v, dO, lse, D, dk, dv, block_mask, H, N, n_kblk, c,     \
-                     scale, Dropout{})
+                     scale, Dropout{}, kv_len)
 #define FA_DKDV_DROP(CC)                                                       \
   hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<CC, false, true>), grid, block, 0,  \
                      stream, q, k, v, dO, lse, D, dk, dv, nullptr, H, N,       \
@@ -1522,7 +1538,7 @@ int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 #define FA_DKDV_PLAIN(DD, CC)                                                  \
   hipLaunchKernelGGL((bwd_dkdv_kernel<DD, CC>), grid, block, 0, stream, q, k,   \
                      v, dO, lse, D, dk, dv, N, n_kblk, c, scale, Dropout{},     \
-                     nullptr, H)
+                     nullptr, H, kv_len)
   if (d == 64 && drop != nullptr) {
     if (causal)
       hipLaunchKernelGGL((bwd_dkdv_kernel<64, true, true>), grid, block, 0,
@@ -1554,7 +1570,7 @@ int launch_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   const uint16_t* dO, const float* lse, const float* D,
                   const uint8_t* block_mask, uint16_t* dq, int B, int H, int N,
                   int d, float scale, int causal, const Dropout* drop,
-                  hipStream_t stream) {
+                  const int32_t* kv_len, hipStream_t stream) {
   if (d != kD && d != 64) return -3;
   if (d != kD && block_mask != nullptr && drop != nullptr) return -3;
   const float c = (float)((double)scale * 1.4426950408889634);
@@ -1569,7 +1585,7 @@ int launch_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 #define FA_DQ_LAUNCH(CC, SS)                                                  \
   hipLaunchKernelGGL((bwd_dq_pipe_kernel<CC, SS>), grid, block, 0, stream, q, \
                      k, v, dO, lse, D, dq, block_mask, H, N, n_qblk, c, scale, \
-                     Dropout{})
+                     Dropout{}, kv_len)
 #define FA_DQ_DROP(CC)                                                        \
   hipLaunchKernelGGL((bwd_dq_pipe_kernel<CC, false, true>), grid, block, 0,   \
                      stream, q, k, v, dO, lse, D, dq, nullptr, H, N, n_qblk,  \
@@ -1589,7 +1605,8 @@ int launch_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   const dim3 grid((unsigned)(B * H * n_qblk)), block(kThreads);
 #define FA_DQ_PLAIN(DD, CC)                                                    \
   hipLaunchKernelGGL((bwd_dq_kernel<DD, CC>), grid, block, 0, stream, q, k, v,  \
-                     dO, lse, D, dq, N, n_qblk, c, scale, Dropout{}, nullptr, H)
+                     dO, lse, D, dq, N, n_qblk, c, scale, Dropout{}, nullptr, H, \
+                     kv_len)
   if (d == 64 && drop != nullptr) {
     if (causal)
       hipLaunchKernelGGL((bwd_dq_kernel<64, true, true>), grid, block, 0,

@@ -36,18 +36,20 @@ int launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, float* D,
                           int B, int H, int N, int d, hipStream_t stream);
 
 // block_mask: device uint8 [H, ceil(N/256), ceil(N/128)] or NULL (dense);
-// drop: dropout parameters or NULL (not both).
+// drop: dropout parameters or NULL (not both); kv_len: device int32 [B] key
+// lengths or NULL (dense calls only).
 int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const uint16_t* dO, const float* lse, const float* D,
                     const uint8_t* block_mask, uint16_t* dk, uint16_t* dv,
                     int B, int H, int N, int d, float scale, int causal,
-                    const Dropout* drop, hipStream_t stream);
+                    const Dropout* drop, const int32_t* kv_len,
+                    hipStream_t stream);
 
 int launch_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   const uint16_t* dO, const float* lse, const float* D,
                   const uint8_t* block_mask, uint16_t* dq, int B, int H, int N,
                   int d, float scale, int causal, const Dropout* drop,
-                  hipStream_t stream);
+                  const int32_t* kv_len, hipStream_t stream);
 
 // FP8 forward (layouts in include/fa.h).  signs: device int8 [d] or NULL.
 int launch_fp8_quantize(const uint16_t* q, const uint16_t* k,

@@ -296,3 +296,21 @@ def test_dropout_threshold_rounding():
     assert fa.dropout_threshold(1.5 / 256) == 2
     assert fa.dropout_threshold(2.5 / 256) == 2
     assert fa.dropout_threshold(0.5) == 128
+
+
+def test_bwd_kvlen_argument_errors():
+    L = fa.lib()
+    nbytes = fa.fa_bwd_workspace_size(1, 2, 64, 128)
+    W = 0x100000
+
+    def bk(ptrs=None, kv=A, d=128, ws=W):
+        p = ptrs or [A] * 9
+        return L.fa_bwd_kvlen(p[0], p[1], p[2], p[3], p[4], p[5], kv, p[6],
+                              p[7], p[8], ws, nbytes, 1, 2, 64, d, 0.1, 1, None)
+    for i in range(9):
+        p = [A] * 9
+        p[i] = None
+        assert bk(p) == NULL, i
+    assert bk(d=96) == HEADDIM
+    assert bk(kv=0x10002) == ALIGN
+    assert bk(ws=None) == WORKSPACE

@@ -137,3 +137,56 @@ def test_workload_d128_fwd_bwd():
     e2 = float(np.abs(sdv - sdo).max())
     report("invariants", sum_dK=e1, sum_dV_minus_sum_dO=e2)
     assert e1 <= tol and e2 <= tol
+
+
+def _check_bwd_kvlen(name, inp, heads=None):
+    import torch
+    import io_aware_tiled_amd as fa
+    from gpu_util import kv_dev
+    from oracle import attention_bwd
+    o, lse = run_fwd(inp)
+    q, k, v, do = (to_dev(inp, n) for n in ("q", "k", "v", "do"))
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=inp["causal"],
+                             scale=inp["scale"], kv_len=kv_dev(inp))
+    torch.cuda.synchronize()
+    sel = (lambda a: a) if heads is None else (lambda a: a[:, heads])
+    ref = attention_bwd(sel(inp["q"]), sel(inp["k"]), sel(inp["v"]),
+                        sel(inp["do"]), inp["scale"], inp["causal"],
+                        inp["kv_len"], workers=8)
+    errs = {nm: max_err(sel(host64(g)), r, f"{name} {nm}")
+            for nm, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref)}
+    report(name, **errs)
+    for nm, e in errs.items():
+        assert e <= TOL_GRAD, (name, nm, e)
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_key_padding(d, causal):
+    """Backward of the key-padded forward (fa_bwd_kvlen): per-batch key
+    lengths 0, 5, a ragged value and N.  (With a single visible key, dV of
+    that key is the sum of all 300 dO rows, |dV| ~ 20-40, whose bf16
+    rounding alone exceeds the absolute bar; 5 keys keep |dV| small.)"""
+    N = 300
+    inp = S.make_case(4, 2, N, d, "bf16", causal, seed=40 + d + causal,
+                      backward=True, kv_len=[0, 5, 217, N])
+    dq, dk, dv = _check_bwd_kvlen(f"bwd kvlen d{d} causal={causal}", inp)
+    assert float(dq[0].float().abs().max()) == 0.0      # no visible key
+    assert float(dk[2, :, 217:].float().abs().max()) == 0.0
+    assert float(dv[2, :, 217:].float().abs().max()) == 0.0
+
+
+def test_bwd_key_padding_bert_shape():
+    """BERT-large-shaped padded training step (16 x 16 x 512 x 64, lengths
+    in [256, 512]): four heads against the oracle."""
+    inp = S.make_case(16, 16, 512, 64, "bf16", False, seed=41, backward=True,
+                      kv_len=np.random.default_rng(309).integers(256, 513, 16))
+    _check_bwd_kvlen("bwd kvlen bert shape", inp, heads=np.array([0, 5, 10, 15]))
+
+
+def test_bwd_key_padding_pipelined_grid():
+    """Head dim 128 on a grid that takes the pipelined kernels."""
+    inp = S.make_case(16, 16, 300, 128, "bf16", True, seed=42, backward=True,
+                      kv_len=np.random.default_rng(11).integers(8, 301, 16))
+    _check_bwd_kvlen("bwd kvlen pipelined", inp, heads=np.array([0, 9]))
