@@ -487,24 +487,40 @@ def summarize_ceiling(path, command) -> int:
     return 0
 
 
-def summarize_trace(w: S.Workload, path, command) -> int:
+def summarize_trace(w: S.Workload, path, command, warmup: int,
+                    steps: int) -> int:
+    """profiles/kernels_<workload>.md from a rocprofv3 kernel trace: per
+    libfa kernel, the timed dispatches only (each kernel runs once per step,
+    so its first `warmup` dispatches are the warmup steps)."""
     import csv
+    per = {}
     with open(path) as f:
-        rows = [r for r in csv.DictReader(f) if "fa::" in r["Name"]]
+        for r in csv.DictReader(f):
+            if "fa::" not in r["Kernel_Name"]:
+                continue
+            ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            per.setdefault(r["Kernel_Name"], []).append(
+                (int(r["Dispatch_Id"]), ns))
     md = os.path.join(PROFILES, f"kernels_{w.name}.md")
+    total = sum(ns for v in per.values() for _, ns in v)
     with open(md, "w") as f:
         f.write(f"# Kernel trace: {w.name} (B={w.B} H={w.H} N={w.N} d={w.d}, "
                 f"causal={w.causal}, {'forward+backward' if w.backward else 'forward'})"
                 f"\n\nCommand (repository root, one MI355X):\n\n```\n{command}"
-                "\n```\n\nrocprofv3 kernel statistics, libfa kernels only "
-                "(durations in microseconds):\n\n| kernel | calls | average | "
-                "min | max | share of GPU time |\n|---|---|---|---|---|---|\n")
-        for r in rows:
-            name = (r["Name"].replace("(anonymous namespace)::", "")
-                    .split("(")[0].replace("void ", ""))
-            f.write(f"| `{name}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.1f}"
-                    f" | {float(r['MinNs'])/1e3:.1f} | {float(r['MaxNs'])/1e3:.1f}"
-                    f" | {float(r['Percentage']):.1f}% |\n")
+                "\n```\n\nrocprofv3 kernel trace, libfa kernels only, the "
+                f"timed dispatches of each kernel (its first {warmup} dispatches "
+                f"are the warmup steps and are skipped; the next {steps} are "
+                "kept; durations in microseconds):\n\n| kernel | timed "
+                "dispatches | average | min | max |\n|---|---|---|---|---|\n")
+        for name, v in sorted(per.items(), key=lambda kv: -sum(x[1] for x in kv[1])):
+            v = sorted(v)[warmup:warmup + steps]
+            if not v:
+                continue
+            d = np.array([ns for _, ns in v], dtype=np.float64) / 1e3
+            short = (name.replace("(anonymous namespace)::", "")
+                     .split("(")[0].replace("void ", ""))
+            f.write(f"| `{short}` | {len(d)} | {d.mean():.1f} | {d.min():.1f} "
+                    f"| {d.max():.1f} |\n")
     print(open(md).read())
     return 0
 
@@ -527,15 +543,20 @@ def main(argv=None) -> int:
                          "collections (FETCH_SIZE, then WRITE_SIZE) of a "
                          "--copy-calibration run into profiles/traffic.json "
                          "(give the same --copy-calibration MIB)")
-    ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
-                    help="no GPU work: write the libfa rows of a rocprofv3 "
-                         "--kernel-trace --stats kernel_stats.csv to "
-                         "profiles/kernels_<workload>.md")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="no GPU work: write the libfa dispatches of a "
+                         "rocprofv3 --kernel-trace kernel_trace.csv to "
+                         "profiles/kernels_<workload>.md, skipping each "
+                         "kernel's first --warmup dispatches and keeping the "
+                         "next --steps (the timed ones)")
     ap.add_argument("--summarize-counters", nargs=2,
                     metavar=("SQ_CSV", "TCC_CSV"),
                     help="no GPU work: turn two rocprofv3 --pmc collections "
                          "(SQ/GRBM counters, then TCC_HIT_sum TCC_MISS_sum) "
                          "into profiles/counters_<workload>.md")
+    ap.add_argument("--no-per-config", dest="per_config", action="store_false",
+                    help="skip the per-config table (the five synthetic "
+                         "configs, each timed and beside its oracle time)")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the vendor-GEMM matrix-core calibration")
     ap.add_argument("--ceiling-only", action="store_true",
@@ -561,7 +582,7 @@ def main(argv=None) -> int:
                                   args.summarize_counters, args.command)
     if args.summarize_trace:
         return summarize_trace(S.WORKLOADS[args.workload], args.summarize_trace,
-                               args.command)
+                               args.command, args.warmup, args.steps)
     if args.traffic_from:
         if not args.copy_calibration:
             ap.error("--traffic-from needs the run's --copy-calibration MIB")
@@ -587,6 +608,27 @@ def main(argv=None) -> int:
     if args.sweep:
         return sweep(dev)
     w = S.WORKLOADS[args.workload]
+    res = time_workload(w, dev, args.steps, args.warmup,
+                        copy_calibration=args.copy_calibration)
+    out = result_line(w, res, args)
+    if args.per_config and w.name == DEFAULT_WORKLOAD:
+        out["per_config"] = per_config(dev, args, res, out)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+# The five synthetic workloads quoted by the metric: (config number, name).
+CONFIGS = ((1, "tiny_f32"), (2, "gpt2_causal"), (3, "bert_keypad"),
+           (4, "tradingday_causal"), (5, "causal_fwd_bwd_d128"))
+
+
+def time_workload(w: S.Workload, dev, steps: int, warmup: int,
+                  copy_calibration: int = 0) -> dict:
+    """Upload the workload's inputs, run `warmup` untimed steps, then time
+    `steps` steps: wall clock around all of them (synchronised on both
+    sides) and HIP events on the launch stream around every kernel."""
+    import torch
+    import io_aware_tiled_amd as fa
     log(f"[bench] generating {w.name} inputs")
     inp = S.make_inputs(w)
 
@@ -614,6 +656,7 @@ def main(argv=None) -> int:
         ws8 = torch.empty(fa.fa_fp8_workspace_size(w.B, w.H, w.N, w.d),
                           dtype=torch.uint8, device=dev)
         score_scale = float(np.float32(scale) / np.float32(w.d))
+    dq = dk = dv = None
     if w.backward:
         ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.N, w.d),
                          dtype=torch.uint8, device=dev)
@@ -675,40 +718,60 @@ def main(argv=None) -> int:
                 fa.fa_bwd_dq(q, k, v, do, lse, dq, ws, scale, causal)
             mark(4)
 
-    log(f"[bench] warmup {args.warmup} steps")
-    for _ in range(args.warmup):
+    log(f"[bench] {w.name}: warmup {warmup} steps")
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    if args.copy_calibration:
-        n = args.copy_calibration * (1 << 20) // 4
+    if copy_calibration:
+        n = copy_calibration * (1 << 20) // 4
         cx = torch.ones(n, dtype=torch.float32, device=dev)
         cy = torch.empty_like(cx)
         for _ in range(3):
             torch.neg(cx, out=cy)
         torch.cuda.synchronize()
         del cx, cy
-        log(f"[bench] copy calibration: 3 x {args.copy_calibration} MiB")
+        log(f"[bench] copy calibration: 3 x {copy_calibration} MiB")
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-          for _ in range(args.steps)]
-    log(f"[bench] timing {args.steps} steps")
+          for _ in range(steps)]
+    log(f"[bench] {w.name}: timing {steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
 
     per_kernel = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]))
                   for j, n in enumerate(names)}
+    # outputs of the timed run must be finite (parity itself is the tests' job)
+    check = {"o_finite": bool(torch.isfinite(o.float()).all()),
+             "lse_finite_or_neg_inf": bool((torch.isfinite(lse) | (lse == -float("inf"))).all())}
+    if w.backward:
+        check["grads_finite"] = bool(all(torch.isfinite(t.float()).all()
+                                         for t in (dq, dk, dv)))
     pairs = visible_pairs(w, inp["kv_len"], inp.get("block_mask"))
+    return {"inp": inp, "names": names, "per_kernel": per_kernel,
+            "ms_step": wall * 1e3 / steps, "pairs": pairs, "fp8": fp8,
+            "dropout": dr, "check": check, "steps": steps, "warmup": warmup}
+
+
+def _peak(w: S.Workload, fp8: bool) -> float:
+    return (PEAK_F32_TFLOPS if w.dtype == "f32" else
+            PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS)
+
+
+def result_line(w: S.Workload, res: dict, args) -> dict:
+    """The JSON line of one timed workload (without per_config)."""
+    import torch
+    dev = torch.device("cuda:0")
+    per_kernel, ms_step, pairs = res["per_kernel"], res["ms_step"], res["pairs"]
+    names, fp8, dr, inp = res["names"], res["fp8"], res["dropout"], res["inp"]
     fwd_flops = linear_flops(w) if w.linear else 4.0 * w.d * pairs
     bwd_flops = 10.0 * w.d * pairs if w.backward else 0.0
     step_flops = fwd_flops + bwd_flops
     value = step_flops / (ms_step * 1e-3) / 1e12
-    peak = (PEAK_F32_TFLOPS if w.dtype == "f32" else
-            PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS)
+    peak = _peak(w, fp8)
 
     if w.backward:
         # fa_bwd_dkdv produces dK and dV: S = Q K^T, dP = dO V^T, dV += P^T dO
@@ -750,13 +813,8 @@ def main(argv=None) -> int:
                     "kernel": dom, "kernel_ms": round(dom_ms, 4),
                     "algorithmic_bytes_per_launch": nbytes,
                     "algorithmic_flop_per_launch": dom_flops}
-
-    # outputs of the timed run must be finite (parity itself is the tests' job)
-    check = {"o_finite": bool(torch.isfinite(o.float()).all()),
-             "lse_finite_or_neg_inf": bool((torch.isfinite(lse) | (lse == -float("inf"))).all())}
-    if w.backward:
-        check["grads_finite"] = bool(all(torch.isfinite(t.float()).all()
-                                         for t in (dq, dk, dv)))
+    if traffic is not None:
+        roofline["traffic_gb_per_s"] = round(traffic / (dom_ms * 1e-3) / 1e9, 1)
 
     ceiling = None
     if not args.no_ceiling and w.dtype == "bf16" and not fp8 and not w.linear:
@@ -771,7 +829,7 @@ def main(argv=None) -> int:
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "n_gpus": 1, "steps": res["steps"], "warmup": res["warmup"],
         "ms_per_step": round(ms_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
         "dtype": "f32" if w.dtype == "f32" else "fp8_e4m3" if fp8 else "bf16",
@@ -789,7 +847,7 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "mfma_ceiling": ceiling,
         "cpu_baseline": cpu,
-        "sanity": check,
+        "sanity": res["check"],
     }
     if dr is not None:
         out["dropout"] = {"p": dr["p"], "seed": dr["seed"],
@@ -809,8 +867,99 @@ def main(argv=None) -> int:
     if w.backward:
         bwd_ms = sum(per_kernel[n] for n in names[1:])
         out["bwd_tflops"] = round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2)
-    print(json.dumps(out), flush=True)
-    return 0
+    return out
+
+
+def oracle_timing(w: S.Workload, inp: dict, runs: int, max_heads=None):
+    """Seconds of the fp64 oracle on the workload (its first max_heads
+    (b, h) heads of batch entry 0 when given, else all of it), median of
+    `runs` runs; returns (seconds, heads timed, algorithmic FLOP timed)."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    kv = inp["kv_len"]
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    do = inp.get("do")
+    B = w.B
+    if max_heads is not None:
+        q, k, v = (a[:1, :max_heads] for a in (q, k, v))
+        do = None if do is None else do[:1, :max_heads]
+        kv = None if kv is None else kv[:1]
+        B = 1
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        oracle.attention_fwd(q, k, v, inp["scale"], inp["causal"], kv,
+                             workers=cores)
+        if w.backward:
+            oracle.attention_bwd(q, k, v, do, inp["scale"], inp["causal"], kv,
+                                 workers=cores)
+        ts.append(time.perf_counter() - t0)
+    nh = q.shape[0] * q.shape[1]
+    sw = S.Workload(w.name, B, q.shape[1], w.N, w.d, w.dtype, w.causal,
+                    w.seeds, w.backward)
+    flops = visible_pairs(sw, kv) * w.d * (4 + (10 if w.backward else 0))
+    return float(np.median(ts)), nh, flops
+
+
+def per_config(dev, args, head_res: dict, head_out: dict) -> dict:
+    """Every synthetic config the metric is quoted on: algorithmic TFLOP/s,
+    fraction of its peak, kernel time, and the fp64 oracle timed on the
+    host cores of this run (configs 1-3 whole, median of 3 runs; configs 4
+    and 5 on a bounded sample of heads, one run)."""
+    cores = len(os.sched_getaffinity(0))
+    table = {}
+    for num, name in CONFIGS:
+        w = S.WORKLOADS[name]
+        if name == head_out["config"]["workload"]:
+            res, line = head_res, head_out
+        else:
+            res = time_workload(w, dev, args.steps, args.warmup)
+            fwd_flops = 4.0 * w.d * res["pairs"]
+            line = {"value": fwd_flops / (res["ms_step"] * 1e-3) / 1e12,
+                    "ms_per_step": res["ms_step"]}
+        fwd_ms = res["per_kernel"]["fwd"]
+        fwd_flops = 4.0 * w.d * res["pairs"]
+        peak = _peak(w, False)
+        ent = {"workload": name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+               "dtype": w.dtype, "causal": w.causal,
+               "pass": "forward+backward" if w.backward else "forward",
+               "visible_pairs": res["pairs"],
+               "tflops": round(line["value"], 2),
+               "frac_of_peak": round(line["value"] / peak, 4),
+               "peak_tflops": peak, "ms_per_step": round(line["ms_per_step"], 4),
+               "kernel_ms": {n: round(t, 4) for n, t in res["per_kernel"].items()},
+               "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
+               "fwd_frac_of_peak": round(fwd_flops / (fwd_ms * 1e-3) / 1e12 / peak, 4)}
+        if w.backward:
+            bwd_ms = sum(res["per_kernel"][n] for n in res["names"][1:])
+            bt = 10.0 * w.d * res["pairs"] / (bwd_ms * 1e-3) / 1e12
+            ent["bwd_tflops"] = round(bt, 2)
+            ent["bwd_frac_of_peak"] = round(bt / peak, 4)
+        if not args.no_cpu_baseline:
+            if num <= 3:
+                log(f"[bench] oracle on config {num} (3 runs)")
+                sec, nh, fl = oracle_timing(w, res["inp"], 3)
+                sample = f"whole workload ({nh} heads), median of 3 runs"
+            elif num == 4:
+                log(f"[bench] oracle on config {num} (1 head)")
+                sec, nh, fl = oracle_timing(w, res["inp"], 1, max_heads=1)
+                sample = "1 of 12 heads (all 23400 rows), one run"
+            else:
+                cb = head_out.get("cpu_baseline") or {}
+                sec, nh, fl = None, None, None
+                sample = cb.get("sample", "")
+                ent["oracle"] = {"tflops": cb.get("value"), "sample": sample,
+                                 "cores": cores}
+            if sec is not None:
+                ent["oracle"] = {"seconds": round(sec, 3), "heads": nh,
+                                 "tflops": fl / sec / 1e12, "cores": cores,
+                                 "sample": sample}
+            if ent["oracle"].get("tflops"):
+                ent["gpu_over_oracle"] = round(
+                    ent["tflops"] / ent["oracle"]["tflops"], 1)
+        table[str(num)] = ent
+        del res
+    return table
 
 
 if __name__ == "__main__":

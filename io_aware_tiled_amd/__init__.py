@@ -282,9 +282,32 @@ def fa_bwd_block_sparse(q, k, v, o, dO, lse, block_mask, dq, dk, dv,
     _check(st, "fa_bwd_block_sparse")
 
 
+def _expect_all(pairs, dtype, shape):
+    for t, n in pairs:
+        _expect(t, dtype, shape, n)
+
+
+def _expect_stage(q, k, v, dO, lse, outs):
+    """dtype and shape checks of the stage-level backward entry points: the
+    C ABI sees only pointers and cannot check buffer sizes."""
+    import torch
+    B, H, N, d = _bhnd(q)
+    _expect_all(((q, "q"), (k, "k"), (v, "v"), (dO, "dO")) + tuple(outs),
+                torch.bfloat16, (B, H, N, d))
+    _expect(lse, torch.float32, (B, H, N), "lse")
+    return B, H, N, d
+
+
+def _expect_mask(block_mask, H, N):
+    import torch
+    _expect(block_mask, torch.uint8,
+            (H, -(-N // SPARSE_BQ), -(-N // SPARSE_BK)), "block_mask")
+
+
 def fa_bwd_dkdv_block_sparse(q, k, v, dO, lse, block_mask, dk, dv,
                              workspace, scale, causal, stream=None):
-    B, H, N, d = _bhnd(q)
+    B, H, N, d = _expect_stage(q, k, v, dO, lse, ((dk, "dk"), (dv, "dv")))
+    _expect_mask(block_mask, H, N)
     wp, wn = _ws(workspace)
     st = lib().fa_bwd_dkdv_block_sparse(
         _ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(block_mask),
@@ -295,7 +318,8 @@ def fa_bwd_dkdv_block_sparse(q, k, v, dO, lse, block_mask, dk, dv,
 
 def fa_bwd_dq_block_sparse(q, k, v, dO, lse, block_mask, dq, workspace,
                            scale, causal, stream=None):
-    B, H, N, d = _bhnd(q)
+    B, H, N, d = _expect_stage(q, k, v, dO, lse, ((dq, "dq"),))
+    _expect_mask(block_mask, H, N)
     wp, wn = _ws(workspace)
     st = lib().fa_bwd_dq_block_sparse(
         _ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(block_mask),
@@ -305,7 +329,9 @@ def fa_bwd_dq_block_sparse(q, k, v, dO, lse, block_mask, dq, workspace,
 
 
 def fa_bwd_preprocess(o, dO, workspace, stream=None):
+    import torch
     B, H, N, d = _bhnd(o)
+    _expect_all(((o, "o"), (dO, "dO")), torch.bfloat16, (B, H, N, d))
     wp, wn = _ws(workspace)
     st = lib().fa_bwd_preprocess(_ptr(o), _ptr(dO), wp, wn, B, H, N, d,
                                  _stream(o, stream))
@@ -314,7 +340,7 @@ def fa_bwd_preprocess(o, dO, workspace, stream=None):
 
 def fa_bwd_dkdv(q, k, v, dO, lse, dk, dv, workspace, scale, causal,
                 stream=None):
-    B, H, N, d = _bhnd(q)
+    B, H, N, d = _expect_stage(q, k, v, dO, lse, ((dk, "dk"), (dv, "dv")))
     wp, wn = _ws(workspace)
     st = lib().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse),
                            _ptr(dk), _ptr(dv), wp, wn, B, H, N, d,
@@ -323,7 +349,7 @@ def fa_bwd_dkdv(q, k, v, dO, lse, dk, dv, workspace, scale, causal,
 
 
 def fa_bwd_dq(q, k, v, dO, lse, dq, workspace, scale, causal, stream=None):
-    B, H, N, d = _bhnd(q)
+    B, H, N, d = _expect_stage(q, k, v, dO, lse, ((dq, "dq"),))
     wp, wn = _ws(workspace)
     st = lib().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse),
                          _ptr(dq), wp, wn, B, H, N, d, float(scale),
@@ -390,7 +416,7 @@ def fa_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, workspace, scale, causal,
 
 def fa_bwd_dkdv_dropout(q, k, v, dO, lse, dk, dv, workspace, scale, causal,
                         p_drop, seed, offset=0, stream=None):
-    B, H, N, d = _bhnd(q)
+    B, H, N, d = _expect_stage(q, k, v, dO, lse, ((dk, "dk"), (dv, "dv")))
     wp, wn = _ws(workspace)
     st = lib().fa_bwd_dkdv_dropout(
         _ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(dk), _ptr(dv),
@@ -401,7 +427,7 @@ def fa_bwd_dkdv_dropout(q, k, v, dO, lse, dk, dv, workspace, scale, causal,
 
 def fa_bwd_dq_dropout(q, k, v, dO, lse, dq, workspace, scale, causal, p_drop,
                       seed, offset=0, stream=None):
-    B, H, N, d = _bhnd(q)
+    B, H, N, d = _expect_stage(q, k, v, dO, lse, ((dq, "dq"),))
     wp, wn = _ws(workspace)
     st = lib().fa_bwd_dq_dropout(
         _ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(dq), wp, wn, B,
@@ -559,7 +585,8 @@ def backward(q, k, v, o, lse, dO, *, causal=False, scale=None, stream=None,
         scale = 1.0 / math.sqrt(d)
     nbytes = fa_bwd_workspace_size(B, H, N, d)
     if nbytes == 0:
-        raise FAError(-3 if d != 128 else -2, "fa_bwd_workspace_size")
+        raise FAError(-3 if d not in (64, 128) else -2,
+                      "fa_bwd_workspace_size")
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     dq = torch.empty_like(q)

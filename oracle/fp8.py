@@ -34,7 +34,8 @@ The readings taken here (each also listed in the design notes):
   * Attention is then the plain definition (oracle.attention) in fp64 on the
     dequantised operands.  The GPU also rounds the softmax weights to E4M3
     before the P V product; that rounding depends on the kernel's running
-    reference and is not modelled here (the tests bound it).
+    reference and is not modelled here (the tests bound it): parity
+    unpinned for that step.
 """
 from __future__ import annotations
 

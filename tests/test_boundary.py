@@ -314,3 +314,41 @@ def test_bwd_kvlen_argument_errors():
     assert bk(d=96) == HEADDIM
     assert bk(kv=0x10002) == ALIGN
     assert bk(ws=None) == WORKSPACE
+
+
+def test_stage_wrappers_check_dtype_and_shape():
+    """The stage-level backward wrappers check every tensor's dtype and
+    shape before marshalling (the C ABI sees only pointers and cannot check
+    buffer sizes); the checks run before the host-tensor refusal, so they
+    are testable without a GPU."""
+    import torch
+    B, H, N, d = 1, 2, 64, 128
+    bf = lambda *s: torch.zeros(*s, dtype=torch.bfloat16)
+    q, k, v, do, dq, dk, dv = (bf(B, H, N, d) for _ in range(7))
+    lse = torch.zeros(B, H, N, dtype=torch.float32)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    mask = torch.ones(H, 1, 1, dtype=torch.uint8)
+    short = bf(B, H, N - 1, d)
+    f32 = torch.zeros(B, H, N, d, dtype=torch.float32)
+    calls = [
+        lambda t: fa.fa_bwd_preprocess(t, do, ws),
+        lambda t: fa.fa_bwd_dkdv(q, k, v, do, lse, t, dv, ws, 0.1, True),
+        lambda t: fa.fa_bwd_dq(q, t, v, do, lse, dq, ws, 0.1, True),
+        lambda t: fa.fa_bwd_dkdv_block_sparse(q, k, t, do, lse, mask, dk, dv,
+                                              ws, 0.1, True),
+        lambda t: fa.fa_bwd_dq_block_sparse(q, k, v, t, lse, mask, dq, ws,
+                                            0.1, True),
+        lambda t: fa.fa_bwd_dkdv_dropout(q, k, v, do, lse, dk, t, ws, 0.1,
+                                         True, 0.1, 1),
+        lambda t: fa.fa_bwd_dq_dropout(q, k, v, do, lse, t, ws, 0.1, True,
+                                       0.1, 1),
+    ]
+    for call in calls:
+        for bad in (short, f32):
+            with pytest.raises(ValueError):
+                call(bad)
+    with pytest.raises(ValueError):    # LSE of the wrong length
+        fa.fa_bwd_dq(q, k, v, do, lse[:, :, :-1], dq, ws, 0.1, True)
+    with pytest.raises(ValueError):    # block mask of the wrong shape
+        fa.fa_bwd_dq_block_sparse(q, k, v, do, lse, mask[:1], dq, ws, 0.1,
+                                  True)
