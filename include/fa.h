@@ -65,7 +65,8 @@ enum fa_status {
   FA_ERR_ALIGN = -4,     /* a tensor pointer is not 16-byte aligned        */
   FA_ERR_WORKSPACE = -5, /* workspace NULL, too small or not 256-B aligned */
   FA_ERR_HIP = -6,       /* the HIP runtime reported a launch error        */
-  FA_ERR_DROPOUT = -7    /* drop probability outside [0, 255.5/256)       */
+  FA_ERR_DROPOUT = -7,   /* drop probability outside [0, 255.5/256)       */
+  FA_ERR_TOO_LARGE = -8  /* B*H*N beyond the fixed scratch of fa_bwd_noalloc */
 };
 
 /* Library version, as 10000*major + 100*minor + patch. */
@@ -265,6 +266,27 @@ int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
            uint16_t* dq, uint16_t* dk, uint16_t* dv, void* workspace,
            size_t workspace_bytes, int B, int H, int N, int d, float scale,
            int causal, void* stream);
+
+/*
+ * fa_bwd without a workspace, for callers that cannot allocate device memory
+ * (code under stream capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, kernels and results as fa_bwd (bitwise); the
+ * D rows live in a fixed array of FA_BWD_NOALLOC_MAX_ROWS float32 (8 MiB)
+ * that the library holds on every GPU it runs on until the process ends.
+ * Its device address is looked up on the first call on each device (the
+ * device current at the call, which must be the device of `stream`); no
+ * call allocates or frees memory.  Errors as fa_bwd (without
+ * FA_ERR_WORKSPACE), plus FA_ERR_TOO_LARGE when B*H*N exceeds
+ * FA_BWD_NOALLOC_MAX_ROWS (returned before any HIP call) and FA_ERR_HIP when
+ * the array's address cannot be obtained.  All calls on one GPU share the
+ * array: calls that overlap on one GPU (streams with no ordering between
+ * them) race and must not be issued.
+ */
+#define FA_BWD_NOALLOC_MAX_ROWS (1 << 21)
+int fa_bwd_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                   const uint16_t* o, const uint16_t* dO, const float* lse,
+                   uint16_t* dq, uint16_t* dk, uint16_t* dv, int B, int H,
+                   int N, int d, float scale, int causal, void* stream);
 
 /*
  * Backward of fa_fwd_kvlen (key padding, the BERT-shaped workload): the

@@ -26,7 +26,8 @@ import os
 __all__ = [
     "FAError", "lib", "lib_path", "fa_version", "fa_status_string",
     "fa_fwd", "fa_fwd_kvlen", "fa_fwd_f32", "fa_bwd_workspace_size",
-    "fa_bwd", "fa_bwd_kvlen", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
+    "fa_bwd", "fa_bwd_kvlen", "fa_bwd_noalloc", "BWD_NOALLOC_MAX_ROWS",
+    "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
     "fa_fwd_block_sparse", "fa_bwd_block_sparse", "fa_bwd_dkdv_block_sparse",
     "fa_bwd_dq_block_sparse", "fa_fp8_workspace_size",
     "fa_fp8_quantize",
@@ -59,6 +60,7 @@ _SIGS = {
     "fa_bwd_workspace_size": (_S, [_I, _I, _I, _I]),
     "fa_bwd": (_I, [_P] * 10 + [_S, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_kvlen": (_I, [_P] * 11 + [_S, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_bwd_noalloc": (_I, [_P] * 9 + [_I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_preprocess": (_I, [_P, _P, _P, _S, _I, _I, _I, _I, _P]),
     "fa_bwd_dkdv": (_I, [_P] * 8 + [_S, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_dq": (_I, [_P] * 7 + [_S, _I, _I, _I, _I, _F, _I, _P]),
@@ -237,6 +239,28 @@ def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, workspace, scale, causal,
                       _ptr(dq), _ptr(dk), _ptr(dv), wp, wn, B, H, N, d,
                       float(scale), int(bool(causal)), _stream(q, stream))
     _check(st, "fa_bwd")
+
+
+def fa_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, scale, causal,
+                   stream=None):
+    """C fa_bwd_noalloc: fa_bwd with its D rows in the library's fixed
+    per-device scratch instead of a workspace (B*H*N at most
+    BWD_NOALLOC_MAX_ROWS); allocates nothing.  Calls that overlap on one GPU
+    race on that scratch."""
+    import torch
+    B, H, N, d = _bhnd(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO"),
+                 (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _expect(t, torch.bfloat16, (B, H, N, d), n)
+    _expect(lse, torch.float32, (B, H, N), "lse")
+    st = lib().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO),
+                              _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N,
+                              d, float(scale), int(bool(causal)),
+                              _stream(q, stream))
+    _check(st, "fa_bwd_noalloc")
+
+
+BWD_NOALLOC_MAX_ROWS = 1 << 21   # FA_BWD_NOALLOC_MAX_ROWS
 
 
 def fa_bwd_kvlen(q, k, v, o, dO, lse, kv_len, dq, dk, dv, workspace, scale,

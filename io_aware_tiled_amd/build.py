@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
 
 SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_fp8.hip", "fa_linear.hip",
-           "fa_api.cpp"]
+           "fa_noalloc.hip", "fa_api.cpp"]
 
 # Per-source flags.  The VALU reads the score MFMAs' results, so MFMA
 # results are kept in VGPRs rather than AGPRs (which the VALU can only reach

@@ -87,6 +87,9 @@ const char* fa_status_string(int status) {
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported a launch error";
     case FA_ERR_DROPOUT:
       return "FA_ERR_DROPOUT: drop probability must lie in [0, 255.5/256)";
+    case FA_ERR_TOO_LARGE:
+      return "FA_ERR_TOO_LARGE: B*H*N exceeds the fixed scratch of fa_bwd_noalloc "
+             "(FA_BWD_NOALLOC_MAX_ROWS rows)";
     default: return "unknown fa status code";
   }
 }
@@ -288,6 +291,32 @@ int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   if (st != FA_OK) return st;
   return fa_bwd_dq(q, k, v, dO, lse, dq, workspace, workspace_bytes, B, H, N,
                    d, scale, causal, stream);
+}
+
+int fa_bwd_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                   const uint16_t* o, const uint16_t* dO, const float* lse,
+                   uint16_t* dq, uint16_t* dk, uint16_t* dv, int B, int H,
+                   int N, int d, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv)
+    return FA_ERR_NULL;
+  int st = check_shape_bwd(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(dO) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv))
+    return FA_ERR_ALIGN;
+  if ((long long)B * H * N > FA_BWD_NOALLOC_MAX_ROWS) return FA_ERR_TOO_LARGE;
+  void* scratch = nullptr;
+  if (fa::noalloc_scratch(&scratch) != 0) return FA_ERR_HIP;
+  float* D = (float*)scratch;
+  const hipStream_t s = (hipStream_t)stream;
+  st = fa::launch_bwd_preprocess(o, dO, D, B, H, N, d, s);
+  if (st != FA_OK) return st;
+  st = fa::launch_bwd_dkdv(q, k, v, dO, lse, D, nullptr, dk, dv, B, H, N, d,
+                           scale, causal != 0, nullptr, nullptr, s);
+  if (st != FA_OK) return st;
+  return fa::launch_bwd_dq(q, k, v, dO, lse, D, nullptr, dq, B, H, N, d,
+                           scale, causal != 0, nullptr, nullptr, s);
 }
 
 int fa_bwd_kvlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -60,6 +60,10 @@ int launch_fwd_fp8(const uint8_t* ws, uint16_t* o, float* lse, int B, int H,
                    int N, int d, float score_scale, int causal,
                    hipStream_t stream);
 
+// Device address of the fixed backward scratch (FA_BWD_NOALLOC_MAX_ROWS
+// float32) on the current device, looked up once per device; 0 or -6.
+int noalloc_scratch(void** addr);
+
 // Causal linear attention forward (chunkwise).  ws: fp32 segment states
 // of linear_workspace_bytes() bytes (NULL when that is 0).
 size_t linear_workspace_bytes(int B, int H, int N, int d);

@@ -16,6 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
 
 OK, NULL, SHAPE, HEADDIM, ALIGN, WORKSPACE, HIP, DROPOUT = 0, -1, -2, -3, -4, -5, -6, -7
+TOO_LARGE = -8
 
 pytestmark = pytest.mark.skipif(not os.path.exists(fa.lib_path()),
                                 reason="libfa.so not built")
@@ -53,11 +54,12 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_status_strings():
     assert fa.fa_version() == 10000
     seen = set()
-    for code in (OK, NULL, SHAPE, HEADDIM, ALIGN, WORKSPACE, HIP, DROPOUT):
+    for code in (OK, NULL, SHAPE, HEADDIM, ALIGN, WORKSPACE, HIP, DROPOUT,
+                 TOO_LARGE):
         s = fa.fa_status_string(code)
         assert s.startswith("FA_"), s
         seen.add(s)
-    assert len(seen) == 8
+    assert len(seen) == 9
     assert "unknown" in fa.fa_status_string(12345)
 
 
@@ -352,3 +354,29 @@ def test_stage_wrappers_check_dtype_and_shape():
     with pytest.raises(ValueError):    # block mask of the wrong shape
         fa.fa_bwd_dq_block_sparse(q, k, v, do, lse, mask[:1], dq, ws, 0.1,
                                   True)
+
+
+def test_bwd_noalloc_argument_errors():
+    """fa_bwd_noalloc: argument errors, including a problem larger than the
+    fixed scratch (B*H*N > FA_BWD_NOALLOC_MAX_ROWS), are returned before
+    any HIP call."""
+    L = fa.lib()
+    max_rows = fa.BWD_NOALLOC_MAX_ROWS
+    assert max_rows == 1 << 21
+
+    def bwd(ptrs=None, B=1, H=1, N=64, d=128):
+        p = ptrs or [A] * 9
+        return L.fa_bwd_noalloc(*p, B, H, N, d, 0.088, 1, None)
+    for i in range(9):
+        p = [A] * 9
+        p[i] = None
+        assert bwd(p) == NULL, i
+    assert bwd(d=96) == HEADDIM
+    assert bwd(N=0) == SHAPE
+    p = [A] * 9
+    p[7] = MIS
+    assert bwd(p) == ALIGN
+    assert bwd(B=2, H=1, N=max_rows // 2 + 1) == TOO_LARGE
+    assert bwd(B=16, H=16, N=max_rows // 256 + 1) == TOO_LARGE
+    text = open(HEADER).read()
+    assert "#define FA_BWD_NOALLOC_MAX_ROWS (1 << 21)" in text
