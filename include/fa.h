@@ -308,16 +308,20 @@ int fa_bwd_preprocess(const uint16_t* o, const uint16_t* dO, void* workspace,
                       size_t workspace_bytes, int B, int H, int N, int d,
                       void* stream);
 
-/* Backward stage 2: one workgroup per 128-key block; recomputes S, P, dP and
- * dS per query tile and writes dK and dV.  Reads D from the workspace. */
+/* Backward stage 2: one workgroup per 128-key block (4 wavefronts with K/V
+ * held in registers for d = 128 on grids that fill the chip, else 8);
+ * recomputes S, P, dP and dS per 64-row query tile and writes dK and dV.
+ * Reads D from the workspace. */
 int fa_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                 const uint16_t* dO, const float* lse, uint16_t* dk,
                 uint16_t* dv, const void* workspace, size_t workspace_bytes,
                 int B, int H, int N, int d, float scale, int causal,
                 void* stream);
 
-/* Backward stage 3: one workgroup per 128-row query block; recomputes S, P,
- * dP and dS per key tile and writes dQ.  Reads D from the workspace. */
+/* Backward stage 3: one workgroup per 256-row query block (d = 128 on grids
+ * with at least 256 such blocks) or per 128-row query block (otherwise);
+ * recomputes S, P, dP and dS per key tile and writes dQ.  Reads D from the
+ * workspace. */
 int fa_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
               const uint16_t* dO, const float* lse, uint16_t* dq,
               const void* workspace, size_t workspace_bytes, int B, int H,

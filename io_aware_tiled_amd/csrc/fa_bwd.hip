@@ -19,15 +19,24 @@
 //
 // Kernels (three launches on one stream, no atomics, deterministic):
 //   1. bwd_preprocess: D_i = dO_i . O_i from the bf16 O and dO.
-//   2. bwd_dkdv: one workgroup per (batch, head, 128-key block); 8
-//      wavefronts, each owning 32 keys and one half of every 64-row query
-//      tile that can see them (causal: tiles wholly before the key block are
-//      skipped).  S, dP, P and dS are recomputed per tile and dK^T, dV^T
-//      accumulate in registers; the two query halves' partials are added
-//      through LDS at the end.
-//   3. bwd_dq: one workgroup per (batch, head, 128-row query block),
-//      streaming K/V tiles like the forward; it recomputes S^T and dP^T and
+//   2. dK/dV: one workgroup per (batch, head, 128-key block) that visits
+//      every 64-row query tile that can see its keys (causal: tiles wholly
+//      before the key block are skipped); S, dP, P and dS are recomputed
+//      per tile and dK^T, dV^T accumulate in registers.
+//        bwd_dkdv_pipe_kernel (head dim 128 on grids that fill the chip):
+//        4 wavefronts of 32 keys (one per SIMD), K and V fragments held in
+//        registers, dK/dV accumulators in AGPRs, query tiles by LDS DMA
+//        through four stages, two software-pipelined phases per tile.
+//        bwd_dkdv_kernel (head dim 64, and small grids): 8 wavefronts, each
+//        owning 32 keys and one half of every query tile; the two halves'
+//        partials are added through LDS at the end.
+//   3. dQ: streams K/V tiles like the forward, recomputes S^T and dP^T and
 //      accumulates dQ^T in registers.
+//        bwd_dq_pipe_kernel (head dim 128 on grids that fill the chip):
+//        256-row query blocks, 8 wavefronts of 32 rows, K/V by LDS DMA
+//        through four stages, software-pipelined over 32-key half-tiles.
+//        bwd_dq_kernel (head dim 64, and small grids): 128-row query
+//        blocks, 4 wavefronts, register-staged double buffer.
 // Splitting dQ from dK/dV costs 4d extra matrix FLOP per (query, key) pair
 // (14d instead of 10d) but removes the float32 atomics that a fused kernel
 // needs for dQ: device-scope atomics are resolved at the memory side, not in
@@ -435,8 +444,11 @@ constexpr int kDqBR = 128;
 static_assert(FA_SPARSE_BQ % kDqBR == 0, "a dQ block lies in one block-mask row");
 constexpr int kDqBC = 64;
 
+// Head dim 128 keeps one wavefront per SIMD (its Q, dO fragments, dQ
+// accumulators and the next tile's staging registers do not fit 256 VGPRs
+// without spilling); head dim 64 two.
 template <int D, bool CAUSAL, bool DROP = false, bool SPARSE = false>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dv,
@@ -580,26 +592,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const uint16_t* kt = smem + (buf ? buf1 : 0);
     const uint16_t* vt = kt + vbase;
 
-    // ---- S^T = K Q^T and dP^T = V dO^T (keys x queries), two 32-key blocks.
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      dp[kb] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const int o = (32 * kb + lq) * kRS + 16 * kk + 8 * hh;
-        s[kb] = mfma32x16(*(const bf16x8*)(&kt[o]), qf[kk], s[kb]);
-        dp[kb] = mfma32x16(*(const bf16x8*)(&vt[o]), gf[kk], dp[kb]);
-      }
-    }
-    // ---- P^T and dS^T in-lane; register r of block kb holds key
-    // k0 + 32kb + 8(r/4) + 4hh + r%4 for this lane's query.
+    // Per 32-key block kb: S^T = K Q^T and dP^T = V dO^T (keys x queries),
+    // then P^T and dS^T in-lane; register r of block kb holds key
+    // k0 + 32kb + 8(r/4) + 4hh + r%4 for this lane's query.  One block's
+    // S^T and dP^T are live at a time (at head dim 128 two would not fit
+    // two wavefronts per SIMD without spilling).
     const bool need_mask = (CAUSAL && k0 + kDqBC - 1 > qw0) || (k0 + kDqBC > kvlim);
     bf16x8 dsb[2][2];
     const float ik = DROP ? 256.f / (float)(256 - drop.p8) : 1.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s_kb = f32x16{}, dp_kb = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const int o = (32 * kb + lq) * kRS + 16 * kk + 8 * hh;
+        s_kb = mfma32x16(*(const bf16x8*)(&kt[o]), qf[kk], s_kb);
+        dp_kb = mfma32x16(*(const bf16x8*)(&vt[o]), gf[kk], dp_kb);
+      }
       // Dropout: kz[m] holds the keep bytes of keys k0 + 32kb + 8m + 4hh + b
       // (byte b) for this lane's query; quad lane w makes the generator
       // call of key group w.  dS = P (Z dP / k - D).
@@ -619,15 +628,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * c + e;
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c_log2, -lse2));
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_kb[r], c_log2, -lse2));
           if (need_mask) {
             const int key = k0 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
             if ((CAUSAL && key > qrow) || key >= kvlim) p = 0.f;
           }
           if constexpr (DROP)
-            x[e] = p * ((drop_keep(kz[r / 4], r % 4, drop.p8) ? dp[kb][r] * ik : 0.f) - dd);
+            x[e] = p * ((drop_keep(kz[r / 4], r % 4, drop.p8) ? dp_kb[r] * ik : 0.f) - dd);
           else
-            x[e] = p * (dp[kb][r] - dd);
+            x[e] = p * (dp_kb[r] - dd);
         }
         dsb[kb][c] = to_bf16x8(x);
       }

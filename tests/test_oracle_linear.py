@@ -11,7 +11,10 @@ The oracle is the quadratic definition O = scale * tril(Q K^T) V.  It is
 pinned by forms computed differently: exactly rounded brute force, the
 recurrent form with a d x d state, the chunkwise intra/inter split with
 ragged chunks, closed forms (N = 1; prefix sums when every score is 1),
-linearity; plus planted mistakes.
+linearity; plus planted mistakes.  The backward oracle (the analytic
+gradient of <dO, O>) is pinned by central finite differences, reverse mode
+through the recurrent form, torch.autograd in float64, the N = 1 closed
+form and the chunkwise backward with ragged chunks.
 """
 import math
 import types
@@ -123,8 +126,128 @@ def pin_linearity(m):
     _close(f(q, 4 * k, v1), 4 * f(q, k, v1), 1e-12)
 
 
+# ---- backward pins: the gradient of <dO, O> computed other ways.
+
+def _loss(m, q, k, v, do, scale):
+    return float(np.sum(do * m.linear_attention_fwd(q, k, v, scale)))
+
+
+def pin_bwd_finite_differences(m):
+    """Central differences of <dO, O> (a cubic polynomial of the inputs,
+    so the O(h^2) truncation is ~1e-12 relative) on every input element."""
+    B, H, N, d = 1, 2, 7, 3
+    q, k, v, do = (_rand(s_, B, H, N, d) for s_ in (30, 31, 32, 33))
+    g = m.linear_attention_bwd(q, k, v, do, 0.8)
+    h = 1e-5
+    for x, gx, name in ((q, g[0], "dQ"), (k, g[1], "dK"), (v, g[2], "dV")):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            x0 = x[idx]
+            x[idx] = x0 + h
+            lp = _loss(m, q, k, v, do, 0.8)
+            x[idx] = x0 - h
+            lm = _loss(m, q, k, v, do, 0.8)
+            x[idx] = x0
+            num[idx] = (lp - lm) / (2 * h)
+        _close(gx, num, 1e-8 * max(1.0, float(np.abs(num).max())), name)
+
+
+def pin_bwd_recurrent(m):
+    """Reverse mode through the RNN form (state S_i = sum_{j<=i} k_j^T v_j,
+    o_i = scale q_i S_i): dq_i = scale dO_i S_i^T; with
+    G_j = scale sum_{t>=j} q_t^T dO_t (a reverse running sum),
+    dk_j = v_j G_j^T and dv_j = k_j G_j."""
+    B, H, N, d = 2, 2, 29, 6
+    q, k, v, do = (_rand(s_, B, H, N, d) for s_ in (34, 35, 36, 37))
+    dq, dk, dv = m.linear_attention_bwd(q, k, v, do, 0.45, row_chunk=8)
+    rq, rk, rv = (np.zeros_like(q) for _ in range(3))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((d, d))
+            for i in range(N):
+                S += np.outer(k[b, h, i], v[b, h, i])
+                rq[b, h, i] = 0.45 * (do[b, h, i] @ S.T)
+            G = np.zeros((d, d))
+            for j in range(N - 1, -1, -1):
+                G += 0.45 * np.outer(q[b, h, j], do[b, h, j])
+                rk[b, h, j] = v[b, h, j] @ G.T
+                rv[b, h, j] = k[b, h, j] @ G
+    _close(dq, rq, 1e-11, "dQ recurrent")
+    _close(dk, rk, 1e-11, "dK recurrent")
+    _close(dv, rv, 1e-11, "dV recurrent")
+
+
+def pin_bwd_autograd(m):
+    """torch.autograd in float64 on the CPU, on tril(Q K^T) V."""
+    import torch
+    B, H, N, d = 1, 3, 40, 5
+    q, k, v, do = (_rand(s_, B, H, N, d) for s_ in (38, 39, 40, 41))
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True)
+                  for x in (q, k, v))
+    o = -1.3 * (torch.tril(tq @ tk.transpose(-1, -2)) @ tv)
+    (o * torch.tensor(do)).sum().backward()
+    g = m.linear_attention_bwd(q, k, v, do, -1.3, row_chunk=16)
+    for gx, t, name in zip(g, (tq, tk, tv), ("dQ", "dK", "dV")):
+        _close(gx, t.grad.numpy(), 1e-11, name + " autograd")
+
+
+def pin_bwd_closed_forms(m):
+    """N = 1: o = scale (q . k) v, so dq = scale (dO . v) k,
+    dk = scale (dO . v) q, dv = scale (q . k) dO."""
+    q, k, v, do = (_rand(s_, 1, 1, 1, 4) for s_ in (42, 43, 44, 45))
+    dq, dk, dv = m.linear_attention_bwd(q, k, v, do, 0.3)
+    qq, kk, vv, gg = q[0, 0, 0], k[0, 0, 0], v[0, 0, 0], do[0, 0, 0]
+    _close(dq[0, 0, 0], 0.3 * (gg @ vv) * kk, 1e-14, "dq N=1")
+    _close(dk[0, 0, 0], 0.3 * (gg @ vv) * qq, 1e-14, "dk N=1")
+    _close(dv[0, 0, 0], 0.3 * (qq @ kk) * gg, 1e-14, "dv N=1")
+
+
+def _chunk_bwd(q, k, v, do, scale, C):
+    """The chunkwise backward: dQ by the causal chunk form of (dO, V, K);
+    dK and dV by the same form walked from the last chunk to the first,
+    the state G = sum over later chunks of Q_u^T dO_u."""
+    B, H, N, d = q.shape
+    dq, dk, dv = (np.zeros_like(q) for _ in range(3))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((d, d))
+            for c0 in range(0, N, C):
+                c1 = min(N, c0 + C)
+                g, vt, kt = do[b, h, c0:c1], v[b, h, c0:c1], k[b, h, c0:c1]
+                dq[b, h, c0:c1] = scale * (np.tril(g @ vt.T) @ kt + g @ S)
+                S = S + vt.T @ kt
+            G = np.zeros((d, d))
+            starts = list(range(0, N, C))
+            for c0 in reversed(starts):
+                c1 = min(N, c0 + C)
+                qt, kt, vt, g = (x[b, h, c0:c1] for x in (q, k, v, do))
+                dv[b, h, c0:c1] = scale * (np.triu(kt @ qt.T) @ g + kt @ G)
+                dk[b, h, c0:c1] = scale * (np.triu(vt @ g.T) @ qt + vt @ G.T)
+                G = G + qt.T @ g
+    return dq, dk, dv
+
+
+def pin_bwd_chunkwise(m):
+    """The chunk split the kernels use, with ragged chunks, equals the
+    oracle; so does the oracle's own row chunking."""
+    B, H, N, d = 1, 2, 45, 7
+    q, k, v, do = (_rand(s_, B, H, N, d) for s_ in (46, 47, 48, 49))
+    ref = m.linear_attention_bwd(q, k, v, do, 0.6)
+    for C in (1, 4, 16, 64):
+        for a, b_, name in zip(ref, _chunk_bwd(q, k, v, do, 0.6, C),
+                               ("dQ", "dK", "dV")):
+            _close(a, b_, 1e-11, f"{name} chunk {C}")
+    for rc in (1, 6, 13):
+        for a, b_, name in zip(ref, m.linear_attention_bwd(q, k, v, do, 0.6,
+                                                           row_chunk=rc),
+                               ("dQ", "dK", "dV")):
+            _close(a, b_, 1e-11, f"{name} row chunk {rc}")
+
+
 PINS = [pin_bruteforce, pin_recurrent, pin_chunkwise, pin_closed_forms,
-        pin_row_subset, pin_linearity]
+        pin_row_subset, pin_linearity, pin_bwd_finite_differences,
+        pin_bwd_recurrent, pin_bwd_autograd, pin_bwd_closed_forms,
+        pin_bwd_chunkwise]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -147,6 +270,20 @@ MUTANTS = [
      "a = q[b, h, rr] @ q[b, h, :n1].T"),
     ("chunk_local_keys", "a = q[b, h, rr] @ k[b, h, :n1].T",
      "a = q[b, h, rr] @ np.concatenate([np.zeros_like(k[b, h, :rr[0]]), k[b, h, rr[0]:n1]]).T"),
+    # backward
+    ("bwd_strict_mask", "vis = j <= i  ", "vis = j < i  "),
+    ("bwd_unmasked_da", "da = np.where(vis, scale", "da = np.where(True, scale"),
+    ("bwd_dq_uses_v", "dq[b, h, r0:r1] = da @ k[b, h, :r1]",
+     "dq[b, h, r0:r1] = da @ v[b, h, :r1]"),
+    ("bwd_dk_uses_k", "dk[b, h, :r1] += da.T @ q[b, h, r0:r1]",
+     "dk[b, h, :r1] += da.T @ k[b, h, r0:r1]"),
+    ("bwd_dv_no_scale", "dv[b, h, :r1] += scale * (a.T @ do[b, h, r0:r1])",
+     "dv[b, h, :r1] += (a.T @ do[b, h, r0:r1])"),
+    ("bwd_dv_overwrites", "dv[b, h, :r1] += scale", "dv[b, h, :r1] = scale"),
+    ("bwd_da_transposed", "scale * (do[b, h, r0:r1] @ v[b, h, :r1].T)",
+     "scale * (v[b, h, r0:r1] @ do[b, h, :r1].T)"),
+    ("bwd_dk_from_a", "dk[b, h, :r1] += da.T @ q[b, h, r0:r1]",
+     "dk[b, h, :r1] += scale * a.T @ q[b, h, r0:r1]"),
 ]
 
 
