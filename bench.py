@@ -112,6 +112,9 @@ def cpu_baseline(w: S.Workload, inp: dict, target_s: float = 15.0) -> dict:
             return
         if w.linear:
             oracle.linear.linear_attention_fwd(q, k, v, inp["scale"])
+            if w.backward:
+                oracle.linear.linear_attention_bwd(q, k, v, inp["do"][sl],
+                                                   inp["scale"])
             return
         if inp.get("signs") is not None:
             oracle.fp8.fp8_forward(q, k, v, inp["scale"], inp["causal"],
@@ -140,8 +143,9 @@ def cpu_baseline(w: S.Workload, inp: dict, target_s: float = 15.0) -> dict:
     pairs = visible_pairs(sw, kv, None if bm is None else bm[:nh])
     flops = pairs * w.d * (4 + (10 if w.backward else 0))
     if w.linear:
-        flops = linear_flops(S.Workload(w.name, 1, nh, w.N, w.d, w.dtype, True,
-                                        w.seeds, linear=True))
+        sw = S.Workload(w.name, 1, nh, w.N, w.d, w.dtype, True, w.seeds,
+                        w.backward, linear=True)
+        flops = linear_flops(sw) + (linear_bwd_flops(sw) if w.backward else 0)
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -152,7 +156,8 @@ def cpu_baseline(w: S.Workload, inp: dict, target_s: float = 15.0) -> dict:
     except OSError:
         pass
     if w.linear:
-        what = "fp64 numpy causal linear attention (quadratic definition)"
+        what = ("fp64 numpy causal linear attention (quadratic definition"
+                + (", analytic gradients)" if w.backward else ")"))
     elif inp.get("signs") is not None:
         what = ("fp64 numpy model of the FP8 path (rotation, block "
                 "quantisation, fp64 attention), forward")
@@ -190,6 +195,17 @@ def linear_flops(w: S.Workload) -> float:
     return w.B * w.H * (4.0 * w.d * intra + 4.0 * w.N * w.d * w.d)
 
 
+def linear_bwd_flops(w: S.Workload) -> float:
+    """Algorithmic FLOPs of the chunkwise linear-attention backward: per
+    visible pair inside a chunk 4d for each of dQ, dK and dV (a score and
+    its product); per row 4d^2 for dQ's state (update and use) and 6d^2
+    for dK and dV (one shared state, which the kernels build twice, and
+    its two uses)."""
+    full, rem = divmod(w.N, LINEAR_CHUNK)
+    intra = full * LINEAR_CHUNK * (LINEAR_CHUNK + 1) // 2 + rem * (rem + 1) // 2
+    return w.B * w.H * (12.0 * w.d * intra + 10.0 * w.N * w.d * w.d)
+
+
 def fp8_workspace_bytes(w: S.Workload) -> int:
     """Quantised Q, K (rows of 144 or 80 bytes) and V (80 bytes per channel
     per 64 keys) of the FP8 path."""
@@ -210,6 +226,8 @@ def algorithmic_bytes(w: S.Workload, kernel: str) -> int:
         return fp8_workspace_bytes(w) + t + r
     if kernel == "linear_fwd":                   # Q,K,V -> O
         return 4 * t
+    if kernel == "linear_bwd":                   # Q,K,V,dO -> dQ,dK,dV
+        return 7 * t
     return {"fwd": 3 * t + t + r,             # Q,K,V -> O, LSE
             "bwd_preprocess": 2 * t + r,      # O, dO -> D
             "bwd_dkdv": 4 * t + 2 * r + 2 * t,  # Q,K,V,dO,LSE,D -> dK,dV
@@ -657,7 +675,9 @@ def time_workload(w: S.Workload, dev, steps: int, warmup: int,
                           dtype=torch.uint8, device=dev)
         score_scale = float(np.float32(scale) / np.float32(w.d))
     dq = dk = dv = None
-    if w.backward:
+    if w.backward and w.linear:
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    elif w.backward:
         ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.N, w.d),
                          dtype=torch.uint8, device=dev)
         dq, dk, dv = (torch.empty_like(q) for _ in range(3))
@@ -669,7 +689,7 @@ def time_workload(w: S.Workload, dev, steps: int, warmup: int,
     if fp8:
         names = ["fp8_quantize", "fwd_fp8"]
     if w.linear:
-        names = ["linear_fwd"]
+        names = ["linear_fwd"] + (["linear_bwd"] if w.backward else [])
 
     def step(events=None):
         def mark(i):
@@ -679,6 +699,9 @@ def time_workload(w: S.Workload, dev, steps: int, warmup: int,
         if w.linear:
             fa.fa_linear_fwd(q, k, v, o, scale, wsl)
             mark(1)
+            if w.backward:
+                fa.fa_linear_bwd(q, k, v, do, dq, dk, dv, scale, wsl)
+                mark(2)
             return
         if fp8:
             fa.fa_fp8_quantize(q, k, v, signs, ws8)
@@ -768,12 +791,17 @@ def result_line(w: S.Workload, res: dict, args) -> dict:
     per_kernel, ms_step, pairs = res["per_kernel"], res["ms_step"], res["pairs"]
     names, fp8, dr, inp = res["names"], res["fp8"], res["dropout"], res["inp"]
     fwd_flops = linear_flops(w) if w.linear else 4.0 * w.d * pairs
-    bwd_flops = 10.0 * w.d * pairs if w.backward else 0.0
+    bwd_flops = ((linear_bwd_flops(w) if w.linear else 10.0 * w.d * pairs)
+                 if w.backward else 0.0)
     step_flops = fwd_flops + bwd_flops
     value = step_flops / (ms_step * 1e-3) / 1e12
     peak = _peak(w, fp8)
 
-    if w.backward:
+    if w.backward and w.linear:
+        # fa_linear_bwd: three chunkwise passes (dQ; dK and dV reversed)
+        dom, dom_flops, src = ("linear_bwd", bwd_flops,
+                               ["fa_linear.hip", "fa_common.h"])
+    elif w.backward:
         # fa_bwd_dkdv produces dK and dV: S = Q K^T, dP = dO V^T, dV += P^T dO
         # and dK += dS^T Q, 2d FLOP each per visible pair.
         dom, dom_flops, src = ("bwd_dkdv", 8.0 * w.d * pairs,
@@ -841,7 +869,8 @@ def result_line(w: S.Workload, res: dict, args) -> dict:
                    "parallelism": "single GPU"},
         "frac_of_peak": round(value / peak, 4),
         "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},
-        "fwd_tflops": round(fwd_flops / (per_kernel[dom if (fp8 or w.linear)
+        "fwd_tflops": round(fwd_flops / (per_kernel["fwd_fp8" if fp8 else
+                                                    "linear_fwd" if w.linear
                                                     else "fwd"]
                                          * 1e-3) / 1e12, 2),
         "roofline": roofline,

@@ -234,6 +234,31 @@ int fa_linear_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 size_t fa_linear_workspace_size(int B, int H, int N, int d);
 
 /*
+ * Causal linear attention, backward ([LA2] abstract: the tiled computation
+ * serves the backward pass as well as the forward; [GLA] "proposed method":
+ * the chunkwise form is what makes training hardware-efficient).  The
+ * gradients of <dO, O> for O = scale * tril(Q K^T) V:
+ *     dQ_i = scale * sum_{j <= i} (dO_i . v_j) k_j
+ *     dK_j = scale * sum_{i >= j} (dO_i . v_j) q_i
+ *     dV_j = scale * sum_{i >= j} (q_i . k_j) dO_i
+ * dQ is the forward's chunk recurrence on (dO, V, K); dK and dV are the same
+ * recurrence walked from the last chunk to the first on (V, dO, Q) and
+ * (K, Q, dO), the state then summing the later chunks.  Three passes on one
+ * stream; float32 states and accumulation, scores and states rounded to bf16
+ * where they enter a matrix product, as in the forward.
+ *   q, k, v, dO   : [B,H,N,d] bf16, read only.
+ *   dq, dk, dv    : [B,H,N,d] bf16, written (must not alias the inputs).
+ *   workspace     : fa_linear_workspace_size(B, H, N, d) bytes (the same
+ *                   as the forward's; NULL allowed when that is 0), reused by
+ *                   each pass in stream order.
+ * d must be 64 or 128.  Errors as fa_linear_fwd.
+ */
+int fa_linear_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                  const uint16_t* dO, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                  void* workspace, size_t workspace_bytes, int B, int H, int N,
+                  int d, float scale, void* stream);
+
+/*
  * The dense backward entry points below take head dimension d = 64 or 128
  * (any other d returns FA_ERR_HEADDIM and fa_bwd_workspace_size returns 0);
  * d = 128 runs the pipelined kernels on grids that fill the chip, d = 64 the

@@ -31,7 +31,8 @@ __all__ = [
     "fa_fwd_block_sparse", "fa_bwd_block_sparse", "fa_bwd_dkdv_block_sparse",
     "fa_bwd_dq_block_sparse", "fa_fp8_workspace_size",
     "fa_fp8_quantize",
-    "fa_fwd_fp8_quantized", "fa_fwd_fp8", "fa_linear_fwd",
+    "fa_fwd_fp8_quantized", "fa_fwd_fp8", "fa_linear_fwd", "fa_linear_bwd",
+    "linear_backward",
     "fa_linear_workspace_size", "fa_fwd_dropout", "fa_bwd_dropout",
     "fa_bwd_dkdv_dropout", "fa_bwd_dq_dropout", "dropout_threshold",
     "forward",
@@ -70,6 +71,7 @@ _SIGS = {
     "fa_fwd_fp8": (_I, [_P] * 7 + [_S, _I, _I, _I, _I, _F, _I, _P]),
     "fa_linear_fwd": (_I, [_P] * 5 + [_S, _I, _I, _I, _I, _F, _P]),
     "fa_linear_workspace_size": (_S, [_I, _I, _I, _I]),
+    "fa_linear_bwd": (_I, [_P] * 8 + [_S, _I, _I, _I, _I, _F, _P]),
     "fa_bwd_block_sparse": (_I, [_P] * 11 + [_S, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_dkdv_block_sparse": (_I, [_P] * 9 + [_S, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_dq_block_sparse": (_I, [_P] * 8 + [_S, _I, _I, _I, _I, _F, _I, _P]),
@@ -539,6 +541,21 @@ def fa_linear_fwd(q, k, v, o, scale, workspace=None, stream=None):
     _check(st, "fa_linear_fwd")
 
 
+def fa_linear_bwd(q, k, v, dO, dq, dk, dv, scale, workspace=None,
+                  stream=None):
+    """C fa_linear_bwd: gradients of causal linear attention (bf16
+    [B,H,N,d]); workspace as fa_linear_fwd's."""
+    import torch
+    B, H, N, d = _bhnd(q)
+    _expect_all(((q, "q"), (k, "k"), (v, "v"), (dO, "dO"), (dq, "dq"),
+                 (dk, "dk"), (dv, "dv")), torch.bfloat16, (B, H, N, d))
+    wp, wn = (None, 0) if workspace is None else _ws(workspace)
+    st = lib().fa_linear_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(dq),
+                             _ptr(dk), _ptr(dv), wp, wn, B, H, N, d,
+                             float(scale), _stream(q, stream))
+    _check(st, "fa_linear_bwd")
+
+
 # ------------------------------------------------------------- convenience
 
 def forward(q, k, v, *, causal=False, scale=None, kv_len=None,
@@ -597,6 +614,20 @@ def linear_forward(q, k, v, *, scale=None, stream=None):
     ws = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
     fa_linear_fwd(q, k, v, o, scale, ws, stream)
     return o
+
+
+def linear_backward(q, k, v, dO, *, scale=None, stream=None):
+    """Gradients (dq, dk, dv) of causal linear attention
+    O = scale tril(Q K^T) V for the output gradient dO."""
+    import torch
+    B, H, N, d = _bhnd(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    n = fa_linear_workspace_size(B, H, N, d)
+    ws = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+    fa_linear_bwd(q, k, v, dO, dq, dk, dv, scale, ws, stream)
+    return dq, dk, dv
 
 
 def backward(q, k, v, o, lse, dO, *, causal=False, scale=None, stream=None,

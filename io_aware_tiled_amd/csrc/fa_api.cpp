@@ -216,6 +216,24 @@ int fa_linear_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                scale, (hipStream_t)stream);
 }
 
+int fa_linear_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                  const uint16_t* dO, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                  void* workspace, size_t workspace_bytes, int B, int H, int N,
+                  int d, float scale, void* stream) {
+  if (!q || !k || !v || !dO || !dq || !dk || !dv) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_ALIGN;
+  const size_t need = fa::linear_workspace_bytes(B, H, N, d);
+  if (need > 0 && (!workspace || ((uintptr_t)workspace & 255u) != 0 ||
+                   workspace_bytes < need))
+    return FA_ERR_WORKSPACE;
+  return fa::launch_linear_bwd(q, k, v, dO, dq, dk, dv, (float*)workspace, B,
+                               H, N, d, scale, (hipStream_t)stream);
+}
+
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   if (check_shape_bwd(B, H, N, d) != FA_OK) return 0;
   return ws_bytes(B, H, N);

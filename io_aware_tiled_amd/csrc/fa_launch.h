@@ -70,5 +70,9 @@ size_t linear_workspace_bytes(int B, int H, int N, int d);
 int launch_linear_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       uint16_t* o, float* ws, int B, int H, int N, int d,
                       float scale, hipStream_t stream);
+int launch_linear_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const uint16_t* dO, uint16_t* dq, uint16_t* dk,
+                      uint16_t* dv, float* ws, int B, int H, int N, int d,
+                      float scale, hipStream_t stream);
 
 }  // namespace fa

@@ -64,7 +64,12 @@ struct LinTile {
 // (no Q, no O).  Otherwise the workgroup produces O for its segment,
 // starting from the sum of the previous segments' states (zero for the
 // first segment or an unsplit sequence).
-template <int D, bool STATE_ONLY>
+// REV: the anti-causal form O_i = scale * sum_{j >= i} (q_i . k_j) v_j that
+// the backward needs: chunks are walked from the last to the first, a query
+// block sees the key blocks at or after it, the diagonal block keeps keys
+// at or after the query, and a segment starts from the states of the
+// segments after it.
+template <int D, bool STATE_ONLY, bool REV = false>
 __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
@@ -86,7 +91,8 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
   const int seg = (rest / NVB) % nseg;
   const int bh = (rest / NVB / nseg) * 8 + xcd;
   if (bh >= BH) return;
-  if (STATE_ONLY && seg == nseg - 1) return;   // no later segment needs it
+  // no other segment needs the state of the last (first, reversed) one
+  if (STATE_ONLY && seg == (REV ? 0 : nseg - 1)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -103,6 +109,13 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
   const int c_begin = seg * seg_chunks;
   const int nchunks = min(seg_chunks, nchunks_all - c_begin);   // this segment
   float* const st_base = seg_state + (size_t)(bh * NVB + vb) * nseg * kVB * D;
+  // Chunk processed at step u (in order, or from the segment's last).
+  auto chunk_of = [&](int u) -> int {
+    return REV ? c_begin + nchunks - 1 - u : c_begin + u;
+  };
+  // Segments whose states the segment starts from: the earlier ones, or
+  // (reversed) the later ones.
+  const int sp_begin = REV ? seg + 1 : 0, sp_end = REV ? nseg : seg;
 
   // ---- chunk loads by LDS DMA (buffer loads that write LDS, 16 bytes per
   // lane): slot p of a stage is 16 bytes of row p / RS; slots that are row
@@ -121,7 +134,7 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
   const unsigned lv0 = lds_addr(&lds_v[0][0]);
   auto dma = [&](int u) __attribute__((always_inline)) {
     const unsigned st = (unsigned)(u % kLS);
-    const int row0 = (c_begin + u) * kLC;
+    const int row0 = chunk_of(u) * kLC;
     // descriptors of this chunk's rows (they end at row N - 1)
     const int bytes = min(N - row0, kLC) * D * 2;
     const size_t base = (size_t)row0 * D;
@@ -172,11 +185,11 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
   // first chunk reads.
   for (int e = tid; e < kVB * T::SST / 8; e += kLThreads)
     *(u32x4*)(&lds_s[1][8 * e]) = u32x4{0u, 0u, 0u, 0u};
-  if (!STATE_ONLY && seg > 0 && w >= 2) {
+  if (!STATE_ONLY && sp_begin < sp_end && w >= 2) {
 #pragma unroll
     for (int i = 0; i < NDT; ++i) {
       const int dt = (w - 2) * NDT + i;
-      for (int sp = 0; sp < seg; ++sp) {
+      for (int sp = sp_begin; sp < sp_end; ++sp) {
         const float* src = st_base + (size_t)sp * kVB * D;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -185,7 +198,7 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
     }
   }
   __syncthreads();
-  if (!STATE_ONLY && seg > 0 && w >= 2) {
+  if (!STATE_ONLY && sp_begin < sp_end && w >= 2) {
 #pragma unroll
     for (int i = 0; i < NDT; ++i) {
       const int dt = (w - 2) * NDT + i;
@@ -210,43 +223,49 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
     __syncthreads();
     if (u + 2 < nchunks) dma(u + 2);
     const int sb = u & 1;
-    const int r0 = (c_begin + u) * kLC;
-    // ---- query block QB (wavefront QB): A^T = K Q^T for key blocks
-    // kb <= QB and the inter-chunk term S_{t-1}^T Q^T, as independent MFMA
-    // chains interleaved (a dependent chain would wait out each MFMA's
-    // latency), then the causal mask, A^T -> bf16 and V_t^T A^T.
+    const int r0 = chunk_of(u) * kLC;
+    // ---- query block QB (wavefront QB): A^T = K Q^T for the key blocks it
+    // sees (kb <= QB; reversed kb >= QB) and the inter-chunk term
+    // S_{t-1}^T Q^T, as independent MFMA chains interleaved (a dependent
+    // chain would wait out each MFMA's latency), then the mask of the
+    // diagonal block, A^T -> bf16 and V_t^T A^T.
     auto query_block = [&](auto qb_tag) __attribute__((always_inline)) {
       constexpr int QB = decltype(qb_tag)::value;
+      constexpr int NK = REV ? 2 - QB : QB + 1;   // key blocks seen
+      constexpr int KB0 = REV ? QB : 0;           // the first of them
+      constexpr int KD = QB - KB0;                // the diagonal one
       const int sr = sb ^ 1;
-      f32x16 s[QB + 1], oin = f32x16{};
+      f32x16 s[NK], oin = f32x16{};
 #pragma unroll
-      for (int kb = 0; kb <= QB; ++kb) s[kb] = f32x16{};
+      for (int i = 0; i < NK; ++i) s[i] = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         const bf16x8 qf =
             *(const bf16x8*)(&lds_q[b][(32 * QB + lq) * T::QST + 16 * kk + 8 * hh]);
 #pragma unroll
-        for (int kb = 0; kb <= QB; ++kb)
-          s[kb] = mfma32x16(
-              *(const bf16x8*)(&lds_k[b][(32 * kb + lq) * T::QST + 16 * kk + 8 * hh]),
-              qf, s[kb]);
+        for (int i = 0; i < NK; ++i)
+          s[i] = mfma32x16(
+              *(const bf16x8*)(&lds_k[b][(32 * (KB0 + i) + lq) * T::QST + 16 * kk + 8 * hh]),
+              qf, s[i]);
         oin = mfma32x16(*(const bf16x8*)(&lds_s[sr][lq * T::SST + 16 * kk + 8 * hh]),
                         qf, oin);
       }
-      // causal mask inside the diagonal block: key 8(r/4) + 4hh + r%4
-      // against query lq.
+      // mask inside the diagonal block: key 8(r/4) + 4hh + r%4 against
+      // query lq (keys after the query hidden; reversed, keys before it).
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (8 * (r / 4) + 4 * hh + (r % 4) > lq) s[QB][r] = 0.f;
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r / 4) + 4 * hh + (r % 4);
+        if (REV ? key < lq : key > lq) s[KD][r] = 0.f;
+      }
       f32x16 oacc = f32x16{};
 #pragma unroll
-      for (int kb = 0; kb <= QB; ++kb)
+      for (int i = 0; i < NK; ++i)
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           f32x8 p;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) p[e] = s[kb][8 * c + e];
-          oacc = mfma32x16(vt_frag(b, kb, c), to_bf16x8(p), oacc);
+          for (int e = 0; e < 8; ++e) p[e] = s[i][8 * c + e];
+          oacc = mfma32x16(vt_frag(b, KB0 + i, c), to_bf16x8(p), oacc);
         }
       // ---- store O rows r0 + 32QB + lq, columns 32vb + 8g + 4hh + 0..3.
       const int row = r0 + 32 * QB + lq;
@@ -359,6 +378,35 @@ int launch_linear_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     FA_LIN_LAUNCH(64, false);
   }
 #undef FA_LIN_LAUNCH
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// Backward of O = scale * tril(Q K^T) V for the loss <dO, O>, as three
+// passes of the chunkwise kernel (the workspace, when the sequence is split,
+// is reused by each pass in stream order):
+//   dQ_i = scale sum_{j <= i} (dO_i . v_j) k_j   causal, (dO, V, K);
+//   dK_j = scale sum_{i >= j} (v_j . dO_i) q_i   reversed, (V, dO, Q);
+//   dV_j = scale sum_{i >= j} (k_j . q_i) dO_i   reversed, (K, Q, dO).
+int launch_linear_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const uint16_t* dO, uint16_t* dq, uint16_t* dk,
+                      uint16_t* dv, float* ws, int B, int H, int N, int d,
+                      float scale, hipStream_t stream) {
+  const int BH = B * H;
+  const int nvb = d / kVB;
+  int nseg, seg_chunks;
+  linear_split(B, H, N, d, nseg, seg_chunks);
+  const dim3 grid((unsigned)(((BH + 7) / 8) * 8 * nvb * nseg)), block(kLThreads);
+#define FA_LIN_PASS(DD, RR, A, BB, C, OUT)                                        do {                                                                              if (nseg > 1)                                                                     hipLaunchKernelGGL((linear_fwd_kernel<DD, true, RR>), grid, block, 0,                              stream, A, BB, C, OUT, ws, BH, N, nseg, seg_chunks,                             scale);                                                    hipLaunchKernelGGL((linear_fwd_kernel<DD, false, RR>), grid, block, 0,                             stream, A, BB, C, OUT, ws, BH, N, nseg, seg_chunks,                             scale);                                                    } while (0)
+  if (d == 128) {
+    FA_LIN_PASS(128, false, dO, v, k, dq);
+    FA_LIN_PASS(128, true, v, dO, q, dk);
+    FA_LIN_PASS(128, true, k, q, dO, dv);
+  } else {
+    FA_LIN_PASS(64, false, dO, v, k, dq);
+    FA_LIN_PASS(64, true, v, dO, q, dk);
+    FA_LIN_PASS(64, true, k, q, dO, dv);
+  }
+#undef FA_LIN_PASS
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

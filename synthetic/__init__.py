@@ -118,6 +118,10 @@ WORKLOADS = {
                  (801, 802, 803), linear=True,
                  description="causal linear attention (chunkwise), head dim "
                              "128"),
+        Workload("linear_causal_fwd_bwd_d128", 4, 16, 4096, 128, "bf16", True,
+                 (801, 802, 803, 804), backward=True, linear=True,
+                 description="causal linear attention forward + backward "
+                             "(chunkwise), head dim 128"),
         Workload("dropout_causal_fwd_bwd_d128", 4, 16, 4096, 128, "bf16", True,
                  (901, 902, 903, 904), backward=True, drop_p=0.1,
                  drop_seed=0x243F6A8885A308D3,

@@ -243,6 +243,19 @@ def test_linear_argument_errors():
     assert fa.fa_linear_workspace_size(4, 16, 4096, 128) == 0
     assert fa.fa_linear_workspace_size(1, 1, 64, 96) == 0
 
+    def lb(ptrs=None, B=1, N=64, d=128, ws=None, wsb=0):
+        p = ptrs or [A] * 7
+        return L.fa_linear_bwd(*p, ws, wsb, B, 2, N, d, 0.1, None)
+    for i in range(7):
+        p = [A] * 7
+        p[i] = None
+        assert lb(p) == NULL, i
+        p[i] = MIS
+        assert lb(p) == ALIGN, i
+    assert lb(B=0) == SHAPE and lb(d=96) == HEADDIM
+    assert lb(N=20000) == WORKSPACE
+    assert lb(N=20000, ws=W, wsb=n - 1) == WORKSPACE
+
 
 def test_python_binding_refuses_host_tensors():
     import torch
