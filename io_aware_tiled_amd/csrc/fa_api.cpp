@@ -5,7 +5,28 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa_launch.h"
+
+namespace fa {
+
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::once_flag once[kMaxDevices];
+  static int cus[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return 256;
+  std::call_once(once[dev], [dev] {
+    int n = 0;
+    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount,
+                                      dev) == hipSuccess && n > 0) ? n : 256;
+  });
+  return cus[dev];
+}
+
+}  // namespace fa
 
 namespace {
 

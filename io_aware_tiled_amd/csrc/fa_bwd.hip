@@ -1521,7 +1521,7 @@ int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   // every block-sparse or dropout call: the pipelined kernel (4 wavefronts,
   // K/V in registers); the rest (and head dim 64, with or without dropout):
   // 8 wavefronts.
-  if (d == kD && ((long long)B * H * n_kblk >= 256 || block_mask != nullptr ||
+  if (d == kD && ((long long)B * H * n_kblk >= device_cu_count() || block_mask != nullptr ||
                   drop != nullptr)) {
     const dim3 grid((unsigned)(B * H * n_kblk)), block(256);
 #define FA_DKDV_LAUNCH(CC, SS)                                                  \
@@ -1588,7 +1588,8 @@ int launch_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   // call: the pipelined kernel; the rest (and head dim 64, with or without
   // dropout): 128-row workgroups, two per CU.
   const long long grid256 = (long long)B * H * ((N + kDqPBR - 1) / kDqPBR);
-  if (d == kD && (grid256 >= 256 || block_mask != nullptr || drop != nullptr)) {
+  if (d == kD && (grid256 >= device_cu_count() || block_mask != nullptr ||
+                  drop != nullptr)) {
     const int n_qblk = (N + kDqPBR - 1) / kDqPBR;
     const dim3 grid((unsigned)(B * H * n_qblk)), block(512);
 #define FA_DQ_LAUNCH(CC, SS)                                                  \

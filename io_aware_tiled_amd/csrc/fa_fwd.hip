@@ -1218,11 +1218,11 @@ int launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   // 128-row workgroups, two per CU.  Block-sparse calls always take the
   // pipelined kernel (one 256-row workgroup per block-mask row), and so do
   // calls with dropout.
-  constexpr int kCUs = 256;
+  const int cus = device_cu_count();
   const bool sparse = block_mask != nullptr;
   const long long grid256 = (long long)B * H * ((N + 255) / 256);
-  const bool pipe = sparse || drop != nullptr || grid256 >= kCUs;
-  const bool two_blocks = d == 64 && grid256 >= 2 * kCUs;
+  const bool pipe = sparse || drop != nullptr || grid256 >= cus;
+  const bool two_blocks = d == 64 && grid256 >= 2 * cus;
   const int br = pipe ? 256 : 128;
   const int n_qblk = (N + br - 1) / br;
   const dim3 grid((unsigned)(B * H * n_qblk));

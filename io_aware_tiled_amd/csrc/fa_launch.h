@@ -60,6 +60,10 @@ int launch_fwd_fp8(const uint8_t* ws, uint16_t* o, float* lse, int B, int H,
                    int N, int d, float score_scale, int causal,
                    hipStream_t stream);
 
+// Compute units of the current device (hipDeviceAttributeMultiprocessorCount,
+// read once per device; 256 if the query fails).
+int device_cu_count();
+
 // Device address of the fixed backward scratch (FA_BWD_NOALLOC_MAX_ROWS
 // float32) on the current device, looked up once per device; 0 or -6.
 int noalloc_scratch(void** addr);

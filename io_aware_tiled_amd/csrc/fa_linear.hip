@@ -338,7 +338,9 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
 }  // namespace
 
 // Split of a head's chunks into segments (one workgroup each) when the
-// heads and value blocks alone leave the chip's CUs idle.
+// heads and value blocks alone leave the chip's CUs idle.  The CU count is
+// MI355X's, fixed so that the workspace size (which depends on the split)
+// does not depend on which device is current when it is queried.
 void linear_split(int B, int H, int N, int d, int& nseg, int& seg_chunks) {
   constexpr int kCUs = 256, kMinSegChunks = 4;
   const long long wgs = (long long)B * H * (d / kVB);
