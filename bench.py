@@ -543,6 +543,102 @@ def summarize_trace(w: S.Workload, path, command, warmup: int,
     return 0
 
 
+MICRO_LIB = os.path.join(ROOT, "microbench", "libmicro.so")
+
+
+def micro(command: str) -> int:
+    """Microbenchmarks of the hardware features the kernels rely on
+    (microbench/micro.hip), one workgroup of 256 x wps threads per CU on
+    every CU; writes profiles/microbench.md.  Cycles are shader-clock cycles
+    per wavefront (s_memtime) over the timed loop; the clock is cycles per
+    microsecond of the 100 MHz constant clock (s_memrealtime)."""
+    import ctypes
+    import torch
+    if not os.path.exists(MICRO_LIB):
+        print(f"{MICRO_LIB} is missing: build it with "
+              "`python -m io_aware_tiled_amd.build`", file=sys.stderr)
+        return 1
+    torch.cuda.init()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    L = ctypes.CDLL(MICRO_LIB)
+    L.micro_run.restype = ctypes.c_int
+    L.micro_run.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_double)] * 3
+
+    def run(which, wps, constant, iters):
+        c, u, ms = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+        st = L.micro_run(which, wps, constant, iters, cus, ctypes.byref(c),
+                         ctypes.byref(u), ctypes.byref(ms))
+        if st != 0:
+            raise RuntimeError(f"micro_run({which}) failed: HIP error {st}")
+        return c.value, u.value, ms.value
+
+    rows = []
+    # matrix cores: 4 independent chains (throughput), 1 chain (latency)
+    for chains, which in ((4, 1), (1, 0)):
+        for constant in (0, 1):
+            for wps in (1, 2):
+                it = 2000
+                c, u, ms = run(which, wps, constant, it)
+                n = it * chains
+                flop = cus * 4 * wps * n * 32768.0
+                rows.append(("v_mfma_f32_32x32x16_bf16", f"{chains} chain(s), "
+                             + ("constant" if constant else "random") + " operands",
+                             wps, f"{c / n:.1f} cycles/MFMA per wave",
+                             f"{flop / (ms * 1e-3) / 1e12:.0f} TFLOP/s, {c / u / 1e3:.2f} GHz"))
+    for which, name in ((2, "v_fma_f32"), (4, "v_add_f32"), (9, "v_exp_f32"),
+                        (3, "v_exp_f32 + v_fma_f32")):
+        for wps in (1, 2, 4):
+            it = 4000
+            c, u, ms = run(which, wps, 0, it)
+            rows.append((name, "8 independent chains", wps,
+                         f"{c / (it * 8):.2f} cycles/instruction per wave, "
+                         f"{c / (it * 8) / wps:.2f} per SIMD",
+                         f"{c / u / 1e3:.2f} GHz"))
+    for wps in (1, 2):
+        it = 2000
+        c0, _, ms0 = run(1, wps, 0, it)
+        c1, u1, ms1 = run(5, wps, 0, it)
+        flop = cus * 4 * wps * it * 4 * 32768.0
+        rows.append(("MFMA + 4 FMA after each", "4 MFMA chains, random", wps,
+                     f"{c1 / (it * 4):.1f} cycles per MFMA slot per wave (MFMA "
+                     f"alone {c0 / (it * 4):.1f})",
+                     f"{flop / (ms1 * 1e-3) / 1e12:.0f} TFLOP/s (MFMA alone "
+                     f"{flop / (ms0 * 1e-3) / 1e12:.0f}), {c1 / u1 / 1e3:.2f} GHz"))
+    for which, name, per, rowb in ((6, "ds_read_b128 (row slices)", 1024, 272),
+                                   (7, "2 x ds_read_b64_tr_b16 (transposed)", 1024, 320)):
+        for wps in (1, 2, 4):
+            it = 4000
+            c, u, ms = run(which, wps, 0, it)
+            byts = 4 * wps * it * 8 * per
+            ghz = c / u / 1e3
+            agg = byts / (ms * 1e-3 * ghz * 1e9)   # per CU over the kernel time
+            rows.append((name, f"8 operands per iteration, {rowb}-byte rows", wps,
+                         f"{byts / c:.0f} bytes/cycle per CU (per-wave loop "
+                         f"time), {agg:.0f} over the kernel time",
+                         f"{ghz:.2f} GHz"))
+    for wps in (1, 2, 4):
+        it = 2000
+        c, u, _ = run(8, wps, 0, it)
+        byts = 4 * wps * it * 8 * 1024
+        rows.append(("buffer_load_dwordx4 ... lds (LDS DMA)",
+                     "8 x 1 KB per wave, L2-resident source", wps,
+                     f"{byts / c:.0f} bytes/cycle per CU",
+                     f"{byts / (c / (c / u)) / 1e3 * cus:.0f} GB/s chip"))
+    md = os.path.join(PROFILES, "microbench.md")
+    with open(md, "w") as f:
+        f.write("# Microbenchmarks (microbench/micro.hip), one MI355X\n\n"
+                f"Command (repository root):\n\n```\n{command}\n```\n\n"
+                f"One workgroup of 256 x wps threads per CU on all {cus} CUs; "
+                "per-wavefront shader cycles (s_memtime) of the timed loop; "
+                "clock = cycles / microseconds of s_memrealtime (100 MHz).\n\n"
+                "| instruction | pattern | waves per SIMD | result | rate / clock |\n"
+                "|---|---|---|---|---|\n")
+        for r in rows:
+            f.write("| " + " | ".join(str(x) for x in r) + " |\n")
+    print(open(md).read(), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -588,6 +684,9 @@ def main(argv=None) -> int:
                     help="time the bf16 forward and backward kernels over "
                          "sequence lengths 1K..32K at a fixed token count "
                          "and print a markdown table")
+    ap.add_argument("--micro", action="store_true",
+                    help="run the hardware microbenchmarks (microbench/) and "
+                         "write profiles/microbench.md")
     ap.add_argument("--command", default="",
                     help="with --traffic-from / --summarize-trace: the "
                          "command that made the CSVs")
@@ -625,6 +724,8 @@ def main(argv=None) -> int:
         return 0
     if args.sweep:
         return sweep(dev)
+    if args.micro:
+        return micro(args.command or "python bench.py --micro")
     w = S.WORKLOADS[args.workload]
     res = time_workload(w, dev, args.steps, args.warmup,
                         copy_calibration=args.copy_calibration)

@@ -58,6 +58,24 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
+MICRO_SRC = os.path.join(ROOT, "microbench", "micro.hip")
+MICRO_LIB = os.path.join(ROOT, "microbench", "libmicro.so")
+
+
+def build_micro(verbose: bool = False) -> str:
+    """Compile the microbenchmark library (not part of libfa) that
+    bench.py --micro drives."""
+    tmp = MICRO_LIB + ".tmp"
+    cmd = [hipcc(), *COMMON, "-shared", MICRO_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for micro.hip:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, MICRO_LIB)
+    if verbose:
+        print(f"built {MICRO_LIB}")
+    return MICRO_LIB
+
+
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     """Compile every source and link libfa.so; returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
@@ -78,3 +96,4 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
 
 if __name__ == "__main__":
     build(verbose=True, extra=sys.argv[1:])
+    build_micro(verbose=True)

@@ -1337,9 +1337,16 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
       return join_bf16(lds_read_tr16(&lds_k[stc][row * kRS + col]),
                        lds_read_tr16(&lds_k[stc][(row + 8) * kRS + col]));
     };
+    // Operand of slot m: the S^T and dP^T products alternate (S_0, dP_0,
+    // S_1, dP_1, ...) so that no MFMA is issued right after one that
+    // accumulates into the same registers (a dependent issue waits out the
+    // instruction's latency); the dQ products follow.
+    auto op_of = [](int m) constexpr -> int {
+      return m < 2 * kS ? ((m & 1) ? kS + (m >> 1) : (m >> 1)) : m;
+    };
     bf16x8 op[kPf];
 #pragma unroll
-    for (int i = 0; i < kPf; ++i) op[i] = fetch(i);
+    for (int i = 0; i < kPf; ++i) op[i] = fetch(op_of(i));
     // VALU: 16 elements as a three-stage pipeline over the MFMA slots
     // (FMA, then exp2, then dS and, per 8 elements, the bf16 conversion);
     // the dQ MFMAs come last, after each half of dS^T is converted.
@@ -1347,11 +1354,12 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
 #pragma unroll
     for (int m = 0; m < kN; ++m) {
       const bf16x8 a = op[m % kPf];
-      if (m + kPf < kN) op[m % kPf] = fetch(m + kPf);
-      if (m < kS) {
-        s[XS] = mfma32x16(a, qf[m], m == 0 ? f32x16{} : s[XS]);
-      } else if (m < 2 * kS) {
-        const int kk = m - kS;
+      if (m + kPf < kN) op[m % kPf] = fetch(op_of(m + kPf));
+      const int i = op_of(m);
+      if (i < kS) {
+        s[XS] = mfma32x16(a, qf[i], i == 0 ? f32x16{} : s[XS]);
+      } else if (i < 2 * kS) {
+        const int kk = i - kS;
         if constexpr (DROP) {
           // The splat of -k D is rebuilt per step from one register (the
           // dropout variant has no registers to keep all sixteen live).
@@ -1372,7 +1380,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
         // Half 0 of dS^T (converted in slot 9) feeds the first D/32 of
         // these MFMAs, half 1 (converted in slot 17) the last D/32, which
         // start at slot 2 kS + D/32 = 20: each half is ready before use.
-        const int pi = m - 2 * kS;
+        const int pi = i - 2 * kS;
         dq_acc[pi % (D / 32)] = mfma32x16(a, dsb[pi / (D / 32)], dq_acc[pi % (D / 32)]);
       }
       if (m < 16) x[m] = __builtin_fmaf(s[XE][m], c_log2, -lse2);

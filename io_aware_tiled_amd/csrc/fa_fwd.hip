@@ -617,31 +617,46 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
     return drop_keep(kz[c][r / 4], r % 4, drop.p8);
   };
 
+  // ---- operands of a step: operand i < kS is K's 32x16 slice i (S^T =
+  // K Q^T), operand kS + pi is V^T's slice pi (O^T += V^T P^T; d-block
+  // pi / 2, 16-key half pi % 2), for the K stage / 32-key half (stk, kbs)
+  // and the V stage / half (stv, kbv).
+  constexpr int kS = D / 16;             // S MFMAs per block
+  constexpr int kP = 2 * (D / 32);       // PV MFMAs per block
+  constexpr int kN = kS + kP;            // operand reads (each used NB times)
+  static_assert(!XP || (kN % kPf == 0 && kPf <= kS), "ring alignment");
+  auto fetch_op = [&](int i, int stk, int kbs, int stv, int kbv) -> bf16x8 {
+    if (i < kS)
+      return *(const bf16x8*)(&lds_k[stk][(32 * kbs + lq) * T::KST + 8 * hh + 16 * i]);
+    const int pi = i - kS;
+    const int db = pi / 2, h = pi % 2;
+    const int dcol = 32 * db + 16 * dsub + 4 * (r16 & 3);
+    const int key = 32 * kbv + 16 * h + 4 * hh + (r16 >> 2);
+    return join_bf16(lds_read_tr16(&lds_v[stv][key * T::VST + dcol]),
+                     lds_read_tr16(&lds_v[stv][(key + 8) * T::VST + dcol]));
+  };
+  // Operand of MFMA slot k (per block).  With one block per wavefront the S
+  // and P V products alternate (S_0, PV_0, S_1, PV_1, ...) so that no MFMA
+  // is issued right after one that accumulates into the same registers (a
+  // dependent issue waits out the instruction's latency, which is longer
+  // than its issue interval); with two blocks the blocks alternate instead.
+  static_assert(NB != 1 || kS == kP, "alternating slots");
+  auto op_of = [](int k) constexpr -> int {
+    return NB == 1 ? ((k & 1) ? kS + (k >> 1) : (k >> 1)) : k;
+  };
+
   auto step = [&](auto xs_tag, int stk, int kbs, int stv, int kbv, int nstk,
-                  int nkbs, int k0n) {
+                  int nkbs, int nstv, int nkbv, int k0n) {
     constexpr int XS = decltype(xs_tag)::value;
     constexpr int XE = 1 - XS;
-    constexpr int kS = D / 16;             // S MFMAs per block
-    constexpr int kP = 2 * (D / 32);       // PV MFMAs per block
-    constexpr int kN = kS + kP;            // operand reads (each used twice)
-    static_assert(!XP || (kN % kPf == 0 && kPf <= kS), "ring alignment");
-    auto fetch = [&](int i) -> bf16x8 {
-      if (i < kS)
-        return *(const bf16x8*)(&lds_k[stk][(32 * kbs + lq) * T::KST + 8 * hh + 16 * i]);
-      const int pi = i - kS;
-      const int db = pi / 2, h = pi % 2;
-      const int dcol = 32 * db + 16 * dsub + 4 * (r16 & 3);
-      const int key = 32 * kbv + 16 * h + 4 * hh + (r16 >> 2);
-      return join_bf16(lds_read_tr16(&lds_v[stv][key * T::VST + dcol]),
-                       lds_read_tr16(&lds_v[stv][(key + 8) * T::VST + dcol]));
-    };
+    auto fetch = [&](int i) -> bf16x8 { return fetch_op(i, stk, kbs, stv, kbv); };
     auto fetch_next = [&](int i) -> bf16x8 {
-      return *(const bf16x8*)(&lds_k[nstk][(32 * nkbs + lq) * T::KST + 8 * hh + 16 * i]);
+      return fetch_op(i, nstk, nkbs, nstv, nkbv);
     };
     bf16x8 op[XP ? 1 : kPf];   // the ring of a step when it is not carried
     if constexpr (!XP) {
 #pragma unroll
-      for (int i = 0; i < kPf; ++i) op[i] = fetch(i);
+      for (int k = 0; k < kPf; ++k) op[k] = fetch(op_of(k));
     }
     // The 16 NB exponentials of the step (16 per block, element el -> block
     // el / 16, half (el / 8) % 2, register el % 8) run as a three-stage
@@ -696,15 +711,16 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
 #pragma unroll
     for (int m = 0; m < kM + 2; ++m) {
       if (m < kM) {
-        const int i = m / NB, c = m % NB;
+        const int k = m / NB, c = m % NB, i = op_of(k);
         bf16x8 a;
         if constexpr (XP) {
-          a = opr[i % kPf];
+          a = opr[k % kPf];
           if (c == NB - 1)
-            opr[i % kPf] = i + kPf < kN ? fetch(i + kPf) : fetch_next(i + kPf - kN);
+            opr[k % kPf] = k + kPf < kN ? fetch(op_of(k + kPf))
+                                        : fetch_next(op_of(k + kPf - kN));
         } else {
-          a = op[i % kPf];
-          if (c == NB - 1 && i + kPf < kN) op[i % kPf] = fetch(i + kPf);
+          a = op[k % kPf];
+          if (c == NB - 1 && k + kPf < kN) op[k % kPf] = fetch(op_of(k + kPf));
         }
         if (i < kS) {
           s[XS][c] = mfma32x16(a, qf[c][i], i == 0 ? f32x16{} : s[XS][c]);
@@ -859,9 +875,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
       gen_end();
     }
     if constexpr (XP) {
+      // the first step's operands: K_0 half 1, and (zeros) V stage NS - 1
 #pragma unroll
-      for (int i = 0; i < kPf; ++i)
-        opr[i] = *(const bf16x8*)(&lds_k[0][(32 + lq) * T::KST + 8 * hh + 16 * i]);
+      for (int k = 0; k < kPf; ++k) opr[k] = fetch_op(op_of(k), 0, 1, NS - 1, 1);
     }
     // Tile j: wait for K_{j+1} and V_j, barrier, issue the next DMAs.  No
     // fence: LDS is only read in the loop, and every read of a stage has
@@ -882,10 +898,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
       top(j, entry(j + LK), entry(j + LV));
       const int st0 = j % NS, st1 = (j + 1) % NS, stm = (j + NS - 1) % NS;
       const int kj = key_tile(ej) * kBC, kj1 = key_tile(ej1) * kBC;
-      step(std::integral_constant<int, 1>{}, st0, 1, stm, 1, st1, 0, kj + 32);
+      step(std::integral_constant<int, 1>{}, st0, 1, stm, 1, st1, 0, st0, 0, kj + 32);
       settle(0);
       mask_half(1, ej, 1);
-      step(std::integral_constant<int, 0>{}, st1, 0, st0, 0, st1, 1, kj1);
+      step(std::integral_constant<int, 0>{}, st1, 0, st0, 0, st1, 1, st0, 1, kj1);
       settle(1);
       if (j + 1 < nt_w) mask_half(0, ej1, 0);
     }
@@ -929,9 +945,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
       gen_end();
     }
     if constexpr (XP) {
+      // the first step's operands: K_0 half 1, and (zeros) V stage 2
 #pragma unroll
-      for (int i = 0; i < kPf; ++i)
-        opr[i] = *(const bf16x8*)(&lds_k[0][(32 + lq) * T::KST + 8 * hh + 16 * i]);
+      for (int k = 0; k < kPf; ++k) opr[k] = fetch_op(op_of(k), 0, 1, 2, 1);
     }
     // Stages: K_j and V_j in stage j % 3.  Tile j stores K_{j+1} and V_j,
     // then loads K_{j+2} and V_{j+1}.
@@ -947,11 +963,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
       if (__builtin_expect(j < nt_w, 1)) {
         const int kj = key_tile(ej) * kBC, kj1 = key_tile(ej1) * kBC;
         // step 2j: S of (j, half 1) || P of (j, half 0); O += (j-1, half 1)
-        step(std::integral_constant<int, 1>{}, st0, 1, stm, 1, st1, 0, kj + 32);
+        step(std::integral_constant<int, 1>{}, st0, 1, stm, 1, st1, 0, st0, 0, kj + 32);
         settle(0);
         mask_half(1, ej, 1);
         // step 2j+1: S of (j+1, half 0) || P of (j, half 1); O += (j, half 0)
-        step(std::integral_constant<int, 0>{}, st1, 0, st0, 0, st1, 1, kj1);
+        step(std::integral_constant<int, 0>{}, st1, 0, st0, 0, st1, 1, st0, 1, kj1);
         settle(1);
         if (j + 1 < nt_w) mask_half(0, ej1, 0);
       } else if (j == nt_w) {
