@@ -53,3 +53,34 @@ def test_algorithmic_bytes():
     assert bench.algorithmic_bytes(w, "fp8_quantize") == 3 * t + ws
     assert bench.algorithmic_bytes(S.WORKLOADS["linear_causal_d128"],
                                    "linear_fwd") == 4 * t
+
+
+def test_linear_backward_counts():
+    """FLOPs and compulsory bytes of the linear-attention backward: 12d per
+    visible pair inside a chunk and 10d^2 per row; Q, K, V, dO read and dQ,
+    dK, dV written once."""
+    w = S.WORKLOADS["linear_causal_fwd_bwd_d128"]
+    assert w.backward and w.linear
+    assert bench.linear_bwd_flops(w) == 64 * (12.0 * 128 * 64 * (64 * 65 // 2)
+                                              + 10.0 * 4096 * 128 * 128)
+    t = 4 * 16 * 4096 * 128 * 2
+    assert bench.algorithmic_bytes(w, "linear_bwd") == 7 * t
+
+
+def test_summarize_trace_keeps_timed_dispatches(tmp_path, monkeypatch):
+    """The kernel-trace summary skips each kernel's warmup dispatches and
+    keeps the next `steps` ones."""
+    import csv
+    path = tmp_path / "trace.csv"
+    with open(path, "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(["Kernel_Name", "Dispatch_Id", "Start_Timestamp",
+                     "End_Timestamp"])
+        for i in range(8):   # 3 warmup dispatches of 900 ns, 5 timed of 100
+            wr.writerow(["void fa::k(int)", i, 0, 900 if i < 3 else 100])
+        wr.writerow(["void other(int)", 99, 0, 5])
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    w = S.WORKLOADS["tiny_f32"]
+    assert bench.summarize_trace(w, str(path), "cmd", 3, 5) == 0
+    text = (tmp_path / "kernels_tiny_f32.md").read_text()
+    assert "| `fa::k` | 5 | 0.1 | 0.1 | 0.1 |" in text
