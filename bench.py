@@ -792,55 +792,69 @@ def time_workload(w: S.Workload, dev, steps: int, warmup: int,
     if w.linear:
         names = ["linear_fwd"] + (["linear_bwd"] if w.backward else [])
 
-    def step(events=None):
-        def mark(i):
-            if events is not None:
-                events[i].record(stream)
-        mark(0)
-        if w.linear:
-            fa.fa_linear_fwd(q, k, v, o, scale, wsl)
-            mark(1)
-            if w.backward:
-                fa.fa_linear_bwd(q, k, v, do, dq, dk, dv, scale, wsl)
-                mark(2)
-            return
-        if fp8:
-            fa.fa_fp8_quantize(q, k, v, signs, ws8)
-            mark(1)
-            fa.fa_fwd_fp8_quantized(ws8, o, lse, score_scale, causal)
-            mark(2)
-            return
-        if w.dtype == "f32":
-            fa.fa_fwd_f32(q, k, v, o, lse, scale, causal)
-        elif dr is not None:
-            fa.fa_fwd_dropout(q, k, v, o, lse, scale, causal, dr["p"],
-                              dr["seed"], dr["offset"])
-        elif bmask is not None:
-            fa.fa_fwd_block_sparse(q, k, v, bmask, o, lse, scale, causal)
-        else:
-            fa.fa_fwd_kvlen(q, k, v, kv, o, lse, scale, causal)
-        mark(1)
+    # One zero-argument binding call per kernel, in step order.
+    if w.linear:
+        stages = [lambda: fa.fa_linear_fwd(q, k, v, o, scale, wsl)]
         if w.backward:
-            fa.fa_bwd_preprocess(o, do, ws)
-            mark(2)
+            stages.append(lambda: fa.fa_linear_bwd(q, k, v, do, dq, dk, dv,
+                                                   scale, wsl))
+    elif fp8:
+        stages = [lambda: fa.fa_fp8_quantize(q, k, v, signs, ws8),
+                  lambda: fa.fa_fwd_fp8_quantized(ws8, o, lse, score_scale,
+                                                  causal)]
+    else:
+        if w.dtype == "f32":
+            fwd = lambda: fa.fa_fwd_f32(q, k, v, o, lse, scale, causal)
+        elif dr is not None:
+            fwd = lambda: fa.fa_fwd_dropout(q, k, v, o, lse, scale, causal,
+                                            dr["p"], dr["seed"], dr["offset"])
+        elif bmask is not None:
+            fwd = lambda: fa.fa_fwd_block_sparse(q, k, v, bmask, o, lse,
+                                                 scale, causal)
+        else:
+            fwd = lambda: fa.fa_fwd_kvlen(q, k, v, kv, o, lse, scale, causal)
+        stages = [fwd]
+        if w.backward:
+            stages.append(lambda: fa.fa_bwd_preprocess(o, do, ws))
             if dr is not None:
-                fa.fa_bwd_dkdv_dropout(q, k, v, do, lse, dk, dv, ws, scale,
-                                       causal, dr["p"], dr["seed"], dr["offset"])
+                stages += [
+                    lambda: fa.fa_bwd_dkdv_dropout(q, k, v, do, lse, dk, dv, ws,
+                                                   scale, causal, dr["p"],
+                                                   dr["seed"], dr["offset"]),
+                    lambda: fa.fa_bwd_dq_dropout(q, k, v, do, lse, dq, ws, scale,
+                                                 causal, dr["p"], dr["seed"],
+                                                 dr["offset"])]
             elif bmask is not None:
-                fa.fa_bwd_dkdv_block_sparse(q, k, v, do, lse, bmask, dk, dv,
-                                            ws, scale, causal)
+                stages += [
+                    lambda: fa.fa_bwd_dkdv_block_sparse(q, k, v, do, lse, bmask,
+                                                        dk, dv, ws, scale,
+                                                        causal),
+                    lambda: fa.fa_bwd_dq_block_sparse(q, k, v, do, lse, bmask,
+                                                      dq, ws, scale, causal)]
             else:
-                fa.fa_bwd_dkdv(q, k, v, do, lse, dk, dv, ws, scale, causal)
-            mark(3)
-            if dr is not None:
-                fa.fa_bwd_dq_dropout(q, k, v, do, lse, dq, ws, scale, causal,
-                                     dr["p"], dr["seed"], dr["offset"])
-            elif bmask is not None:
-                fa.fa_bwd_dq_block_sparse(q, k, v, do, lse, bmask, dq, ws,
-                                          scale, causal)
-            else:
-                fa.fa_bwd_dq(q, k, v, do, lse, dq, ws, scale, causal)
-            mark(4)
+                stages += [
+                    lambda: fa.fa_bwd_dkdv(q, k, v, do, lse, dk, dv, ws, scale,
+                                           causal),
+                    lambda: fa.fa_bwd_dq(q, k, v, do, lse, dq, ws, scale,
+                                         causal)]
+    assert len(stages) == len(names)
+    # Each stage's C calls, marshalled once by the binding (which validates
+    # the arguments and turns them into pointers, sizes and the stream); the
+    # steps then call the C entry points directly, so a step's host work is
+    # a few ctypes calls and event records and short kernels are not left
+    # waiting for the host between launches.
+    calls = [record_calls(fa, st) for st in stages]
+
+    def step(events=None):
+        if events is not None:
+            events[0].record(stream)
+        for i, cs in enumerate(calls):
+            for fn, args in cs:
+                st = fn(*args)
+                if st != 0:
+                    raise fa.FAError(st, names[i])
+            if events is not None:
+                events[i + 1].record(stream)
 
     log(f"[bench] {w.name}: warmup {warmup} steps")
     for _ in range(warmup):
@@ -878,6 +892,29 @@ def time_workload(w: S.Workload, dev, steps: int, warmup: int,
     return {"inp": inp, "names": names, "per_kernel": per_kernel,
             "ms_step": wall * 1e3 / steps, "pairs": pairs, "fp8": fp8,
             "dropout": dr, "check": check, "steps": steps, "warmup": warmup}
+
+
+def record_calls(fa, stage):
+    """The C calls (function, argument tuple) that one binding call makes,
+    recorded instead of executed."""
+    real = fa.lib()
+    rec = []
+
+    class Recorder:
+        def __getattr__(self, name):
+            fn = getattr(real, name)
+
+            def call(*args):
+                rec.append((fn, args))
+                return 0
+            return call
+    saved = fa._lib
+    fa._lib = Recorder()
+    try:
+        stage()
+    finally:
+        fa._lib = saved
+    return rec
 
 
 def _peak(w: S.Workload, fp8: bool) -> float:
