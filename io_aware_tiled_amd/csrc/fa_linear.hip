@@ -24,11 +24,11 @@
 //     A^T = K_t Q_t^T on v_mfma_f32_32x32x16_bf16 (only key blocks <= the
 //     query block), the causal mask on the diagonal block, A^T -> bf16
 //     (already the B operand of the next product, as P in the softmax
-//     kernels), O^T = V_t^T A^T + S_{t-1}^T Q_t^T, with S_{t-1}^T read from
-//     LDS as bf16;
+//     kernels), O^T = V_t^T A^T + S_{t-1}^T Q_t^T in one accumulator, with
+//     S_{t-1} read from LDS as bf16 (transposed reads);
 //   * wavefronts 2 and 3 own the state: S^T += V_t^T K_t in fp32 registers
 //     (the same V_t^T operand; K_t's columns by transposed LDS reads), then
-//     write S_t^T as bf16 to the LDS buffer the next chunk reads.
+//     write S_t as bf16 to the LDS buffer the next chunk reads.
 // Chunks go from HBM to LDS by DMA two chunks ahead through three stages;
 // one barrier per chunk orders every producer and consumer.  When heads and
 // value blocks leave CUs idle (few heads, long sequences), the chunks of a
@@ -56,8 +56,16 @@ struct LinTile {
   static constexpr int QST = D + 8;          // Q/K rows: 16-B pad (row reads)
   static constexpr int VST = kVB;            // V rows of 64 B: transposed
                                              // reads conflict-free
-  static constexpr int SST = D + 8;          // S^T rows (row reads)
+  static constexpr int SST = kVB;            // S rows (d x value columns),
+                                             // read transposed like V
 };
+
+// Wait until at most N vector-memory operations of this wavefront are
+// outstanding (N a compile-time constant).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // STATE_ONLY: the first pass of a split sequence -- each workgroup sums
 // K_t^T V_t over its segment and writes that fp32 state to the workspace
@@ -77,10 +85,11 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
     float scale) {
   using T = LinTile<D>;
   constexpr int NVB = D / kVB;
+  constexpr int NKK = D / 16;                // contraction slices of d
   __shared__ __attribute__((aligned(16))) uint16_t lds_q[kLS][kLC * T::QST];
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[kLS][kLC * T::QST];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[kLS][kLC * T::VST];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_s[2][kVB * T::SST];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_s[2][D * T::SST];
 
   // Workgroup -> (head, value block, segment): workgroups are dispatched
   // round-robin over the 8 XCDs, so id % 8 picks the XCD and every value
@@ -120,18 +129,37 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
   // ---- chunk loads by LDS DMA (buffer loads that write LDS, 16 bytes per
   // lane): slot p of a stage is 16 bytes of row p / RS; slots that are row
   // padding, and rows >= N (the descriptors end at the head's last row),
-  // read zero.  Transfer g of a chunk (Q's, then K's, then V's) is issued
-  // by wavefront g % 4.
+  // read zero.  A chunk of Q (and of K) is QI transfers of 1 KB, V is VI;
+  // wavefront w issues transfers w + 4u of each (u < QI / 4, VI / 4), and
+  // the QI % 4 remaining Q and K transfers go one each to wavefronts 0, 1,
+  // ...  The lane offsets of a wavefront's transfers are the same for
+  // every chunk and are computed once.
   constexpr int QRS = T::QST / 8, VRS = T::VST / 8;     // 16-B slots per row
   constexpr int QI = kLC * QRS / 64, VI = kLC * VRS / 64;
-  constexpr int NI = 2 * QI + VI;                       // transfers per chunk
-  constexpr int kIW = (NI + 3) / 4;
-  constexpr int kMinBatch = (STATE_ONLY ? NI - QI : NI) / 4;   // per wavefront
-  static_assert(kLC * QRS % 64 == 0 && kLC * VRS % 64 == 0 && kMinBatch < 60,
+  constexpr int QU = QI / 4, QX = QI % 4, VU = VI / 4;
+  static_assert(kLC * QRS % 64 == 0 && kLC * VRS % 64 == 0 && VI % 4 == 0 &&
+                    2 * QX <= 4 && VRS == D / 8 / NVB,
                 "DMA layout");
   constexpr unsigned kOut = 1u << 30;
+  auto qk_off = [&](int gi) -> unsigned {
+    const int p = 64 * gi + lane, row = p / QRS, c = p % QRS;
+    return c < D / 8 ? (unsigned)((row * D + 8 * c) * 2) : kOut;
+  };
+  unsigned qoff[QU], voff[VU];
+#pragma unroll
+  for (int u = 0; u < QU; ++u) qoff[u] = qk_off(w + 4 * u);
+#pragma unroll
+  for (int u = 0; u < VU; ++u) {
+    const int p = 64 * (w + 4 * u) + lane;
+    voff[u] = (unsigned)(((p / VRS) * D + 8 * (p % VRS)) * 2);
+  }
+  // the remaining transfer of wavefront w (Q for w < QX, K for the next QX)
+  const bool xq = !STATE_ONLY && w < QX, xk = w >= QX && w < 2 * QX;
+  const int xgi = 4 * QU + (w < QX ? w : w - QX);
+  const unsigned xoff = qk_off(min(xgi, QI - 1));
   const unsigned lq0 = lds_addr(&lds_q[0][0]), lk0 = lds_addr(&lds_k[0][0]);
   const unsigned lv0 = lds_addr(&lds_v[0][0]);
+  constexpr unsigned QSB = kLC * T::QST * 2, VSB = kLC * T::VST * 2;
   auto dma = [&](int u) __attribute__((always_inline)) {
     const unsigned st = (unsigned)(u % kLS);
     const int row0 = chunk_of(u) * kLC;
@@ -144,23 +172,46 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
                                                       bytes, 0x00020000);
     const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)(Vh + base), (short)0,
                                                       bytes - kVB * vb * 2, 0x00020000);
+    const unsigned qs = lq0 + st * QSB + 1024u * w, ks = lk0 + st * QSB + 1024u * w;
+    const unsigned vs = lv0 + st * VSB + 1024u * w;
+    if constexpr (!STATE_ONLY) {
 #pragma unroll
-    for (int u = 0; u < kIW; ++u) {
-      const int g = w + 4 * u;
-      if (g < 2 * QI) {
-        if (STATE_ONLY && g < QI) continue;         // no Q in the state pass
-        const int gi = g % QI;
-        const int p = 64 * gi + lane, row = p / QRS, c = p % QRS;
-        const unsigned off = c < D / 8 ? (unsigned)((row * D + 8 * c) * 2) : kOut;
-        const unsigned lds = (g < QI ? lq0 : lk0) +
-                             st * (unsigned)(kLC * T::QST * 2) + 1024u * gi;
-        lds_dma16(g < QI ? rq : rk, lds, off);
-      } else if (g < NI) {
-        const int gi = g - 2 * QI;
-        const int p = 64 * gi + lane, row = p / VRS, c = p % VRS;
-        const unsigned off = (unsigned)((row * D + 8 * c) * 2);
-        lds_dma16(rv, lv0 + st * (unsigned)(kLC * T::VST * 2) + 1024u * gi, off);
-      }
+      for (int i = 0; i < QU; ++i) lds_dma16(rq, qs + 4096u * i, qoff[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < QU; ++i) lds_dma16(rk, ks + 4096u * i, qoff[i]);
+#pragma unroll
+    for (int i = 0; i < VU; ++i) lds_dma16(rv, vs + 4096u * i, voff[i]);
+    if constexpr (QX > 0) {
+      if (xq)
+        lds_dma16(rq, lq0 + st * QSB + 1024u * xgi, xoff);
+      else if (xk)
+        lds_dma16(rk, lk0 + st * QSB + 1024u * xgi, xoff);
+    }
+  };
+  // Vector-memory operations this wavefront issues per chunk: its
+  // transfers, and (query wavefronts) the 4 stores of its output rows,
+  // which are buffer stores whose descriptor ends at the head's last row,
+  // so that they are issued for every chunk.
+  constexpr int kNT = (STATE_ONLY ? 0 : QU) + QU + VU;
+  constexpr int kNS = 4;
+  const bool has_x = xq || xk;
+  const bool stores = !STATE_ONLY && w < 2;
+  // Chunk u's transfers were issued two chunks earlier; after them this
+  // wavefront issued chunk u - 2's stores, chunk u + 1's transfers (when
+  // there is one) and chunk u - 1's stores.  Wait until only those (or
+  // fewer) are outstanding; the counts below never exceed them.
+  auto wait_chunk = [&](int u) __attribute__((always_inline)) {
+    if (u + 1 >= nchunks) {
+      wait_vm<0>();
+    } else if (u == 0 || (u == 1 && !stores)) {
+      if (has_x) wait_vm<kNT + 1>(); else wait_vm<kNT>();
+    } else if (u == 1) {
+      if (has_x) wait_vm<kNT + 1 + kNS>(); else wait_vm<kNT + kNS>();
+    } else if (stores) {
+      if (has_x) wait_vm<kNT + 1 + 2 * kNS>(); else wait_vm<kNT + 2 * kNS>();
+    } else {
+      if (has_x) wait_vm<kNT + 1>(); else wait_vm<kNT>();
     }
   };
 
@@ -172,19 +223,40 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
     return join_bf16(lds_read_tr16(&lds_v[b][key * T::VST + col]),
                      lds_read_tr16(&lds_v[b][(key + 8) * T::VST + col]));
   };
+  // S^T operand (A: rows = value columns, contraction = d) of slice kk, read
+  // transposed from S (d rows of the value columns) in LDS buffer sb:
+  // element e is d = 16kk + 8hh + e (the order of a row read of Q).
+  auto st_frag = [&](int sb, int kk) __attribute__((always_inline)) -> bf16x8 {
+    const int d = 16 * kk + 8 * hh + (r16 >> 2);
+    const int col = 16 * dsub + 4 * (r16 & 3);
+    return join_bf16(lds_read_tr16(&lds_s[sb][d * T::SST + col]),
+                     lds_read_tr16(&lds_s[sb][(d + 4) * T::SST + col]));
+  };
 
   // The state S^T (value columns x d) of this workgroup: wavefronts 2 and 3
   // own d-blocks of 32; fp32 accumulators, C layout (value column
-  // 8(r/4) + 4hh + r%4, d = 32 dt + lq).
+  // 8(r/4) + 4hh + r%4, d = 32 dt + lq).  As bf16 it goes to LDS as S
+  // (row d, the value columns), 8 bytes per store.
   constexpr int NDT = D / 32 / 2;            // d-blocks per state wavefront
   f32x16 sacc[NDT];
 #pragma unroll
   for (int i = 0; i < NDT; ++i) sacc[i] = f32x16{};
+  auto put_state = [&](int sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NDT; ++i) {
+      const int dt = (w - 2) * NDT + i;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = sacc[i][4 * g + e];
+        *(bf16x4*)(&lds_s[sb][(32 * dt + lq) * T::SST + 8 * g + 4 * hh]) = to_bf16x4(x);
+      }
+    }
+  };
   // The state entering the segment: zero, or the sum of the previous
   // segments' states (state wavefronts, fp32); as bf16 in the buffer the
   // first chunk reads.
-  for (int e = tid; e < kVB * T::SST / 8; e += kLThreads)
-    *(u32x4*)(&lds_s[1][8 * e]) = u32x4{0u, 0u, 0u, 0u};
   if (!STATE_ONLY && sp_begin < sp_end && w >= 2) {
 #pragma unroll
     for (int i = 0; i < NDT; ++i) {
@@ -197,17 +269,21 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
       }
     }
   }
-  __syncthreads();
-  if (!STATE_ONLY && sp_begin < sp_end && w >= 2) {
-#pragma unroll
-    for (int i = 0; i < NDT; ++i) {
-      const int dt = (w - 2) * NDT + i;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        lds_s[1][(8 * (r / 4) + 4 * hh + (r % 4)) * T::SST + 32 * dt + lq] =
-            __builtin_bit_cast(uint16_t, (__bf16)sacc[i][r]);
-    }
+  if constexpr (!STATE_ONLY) {
+    if (w >= 2) put_state(1);
   }
+  // (the loads above complete before any transfer is issued, so that the
+  // vmcnt counts of the loop see only transfers and stores)
+  wait_vm<0>();
+
+  // Output rows of the chunk at step u: buffer stores whose descriptor ends
+  // at the head's last row, so rows >= N are dropped.
+  auto out_rsrc = [&](int u) __attribute__((always_inline)) {
+    const int row0 = chunk_of(u) * kLC;
+    return __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(O + head + (size_t)row0 * D + kVB * vb), (short)0,
+        min(N - row0, kLC) * D * 2 - kVB * vb * 2, 0x00020000);
+  };
 
   // Chunk t waits for its own transfers (issued two chunks earlier), then
   // the barrier publishes them and the state chunk t - 1 wrote; the stage
@@ -216,39 +292,53 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
   if (nchunks > 1) dma(1);
   for (int u = 0; u < nchunks; ++u) {
     const int b = u % kLS;
-    if (u + 1 < nchunks)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kMinBatch) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_chunk(u);
     __syncthreads();
     if (u + 2 < nchunks) dma(u + 2);
     const int sb = u & 1;
-    const int r0 = chunk_of(u) * kLC;
-    // ---- query block QB (wavefront QB): A^T = K Q^T for the key blocks it
-    // sees (kb <= QB; reversed kb >= QB) and the inter-chunk term
-    // S_{t-1}^T Q^T, as independent MFMA chains interleaved (a dependent
-    // chain would wait out each MFMA's latency), then the mask of the
-    // diagonal block, A^T -> bf16 and V_t^T A^T.
+    // ---- query block QB (wavefront QB): the inter-chunk term S_{t-1}^T
+    // Q^T and A^T = K Q^T for the key blocks it sees (kb <= QB; reversed
+    // kb >= QB), as independent MFMA chains interleaved (a dependent chain
+    // would wait out each MFMA's latency), then the mask of the diagonal
+    // block, A^T -> bf16 and V_t^T A^T onto the inter-chunk term.  The
+    // operands of slice kk are read from LDS two slices ahead (scheduling
+    // barriers keep that order), and V's with the last two slices.
     auto query_block = [&](auto qb_tag) __attribute__((always_inline)) {
       constexpr int QB = decltype(qb_tag)::value;
       constexpr int NK = REV ? 2 - QB : QB + 1;   // key blocks seen
       constexpr int KB0 = REV ? QB : 0;           // the first of them
       constexpr int KD = QB - KB0;                // the diagonal one
       const int sr = sb ^ 1;
-      f32x16 s[NK], oin = f32x16{};
-#pragma unroll
-      for (int i = 0; i < NK; ++i) s[i] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 qf =
-            *(const bf16x8*)(&lds_q[b][(32 * QB + lq) * T::QST + 16 * kk + 8 * hh]);
+      bf16x8 qf[NKK], kf[NK][NKK], sf[NKK], vf[NK][2];
+      auto fetch = [&](int kk) __attribute__((always_inline)) {
+        qf[kk] = *(const bf16x8*)(&lds_q[b][(32 * QB + lq) * T::QST + 16 * kk + 8 * hh]);
 #pragma unroll
         for (int i = 0; i < NK; ++i)
-          s[i] = mfma32x16(
-              *(const bf16x8*)(&lds_k[b][(32 * (KB0 + i) + lq) * T::QST + 16 * kk + 8 * hh]),
-              qf, s[i]);
-        oin = mfma32x16(*(const bf16x8*)(&lds_s[sr][lq * T::SST + 16 * kk + 8 * hh]),
-                        qf, oin);
+          kf[i][kk] = *(const bf16x8*)(
+              &lds_k[b][(32 * (KB0 + i) + lq) * T::QST + 16 * kk + 8 * hh]);
+        sf[kk] = st_frag(sr, kk);
+      };
+      f32x16 s[NK], acc = f32x16{};
+#pragma unroll
+      for (int i = 0; i < NK; ++i) s[i] = f32x16{};
+      fetch(0);
+      fetch(1);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        if (kk + 2 < NKK) fetch(kk + 2);
+        if (kk + 2 == NKK) {
+#pragma unroll
+          for (int i = 0; i < NK; ++i) vf[i][0] = vt_frag(b, KB0 + i, 0);
+        }
+        if (kk + 1 == NKK) {
+#pragma unroll
+          for (int i = 0; i < NK; ++i) vf[i][1] = vt_frag(b, KB0 + i, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        acc = mfma32x16(sf[kk], qf[kk], acc);
+#pragma unroll
+        for (int i = 0; i < NK; ++i) s[i] = mfma32x16(kf[i][kk], qf[kk], s[i]);
+        __builtin_amdgcn_sched_barrier(0);
       }
       // mask inside the diagonal block: key 8(r/4) + 4hh + r%4 against
       // query lq (keys after the query hidden; reversed, keys before it).
@@ -257,7 +347,6 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
         const int key = 8 * (r / 4) + 4 * hh + (r % 4);
         if (REV ? key < lq : key > lq) s[KD][r] = 0.f;
       }
-      f32x16 oacc = f32x16{};
 #pragma unroll
       for (int i = 0; i < NK; ++i)
 #pragma unroll
@@ -265,20 +354,18 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
           f32x8 p;
 #pragma unroll
           for (int e = 0; e < 8; ++e) p[e] = s[i][8 * c + e];
-          oacc = mfma32x16(vt_frag(b, KB0 + i, c), to_bf16x8(p), oacc);
+          acc = mfma32x16(vf[i][c], to_bf16x8(p), acc);
         }
-      // ---- store O rows r0 + 32QB + lq, columns 32vb + 8g + 4hh + 0..3.
-      const int row = r0 + 32 * QB + lq;
-      if (row < N) {
-        uint16_t* orow = O + head + (size_t)row * D + kVB * vb;
+      // ---- store O rows 32QB + lq of the chunk, columns 32vb + 8g + 4hh + 0..3.
+      const auto ro = out_rsrc(u);
+      const unsigned ooff = (unsigned)(((32 * QB + lq) * D + 4 * hh) * 2);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 x;
+      for (int g = 0; g < 4; ++g) {
+        f32x4 x;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            x[e] = (oacc[4 * g + e] + oin[4 * g + e]) * scale;
-          *(bf16x4*)(orow + 8 * g + 4 * hh) = to_bf16x4(x);
-        }
+        for (int e = 0; e < 4; ++e) x[e] = acc[4 * g + e] * scale;
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(u32x2, to_bf16x4(x)), ro, ooff + 16u * g, 0, 0);
       }
     };
     if (STATE_ONLY && w < 2) {
@@ -289,8 +376,8 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
       query_block(std::integral_constant<int, 1>{});
     } else {
       // ---- state: S^T += V_t^T K_t for the d-blocks of this wavefront
-      // (their chains interleaved), then S_t^T -> bf16 into the buffer
-      // chunk t + 1 reads.
+      // (their chains interleaved), then S_t as bf16 into the buffer chunk
+      // t + 1 reads.
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -306,21 +393,7 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
             sacc[i] = mfma32x16(vt, kc, sacc[i]);
           }
         }
-#pragma unroll
-      for (int i = 0; i < NDT; ++i) {
-        const int dt = (w - 2) * NDT + i;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 x;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = sacc[i][4 * g + e];
-          const bf16x4 y = to_bf16x4(x);
-          const i16x4 yi = __builtin_bit_cast(i16x4, y);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            lds_s[sb][(8 * g + 4 * hh + e) * T::SST + 32 * dt + lq] = (uint16_t)yi[e];
-        }
-      }
+      if constexpr (!STATE_ONLY) put_state(sb);
     }
   }
   if (STATE_ONLY && w >= 2) {
@@ -334,7 +407,6 @@ __global__ __launch_bounds__(kLThreads, 1) void linear_fwd_kernel(
     }
   }
 }
-
 }  // namespace
 
 // Split of a head's chunks into segments (one workgroup each) when the
