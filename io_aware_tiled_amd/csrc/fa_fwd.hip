@@ -1194,8 +1194,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
 namespace {
 
 template <int D, bool CAUSAL, bool KVLEN, bool SPARSE, bool DROP = false>
-void fwd_bf16_dispatch(bool pipe, bool two_blocks, dim3 grid, dim3 block,
-                       hipStream_t stream, const uint16_t* q,
+void fwd_bf16_dispatch(bool pipe, bool two_blocks, bool narrow, dim3 grid,
+                       dim3 block, hipStream_t stream, const uint16_t* q,
                        const uint16_t* k, const uint16_t* v,
                        uint16_t* o, float* lse, const int32_t* kv_len,
                        const uint8_t* bmask, int H, int N, int n_qblk,
@@ -1207,6 +1207,14 @@ void fwd_bf16_dispatch(bool pipe, bool two_blocks, dim3 grid, dim3 block,
                          grid, block, 0, stream, q, k, v, o, lse, kv_len,
                          bmask, H, N, n_qblk, c, drop);
       return;
+    }
+    if constexpr (!SPARSE) {
+      if (pipe && narrow) {
+        hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, 4, 1, CAUSAL, KVLEN, false, false>),
+                           grid, block, 0, stream, q, k, v, o, lse, kv_len,
+                           bmask, H, N, n_qblk, c, drop);
+        return;
+      }
     }
   }
   if (pipe || SPARSE || DROP)
@@ -1227,31 +1235,33 @@ int launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     hipStream_t stream) {
   // Grids with at least one 256-row workgroup per CU use the pipelined
   // kernel: head dim 64 with 4 wavefronts of two 32-row blocks when there
-  // are two such workgroups per CU (two resident per CU), else 8 wavefronts
-  // of one block (more wavefronts for a grid that fills the chip once);
-  // head dim 128 with 8 wavefronts of one block (its two blocks would not
-  // fit two wavefronts per SIMD).  Smaller grids use the plain kernel with
-  // 128-row workgroups, two per CU.  Block-sparse calls always take the
-  // pipelined kernel (one 256-row workgroup per block-mask row), and so do
-  // calls with dropout.
+  // are two such workgroups per CU (two resident per CU), else 4 wavefronts
+  // of one block (128-row workgroups, two resident per CU, which spread a
+  // grid that fills the chip less than twice more evenly than 8-wavefront
+  // ones); head dim 128 with 8 wavefronts of one block (its two blocks
+  // would not fit two wavefronts per SIMD).  Smaller grids use the plain
+  // kernel with 128-row workgroups, two per CU.  Block-sparse calls always
+  // take the pipelined kernel with 8 wavefronts (one 256-row workgroup per
+  // block-mask row), and so do calls with dropout.
   const int cus = device_cu_count();
   const bool sparse = block_mask != nullptr;
   const long long grid256 = (long long)B * H * ((N + 255) / 256);
   const bool pipe = sparse || drop != nullptr || grid256 >= cus;
   const bool two_blocks = d == 64 && grid256 >= 2 * cus;
-  const int br = pipe ? 256 : 128;
+  const bool narrow = d == 64 && pipe && !two_blocks && !sparse && !drop;
+  const int br = pipe && !narrow ? 256 : 128;
   const int n_qblk = (N + br - 1) / br;
   const dim3 grid((unsigned)(B * H * n_qblk));
-  const dim3 block(pipe && !two_blocks ? 512 : 256);
+  const dim3 block(pipe && !two_blocks && !narrow ? 512 : 256);
   const float c = (float)((double)scale * 1.4426950408889634);
   const bool kv = kv_len != nullptr;
 #define FA_FWD_LAUNCH(DD, CC, KK, SS)                                          \
-  fwd_bf16_dispatch<DD, CC, KK, SS>(pipe, two_blocks, grid, block, stream, q,  \
-                                    k, v, o, lse, kv_len, block_mask, H, N,    \
-                                    n_qblk, c, Dropout{})
+  fwd_bf16_dispatch<DD, CC, KK, SS>(pipe, two_blocks, narrow, grid, block,    \
+                                    stream, q, k, v, o, lse, kv_len,           \
+                                    block_mask, H, N, n_qblk, c, Dropout{})
 #define FA_FWD_DROP(DD, CC)                                                    \
   fwd_bf16_dispatch<DD, CC, false, false, true>(                               \
-      pipe, two_blocks, grid, block, stream, q, k, v, o, lse, nullptr,         \
+      pipe, two_blocks, narrow, grid, block, stream, q, k, v, o, lse, nullptr, \
       nullptr, H, N, n_qblk, c, *drop)
   // Dropout: dense heads without key padding (the C layer checks).
   if (drop) {

@@ -120,11 +120,12 @@ def test_fwd_bitwise_repeatable():
         assert torch.equal(o, o0) and torch.equal(lse, l0)
 
 
-# ------------------------------------------- wide grids (256-row kernels)
-# Grids of at least 256 workgroups of 256 rows select the 256-row kernels
-# (head dim 64: the pipelined kernel; head dim 128 from 512 such
-# workgroups: the 8-wavefront kernel).  Many heads at small N reach them
-# with an oracle that still runs every row.
+# ------------------------------------------- wide grids (pipelined kernels)
+# Grids of at least 256 blocks of 256 rows select the pipelined kernels
+# (head dim 64: 128-row workgroups of one block per wavefront below 512
+# such blocks, 256-row workgroups of two blocks per wavefront from 512;
+# head dim 128: 256-row workgroups of 8 wavefronts).  Many heads at small
+# N reach them with an oracle that still runs every row.
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d,BH,N", [(64, (16, 16), 1), (64, (16, 16), 65),
@@ -138,17 +139,16 @@ def test_fwd_wide_grid_ragged(causal, d, BH, N):
     _check(f"wide d={d} B={B} H={H} N={N} causal={causal}", inp)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d,B", [(64, 32), (64, 64), (128, 128)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fwd_wide_grid_kvlen(d, causal):
+def test_fwd_wide_grid_kvlen(d, B, causal):
     N = 300
-    B = 64 if d == 64 else 128
-    rng = np.random.default_rng(77 + d)
+    rng = np.random.default_rng(77 + d + B)
     kv = rng.integers(0, N + 1, B)
     kv[:8] = [0, 1, 63, 64, 65, 256, 299, 300]
     inp = S.make_case(B, 4, N, d, "bf16", causal, seed=12 + d,
                       kv_len=kv.tolist())
-    _check(f"wide kvlen d={d} causal={causal}", inp)
+    _check(f"wide kvlen d={d} B={B} causal={causal}", inp)
 
 
 @pytest.mark.parametrize("d", [64, 128])
