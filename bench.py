@@ -590,10 +590,14 @@ def micro(command: str) -> int:
         for wps in (1, 2, 4):
             it = 4000
             c, u, ms = run(which, wps, 0, it)
+            ghz = c / u / 1e3
+            # SIMD cycles per instruction over the whole kernel (the waves of
+            # a SIMD need not run their loops at the same time)
+            simd = ms * 1e-3 * ghz * 1e9 / (it * 8 * wps)
             rows.append((name, "8 independent chains", wps,
                          f"{c / (it * 8):.2f} cycles/instruction per wave, "
-                         f"{c / (it * 8) / wps:.2f} per SIMD",
-                         f"{c / u / 1e3:.2f} GHz"))
+                         f"{simd:.2f} SIMD cycles per instruction over the "
+                         f"kernel time", f"{ghz:.2f} GHz"))
     for wps in (1, 2):
         it = 2000
         c0, _, ms0 = run(1, wps, 0, it)
