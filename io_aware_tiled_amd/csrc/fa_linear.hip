@@ -56,8 +56,12 @@ struct LinTile {
   static constexpr int QST = D + 8;          // Q/K rows: 16-B pad (row reads)
   static constexpr int VST = kVB;            // V rows of 64 B: transposed
                                              // reads conflict-free
-  static constexpr int SST = kVB;            // S rows (d x value columns),
-                                             // read transposed like V
+  static constexpr int SST = kVB + 8;        // S rows (d x value columns),
+                                             // read transposed like V; the
+                                             // 16-B pad spreads the 8-byte
+                                             // writes of 32 rows over the
+                                             // banks (64-B rows put them in
+                                             // 4 bank groups)
 };
 
 // Wait until at most N vector-memory operations of this wavefront are
