@@ -508,8 +508,9 @@ def summarize_ceiling(path, command) -> int:
 def summarize_trace(w: S.Workload, path, command, warmup: int,
                     steps: int) -> int:
     """profiles/kernels_<workload>.md from a rocprofv3 kernel trace: per
-    libfa kernel, the timed dispatches only (each kernel runs once per step,
-    so its first `warmup` dispatches are the warmup steps)."""
+    libfa kernel, the timed dispatches only.  A kernel that the step runs c
+    times (its dispatch count is c (warmup + steps)) has its first c warmup
+    dispatches skipped and the next c steps kept."""
     import csv
     per = {}
     with open(path) as f:
@@ -526,12 +527,15 @@ def summarize_trace(w: S.Workload, path, command, warmup: int,
                 f"causal={w.causal}, {'forward+backward' if w.backward else 'forward'})"
                 f"\n\nCommand (repository root, one MI355X):\n\n```\n{command}"
                 "\n```\n\nrocprofv3 kernel trace, libfa kernels only, the "
-                f"timed dispatches of each kernel (its first {warmup} dispatches "
-                f"are the warmup steps and are skipped; the next {steps} are "
-                "kept; durations in microseconds):\n\n| kernel | timed "
-                "dispatches | average | min | max |\n|---|---|---|---|---|\n")
+                f"timed dispatches of each kernel (the dispatches of its first "
+                f"{warmup} steps are the warmup and are skipped, those of the "
+                f"next {steps} are kept; durations in microseconds):\n\n"
+                "| kernel | timed dispatches | average | min | max |\n"
+                "|---|---|---|---|---|\n")
         for name, v in sorted(per.items(), key=lambda kv: -sum(x[1] for x in kv[1])):
-            v = sorted(v)[warmup:warmup + steps]
+            n_steps = warmup + steps
+            c = len(v) // n_steps if len(v) % n_steps == 0 and len(v) >= n_steps else 1
+            v = sorted(v)[c * warmup:c * (warmup + steps)]
             if not v:
                 continue
             d = np.array([ns for _, ns in v], dtype=np.float64) / 1e3

@@ -84,3 +84,21 @@ def test_summarize_trace_keeps_timed_dispatches(tmp_path, monkeypatch):
     assert bench.summarize_trace(w, str(path), "cmd", 3, 5) == 0
     text = (tmp_path / "kernels_tiny_f32.md").read_text()
     assert "| `fa::k` | 5 | 0.1 | 0.1 | 0.1 |" in text
+
+
+def test_summarize_trace_kernel_run_twice_per_step(tmp_path, monkeypatch):
+    """A kernel the step runs twice: the dispatches of the warmup steps (2
+    per step) are skipped and those of the timed steps (2 per step) kept."""
+    import csv
+    path = tmp_path / "trace.csv"
+    with open(path, "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(["Kernel_Name", "Dispatch_Id", "Start_Timestamp",
+                     "End_Timestamp"])
+        for i in range(16):  # 3 warmup steps x 2 of 900 ns, 5 timed x 2 of 100
+            wr.writerow(["void fa::k(int)", i, 0, 900 if i < 6 else 100])
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    w = S.WORKLOADS["tiny_f32"]
+    assert bench.summarize_trace(w, str(path), "cmd", 3, 5) == 0
+    text = (tmp_path / "kernels_tiny_f32.md").read_text()
+    assert "| `fa::k` | 10 | 0.1 | 0.1 | 0.1 |" in text
