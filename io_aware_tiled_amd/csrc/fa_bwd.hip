@@ -887,49 +887,72 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
 
   // ---- one phase.  A: S, dP of block ca from stage sta.  B: dV, dK of
   // block cb from stage stb.  VALU: P, dS of block cv with LSE / D from
-  // stage stv.  B_FIRST orders the B products before the A ones.
-  auto phase = [&](auto b_first, int sta, int ca, int stb, int cb,
-                   int stv, int cv, int qtn, int cvn) {
+  // stage stv.  B_FIRST orders the B products before the A ones.  The
+  // operand of MFMA slot m is read from LDS kPf slots ahead, and the ring
+  // runs on across phases: the last kPf slots of a phase read the first
+  // operands of the next phase (stages nsta, nstb, blocks nca, ncb; its
+  // B_FIRST is the opposite), and the LSE / -D rows of the next phase are
+  // read kPf slots before its start, so no phase begins by waiting for LDS.
+  constexpr int kA = 2 * (D / 16);       // S and dP MFMAs
+  constexpr int kB = 4 * (D / 32);       // dV and dK MFMAs
+  constexpr int kN = kA + kB;
+  constexpr int kPf = 4;
+  static_assert(kN % kPf == 0, "the ring position repeats per phase");
+  auto fetch = [&](auto b_first, int i, int sta, int ca, int stb,
+                   int cb) __attribute__((always_inline)) -> bf16x8 {
     constexpr bool BF = decltype(b_first)::value;
-    constexpr int kA = 2 * (D / 16);       // S and dP MFMAs
-    constexpr int kB = 4 * (D / 32);       // dV and dK MFMAs
-    constexpr int kN = kA + kB;
-    constexpr int kPf = 4;
-    auto fetch = [&](int i) -> bf16x8 {
-      const bool is_a = BF ? (i >= kB) : (i < kA);
-      if (is_a) {
-        const int ai = BF ? i - kB : i;
-        const int kk = ai / 2;
-        const uint16_t* t = (ai % 2 == 0) ? lds_q[sta] : lds_g[sta];
-        return *(const bf16x8*)(&t[(32 * ca + l32) * kRS + 16 * kk + 8 * hh]);
-      }
-      const int bi = BF ? i : i - kA;
-      const int which = bi / (kB / 2);           // 0: dO^T (dV), 1: Q^T (dK)
-      const int h = (bi % (kB / 2)) / (D / 32), db = bi % (D / 32);
-      const uint16_t* t = which == 0 ? lds_g[stb] : lds_q[stb];
-      const int col = 32 * db + 16 * dsub + 4 * (r16 & 3);
-      const int row = 32 * cb + 16 * h + 4 * hh + (r16 >> 2);
-      return join_bf16(lds_read_tr16(&t[row * kRS + col]),
-                       lds_read_tr16(&t[(row + 8) * kRS + col]));
-    };
-    bf16x8 op[kPf];
-#pragma unroll
-    for (int i = 0; i < kPf; ++i) op[i] = fetch(i);
-    // LSE of the lane's 16 rows of block cv, -D of those of block ca:
-    // register r <-> row 32 c + 8 (r / 4) + 4 hh + r % 4.  dP accumulates
-    // onto -D, so the VALU forms dS = P (dP - D) with one product.
-    f32x4 l4[4];
-    f32x16 negd, negd_v;
+    const bool is_a = BF ? (i >= kB) : (i < kA);
+    if (is_a) {
+      const int ai = BF ? i - kB : i;
+      const int kk = ai / 2;
+      const uint16_t* t = (ai % 2 == 0) ? lds_q[sta] : lds_g[sta];
+      return *(const bf16x8*)(&t[(32 * ca + l32) * kRS + 16 * kk + 8 * hh]);
+    }
+    const int bi = BF ? i : i - kA;
+    const int which = bi / (kB / 2);           // 0: dO^T (dV), 1: Q^T (dK)
+    const int h = (bi % (kB / 2)) / (D / 32), db = bi % (D / 32);
+    const uint16_t* t = which == 0 ? lds_g[stb] : lds_q[stb];
+    const int col = 32 * db + 16 * dsub + 4 * (r16 & 3);
+    const int row = 32 * cb + 16 * h + 4 * hh + (r16 >> 2);
+    return join_bf16(lds_read_tr16(&t[row * kRS + col]),
+                     lds_read_tr16(&t[(row + 8) * kRS + col]));
+  };
+  // LSE of the lane's 16 rows of block cv, -D of those of block ca (and,
+  // with dropout, of block cv): register r <-> row 32 c + 8 (r / 4) + 4 hh
+  // + r % 4.  dP accumulates onto -D, so the VALU forms dS = P (dP - D)
+  // with one product.
+  bf16x8 op[kPf];
+  f32x4 l4[4], nd4[4], nv4[4];
+  auto fetch_rows = [&](int sta, int ca, int stv, int cv) __attribute__((always_inline)) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       l4[g] = *(const f32x4*)(&lds_lse[stv][32 * cv + 8 * g + 4 * hh]);
-      const f32x4 nd = *(const f32x4*)(&lds_d[sta][32 * ca + 8 * g + 4 * hh]);
+      nd4[g] = *(const f32x4*)(&lds_d[sta][32 * ca + 8 * g + 4 * hh]);
+      if constexpr (DROP)
+        nv4[g] = *(const f32x4*)(&lds_d[stv][32 * cv + 8 * g + 4 * hh]);
+    }
+  };
+  // Operands and rows of the first phase (the ring's start).
+  auto prefetch = [&](auto b_first, int sta, int ca, int stb, int cb, int stv,
+                      int cv) __attribute__((always_inline)) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) negd[4 * g + e] = nd[e];
-      if constexpr (DROP) {
-        const f32x4 nv = *(const f32x4*)(&lds_d[stv][32 * cv + 8 * g + 4 * hh]);
+    for (int i = 0; i < kPf; ++i) op[i] = fetch(b_first, i, sta, ca, stb, cb);
+    fetch_rows(sta, ca, stv, cv);
+  };
+  auto phase = [&](auto b_first, int sta, int ca, int stb, int cb,
+                   int stv, int cv, int qtn, int cvn, int nsta, int nca,
+                   int nstb, int ncb, int nstv, int ncv) {
+    constexpr bool BF = decltype(b_first)::value;
+    using NextBF = std::integral_constant<bool, !BF>;
+    f32x4 lv[4];
+    f32x16 negd, negd_v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) negd_v[4 * g + e] = nv[e];
+    for (int g = 0; g < 4; ++g) {
+      lv[g] = l4[g];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        negd[4 * g + e] = nd4[g][e];
+        if constexpr (DROP) negd_v[4 * g + e] = nv4[g][e];
       }
     }
     // Dropout: with Z the keep mask and k the keep probability,
@@ -947,7 +970,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
 #pragma unroll
     for (int m = 0; m < kN; ++m) {
       const bf16x8 a = op[m % kPf];
-      if (m + kPf < kN) op[m % kPf] = fetch(m + kPf);
+      if (m + kPf < kN)
+        op[m % kPf] = fetch(b_first, m + kPf, sta, ca, stb, cb);
+      else
+        op[m % kPf] = fetch(NextBF{}, m + kPf - kN, nsta, nca, nstb, ncb);
+      if (m == kN - kPf) fetch_rows(nsta, nca, nstv, ncv);
       const bool is_a = BF ? (m >= kB) : (m < kA);
       if (is_a) {
         const int ai = BF ? m - kB : m;
@@ -965,7 +992,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
         else
           mfma_agpr(dk_acc[db], a, dsb[cb][h]);
       }
-      if (m < 16) x[m] = __builtin_fmaf(s[cv][m], c_log2, -l4[m / 4][m % 4]);
+      if (m < 16) x[m] = __builtin_fmaf(s[cv][m], c_log2, -lv[m / 4][m % 4]);
       if (m >= 1 && m - 1 < 16) pe[m - 1] = __builtin_amdgcn_exp2f(x[m - 1]);
       if (m >= 2 && m - 2 < 16) {
         const int el = m - 2;
@@ -1082,6 +1109,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
     // tile i+1 (its DMA has landed, its LSE / D are stored), then issues
     // tile i+2 into the stage of tile i-2, last read in iteration i-1.
     int sp = 3, s0 = 0, s1 = 1;   // stages of tiles i-1, i, i+1
+    prefetch(std::false_type{}, s0, 1, sp, 1, s0, 0);
     for (int i = 0; i < n_vis; ++i) {
       const int ei = qtile(i), ei1 = qtile(i + 1), ei2 = qtile(min(i + 2, last));
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -1089,11 +1117,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
       __syncthreads();
       if (i + 2 <= last) dma_tile(ei2, (s1 + 1) & 3);
       load_stats(ei2);
-      // phase 1: A_1(i), B_1(i-1) || V_0(i)
-      phase(std::false_type{}, s0, 1, sp, 1, s0, 0, ei, 1);
+      // phase 1: A_1(i), B_1(i-1) || V_0(i); the ring then reads phase 2's
+      phase(std::false_type{}, s0, 1, sp, 1, s0, 0, ei, 1, s1, 0, s0, 0, s0, 1);
       mask_block(1, ei);
-      // phase 2: B_0(i), A_0(i+1) || V_1(i)
-      phase(std::true_type{}, s1, 0, s0, 0, s0, 1, ei1, 0);
+      // phase 2: B_0(i), A_0(i+1) || V_1(i); the ring then reads phase 1 of
+      // tile i+1 (stages s1 and s0 after the rotation below)
+      phase(std::true_type{}, s1, 0, s0, 0, s0, 1, ei1, 0, s1, 1, s0, 1, s1, 0);
       if (i + 1 < n_vis) mask_block(0, ei1);
       sp = s0;
       s0 = s1;
