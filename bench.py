@@ -463,6 +463,77 @@ def mfma_ceiling(dev, n: int = 8192, iters: int = 20) -> dict:
     return out
 
 
+STALL_COUNTERS = (
+    ("SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY "
+     "SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS "
+     "SQ_ACTIVE_INST_SCA GRBM_GUI_ACTIVE"),
+    ("SQ_WAIT_INST_LDS SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU "
+     "SQ_INSTS_VALU_TRANS_F32 SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_MISC "
+     "GRBM_GUI_ACTIVE"))
+
+
+def _pmc_means(csvs) -> dict:
+    """{kernel key: {counter: mean over dispatches}} of rocprofv3 --pmc
+    counter_collection CSVs (libfa kernels only)."""
+    import csv
+    vals = {}
+    for path in csvs:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"]
+                key = None
+                for frag, k in KERNEL_KEYS:
+                    if "fa::" in name and frag in name:
+                        key = k
+                if key is None:
+                    continue
+                vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+    return {k: {c: float(np.mean(x)) for c, x in d.items()} for k, d in vals.items()}
+
+
+def summarize_stalls(w: S.Workload, csvs, command) -> int:
+    """profiles/stalls_<workload>.md: where the wavefronts' cycles go (SQ
+    wave-cycle counters as fractions of SQ_WAVE_CYCLES, the same units) and
+    the instruction mix per MFMA, from two rocprofv3 --pmc collections
+    (STALL_COUNTERS) of a bench run."""
+    v = _pmc_means(csvs)
+    md = os.path.join(PROFILES, f"stalls_{w.name}.md")
+    frac = (("SQ_ACTIVE_INST_ANY", "issuing any"), ("SQ_ACTIVE_INST_VALU", "VALU"),
+            ("SQ_ACTIVE_INST_LDS", "LDS"), ("SQ_ACTIVE_INST_SCA", "scalar"),
+            ("SQ_ACTIVE_INST_MISC", "misc"), ("SQ_WAIT_INST_ANY", "waiting to issue"),
+            ("SQ_WAIT_INST_LDS", "waiting on LDS issue"), ("SQ_WAIT_ANY", "waiting (any)"))
+    with open(md, "w") as f:
+        f.write(f"# Where the cycles go: {w.name} (B={w.B} H={w.H} N={w.N} d={w.d}, "
+                f"causal={w.causal})\n\nCommands (repository root, one MI355X):"
+                f"\n\n```\n{command}\n```\n\nPer dispatch (mean over the run's "
+                "dispatches).  The SQ wave-cycle counters are given as fractions "
+                "of SQ_WAVE_CYCLES (summed over wavefronts, same units); a "
+                "wavefront can be issuing one kind of instruction while waiting "
+                "on another, so the fractions do not add up to one.  MFMA busy = "
+                "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8).  "
+                "Instruction counts are per MFMA instruction (SQ_INSTS_*; "
+                "transcendental = SQ_INSTS_VALU_TRANS_F32).\n\n")
+        f.write("| kernel | MFMA busy | " + " | ".join(n for _, n in frac) +
+                " | VALU / MFMA | transc. / MFMA | LDS / MFMA | SALU / MFMA |\n")
+        f.write("|---" * (6 + len(frac)) + "|\n")
+        for k in sorted(v):
+            c = v[k]
+            wc = c.get("SQ_WAVE_CYCLES", float("nan"))
+            cyc = c.get("GRBM_GUI_ACTIVE", float("nan")) / 8
+            busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (1024 * cyc)
+            # (SQ_INSTS_VALU counts the MFMA instructions too)
+            nm = c.get("SQ_INSTS_MFMA", float("nan"))
+            cells = [f"{busy:.1%}"] + [f"{c.get(n, float('nan')) / wc:.3f}"
+                                       for n, _ in frac]
+            cells += [f"{c.get(n, float('nan')) / nm:.2f}" if nm else "—" for n in (
+                "SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS",
+                "SQ_INSTS_SALU")]
+            f.write(f"| {k} | " + " | ".join(cells) + " |\n")
+    print(open(md).read())
+    return 0
+
+
 def summarize_ceiling(path, command) -> int:
     """profiles/mfma_ceiling.md from a rocprofv3 --pmc GRBM_GUI_ACTIVE
     SQ_VALU_MFMA_BUSY_CYCLES collection of a --ceiling-only run: duration,
@@ -676,6 +747,10 @@ def main(argv=None) -> int:
                     help="no GPU work: turn two rocprofv3 --pmc collections "
                          "(SQ/GRBM counters, then TCC_HIT_sum TCC_MISS_sum) "
                          "into profiles/counters_<workload>.md")
+    ap.add_argument("--summarize-stalls", nargs=2, metavar=("PMC1_CSV", "PMC2_CSV"),
+                    help="no GPU work: turn two rocprofv3 --pmc collections "
+                         "(the two counter sets of STALL_COUNTERS) into "
+                         "profiles/stalls_<workload>.md")
     ap.add_argument("--no-per-config", dest="per_config", action="store_false",
                     help="skip the per-config table (the five synthetic "
                          "configs, each timed and beside its oracle time)")
@@ -702,6 +777,9 @@ def main(argv=None) -> int:
 
     if args.summarize_ceiling:
         return summarize_ceiling(args.summarize_ceiling, args.command)
+    if args.summarize_stalls:
+        return summarize_stalls(S.WORKLOADS[args.workload],
+                                args.summarize_stalls, args.command)
     if args.summarize_counters:
         return summarize_counters(S.WORKLOADS[args.workload],
                                   args.summarize_counters, args.command)

@@ -102,3 +102,30 @@ def test_summarize_trace_kernel_run_twice_per_step(tmp_path, monkeypatch):
     assert bench.summarize_trace(w, str(path), "cmd", 3, 5) == 0
     text = (tmp_path / "kernels_tiny_f32.md").read_text()
     assert "| `fa::k` | 10 | 0.1 | 0.1 | 0.1 |" in text
+
+
+def test_summarize_stalls_fractions(tmp_path, monkeypatch):
+    """The stall table gives wave-cycle counters as fractions of
+    SQ_WAVE_CYCLES and instruction counts per MFMA."""
+    import csv
+    p1, p2 = tmp_path / "a.csv", tmp_path / "b.csv"
+    rows1 = {"SQ_WAVE_CYCLES": 1000, "SQ_ACTIVE_INST_VALU": 250,
+             "SQ_WAIT_INST_ANY": 400, "GRBM_GUI_ACTIVE": 8000}
+    rows2 = {"SQ_INSTS_MFMA": 10, "SQ_INSTS_VALU": 35,
+             "SQ_VALU_MFMA_BUSY_CYCLES": 512000, "GRBM_GUI_ACTIVE": 8000}
+    for path, rows in ((p1, rows1), (p2, rows2)):
+        with open(path, "w", newline="") as f:
+            wr = csv.writer(f)
+            wr.writerow(["Kernel_Name", "Counter_Name", "Counter_Value"])
+            for c, val in rows.items():
+                wr.writerow(["void fa::bwd_dkdv_pipe_kernel<true>(int)", c, val])
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    w = S.WORKLOADS["tiny_f32"]
+    assert bench.summarize_stalls(w, [str(p1), str(p2)], "cmd") == 0
+    text = (tmp_path / "stalls_tiny_f32.md").read_text()
+    line = [l for l in text.splitlines() if l.startswith("| bwd_dkdv")][0]
+    cells = [c.strip() for c in line.strip("|").split("|")]
+    assert cells[1] == "50.0%"          # 512000 / (1024 * 8000 / 8)
+    assert cells[3] == "0.250"          # VALU / wave cycles
+    assert cells[7] == "0.400"          # waiting to issue
+    assert cells[10] == "3.50"          # VALU per MFMA
