@@ -805,20 +805,33 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
   // list entry of tile j.
   auto mask_half = [&](int x, unsigned e, int kb) {
     const int k0 = key_tile(e) * kBC + 32 * kb;
+    bool need[NB], any = false;
 #pragma unroll
     for (int c = 0; c < NB; ++c) {
-      const bool need_mask =
-          (CAUSAL && k0 + 31 > qlo[c]) || (k0 + 32 > kvlim);
-      if (__builtin_expect(need_mask, 0)) {
+      need[c] = (CAUSAL && k0 + 31 > qlo[c]) || (k0 + 32 > kvlim);
+      any = any || need[c];
+    }
+    if (__builtin_expect(any, 0)) {
+      // (k0 made opaque here, so that the compiler does not compute the
+      // 16 keys ahead of the branch on every step)
+      int kb0 = k0;
+      asm volatile("" : "+s"(kb0));
+      int key[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 8 * (r / 4) + 4 * hh + (r % 4);
-          const bool hide = (CAUSAL && key > qrow[c]) || key >= kvlim;
-          if (hide) s[x][c][r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) key[r] = kb0 + 8 * (r / 4) + 4 * hh + (r % 4);
+#pragma unroll
+      for (int c = 0; c < NB; ++c) {
+        if (need[c]) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool hide = (CAUSAL && key[r] > qrow[c]) || key[r] >= kvlim;
+            if (hide) s[x][c][r] = -INFINITY;
+          }
         }
       }
     }
   };
+
 
   // ---- O += V^T P^T for the last half-tile (no exponentials left).
   auto pv_only = [&](int x, int stv, int kbv) {
