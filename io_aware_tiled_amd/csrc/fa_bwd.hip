@@ -23,13 +23,15 @@
 //      every 64-row query tile that can see its keys (causal: tiles wholly
 //      before the key block are skipped); S, dP, P and dS are recomputed
 //      per tile and dK^T, dV^T accumulate in registers.
-//        bwd_dkdv_pipe_kernel (head dim 128 on grids that fill the chip):
-//        4 wavefronts of 32 keys (one per SIMD), K and V fragments held in
-//        registers, dK/dV accumulators in AGPRs, query tiles by LDS DMA
-//        through four stages, two software-pipelined phases per tile.
-//        bwd_dkdv_kernel (head dim 64, and small grids): 8 wavefronts, each
-//        owning 32 keys and one half of every query tile; the two halves'
-//        partials are added through LDS at the end.
+//        bwd_dkdv_pipe_kernel (grids that fill the chip): 4 wavefronts of
+//        32 keys, K and V fragments held in registers, dK/dV accumulators
+//        in AGPRs, query tiles by LDS DMA through four stages, two
+//        software-pipelined phases per tile; one workgroup per CU at head
+//        dim 128, two at head dim 64 (fewer registers, smaller tiles).
+//        bwd_dkdv_kernel (small grids, and head dim 64 with dropout or a
+//        block mask): 8 wavefronts, each owning 32 keys and one half of
+//        every query tile; the two halves' partials are added through LDS
+//        at the end.
 //   3. dQ: streams K/V tiles like the forward, recomputes S^T and dP^T and
 //      accumulates dQ^T in registers.
 //        bwd_dq_pipe_kernel (head dim 128 on grids that fill the chip):
@@ -684,7 +686,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t bwd_rsrc(const uint16_t* p,
 
 // ---------------------------------------------------------------------------
 // Pipelined dK/dV kernel: one workgroup per (batch, head, 128-key block), 4
-// wavefronts (one per SIMD) of 32 keys.  The K and V fragments of a
+// wavefronts of 32 keys (one per SIMD; at head dim 64 two workgroups share
+// a CU, its registers and LDS allowing it).  The K and V fragments of a
 // wavefront's keys stay in registers for the whole kernel, so LDS only
 // carries the streamed 64-row query tiles (Q, dO, LSE, D).  A tile is two
 // 32-row blocks; work item A_c is S = Q_c K^T and dP = dO_c V^T, V_c the
@@ -699,8 +702,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t bwd_rsrc(const uint16_t* p,
 // each, transformed on the way) pass through wavefront 0's registers.
 constexpr int kKvPBK = 128;
 
-template <bool CAUSAL, bool SPARSE, bool DROP = false>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
+template <bool CAUSAL, bool SPARSE, bool DROP = false, int D = kD>
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_pipe_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dv,
@@ -708,8 +711,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
     const uint8_t* __restrict__ bmask, int H, int N, int n_kblk,
     float c_log2, float scale, Dropout drop,
     const int32_t* __restrict__ kv_len = nullptr) {
-  constexpr int D = kD;
-  constexpr int QE = kBQ2 * kRS;                 // elements per tile stage
+  static_assert(D == kD || (D == 64 && !DROP), "head dimension");
+  // Padded row stride of the query tiles: 304-byte rows at head dim 128
+  // (as RS); at head dim 64, 144-byte rows, which keep the row reads
+  // conflict-free and let two workgroups share a CU.
+  constexpr int RS = D == 64 ? D + 8 : kRS;
+  constexpr int QE = kBQ2 * RS;                  // elements per tile stage
   constexpr int THREADS = 256;
   __shared__ __attribute__((aligned(16))) uint16_t lds_q[4][QE];
   __shared__ __attribute__((aligned(16))) uint16_t lds_g[4][QE];   // dO
@@ -806,7 +813,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
   // ---- query-tile staging.  Q and dO: DMA instruction u of wavefront w
   // fills the 1 KB of the (padded) stage at 1024 (w + 4u), 16 bytes per
   // lane; lanes on row padding, and rows past N, read zeros.
-  constexpr int RCH = kRS / 8;                       // 16-B slots per row
+  constexpr int RCH = RS / 8;                       // 16-B slots per row
   constexpr int TI = kBQ2 * RCH / 64;                // DMA instructions per tile
   constexpr int TIW = (TI + 3) / 4;
   static_assert(QE % 512 == 0, "tile stage must be whole 1 KB blocks");
@@ -898,6 +905,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
   constexpr int kN = kA + kB;
   constexpr int kPf = 4;
   static_assert(kN % kPf == 0, "the ring position repeats per phase");
+  // VALU elements per MFMA slot: the 16 elements of a block run through a
+  // three-slot pipeline, so a phase of kN slots carries one per slot at
+  // head dim 128 (32 slots) and two at head dim 64 (16 slots).
+  constexpr int kG = kN >= 18 ? 1 : 2;
+  static_assert(kG * (kN - 2) >= 16, "the VALU pipeline fits the phase");
   auto fetch = [&](auto b_first, int i, int sta, int ca, int stb,
                    int cb) __attribute__((always_inline)) -> bf16x8 {
     constexpr bool BF = decltype(b_first)::value;
@@ -906,7 +918,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
       const int ai = BF ? i - kB : i;
       const int kk = ai / 2;
       const uint16_t* t = (ai % 2 == 0) ? lds_q[sta] : lds_g[sta];
-      return *(const bf16x8*)(&t[(32 * ca + l32) * kRS + 16 * kk + 8 * hh]);
+      return *(const bf16x8*)(&t[(32 * ca + l32) * RS + 16 * kk + 8 * hh]);
     }
     const int bi = BF ? i : i - kA;
     const int which = bi / (kB / 2);           // 0: dO^T (dV), 1: Q^T (dK)
@@ -914,8 +926,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
     const uint16_t* t = which == 0 ? lds_g[stb] : lds_q[stb];
     const int col = 32 * db + 16 * dsub + 4 * (r16 & 3);
     const int row = 32 * cb + 16 * h + 4 * hh + (r16 >> 2);
-    return join_bf16(lds_read_tr16(&t[row * kRS + col]),
-                     lds_read_tr16(&t[(row + 8) * kRS + col]));
+    return join_bf16(lds_read_tr16(&t[row * RS + col]),
+                     lds_read_tr16(&t[(row + 8) * RS + col]));
   };
   // LSE of the lane's 16 rows of block cv, -D of those of block ca (and,
   // with dropout, of block cv): register r <-> row 32 c + 8 (r / 4) + 4 hh
@@ -992,10 +1004,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
         else
           mfma_agpr(dk_acc[db], a, dsb[cb][h]);
       }
-      if (m < 16) x[m] = __builtin_fmaf(s[cv][m], c_log2, -lv[m / 4][m % 4]);
-      if (m >= 1 && m - 1 < 16) pe[m - 1] = __builtin_amdgcn_exp2f(x[m - 1]);
-      if (m >= 2 && m - 2 < 16) {
-        const int el = m - 2;
+#pragma unroll
+      for (int u = 0; u < kG; ++u) {
+      const int mf = kG * m + u, me = kG * (m - 1) + u, md = kG * (m - 2) + u;
+      if (mf < 16) x[mf] = __builtin_fmaf(s[cv][mf], c_log2, -lv[mf / 4][mf % 4]);
+      if (m >= 1 && me < 16) pe[me] = __builtin_amdgcn_exp2f(x[me]);
+      if (m >= 2 && md < 16) {
+        const int el = md;
         if constexpr (DROP) {
           const bool kept = drop_keep(kz[el / 4], el % 4, drop.p8);
           dsv[el] = pe[el] * (kept ? dp[cv][el] : negd_v[el]);
@@ -1013,6 +1028,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
           pb[cv][el / 8] = to_bf16x8(vp);
           dsb[cv][el / 8] = to_bf16x8(vd);
         }
+      }
       }
       if constexpr (DROP) {
         static_assert(kN >= 29, "generator rounds fit after the VALU work");
@@ -1050,8 +1066,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
       const uint16_t* t = which == 0 ? lds_g[stb] : lds_q[stb];
       const int col = 32 * db + 16 * dsub + 4 * (r16 & 3);
       const int row = 32 + 16 * h + 4 * hh + (r16 >> 2);
-      const bf16x8 a = join_bf16(lds_read_tr16(&t[row * kRS + col]),
-                                 lds_read_tr16(&t[(row + 8) * kRS + col]));
+      const bf16x8 a = join_bf16(lds_read_tr16(&t[row * RS + col]),
+                                 lds_read_tr16(&t[(row + 8) * RS + col]));
       if (which == 0)
         mfma_agpr(dv_acc[db], a, pb[1][h]);
       else
@@ -1092,7 +1108,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_pipe_kernel(
     }
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const int o = l32 * kRS + 16 * kk + 8 * hh;
+      const int o = l32 * RS + 16 * kk + 8 * hh;
       s[0] = mfma32x16(*(const bf16x8*)(&lds_q[0][o]), kf[kk], kk == 0 ? f32x16{} : s[0]);
       dp[0] = mfma32x16(*(const bf16x8*)(&lds_g[0][o]), vf[kk], kk == 0 ? negd0 : dp[0]);
     }
@@ -1556,10 +1572,22 @@ int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   const float c = (float)((double)scale * 1.4426950408889634);
   // Head dim 128 on grids with at least one 128-key workgroup per CU, and
   // every block-sparse or dropout call: the pipelined kernel (4 wavefronts,
-  // K/V in registers); the rest (and head dim 64, with or without dropout):
-  // 8 wavefronts.
-  if (d == kD && ((long long)B * H * n_kblk >= device_cu_count() || block_mask != nullptr ||
-                  drop != nullptr)) {
+  // K/V in registers); head dim 64 on such grids without dropout or a block
+  // mask: the pipelined kernel at head dim 64; the rest: 8 wavefronts.
+  const bool fills = (long long)B * H * n_kblk >= device_cu_count();
+  if (d == 64 && fills && drop == nullptr && block_mask == nullptr) {
+    const dim3 grid((unsigned)(B * H * n_kblk)), block(256);
+    if (causal)
+      hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<true, false, false, 64>), grid,
+                         block, 0, stream, q, k, v, dO, lse, D, dk, dv, nullptr,
+                         H, N, n_kblk, c, scale, Dropout{}, kv_len);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<false, false, false, 64>), grid,
+                         block, 0, stream, q, k, v, dO, lse, D, dk, dv, nullptr,
+                         H, N, n_kblk, c, scale, Dropout{}, kv_len);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+  }
+  if (d == kD && (fills || block_mask != nullptr || drop != nullptr)) {
     const dim3 grid((unsigned)(B * H * n_kblk)), block(256);
 #define FA_DKDV_LAUNCH(CC, SS)                                                  \
   hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<CC, SS>), grid, block, 0, stream, q, \

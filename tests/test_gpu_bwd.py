@@ -49,20 +49,24 @@ def test_bwd_ragged(causal, N):
 
 
 # Grids of at least 256 workgroups of 256 query rows select the pipelined dQ
-# kernel; many heads at small N reach it with a full oracle comparison.
+# kernel, and grids of at least 256 128-key workgroups the pipelined dK/dV
+# kernel (at head dim 64 too); many heads at small N reach them with a full
+# oracle comparison.
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 65, 200])
-def test_bwd_wide_grid(causal, N):
-    inp = S.make_case(16, 16, N, 128, "bf16", causal, seed=300 + N + causal,
+def test_bwd_wide_grid(d, causal, N):
+    inp = S.make_case(16, 16, N, d, "bf16", causal, seed=300 + N + causal + d,
                       backward=True)
-    _check_bwd(f"wide bwd causal={causal} N={N}", inp)
+    _check_bwd(f"wide bwd d={d} causal={causal} N={N}", inp)
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("scale", [-0.08, 0.0])
-def test_bwd_wide_grid_scales(scale):
-    inp = S.make_case(16, 16, 100, 128, "bf16", True, seed=17, backward=True,
+def test_bwd_wide_grid_scales(d, scale):
+    inp = S.make_case(16, 16, 100, d, "bf16", True, seed=17 + d, backward=True,
                       scale=scale)
-    _check_bwd(f"wide bwd scale={scale}", inp)
+    _check_bwd(f"wide bwd d={d} scale={scale}", inp)
 
 
 def test_bwd_bitwise_repeatable():
@@ -175,15 +179,17 @@ PIPE_KV = [0, 32, 128, 256, 300, 8, 63, 64, 65, 127, 129, 200, 255, 257, 299,
            17]
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_bwd_key_padding_pipelined_grid(causal):
-    """Head dim 128 on a grid that takes the pipelined kernels (16 x 16
-    heads of 300 rows), every head against the oracle; a batch entry with
-    no visible key gets dQ = 0, keys at or past kv_len get dK = dV = 0."""
+def test_bwd_key_padding_pipelined_grid(d, causal):
+    """A grid that takes the pipelined dK/dV kernel (16 x 16 heads of 300
+    rows; at head dim 64 the two-workgroups-per-CU form), every head
+    against the oracle; a batch entry with no visible key gets dQ = 0, keys
+    at or past kv_len get dK = dV = 0."""
     N = 300
-    inp = S.make_case(16, 16, N, 128, "bf16", causal, seed=42 + causal,
+    inp = S.make_case(16, 16, N, d, "bf16", causal, seed=42 + causal + d,
                       backward=True, kv_len=PIPE_KV)
-    dq, dk, dv = _check_bwd_kvlen(f"bwd kvlen pipelined causal={causal}", inp)
+    dq, dk, dv = _check_bwd_kvlen(f"bwd kvlen pipelined d={d} causal={causal}", inp)
     assert float(dq[0].float().abs().max()) == 0.0
     for b, L in enumerate(PIPE_KV):
         if L < N:
