@@ -34,11 +34,12 @@
 //        at the end.
 //   3. dQ: streams K/V tiles like the forward, recomputes S^T and dP^T and
 //      accumulates dQ^T in registers.
-//        bwd_dq_pipe_kernel (head dim 128 on grids that fill the chip):
-//        256-row query blocks, 8 wavefronts of 32 rows, K/V by LDS DMA
-//        through four stages, software-pipelined over 32-key half-tiles.
-//        bwd_dq_kernel (head dim 64, and small grids): 128-row query
-//        blocks, 4 wavefronts, register-staged double buffer.
+//        bwd_dq_pipe_kernel (grids that fill the chip): 256-row query
+//        blocks, 8 wavefronts of 32 rows, K/V by LDS DMA through four
+//        stages, software-pipelined over 32-key half-tiles.
+//        bwd_dq_kernel (small grids, and head dim 64 with dropout or a
+//        block mask): 128-row query blocks, 4 wavefronts, register-staged
+//        double buffer.
 // Splitting dQ from dK/dV costs 4d extra matrix FLOP per (query, key) pair
 // (14d instead of 10d) but removes the float32 atomics that a fused kernel
 // needs for dQ: device-scope atomics are resolved at the memory side, not in
@@ -1184,7 +1185,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_pipe_kernel(
 // The DMA descriptor ends at the head's last key: keys past N read as zero.
 constexpr int kDqPBR = 256;
 
-template <bool CAUSAL, bool SPARSE, bool DROP = false>
+template <bool CAUSAL, bool SPARSE, bool DROP = false, int D = kD>
 __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -1193,8 +1194,10 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
     int N, int n_qblk, float c_log2, float scale, Dropout drop,
     const int32_t* __restrict__ kv_len = nullptr) {
   static_assert(!SPARSE || kDqPBR == FA_SPARSE_BQ, "a workgroup is a mask row");
-  constexpr int D = kD;
-  constexpr int TE = kDqBC * kRS;                 // elements per tile stage
+  static_assert(D == kD || (D == 64 && !DROP), "head dimension");
+  // Padded row stride of the K/V tiles (as in the dK/dV kernel).
+  constexpr int RS = D == 64 ? D + 8 : kRS;
+  constexpr int TE = kDqBC * RS;                  // elements per tile stage
   constexpr int THREADS = 512;
   constexpr int NW = THREADS / 64;
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[4][TE];
@@ -1313,7 +1316,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
   // ---- K/V tile DMA: instruction u of wavefront w fills the 1 KB of the
   // (padded) stage at 1024 (w + NW u), 16 bytes per lane; lanes on row
   // padding, and keys past N, read zeros.
-  constexpr int RCH = kRS / 8;                       // 16-B slots per row
+  constexpr int RCH = RS / 8;                       // 16-B slots per row
   constexpr int TI = kDqBC * RCH / 64;               // DMA instructions per tile
   constexpr int TIW = (TI + NW - 1) / NW;
   constexpr int kMinBatch = 2 * (TI / NW);           // fewest a wave issues per tile
@@ -1370,17 +1373,21 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
     constexpr int kQ = 2 * (D / 32);     // MFMAs for dQ^T
     constexpr int kN = 2 * kS + kQ;
     constexpr int kPf = 3;
+    // VALU elements per MFMA slot (the 16 elements' three-slot pipeline
+    // over a step of kN slots): one at head dim 128, two at head dim 64.
+    constexpr int kG = kN >= 18 ? 1 : 2;
+    static_assert(kG * (kN - 2) >= 16, "the VALU pipeline fits the step");
     auto fetch = [&](int i) -> bf16x8 {
       if (i < kS)
-        return *(const bf16x8*)(&lds_k[stn][(32 * kbn + lq) * kRS + 8 * hh + 16 * i]);
+        return *(const bf16x8*)(&lds_k[stn][(32 * kbn + lq) * RS + 8 * hh + 16 * i]);
       if (i < 2 * kS)
-        return *(const bf16x8*)(&lds_v[stn][(32 * kbn + lq) * kRS + 8 * hh + 16 * (i - kS)]);
+        return *(const bf16x8*)(&lds_v[stn][(32 * kbn + lq) * RS + 8 * hh + 16 * (i - kS)]);
       const int pi = i - 2 * kS;
       const int h = pi / (D / 32), db = pi % (D / 32);
       const int col = 32 * db + 16 * dsub + 4 * (r16 & 3);
       const int row = 32 * kbc + 16 * h + 4 * hh + (r16 >> 2);
-      return join_bf16(lds_read_tr16(&lds_k[stc][row * kRS + col]),
-                       lds_read_tr16(&lds_k[stc][(row + 8) * kRS + col]));
+      return join_bf16(lds_read_tr16(&lds_k[stc][row * RS + col]),
+                       lds_read_tr16(&lds_k[stc][(row + 8) * RS + col]));
     };
     // Operand of slot m: the S^T and dP^T products alternate (S_0, dP_0,
     // S_1, dP_1, ...) so that no MFMA is issued right after one that
@@ -1428,10 +1435,13 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
         const int pi = i - 2 * kS;
         dq_acc[pi % (D / 32)] = mfma32x16(a, dsb[pi / (D / 32)], dq_acc[pi % (D / 32)]);
       }
-      if (m < 16) x[m] = __builtin_fmaf(s[XE][m], c_log2, -lse2);
-      if (m >= 1 && m - 1 < 16) pe[m - 1] = __builtin_amdgcn_exp2f(x[m - 1]);
-      if (m >= 2 && m - 2 < 16) {
-        const int el = m - 2;
+#pragma unroll
+      for (int u = 0; u < kG; ++u) {
+      const int mf = kG * m + u, me = kG * (m - 1) + u, md = kG * (m - 2) + u;
+      if (mf < 16) x[mf] = __builtin_fmaf(s[XE][mf], c_log2, -lse2);
+      if (m >= 1 && me < 16) pe[me] = __builtin_amdgcn_exp2f(x[me]);
+      if (m >= 2 && md < 16) {
+        const int el = md;
         if constexpr (DROP)
           dsv[el] = pe[el] * (drop_keep(kz[el / 4], el % 4, drop.p8) ? dp[XE][el]
                                                                     : negd_s);
@@ -1443,6 +1453,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
           for (int e = 0; e < 8; ++e) v[e] = dsv[el - 7 + e];
           dsb[el / 8] = to_bf16x8(v);
         }
+      }
       }
       if constexpr (DROP) {
         // Slots 18 .. 22: two generator rounds each; slot 23: exchange.
@@ -1485,7 +1496,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
       dp[0] = negd;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const int o = lq * kRS + 8 * hh + 16 * kk;
+        const int o = lq * RS + 8 * hh + 16 * kk;
         s[0] = mfma32x16(*(const bf16x8*)(&lds_k[0][o]), qf[kk], s[0]);
         dp[0] = mfma32x16(*(const bf16x8*)(&lds_v[0][o]), gf[kk], dp[0]);
       }
@@ -1650,9 +1661,25 @@ int launch_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   const float c = (float)((double)scale * 1.4426950408889634);
   // Head dim 128 on grids with at least one 256-row workgroup per CU, and
   // every block-sparse call (a workgroup is one block-mask row) or dropout
-  // call: the pipelined kernel; the rest (and head dim 64, with or without
-  // dropout): 128-row workgroups, two per CU.
+  // call: the pipelined kernel; head dim 64 on such grids without dropout or
+  // a block mask: the pipelined kernel at head dim 64; the rest: 128-row
+  // workgroups, two per CU.
   const long long grid256 = (long long)B * H * ((N + kDqPBR - 1) / kDqPBR);
+  if (d == 64 && drop == nullptr && block_mask == nullptr &&
+      grid256 >= device_cu_count()) {
+    // head dim 64 on grids that fill the chip: the pipelined kernel
+    const int n_qblk = (N + kDqPBR - 1) / kDqPBR;
+    const dim3 grid((unsigned)(B * H * n_qblk)), block(512);
+    if (causal)
+      hipLaunchKernelGGL((bwd_dq_pipe_kernel<true, false, false, 64>), grid,
+                         block, 0, stream, q, k, v, dO, lse, D, dq, nullptr, H,
+                         N, n_qblk, c, scale, Dropout{}, kv_len);
+    else
+      hipLaunchKernelGGL((bwd_dq_pipe_kernel<false, false, false, 64>), grid,
+                         block, 0, stream, q, k, v, dO, lse, D, dq, nullptr, H,
+                         N, n_qblk, c, scale, Dropout{}, kv_len);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+  }
   if (d == kD && (grid256 >= device_cu_count() || block_mask != nullptr ||
                   drop != nullptr)) {
     const int n_qblk = (N + kDqPBR - 1) / kDqPBR;

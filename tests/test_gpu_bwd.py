@@ -85,7 +85,8 @@ def test_bwd_bitwise_repeatable():
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 33, 64, 300, 1000])
 def test_bwd_head_dim_64(causal, N):
-    """Head dimension 64 (the 8-wavefront dK/dV and 4-wavefront dQ kernels)."""
+    """Head dimension 64 on small grids (the 8-wavefront dK/dV and 4-wavefront
+    dQ kernels)."""
     B, H = (1, 3) if N <= 300 else (2, 2)
     inp = S.make_case(B, H, N, 64, "bf16", causal, seed=500 + N + causal,
                       backward=True)
