@@ -28,8 +28,8 @@
 //        in AGPRs, query tiles by LDS DMA through four stages, two
 //        software-pipelined phases per tile; one workgroup per CU at head
 //        dim 128, two at head dim 64 (fewer registers, smaller tiles).
-//        bwd_dkdv_kernel (small grids, and head dim 64 with dropout or a
-//        block mask): 8 wavefronts, each owning 32 keys and one half of
+//        bwd_dkdv_kernel (small grids without a block mask, and head dim 64
+//        with dropout): 8 wavefronts, each owning 32 keys and one half of
 //        every query tile; the two halves' partials are added through LDS
 //        at the end.
 //   3. dQ: streams K/V tiles like the forward, recomputes S^T and dP^T and
@@ -37,8 +37,8 @@
 //        bwd_dq_pipe_kernel (grids that fill the chip): 256-row query
 //        blocks, 8 wavefronts of 32 rows, K/V by LDS DMA through four
 //        stages, software-pipelined over 32-key half-tiles.
-//        bwd_dq_kernel (small grids, and head dim 64 with dropout or a
-//        block mask): 128-row query blocks, 4 wavefronts, register-staged
+//        bwd_dq_kernel (small grids without a block mask, and head dim 64
+//        with dropout): 128-row query blocks, 4 wavefronts, register-staged
 //        double buffer.
 // Splitting dQ from dK/dV costs 4d extra matrix FLOP per (query, key) pair
 // (14d instead of 10d) but removes the float32 atomics that a fused kernel
@@ -1583,19 +1583,21 @@ int launch_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   const float c = (float)((double)scale * 1.4426950408889634);
   // Head dim 128 on grids with at least one 128-key workgroup per CU, and
   // every block-sparse or dropout call: the pipelined kernel (4 wavefronts,
-  // K/V in registers); head dim 64 on such grids without dropout or a block
-  // mask: the pipelined kernel at head dim 64; the rest: 8 wavefronts.
+  // K/V in registers); head dim 64 without dropout on such grids or with a
+  // block mask: the pipelined kernel at head dim 64; the rest: 8 wavefronts.
   const bool fills = (long long)B * H * n_kblk >= device_cu_count();
-  if (d == 64 && fills && drop == nullptr && block_mask == nullptr) {
+  if (d == 64 && drop == nullptr && (fills || block_mask != nullptr)) {
     const dim3 grid((unsigned)(B * H * n_kblk)), block(256);
-    if (causal)
-      hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<true, false, false, 64>), grid,
-                         block, 0, stream, q, k, v, dO, lse, D, dk, dv, nullptr,
-                         H, N, n_kblk, c, scale, Dropout{}, kv_len);
-    else
-      hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<false, false, false, 64>), grid,
-                         block, 0, stream, q, k, v, dO, lse, D, dk, dv, nullptr,
-                         H, N, n_kblk, c, scale, Dropout{}, kv_len);
+#define FA_DKDV64(CC, SS)                                                      \
+  hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<CC, SS, false, 64>), grid, block, 0, \
+                     stream, q, k, v, dO, lse, D, dk, dv, block_mask, H, N,     \
+                     n_kblk, c, scale, Dropout{}, kv_len)
+    if (block_mask) {
+      if (causal) FA_DKDV64(true, true); else FA_DKDV64(false, true);
+    } else {
+      if (causal) FA_DKDV64(true, false); else FA_DKDV64(false, false);
+    }
+#undef FA_DKDV64
     return hipGetLastError() == hipSuccess ? 0 : -6;
   }
   if (d == kD && (fills || block_mask != nullptr || drop != nullptr)) {
@@ -1661,23 +1663,26 @@ int launch_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   const float c = (float)((double)scale * 1.4426950408889634);
   // Head dim 128 on grids with at least one 256-row workgroup per CU, and
   // every block-sparse call (a workgroup is one block-mask row) or dropout
-  // call: the pipelined kernel; head dim 64 on such grids without dropout or
-  // a block mask: the pipelined kernel at head dim 64; the rest: 128-row
+  // call: the pipelined kernel; head dim 64 without dropout on such grids or
+  // with a block mask: the pipelined kernel at head dim 64; the rest: 128-row
   // workgroups, two per CU.
   const long long grid256 = (long long)B * H * ((N + kDqPBR - 1) / kDqPBR);
-  if (d == 64 && drop == nullptr && block_mask == nullptr &&
-      grid256 >= device_cu_count()) {
-    // head dim 64 on grids that fill the chip: the pipelined kernel
+  if (d == 64 && drop == nullptr &&
+      (grid256 >= device_cu_count() || block_mask != nullptr)) {
+    // head dim 64 on grids that fill the chip, or with a block mask: the
+    // pipelined kernel
     const int n_qblk = (N + kDqPBR - 1) / kDqPBR;
     const dim3 grid((unsigned)(B * H * n_qblk)), block(512);
-    if (causal)
-      hipLaunchKernelGGL((bwd_dq_pipe_kernel<true, false, false, 64>), grid,
-                         block, 0, stream, q, k, v, dO, lse, D, dq, nullptr, H,
-                         N, n_qblk, c, scale, Dropout{}, kv_len);
-    else
-      hipLaunchKernelGGL((bwd_dq_pipe_kernel<false, false, false, 64>), grid,
-                         block, 0, stream, q, k, v, dO, lse, D, dq, nullptr, H,
-                         N, n_qblk, c, scale, Dropout{}, kv_len);
+#define FA_DQ64(CC, SS)                                                        \
+  hipLaunchKernelGGL((bwd_dq_pipe_kernel<CC, SS, false, 64>), grid, block, 0,   \
+                     stream, q, k, v, dO, lse, D, dq, block_mask, H, N, n_qblk, \
+                     c, scale, Dropout{}, kv_len)
+    if (block_mask) {
+      if (causal) FA_DQ64(true, true); else FA_DQ64(false, true);
+    } else {
+      if (causal) FA_DQ64(true, false); else FA_DQ64(false, false);
+    }
+#undef FA_DQ64
     return hipGetLastError() == hipSuccess ? 0 : -6;
   }
   if (d == kD && (grid256 >= device_cu_count() || block_mask != nullptr ||

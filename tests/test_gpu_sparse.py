@@ -155,9 +155,9 @@ def test_sparse_bwd_small(d, causal, N):
 
 
 def test_sparse_bwd_d64_alternate_columns_and_empty_rows():
-    """Head dim 64 (the 8-wavefront dK/dV and 4-wavefront dQ kernels with
-    tile lists): a key column no query keeps gets dK = dV = 0, a block row
-    with no kept block dQ = 0."""
+    """Head dim 64 (the pipelined kernels at head dim 64 with tile lists): a
+    key column no query keeps gets dK = dV = 0, a block row with no kept
+    block dQ = 0."""
     N, H = 640, 2
     tq, tk = -(-N // 256), -(-N // 128)
     m = np.zeros((H, tq, tk), dtype=np.uint8)
@@ -172,13 +172,15 @@ def test_sparse_bwd_d64_alternate_columns_and_empty_rows():
 
 
 def test_sparse_bwd_d64_all_ones_equals_dense_bitwise():
-    """At head dim 64 both calls take the same non-pipelined kernels."""
+    """At head dim 64 on a grid that fills the chip (16 x 16 heads) both calls
+    take the pipelined kernels, so an all-ones mask gives the dense result
+    bit for bit."""
     import torch
     import io_aware_tiled_amd as fa
-    inp = S.make_case(2, 4, 700, 64, "bf16", True, seed=65, backward=True)
+    inp = S.make_case(16, 16, 300, 64, "bf16", True, seed=65, backward=True)
     q, k, v, do = (to_dev(inp, n) for n in ("q", "k", "v", "do"))
     o, lse = fa.forward(q, k, v, causal=True, scale=inp["scale"])
-    ones = torch.ones((4, 3, 6), dtype=torch.uint8, device=DEV)
+    ones = torch.ones((16, 2, 3), dtype=torch.uint8, device=DEV)
     g_sparse = fa.backward(q, k, v, o, lse, do, causal=True,
                            scale=inp["scale"], block_mask=ones)
     g_dense = fa.backward(q, k, v, o, lse, do, causal=True, scale=inp["scale"])
