@@ -683,6 +683,24 @@ def micro(command: str) -> int:
                      f"alone {c0 / (it * 4):.1f})",
                      f"{flop / (ms1 * 1e-3) / 1e12:.0f} TFLOP/s (MFMA alone "
                      f"{flop / (ms0 * 1e-3) / 1e12:.0f}), {c1 / u1 / 1e3:.2f} GHz"))
+    for which, name in ((10, "MFMA + 4 SALU after each"),
+                        (11, "MFMA + 4 s_nop 0 after each"),
+                        (12, "MFMA + 4 s_waitcnt after each"),
+                        (13, "MFMA + 4 ds_read_b128 after each"),
+                        (14, "MFMA + 1 ds_read_b128 after each"),
+                        (15, "MFMA + 2 ds_read_b64_tr_b16 after each"),
+                        (16, "MFMA (AGPR acc.) + 1 ds_read_b128 after each"),
+                        (17, "MFMA (AGPR acc.) alone")):
+        for wps in (1, 2):
+            it = 2000
+            c0, _, ms0 = run(1, wps, 0, it)
+            c1, u1, ms1 = run(which, wps, 0, it)
+            flop = cus * 4 * wps * it * 4 * 32768.0
+            rows.append((name, "4 MFMA chains, random", wps,
+                         f"{c1 / (it * 4):.1f} cycles per MFMA slot per wave (MFMA "
+                         f"alone {c0 / (it * 4):.1f})",
+                         f"{flop / (ms1 * 1e-3) / 1e12:.0f} TFLOP/s (MFMA alone "
+                         f"{flop / (ms0 * 1e-3) / 1e12:.0f}), {c1 / u1 / 1e3:.2f} GHz"))
     for which, name, per, rowb in ((6, "ds_read_b128 (row slices)", 1024, 272),
                                    (7, "2 x ds_read_b64_tr_b16 (transposed)", 1024, 320)):
         for wps in (1, 2, 4):

@@ -142,18 +142,17 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 // the compiler, which cannot tell the stage being filled from the stages
 // being read, does not wait for the transfer before every LDS read; callers
 // wait for it explicitly (vmcnt) before the barrier that publishes the
-// stage.  M0 carries the LDS base and is saved and restored around it.
+// stage.  M0 carries the LDS base: it is an operand of the statement, so
+// the compiler writes it (once for consecutive transfers with one base) and
+// nothing is saved or restored; the s_nop is the wait state between an M0
+// write and the transfer that reads it.
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs,
                                           unsigned lds, unsigned voffset) {
-  unsigned saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voffset), "s"(rs)
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "{m0}"(lds), "v"(voffset), "s"(rs)
       : "memory");
 }
 

@@ -173,6 +173,95 @@ __global__ __launch_bounds__(1024) void mixed_kernel(int iters, int constant,
   if (lane == 0) st[(blockIdx.x * blockDim.x + threadIdx.x) >> 6] = {c1 - c0, t1 - t0};
 }
 
+// Issue cost of other instruction kinds between MFMAs: each iteration
+// issues 4 independent MFMAs, each followed by 4 instructions of one kind.
+// kind 0: s_add_u32 on independent SGPRs (SALU); 1: s_nop 0;
+// 2: s_waitcnt lgkmcnt(0) with nothing outstanding; 3: ds_read_b128 (the
+// results are taken once per iteration, after one wait, by an empty asm
+// statement, so no other instruction is added).  Kinds 4..7 put one LDS
+// operand's worth of reads after each MFMA, as the attention kernels do:
+// 4: one ds_read_b128; 5: two ds_read_b64_tr_b16; 6: as 4 with the
+// accumulators in AGPRs; 7: no reads, accumulators in AGPRs.  At most 2
+// waves per SIMD.
+template <int KIND>
+__global__ __launch_bounds__(512) void issue_kernel(int iters, int constant,
+                                                     float* sink, Stamp* st) {
+  constexpr int NCH = 4;
+  __shared__ __attribute__((aligned(16))) u32x4 buf[1024];   // 16 KB
+  const int lane = threadIdx.x & 63;
+  for (int i = threadIdx.x; i < 1024; i += blockDim.x)
+    buf[i] = u32x4{(uint32_t)i, 1u, 2u, 3u};
+  bf16x8 a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = operand(lane, i, constant != 0);
+    b[i] = operand(lane, i + 4, constant != 0);
+    asm volatile("" : "+v"(a[i]), "+v"(b[i]));
+  }
+  f32x16 acc[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) acc[c] = f32x16{};
+  uint32_t s0 = 1, s1 = 2, s2 = 3, s3 = 4;
+  __syncthreads();
+  const uint64_t c0 = cyc(), t0 = rt();
+  for (int it = 0; it < iters; ++it) {
+    u32x4 r[NCH][4];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if (KIND >= 6)
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                     : "+a"(acc[c]) : "v"(a[c]), "v"(b[c]));
+      else
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c], b[c], acc[c], 0, 0, 0);
+      if (KIND == 0) {
+        asm volatile("s_add_u32 %0, %0, 1" : "+s"(s0));
+        asm volatile("s_add_u32 %0, %0, 1" : "+s"(s1));
+        asm volatile("s_add_u32 %0, %0, 1" : "+s"(s2));
+        asm volatile("s_add_u32 %0, %0, 1" : "+s"(s3));
+      } else if (KIND == 1) {
+        asm volatile("s_nop 0\n\ts_nop 0\n\ts_nop 0\n\ts_nop 0");
+      } else if (KIND == 2) {
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\t"
+                     "s_waitcnt lgkmcnt(0)\n\ts_waitcnt lgkmcnt(0)" ::: "memory");
+      } else if (KIND == 3) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[c][e] = buf[(lane + 64 * (4 * c + e)) & 1023];
+      } else if (KIND == 4 || KIND == 6) {
+        r[c][0] = buf[(lane + 64 * c) & 1023];
+      } else if (KIND == 5) {
+        // the forward's V operand reads: 320-byte rows, rows 0..15
+        const uint16_t* tile = (const uint16_t*)&buf[0];
+        const int r16 = lane & 15, dsub = (lane >> 4) & 1, hh = lane >> 5;
+        const int col = 32 * (c & 3) + 16 * dsub + 4 * (r16 & 3);
+        const int row = 4 * hh + (r16 >> 2);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&tile[row * 160 + col]);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&tile[(row + 8) * 160 + col]);
+        r[c][0] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (KIND == 3) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) asm volatile("" :: "v"(r[c][e]));
+    }
+    if (KIND == 4 || KIND == 5 || KIND == 6) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) asm volatile("" :: "v"(r[c][0]));
+    }
+  }
+  if (KIND >= 6) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  const uint64_t c1 = cyc(), t1 = rt();
+  float s = (float)(s0 + s1 + s2 + s3);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
+  if (lane == 0) st[(blockIdx.x * blockDim.x + threadIdx.x) >> 6] = {c1 - c0, t1 - t0};
+}
+
 // LDS read bandwidth.  kind 0: ds_read_b128 of 16-byte row slices (lane l
 // reads row l % 32 of a 32-row tile with a 272-byte padded stride, half
 // (l / 32) of a 32-byte slice: the attention kernels' K operand reads);
@@ -261,7 +350,9 @@ __global__ __launch_bounds__(1024) void dma_kernel(const uint16_t* src,
 
 // Runs one microbenchmark on the current device: `which` selects the kernel
 // (0 MFMA 1 chain, 1 MFMA 4 chains, 2 FMA, 3 exp2, 4 add, 5 MFMA+FMA mixed,
-// 6 LDS row reads, 7 LDS transposed reads, 8 LDS DMA, 9 exp-only chains),
+// 6 LDS row reads, 7 LDS transposed reads, 8 LDS DMA, 9 exp-only chains,
+// 10..13 MFMA + 4 SALU / s_nop / s_waitcnt / ds_read_b128 after each,
+// 14..17 MFMA + one operand of LDS reads, see issue_kernel),
 // `wps` wavefronts per SIMD (one workgroup of 256 wps threads per CU over
 // `cus` CUs), `constant` the MFMA operand kind.  Outputs: mean shader cycles
 // and mean microseconds of the timed loop per wavefront, and the kernel time
@@ -294,6 +385,14 @@ extern "C" int micro_run(int which, int wps, int constant, int iters, int cus,
       case 7: hipLaunchKernelGGL(lds_kernel<1>, g, b, 0, 0, iters, sink, st); break;
       case 8: hipLaunchKernelGGL(dma_kernel, g, b, 0, 0, src, iters, sink, st); break;
       case 9: hipLaunchKernelGGL(exp_kernel, g, b, 0, 0, iters, sink, st); break;
+      case 10: hipLaunchKernelGGL(issue_kernel<0>, g, b, 0, 0, iters, constant, sink, st); break;
+      case 11: hipLaunchKernelGGL(issue_kernel<1>, g, b, 0, 0, iters, constant, sink, st); break;
+      case 12: hipLaunchKernelGGL(issue_kernel<2>, g, b, 0, 0, iters, constant, sink, st); break;
+      case 13: hipLaunchKernelGGL(issue_kernel<3>, g, b, 0, 0, iters, constant, sink, st); break;
+      case 14: hipLaunchKernelGGL(issue_kernel<4>, g, b, 0, 0, iters, constant, sink, st); break;
+      case 15: hipLaunchKernelGGL(issue_kernel<5>, g, b, 0, 0, iters, constant, sink, st); break;
+      case 16: hipLaunchKernelGGL(issue_kernel<6>, g, b, 0, 0, iters, constant, sink, st); break;
+      case 17: hipLaunchKernelGGL(issue_kernel<7>, g, b, 0, 0, iters, constant, sink, st); break;
       default: break;
     }
   };
