@@ -702,7 +702,9 @@ def micro(command: str) -> int:
                          f"{flop / (ms1 * 1e-3) / 1e12:.0f} TFLOP/s (MFMA alone "
                          f"{flop / (ms0 * 1e-3) / 1e12:.0f}), {c1 / u1 / 1e3:.2f} GHz"))
     for which, name, per, rowb in ((6, "ds_read_b128 (row slices)", 1024, 272),
-                                   (7, "2 x ds_read_b64_tr_b16 (transposed)", 1024, 320)):
+                                   (7, "2 x ds_read_b64_tr_b16 (transposed)", 1024, 320),
+                                   (18, "ds_read_b128 (row slices)", 1024, 304),
+                                   (19, "2 x ds_read_b64_tr_b16 (transposed)", 1024, 304)):
         for wps in (1, 2, 4):
             it = 4000
             c, u, ms = run(which, wps, 0, it)

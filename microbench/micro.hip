@@ -266,14 +266,15 @@ __global__ __launch_bounds__(512) void issue_kernel(int iters, int constant,
 // reads row l % 32 of a 32-row tile with a 272-byte padded stride, half
 // (l / 32) of a 32-byte slice: the attention kernels' K operand reads);
 // kind 1: pairs of ds_read_b64_tr_b16 (the transposed V operand reads) on
-// 320-byte rows, the forward's conflict-free V stride.  8 operands per
-// wave per iteration.
+// 320-byte rows, the forward's V stride.  8 operands per wave per
+// iteration.  STRIDE (elements per row) defaults to the forward's strides;
+// 152 (304-byte rows) is the backward's, shared by both read kinds.
 constexpr int kLdsRows = 64;
 
-template <int KIND>
+template <int KIND, int STRIDE = (KIND == 0 ? 136 : 160)>
 __global__ __launch_bounds__(1024) void lds_kernel(int iters, float* sink,
                                                    Stamp* st) {
-  constexpr int kLdsStride = KIND == 0 ? 136 : 160;   // elements per row
+  constexpr int kLdsStride = STRIDE;   // elements per row
   __shared__ __attribute__((aligned(16))) uint16_t tile[kLdsRows * kLdsStride];
   for (int i = threadIdx.x; i < kLdsRows * kLdsStride; i += blockDim.x)
     tile[i] = (uint16_t)(i * 7);
@@ -352,7 +353,8 @@ __global__ __launch_bounds__(1024) void dma_kernel(const uint16_t* src,
 // (0 MFMA 1 chain, 1 MFMA 4 chains, 2 FMA, 3 exp2, 4 add, 5 MFMA+FMA mixed,
 // 6 LDS row reads, 7 LDS transposed reads, 8 LDS DMA, 9 exp-only chains,
 // 10..13 MFMA + 4 SALU / s_nop / s_waitcnt / ds_read_b128 after each,
-// 14..17 MFMA + one operand of LDS reads, see issue_kernel),
+// 14..17 MFMA + one operand of LDS reads, see issue_kernel, 18 and 19 as
+// 6 and 7 on the backward's 304-byte rows),
 // `wps` wavefronts per SIMD (one workgroup of 256 wps threads per CU over
 // `cus` CUs), `constant` the MFMA operand kind.  Outputs: mean shader cycles
 // and mean microseconds of the timed loop per wavefront, and the kernel time
@@ -393,6 +395,8 @@ extern "C" int micro_run(int which, int wps, int constant, int iters, int cus,
       case 15: hipLaunchKernelGGL(issue_kernel<5>, g, b, 0, 0, iters, constant, sink, st); break;
       case 16: hipLaunchKernelGGL(issue_kernel<6>, g, b, 0, 0, iters, constant, sink, st); break;
       case 17: hipLaunchKernelGGL(issue_kernel<7>, g, b, 0, 0, iters, constant, sink, st); break;
+      case 18: hipLaunchKernelGGL((lds_kernel<0, 152>), g, b, 0, 0, iters, sink, st); break;
+      case 19: hipLaunchKernelGGL((lds_kernel<1, 152>), g, b, 0, 0, iters, sink, st); break;
       default: break;
     }
   };
