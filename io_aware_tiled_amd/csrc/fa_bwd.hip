@@ -1076,6 +1076,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_pipe_kernel(
     }
   };
 
+  int free_stage = 2;   // a stage no wavefront reads after the tile loop
   if (n_vis > 0) {
     const int last = n_vis - 1;      // list positions
     // Prologue: the first tile in stage 0, the second in stage 1 (its LSE /
@@ -1147,29 +1148,43 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_pipe_kernel(
     }
     b_only(sp);
     agpr_hazard_pad();   // last MFMA -> epilogue reads
+    // Tile last+2's stage: no transfer fills it and no wavefront reads it
+    // after the last iteration's barrier.
+    free_stage = s1;
   }
 
   // ---- epilogue: dK = scale * dK^T, dV = dV^T (lane = key, regs = d);
-  // with dropout both are divided by the keep probability.
+  // with dropout both are divided by the keep probability.  A lane holds
+  // 8-byte pieces of its key's row, so stores straight from the registers
+  // would touch 32 rows per instruction; instead each wavefront writes its
+  // 32 rows in bf16 to its own area of the free stage (rows padded to
+  // D + 8 elements) and reads them back 16 bytes per lane, so that every
+  // store instruction writes whole rows.
   const float sk = DROP ? scale / kp : scale, sv = DROP ? 1.f / kp : 1.f;
-  if (mykey < N) {
-    uint16_t* dkr = dK + head + (size_t)mykey * D;
-    uint16_t* dvr = dV + head + (size_t)mykey * D;
+  constexpr int ES = D + 8;                  // row stride of the area
+  constexpr int CPR = D / 8;                 // 16-byte pieces per row
+  static_assert(2 * 32 * ES <= QE, "two wavefronts' rows fit a stage array");
+  uint16_t* area = (w < 2 ? lds_q[free_stage] : lds_g[free_stage]) + (w & 1) * 32 * ES;
+  auto store_rows = [&](f32x16* acc, float mul, uint16_t* out) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        f32x4 a, b;
+        f32x4 a;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = dk_acc[db][4 * g + e] * sk;
-          b[e] = dv_acc[db][4 * g + e] * sv;
-        }
-        *(bf16x4*)(dkr + 32 * db + 8 * g + 4 * hh) = to_bf16x4(a);
-        *(bf16x4*)(dvr + 32 * db + 8 * g + 4 * hh) = to_bf16x4(b);
+        for (int e = 0; e < 4; ++e) a[e] = acc[db][4 * g + e] * mul;
+        *(bf16x4*)(area + l32 * ES + 32 * db + 8 * g + 4 * hh) = to_bf16x4(a);
       }
     }
-  }
+#pragma unroll
+    for (int i = 0; i < 32 * CPR / 64; ++i) {
+      const int row = i * (64 / CPR) + lane / CPR, c = lane % CPR;
+      const u32x4 v = *(const u32x4*)(area + row * ES + 8 * c);
+      if (wk0 + row < N) *(u32x4*)(out + head + (size_t)(wk0 + row) * D + 8 * c) = v;
+    }
+  };
+  store_rows(dk_acc, sk, dK);
+  store_rows(dv_acc, sv, dV);
 }
 
 // ---------------------------------------------------------------------------
