@@ -1550,20 +1550,33 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
   }
 
   // ---- epilogue: dQ = scale * dQ^T (lane = query, regs = d); with
-  // dropout divided by the keep probability.
+  // dropout divided by the keep probability.  A lane holds 8-byte pieces of
+  // its query's row, so stores straight from the registers would touch 32
+  // rows per instruction; instead, once every wavefront is done with the
+  // K/V stages, each writes its 32 rows in bf16 to its own area of them
+  // (rows padded to D + 8 elements) and reads them back 16 bytes per lane,
+  // so that every store instruction writes whole rows.
   const float sq = DROP ? scale / kp : scale;
-  if (qrow < N) {
-    uint16_t* out = dQ + head + (size_t)qrow * D;
+  constexpr int ES = D + 8;                  // row stride of the area
+  constexpr int CPR = D / 8;                 // 16-byte pieces per row
+  static_assert(NW * 32 * ES <= 4 * TE, "the rows fit the K stages");
+  __syncthreads();
+  uint16_t* area = &lds_k[0][0] + w * 32 * ES;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+  for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 xo;
+    for (int g = 0; g < 4; ++g) {
+      f32x4 xo;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) xo[e] = dq_acc[db][4 * g + e] * sq;
-        *(bf16x4*)(out + 32 * db + 8 * g + 4 * hh) = to_bf16x4(xo);
-      }
+      for (int e = 0; e < 4; ++e) xo[e] = dq_acc[db][4 * g + e] * sq;
+      *(bf16x4*)(area + lq * ES + 32 * db + 8 * g + 4 * hh) = to_bf16x4(xo);
     }
+  }
+#pragma unroll
+  for (int i = 0; i < 32 * CPR / 64; ++i) {
+    const int row = i * (64 / CPR) + lane / CPR, c = lane % CPR;
+    const u32x4 v = *(const u32x4*)(area + row * ES + 8 * c);
+    if (qlo + row < N) *(u32x4*)(dQ + head + (size_t)(qlo + row) * D + 8 * c) = v;
   }
 }
 

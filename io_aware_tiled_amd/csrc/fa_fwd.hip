@@ -994,29 +994,54 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D == 64) ? 2 : 1) void fwd_bf1
     if (nt_w == ntiles && nt_w > 0) pv_only(1, stm, 1);
   }
 
-  // ---- epilogue: combine half-wave sums, normalise, store O and LSE.
+  // ---- epilogue: combine half-wave sums, normalise, store O and LSE.  A
+  // lane holds 8-byte pieces of its query's row, so stores straight from
+  // the registers touch 32 rows per instruction.  With one block per
+  // wavefront, once every wavefront is done with the K/V stages, each
+  // writes its rows in bf16 to its own area of them (rows padded to D + 8
+  // elements) and reads them back 16 bytes per lane, so that every store
+  // instruction writes whole rows; with two blocks per wavefront (whose
+  // kernels fill the register file) the lanes store their pieces directly.
+  constexpr int ES = D + 8;                  // row stride of the area
+  constexpr int CPR = D / 8;                 // 16-byte pieces per row
+  constexpr int AREA = NW * NB * 32 * ES;
+  constexpr bool IN_K = AREA <= NS * T::KELEMS;
+  static_assert(NB != 1 || IN_K || AREA <= NS * T::VELEMS,
+                "the rows fit the K or V stages");
+  if constexpr (NB == 1) __syncthreads();
+  uint16_t* area = (IN_K ? &lds_k[0][0] : &lds_v[0][0]) + w * NB * 32 * ES;
 #pragma unroll
   for (int c = 0; c < NB; ++c) {
     const float l_tot = sum_halves(l_run[c]);
     float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     // Dropout: kept weights are divided by the keep probability.
     if constexpr (DROP) inv *= 256.f / (float)(256 - drop.p8);
-    if (qrow[c] < N) {
-      uint16_t* orow = O + head + (size_t)qrow[c] * D;
+    uint16_t* orow = O + head + (size_t)qrow[c] * D;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 x;
+      for (int g = 0; g < 4; ++g) {
+        f32x4 x;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = oacc[c][db][4 * g + e] * inv;
+        for (int e = 0; e < 4; ++e) x[e] = oacc[c][db][4 * g + e] * inv;
+        if constexpr (NB == 1)
+          *(bf16x4*)(area + lq * ES + 32 * db + 8 * g + 4 * hh) = to_bf16x4(x);
+        else if (qrow[c] < N)
           *(bf16x4*)(orow + 32 * db + 8 * g + 4 * hh) = to_bf16x4(x);
-        }
-      if (hh == 0) {
-        LSE[(size_t)bh * N + qrow[c]] =
-            l_tot > 0.f ? (m_ref[c] + __builtin_amdgcn_logf(l_tot)) * kLn2
-                        : -INFINITY;
       }
+    if (hh == 0 && qrow[c] < N) {
+      LSE[(size_t)bh * N + qrow[c]] =
+          l_tot > 0.f ? (m_ref[c] + __builtin_amdgcn_logf(l_tot)) * kLn2
+                      : -INFINITY;
+    }
+  }
+  if constexpr (NB == 1) {
+#pragma unroll
+    for (int i = 0; i < 32 * CPR / 64; ++i) {
+      const int row = i * (64 / CPR) + lane / CPR, cc = lane % CPR;
+      const u32x4 v = *(const u32x4*)(area + row * ES + 8 * cc);
+      if (qlo[0] + row < N)
+        *(u32x4*)(O + head + (size_t)(qlo[0] + row) * D + 8 * cc) = v;
     }
   }
 }
