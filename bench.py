@@ -21,7 +21,10 @@ kernels execute 14d per pair).  The roofline's dominant kernel is fa_bwd_dkdv
 line with a "roofline" object for the dominant kernel (its average launch
 duration from HIP events recorded on the launch stream during the timed
 steps) and a "cpu_baseline" object (the fp64 oracle timed on a bounded
-sample of heads on the host cores).
+sample of heads on the host cores).  A "steady_state" object repeats the
+timing after --steady-s more seconds of untimed steps: a GPU that was idle
+while the inputs were generated runs its first steps at a lower clock, so
+that object gives the rate under sustained load beside the contract's one.
 """
 from __future__ import annotations
 
@@ -745,6 +748,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     choices=sorted(S.WORKLOADS))
+    ap.add_argument("--steady-s", type=float, default=0.3, metavar="SECONDS",
+                    help="after the timed steps, step untimed for this long "
+                         "and time the steps again (steady_state; 0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -834,7 +840,8 @@ def main(argv=None) -> int:
         return micro(args.command or "python bench.py --micro")
     w = S.WORKLOADS[args.workload]
     res = time_workload(w, dev, args.steps, args.warmup,
-                        copy_calibration=args.copy_calibration)
+                        copy_calibration=args.copy_calibration,
+                        steady_s=args.steady_s)
     out = result_line(w, res, args)
     if args.per_config and w.name == DEFAULT_WORKLOAD:
         out["per_config"] = per_config(dev, args, res, out)
@@ -848,10 +855,16 @@ CONFIGS = ((1, "tiny_f32"), (2, "gpt2_causal"), (3, "bert_keypad"),
 
 
 def time_workload(w: S.Workload, dev, steps: int, warmup: int,
-                  copy_calibration: int = 0) -> dict:
+                  copy_calibration: int = 0, steady_s: float = 0.0) -> dict:
     """Upload the workload's inputs, run `warmup` untimed steps, then time
     `steps` steps: wall clock around all of them (synchronised on both
-    sides) and HIP events on the launch stream around every kernel."""
+    sides) and HIP events on the launch stream around every kernel.
+
+    With steady_s > 0, after that timed region: keep stepping (untimed) for
+    at least steady_s seconds, then time `steps` more steps the same way
+    (result["steady"]).  A GPU that has been idle runs its first steps at
+    a lower clock, so a few warmup steps after input generation measure
+    part of the clock ramp; the second pass gives the sustained rate."""
     import torch
     import io_aware_tiled_amd as fa
     log(f"[bench] generating {w.name} inputs")
@@ -976,18 +989,37 @@ def time_workload(w: S.Workload, dev, steps: int, warmup: int,
         del cx, cy
         log(f"[bench] copy calibration: 3 x {copy_calibration} MiB")
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-          for _ in range(steps)]
-    log(f"[bench] {w.name}: timing {steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(ev[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    def timed():
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(ev[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per_kernel = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]))
+                      for j, n in enumerate(names)}
+        return per_kernel, wall
 
-    per_kernel = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]))
-                  for j, n in enumerate(names)}
+    log(f"[bench] {w.name}: timing {steps} steps")
+    per_kernel, wall = timed()
+    steady = None
+    if steady_s > 0:
+        # batches of about 20 ms of GPU work between host synchronisations
+        batch = max(1, int(20.0 / max(wall * 1e3 / steps, 1e-3)))
+        n_warm, t1 = 0, time.perf_counter()
+        while time.perf_counter() - t1 < steady_s:
+            for _ in range(batch):
+                step()
+            n_warm += batch
+            torch.cuda.synchronize()
+        warm_s = time.perf_counter() - t1
+        log(f"[bench] {w.name}: {n_warm} more steps ({warm_s:.2f} s), "
+            f"timing {steps} steps again")
+        pk2, wall2 = timed()
+        steady = {"warm_steps": n_warm, "warm_s": warm_s, "per_kernel": pk2,
+                  "ms_step": wall2 * 1e3 / steps}
     # outputs of the timed run must be finite (parity itself is the tests' job)
     check = {"o_finite": bool(torch.isfinite(o.float()).all()),
              "lse_finite_or_neg_inf": bool((torch.isfinite(lse) | (lse == -float("inf"))).all())}
@@ -997,7 +1029,8 @@ def time_workload(w: S.Workload, dev, steps: int, warmup: int,
     pairs = visible_pairs(w, inp["kv_len"], inp.get("block_mask"))
     return {"inp": inp, "names": names, "per_kernel": per_kernel,
             "ms_step": wall * 1e3 / steps, "pairs": pairs, "fp8": fp8,
-            "dropout": dr, "check": check, "steps": steps, "warmup": warmup}
+            "dropout": dr, "check": check, "steps": steps, "warmup": warmup,
+            "steady": steady}
 
 
 def record_calls(fa, stage):
@@ -1140,6 +1173,24 @@ def result_line(w: S.Workload, res: dict, args) -> dict:
     if w.backward:
         bwd_ms = sum(per_kernel[n] for n in names[1:])
         out["bwd_tflops"] = round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2)
+    st = res.get("steady")
+    if st:
+        spk, sms = st["per_kernel"], st["ms_step"]
+        sd = spk[dom]
+        sa = (algorithmic_bytes(w, dom) / (sd * 1e-3) / 1e9
+              if roofline["unit"] == "GB/s" else dom_flops / (sd * 1e-3) / 1e12)
+        sv = step_flops / (sms * 1e-3) / 1e12
+        out["steady_state"] = {
+            "what": ("the same steps timed again after more untimed steps, "
+                     "at the clock the GPU sustains under load; value and "
+                     "roofline above are the measurement after --warmup steps"),
+            "warm_steps": st["warm_steps"], "warm_s": round(st["warm_s"], 2),
+            "value": round(sv, 2), "frac_of_peak": round(sv / peak, 4),
+            "ms_per_step": round(sms, 4),
+            "kernel_ms": {n: round(t, 4) for n, t in spk.items()},
+            "dominant": {"kernel": dom, "achieved": round(sa, 2),
+                         "unit": roofline["unit"],
+                         "frac": round(sa / roofline["peak"], 4)}}
     return out
 
 
@@ -1178,7 +1229,8 @@ def per_config(dev, args, head_res: dict, head_out: dict) -> dict:
     """Every synthetic config the metric is quoted on: algorithmic TFLOP/s,
     fraction of its peak, kernel time, and the fp64 oracle timed on the
     host cores of this run (configs 1-3 whole, median of 3 runs; configs 4
-    and 5 on a bounded sample of heads, one run)."""
+    and 5 on a bounded sample of heads, one run); with --steady-s, each
+    config's rate under sustained load as well."""
     cores = len(os.sched_getaffinity(0))
     table = {}
     for num, name in CONFIGS:
@@ -1186,7 +1238,8 @@ def per_config(dev, args, head_res: dict, head_out: dict) -> dict:
         if name == head_out["config"]["workload"]:
             res, line = head_res, head_out
         else:
-            res = time_workload(w, dev, args.steps, args.warmup)
+            res = time_workload(w, dev, args.steps, args.warmup,
+                                steady_s=args.steady_s)
             fwd_flops = 4.0 * w.d * res["pairs"]
             line = {"value": fwd_flops / (res["ms_step"] * 1e-3) / 1e12,
                     "ms_per_step": res["ms_step"]}
@@ -1208,6 +1261,16 @@ def per_config(dev, args, head_res: dict, head_out: dict) -> dict:
             bt = 10.0 * w.d * res["pairs"] / (bwd_ms * 1e-3) / 1e12
             ent["bwd_tflops"] = round(bt, 2)
             ent["bwd_frac_of_peak"] = round(bt / peak, 4)
+        st = res.get("steady")
+        if st:
+            step_flops = (14.0 if w.backward else 4.0) * w.d * res["pairs"]
+            sv = step_flops / (st["ms_step"] * 1e-3) / 1e12
+            sf = fwd_flops / (st["per_kernel"]["fwd"] * 1e-3) / 1e12
+            ent["steady_state"] = {
+                "warm_steps": st["warm_steps"], "tflops": round(sv, 2),
+                "frac_of_peak": round(sv / peak, 4),
+                "fwd_tflops": round(sf, 2), "fwd_frac_of_peak": round(sf / peak, 4),
+                "kernel_ms": {n: round(t, 4) for n, t in st["per_kernel"].items()}}
         if not args.no_cpu_baseline:
             if num <= 3:
                 log(f"[bench] oracle on config {num} (3 runs)")
