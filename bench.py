@@ -580,11 +580,15 @@ def summarize_ceiling(path, command) -> int:
 
 
 def summarize_trace(w: S.Workload, path, command, warmup: int,
-                    steps: int) -> int:
+                    steps: int, steady_warm: int = -1) -> int:
     """profiles/kernels_<workload>.md from a rocprofv3 kernel trace: per
-    libfa kernel, the timed dispatches only.  A kernel that the step runs c
-    times (its dispatch count is c (warmup + steps)) has its first c warmup
-    dispatches skipped and the next c steps kept."""
+    libfa kernel, the timed dispatches only.  The run made T = warmup +
+    steps steps, or, when it made a steady-state pass of steady_warm
+    untimed steps and `steps` timed ones (bench.py logs the count), T =
+    warmup + 2 steps + steady_warm.  A kernel that each step runs c times
+    (c T dispatches) has its first c warmup dispatches skipped and the next
+    c steps kept; with a steady-state pass its last c steps are reported
+    beside them."""
     import csv
     per = {}
     with open(path) as f:
@@ -595,7 +599,12 @@ def summarize_trace(w: S.Workload, path, command, warmup: int,
             per.setdefault(r["Kernel_Name"], []).append(
                 (int(r["Dispatch_Id"]), ns))
     md = os.path.join(PROFILES, f"kernels_{w.name}.md")
-    total = sum(ns for v in per.values() for _, ns in v)
+    steady = steady_warm >= 0
+    n_run = warmup + steps + (steps + steady_warm if steady else 0)
+    for name, v in per.items():
+        if len(v) % n_run:
+            raise SystemExit(f"{name}: {len(v)} dispatches, not a multiple of "
+                             f"the run's {n_run} steps")
     with open(md, "w") as f:
         f.write(f"# Kernel trace: {w.name} (B={w.B} H={w.H} N={w.N} d={w.d}, "
                 f"causal={w.causal}, {'forward+backward' if w.backward else 'forward'})"
@@ -603,20 +612,30 @@ def summarize_trace(w: S.Workload, path, command, warmup: int,
                 "\n```\n\nrocprofv3 kernel trace, libfa kernels only, the "
                 f"timed dispatches of each kernel (the dispatches of its first "
                 f"{warmup} steps are the warmup and are skipped, those of the "
-                f"next {steps} are kept; durations in microseconds):\n\n"
-                "| kernel | timed dispatches | average | min | max |\n"
-                "|---|---|---|---|---|\n")
+                f"next {steps} are kept; durations in microseconds)")
+        if steady:
+            f.write(f", and beside them the last {steps} steps of the run "
+                    f"(the steady-state pass: {steady_warm} more untimed "
+                    "steps, then those)")
+        f.write(":\n\n| kernel | timed dispatches | average | min | max |"
+                + (" steady average | steady min | steady max |" if steady else "")
+                + "\n|---|---|---|---|---|" + ("---|---|---|" if steady else "")
+                + "\n")
         for name, v in sorted(per.items(), key=lambda kv: -sum(x[1] for x in kv[1])):
-            n_steps = warmup + steps
-            c = len(v) // n_steps if len(v) % n_steps == 0 and len(v) >= n_steps else 1
-            v = sorted(v)[c * warmup:c * (warmup + steps)]
-            if not v:
+            c = len(v) // n_run
+            v = sorted(v)
+            d = np.array([ns for _, ns in v[c * warmup:c * (warmup + steps)]],
+                         dtype=np.float64) / 1e3
+            if not len(d):
                 continue
-            d = np.array([ns for _, ns in v], dtype=np.float64) / 1e3
             short = (name.replace("(anonymous namespace)::", "")
                      .split("(")[0].replace("void ", ""))
-            f.write(f"| `{short}` | {len(d)} | {d.mean():.1f} | {d.min():.1f} "
-                    f"| {d.max():.1f} |\n")
+            row = (f"| `{short}` | {len(d)} | {d.mean():.1f} | {d.min():.1f} "
+                   f"| {d.max():.1f} |")
+            if steady:
+                e = np.array([ns for _, ns in v[-c * steps:]], dtype=np.float64) / 1e3
+                row += f" {e.mean():.1f} | {e.min():.1f} | {e.max():.1f} |"
+            f.write(row + "\n")
     print(open(md).read())
     return 0
 
@@ -768,6 +787,10 @@ def main(argv=None) -> int:
                          "profiles/kernels_<workload>.md, skipping each "
                          "kernel's first --warmup dispatches and keeping the "
                          "next --steps (the timed ones)")
+    ap.add_argument("--steady-warm", type=int, default=-1, metavar="N",
+                    help="with --summarize-trace: the traced run made a "
+                         "steady-state pass of N untimed steps (its log "
+                         "gives N); -1: it made none")
     ap.add_argument("--summarize-counters", nargs=2,
                     metavar=("SQ_CSV", "TCC_CSV"),
                     help="no GPU work: turn two rocprofv3 --pmc collections "
@@ -811,7 +834,8 @@ def main(argv=None) -> int:
                                   args.summarize_counters, args.command)
     if args.summarize_trace:
         return summarize_trace(S.WORKLOADS[args.workload], args.summarize_trace,
-                               args.command, args.warmup, args.steps)
+                               args.command, args.warmup, args.steps,
+                               args.steady_warm)
     if args.traffic_from:
         if not args.copy_calibration:
             ap.error("--traffic-from needs the run's --copy-calibration MIB")

@@ -104,6 +104,30 @@ def test_summarize_trace_kernel_run_twice_per_step(tmp_path, monkeypatch):
     assert "| `fa::k` | 10 | 0.1 | 0.1 | 0.1 |" in text
 
 
+def test_summarize_trace_steady_pass(tmp_path, monkeypatch):
+    """With a steady-state pass (7 untimed steps, then 5 timed ones after
+    the 3 warmup and 5 timed steps), a kernel run twice per step keeps its
+    timed dispatches and reports the last 5 steps beside them; a dispatch
+    count that does not fit the run's steps is an error."""
+    import csv
+    path = tmp_path / "trace.csv"
+    n = 2 * (3 + 5 + 7 + 5)
+    with open(path, "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(["Kernel_Name", "Dispatch_Id", "Start_Timestamp",
+                     "End_Timestamp"])
+        for i in range(n):   # warmup 900 ns, timed 100, untimed 700, last 300
+            ns = 900 if i < 6 else 100 if i < 16 else 700 if i < 30 else 300
+            wr.writerow(["void fa::k(int)", i, 0, ns])
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    w = S.WORKLOADS["tiny_f32"]
+    assert bench.summarize_trace(w, str(path), "cmd", 3, 5, steady_warm=7) == 0
+    text = (tmp_path / "kernels_tiny_f32.md").read_text()
+    assert "| `fa::k` | 10 | 0.1 | 0.1 | 0.1 | 0.3 | 0.3 | 0.3 |" in text
+    with pytest.raises(SystemExit):
+        bench.summarize_trace(w, str(path), "cmd", 3, 5, steady_warm=6)
+
+
 def test_summarize_stalls_fractions(tmp_path, monkeypatch):
     """The stall table gives wave-cycle counters as fractions of
     SQ_WAVE_CYCLES and instruction counts per MFMA."""
