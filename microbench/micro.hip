@@ -262,6 +262,78 @@ __global__ __launch_bounds__(512) void issue_kernel(int iters, int constant,
   if (lane == 0) st[(blockIdx.x * blockDim.x + threadIdx.x) >> 6] = {c1 - c0, t1 - t0};
 }
 
+// v_mfma_f32_16x16x32_bf16 chains fed from LDS through a four-deep operand
+// ring, as the attention kernels feed theirs (the compiler waits for each
+// operand before its MFMA): KIND 0 register operands only; 1 one
+// ds_read_b128 (16-byte row read, B operand layout: lane l reads row l % 16,
+// elements 8 (l / 16) .. + 8 of a 32-element slice) per MFMA; 2 two
+// ds_read_b64_tr_b16 (the transposed reads) per MFMA; 3 the two
+// alternating, the backward's mix.  Rows of 304 bytes (the backward's
+// stride), 64 rows; every read stays inside the tile.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int KIND>
+__global__ __launch_bounds__(512) void issue16_kernel(int iters, int constant,
+                                                      float* sink, Stamp* st) {
+  constexpr int S = 152;   // elements per row
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * S];
+  // finite bf16 values in [2^-7, 2^-5)
+  for (int i = threadIdx.x; i < 64 * S; i += blockDim.x)
+    tile[i] = (uint16_t)(0x3C00u | (((uint32_t)i * 0x9E37u) >> 3 & 0x1FFu));
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4, hh = lane >> 5;
+  const int dsub = (lane >> 4) & 1;
+  bf16x8 a[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) a[c] = operand(lane, c, constant != 0);
+  f32x4 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto fetch = [&](int k, int it) -> bf16x8 {
+    const bool tr = KIND == 2 || (KIND == 3 && (k & 1));
+    if (!tr) {
+      const int row = (((k >> 2) + it + w) & 3) * 16 + r16;     // <= 63
+      const int col = 32 * (k & 3) + 8 * g4;                     // <= 120 (+8)
+      return *(const bf16x8*)&tile[row * S + col];
+    }
+    const int col = 32 * (k & 3) + 16 * dsub + 4 * (r16 & 3);    // <= 124 (+4)
+    const int row = (((k >> 2) + it) & 1) * 32 + 4 * hh + (r16 >> 2);   // <= 39 (+8)
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&tile[row * S + col]);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&tile[(row + 8) * S + col]);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  bf16x8 op[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) op[k] = KIND == 0 ? a[k] : fetch(k, 0);
+  __syncthreads();
+  const uint64_t c0 = cyc(), t0 = rt();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int c = k & 3;
+      if (KIND == 0) {
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c], a[(c + 1) & 3], acc[c], 0, 0, 0);
+      } else {
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c], op[k & 3], acc[c], 0, 0, 0);
+        op[k & 3] = fetch((k + 4) & 15, it + ((k + 4) >> 4));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  const uint64_t c1 = cyc(), t1 = rt();
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s += acc[c][r];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) s += (float)op[k][0];
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
+  if (lane == 0) st[(blockIdx.x * blockDim.x + threadIdx.x) >> 6] = {c1 - c0, t1 - t0};
+}
+
 // LDS read bandwidth.  kind 0: ds_read_b128 of 16-byte row slices (lane l
 // reads row l % 32 of a 32-row tile with a 272-byte padded stride, half
 // (l / 32) of a 32-byte slice: the attention kernels' K operand reads);
@@ -354,7 +426,8 @@ __global__ __launch_bounds__(1024) void dma_kernel(const uint16_t* src,
 // 6 LDS row reads, 7 LDS transposed reads, 8 LDS DMA, 9 exp-only chains,
 // 10..13 MFMA + 4 SALU / s_nop / s_waitcnt / ds_read_b128 after each,
 // 14..17 MFMA + one operand of LDS reads, see issue_kernel, 18 and 19 as
-// 6 and 7 on the backward's 304-byte rows),
+// 6 and 7 on the backward's 304-byte rows, 20..23 16x16x32 MFMA chains
+// fed from LDS, see issue16_kernel),
 // `wps` wavefronts per SIMD (one workgroup of 256 wps threads per CU over
 // `cus` CUs), `constant` the MFMA operand kind.  Outputs: mean shader cycles
 // and mean microseconds of the timed loop per wavefront, and the kernel time
@@ -397,6 +470,10 @@ extern "C" int micro_run(int which, int wps, int constant, int iters, int cus,
       case 17: hipLaunchKernelGGL(issue_kernel<7>, g, b, 0, 0, iters, constant, sink, st); break;
       case 18: hipLaunchKernelGGL((lds_kernel<0, 152>), g, b, 0, 0, iters, sink, st); break;
       case 19: hipLaunchKernelGGL((lds_kernel<1, 152>), g, b, 0, 0, iters, sink, st); break;
+      case 20: hipLaunchKernelGGL(issue16_kernel<0>, g, b, 0, 0, iters, constant, sink, st); break;
+      case 21: hipLaunchKernelGGL(issue16_kernel<1>, g, b, 0, 0, iters, constant, sink, st); break;
+      case 22: hipLaunchKernelGGL(issue16_kernel<2>, g, b, 0, 0, iters, constant, sink, st); break;
+      case 23: hipLaunchKernelGGL(issue16_kernel<3>, g, b, 0, 0, iters, constant, sink, st); break;
       default: break;
     }
   };
