@@ -735,6 +735,17 @@ def micro(command: str) -> int:
                          wps, f"{c1 / (it * 16):.1f} cycles per MFMA per wave",
                          f"{flop / (ms1 * 1e-3) / 1e12:.0f} TFLOP/s, "
                          f"{c1 / u1 / 1e3:.2f} GHz"))
+    for which, name in ((24, "32x32x16 MFMA + 1 ds_read_b128 operand each"),
+                        (25, "32x32x16 MFMA + 2 ds_read_b64_tr_b16 operand each"),
+                        (26, "32x32x16 MFMA + the two alternating")):
+        for wps in (1, 2):
+            it = 2000
+            c1, u1, ms1 = run(which, wps, 0, it)
+            flop = cus * 4 * wps * it * 16 * 32768.0
+            rows.append((name, "4 chains, operand ring 4 deep, 304-byte rows, random",
+                         wps, f"{c1 / (it * 16):.1f} cycles per MFMA per wave",
+                         f"{flop / (ms1 * 1e-3) / 1e12:.0f} TFLOP/s, "
+                         f"{c1 / u1 / 1e3:.2f} GHz"))
     for which, name, per, rowb in ((6, "ds_read_b128 (row slices)", 1024, 272),
                                    (7, "2 x ds_read_b64_tr_b16 (transposed)", 1024, 320),
                                    (18, "ds_read_b128 (row slices)", 1024, 304),

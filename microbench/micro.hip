@@ -334,6 +334,67 @@ __global__ __launch_bounds__(512) void issue16_kernel(int iters, int constant,
   if (lane == 0) st[(blockIdx.x * blockDim.x + threadIdx.x) >> 6] = {c1 - c0, t1 - t0};
 }
 
+// The same for v_mfma_f32_32x32x16_bf16 (the kernels' shape): four chains
+// fed through a four-deep operand ring from 304-byte rows; KIND 1 one
+// ds_read_b128 per MFMA (lane l reads row l % 32, elements 8 (l / 32) .. + 8
+// of a 16-element slice), 2 two ds_read_b64_tr_b16, 3 the two alternating.
+template <int KIND>
+__global__ __launch_bounds__(512) void issue32r_kernel(int iters, int constant,
+                                                       float* sink, Stamp* st) {
+  constexpr int S = 152;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * S];
+  for (int i = threadIdx.x; i < 64 * S; i += blockDim.x)
+    tile[i] = (uint16_t)(0x3C00u | (((uint32_t)i * 0x9E37u) >> 3 & 0x1FFu));
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int l32 = lane & 31, r16 = lane & 15, hh = lane >> 5;
+  const int dsub = (lane >> 4) & 1;
+  bf16x8 a[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) a[c] = operand(lane, c, constant != 0);
+  f32x16 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = f32x16{};
+  auto fetch = [&](int k, int it) -> bf16x8 {
+    const bool tr = KIND == 2 || (KIND == 3 && (k & 1));
+    if (!tr) {
+      const int row = (((k >> 3) + it + w) & 1) * 32 + l32;      // <= 63
+      const int col = 16 * (k & 7) + 8 * hh;                     // <= 120 (+8)
+      return *(const bf16x8*)&tile[row * S + col];
+    }
+    const int col = 32 * (k & 3) + 16 * dsub + 4 * (r16 & 3);    // <= 124 (+4)
+    const int row = (((k >> 2) + it) & 1) * 32 + 4 * hh + (r16 >> 2);   // <= 39 (+8)
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&tile[row * S + col]);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&tile[(row + 8) * S + col]);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  bf16x8 op[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) op[k] = fetch(k, 0);
+  __syncthreads();
+  const uint64_t c0 = cyc(), t0 = rt();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int c = k & 3;
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c], op[k & 3], acc[c], 0, 0, 0);
+      op[k & 3] = fetch((k + 4) & 15, it + ((k + 4) >> 4));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  const uint64_t c1 = cyc(), t1 = rt();
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) s += (float)op[k][0];
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
+  if (lane == 0) st[(blockIdx.x * blockDim.x + threadIdx.x) >> 6] = {c1 - c0, t1 - t0};
+}
+
 // LDS read bandwidth.  kind 0: ds_read_b128 of 16-byte row slices (lane l
 // reads row l % 32 of a 32-row tile with a 272-byte padded stride, half
 // (l / 32) of a 32-byte slice: the attention kernels' K operand reads);
@@ -427,7 +488,8 @@ __global__ __launch_bounds__(1024) void dma_kernel(const uint16_t* src,
 // 10..13 MFMA + 4 SALU / s_nop / s_waitcnt / ds_read_b128 after each,
 // 14..17 MFMA + one operand of LDS reads, see issue_kernel, 18 and 19 as
 // 6 and 7 on the backward's 304-byte rows, 20..23 16x16x32 MFMA chains
-// fed from LDS, see issue16_kernel),
+// fed from LDS, see issue16_kernel, 24..26 the same for 32x32x16, see
+// issue32r_kernel),
 // `wps` wavefronts per SIMD (one workgroup of 256 wps threads per CU over
 // `cus` CUs), `constant` the MFMA operand kind.  Outputs: mean shader cycles
 // and mean microseconds of the timed loop per wavefront, and the kernel time
@@ -474,6 +536,9 @@ extern "C" int micro_run(int which, int wps, int constant, int iters, int cus,
       case 21: hipLaunchKernelGGL(issue16_kernel<1>, g, b, 0, 0, iters, constant, sink, st); break;
       case 22: hipLaunchKernelGGL(issue16_kernel<2>, g, b, 0, 0, iters, constant, sink, st); break;
       case 23: hipLaunchKernelGGL(issue16_kernel<3>, g, b, 0, 0, iters, constant, sink, st); break;
+      case 24: hipLaunchKernelGGL(issue32r_kernel<1>, g, b, 0, 0, iters, constant, sink, st); break;
+      case 25: hipLaunchKernelGGL(issue32r_kernel<2>, g, b, 0, 0, iters, constant, sink, st); break;
+      case 26: hipLaunchKernelGGL(issue32r_kernel<3>, g, b, 0, 0, iters, constant, sink, st); break;
       default: break;
     }
   };
