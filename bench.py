@@ -491,8 +491,9 @@ CONTEXT_WORKLOADS = ("gpt2_causal", "bert_keypad", "tradingday_causal")
 
 def standard_attention(q, k, v, scale: float, causal: bool, kv_len):
     """The standard attention the pages compare against: S = scale Q K^T
-    written out (bf16), masked, softmax in fp32, P written out (bf16),
-    O = P V.  Measurement only (timing and memory beside fa_fwd)."""
+    written out (in the inputs' dtype, bf16 here), masked, softmax in fp32,
+    P written out in the inputs' dtype, O = P V.  Measurement only (timing
+    and memory beside fa_fwd)."""
     import torch
     s = torch.matmul(q, k.transpose(-1, -2).contiguous())
     s.mul_(scale)
@@ -504,7 +505,7 @@ def standard_attention(q, k, v, scale: float, causal: bool, kv_len):
         keys = torch.arange(n, device=q.device)
         s.masked_fill_((keys[None, :] >= kv_len[:, None].long())[:, None, None, :],
                        float("-inf"))
-    p = torch.softmax(s, dim=-1, dtype=torch.float32).to(torch.bfloat16)
+    p = torch.softmax(s, dim=-1, dtype=torch.float32).to(q.dtype)
     del s
     return torch.matmul(p, v)
 

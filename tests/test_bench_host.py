@@ -153,3 +153,21 @@ def test_summarize_stalls_fractions(tmp_path, monkeypatch):
     assert cells[3] == "0.250"          # VALU / wave cycles
     assert cells[7] == "0.400"          # waiting to issue
     assert cells[10] == "3.50"          # VALU per MFMA
+
+
+@pytest.mark.parametrize("causal,padded", [(True, False), (False, True)])
+def test_standard_attention_matches_the_oracle(causal, padded):
+    """The standard attention that the context comparison times computes
+    attention (on the CPU here, float32): causal and key-padded cases
+    against the fp64 oracle."""
+    import torch
+    rng = np.random.default_rng(7)
+    B, H, N, d = 2, 2, 70, 16
+    q, k, v = (rng.standard_normal((B, H, N, d)) for _ in range(3))
+    kv = np.array([70, 33], dtype=np.int32) if padded else None
+    scale = 1.0 / np.sqrt(d)
+    t = lambda a: torch.from_numpy(a.astype(np.float32))
+    o = bench.standard_attention(t(q), t(k), t(v), scale, causal,
+                                 None if kv is None else torch.from_numpy(kv))
+    ref, _ = oracle.attention_fwd(q, k, v, scale, causal=causal, kv_len=kv)
+    assert np.abs(o.double().numpy() - ref).max() < 1e-5
