@@ -260,10 +260,12 @@ int fa_linear_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 
 /*
  * The dense backward entry points below take head dimension d = 64 or 128
- * (any other d returns FA_ERR_HEADDIM and fa_bwd_workspace_size returns 0);
- * d = 128 runs the pipelined kernels on grids that fill the chip, d = 64 the
- * 8-wavefront dK/dV and 4-wavefront dQ kernels (so do the block-sparse and
- * dropout variants).
+ * (any other d returns FA_ERR_HEADDIM and fa_bwd_workspace_size returns 0).
+ * Grids that fill the chip run the pipelined kernels at either d (at d = 64
+ * only without dropout); smaller grids run the 8-wavefront dK/dV and
+ * 4-wavefront dQ kernels.  The block-sparse variants always run the
+ * pipelined kernels, and so do the dropout variants at d = 128 (at d = 64
+ * they run the 8- and 4-wavefront kernels).
  *
  * Bytes of device workspace the backward needs: D [B,H,N] float32 (the row
  * dot products dO_i . O_i), rounded up to 256 bytes.  Returns 0 for invalid
@@ -333,20 +335,21 @@ int fa_bwd_preprocess(const uint16_t* o, const uint16_t* dO, void* workspace,
                       size_t workspace_bytes, int B, int H, int N, int d,
                       void* stream);
 
-/* Backward stage 2: one workgroup per 128-key block (4 wavefronts with K/V
- * held in registers for d = 128 on grids that fill the chip, else 8);
- * recomputes S, P, dP and dS per 64-row query tile and writes dK and dV.
- * Reads D from the workspace. */
+/* Backward stage 2: one workgroup per 128-key block (the pipelined kernel:
+ * 4 wavefronts, each with its 32 keys' K/V held in registers, on grids with
+ * at least one such block per CU; else 8 wavefronts); recomputes S, P, dP
+ * and dS per 64-row query tile and writes dK and dV.  Reads D from the
+ * workspace. */
 int fa_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                 const uint16_t* dO, const float* lse, uint16_t* dk,
                 uint16_t* dv, const void* workspace, size_t workspace_bytes,
                 int B, int H, int N, int d, float scale, int causal,
                 void* stream);
 
-/* Backward stage 3: one workgroup per 256-row query block (d = 128 on grids
- * with at least 256 such blocks) or per 128-row query block (otherwise);
- * recomputes S, P, dP and dS per key tile and writes dQ.  Reads D from the
- * workspace. */
+/* Backward stage 3: one workgroup per 256-row query block (the pipelined
+ * kernel, on grids with at least one such block per CU) or per 128-row
+ * query block (otherwise); recomputes S, P, dP and dS per key tile and
+ * writes dQ.  Reads D from the workspace. */
 int fa_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
               const uint16_t* dO, const float* lse, uint16_t* dq,
               const void* workspace, size_t workspace_bytes, int B, int H,
