@@ -54,8 +54,11 @@
 //   * bwd_dq computes S^T and dP^T with one query per lane (as the forward),
 //     so P^T and dS^T need only the lane's own LSE and D, and dS^T is the B
 //     operand of dQ^T += K_j^T dS^T with K_j^T read transposed from LDS.
-//   * LDS rows are padded to 304 bytes: conflict-free 16-byte row reads and
-//     at most 2-way transposed reads.
+//   * The pipelined kernels' streamed tiles sit in LDS rows padded to 272
+//     bytes, placed by tile_slot so that both the 16-byte row reads and the
+//     transposed reads are free of bank conflicts; the small-grid kernels
+//     pad rows to 304 bytes (conflict-free row reads, at most 2-way
+//     transposed reads).
 #include "fa.h"
 #include "fa_common.h"
 #include "fa_launch.h"
@@ -103,10 +106,10 @@ __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(
 constexpr int kBwdThreads = 512;
 constexpr int kBQ2 = 64;   // query rows per tile
 
-// Padded row stride (elements): 304-byte rows for the 256-byte K/V/Q/dO rows
-// keep the 16-byte row reads conflict-free and the transposed 8-byte reads at
-// most 2-way.  Linear layouts let every operand address be one per-lane base
-// plus an immediate offset.
+// Padded row stride (elements) of the small-grid kernels: 304-byte rows for
+// the 256-byte K/V/Q/dO rows keep the 16-byte row reads conflict-free and the
+// transposed 8-byte reads at most 2-way.  Linear layouts let every operand
+// address be one per-lane base plus an immediate offset.
 constexpr int kRS = 152;   // K, V, Q, dO row stride
 
 template <int D, bool CAUSAL, bool DROP = false, bool SPARSE = false>
@@ -701,6 +704,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t bwd_rsrc(const uint16_t* p,
 // four LDS stages with one barrier per tile.  Q and dO tiles go from HBM
 // straight into LDS by DMA, issued two tiles ahead; LSE and D (64 floats
 // each, transformed on the way) pass through wavefront 0's registers.
+// Row placement of the streamed tiles of the pipelined backward kernels
+// (query tiles in dK/dV, key tiles in dQ).  Two access patterns read a
+// tile: row reads (16 lanes on 16 consecutive rows, 16 bytes each) and
+// transposed reads (16 or 32 lanes on 4 consecutive rows, 32 or 64 bytes
+// each).  Rows are padded to an odd number of 16-byte chunks (272 bytes at
+// head dim 128, 144 at 64), and within each group of 16 rows row r sits in
+// slot 4 (r mod 4) + r / 4 (its two base-4 digits swapped, so the map is
+// its own inverse).  16 consecutive rows then fill 16 distinct slots, and 4
+// consecutive rows from a multiple of 4 land in slots 4 apart, so that
+// neither pattern meets an LDS bank conflict; a padded stride alone serves
+// only one of the two.
+__device__ __forceinline__ int tile_slot(int r) {
+  return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3);
+}
+
 constexpr int kKvPBK = 128;
 
 template <bool CAUSAL, bool SPARSE, bool DROP = false, int D = kD>
@@ -713,11 +731,11 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_pipe_kernel(
     float c_log2, float scale, Dropout drop,
     const int32_t* __restrict__ kv_len = nullptr) {
   static_assert(D == kD || (D == 64 && !DROP), "head dimension");
-  // Padded row stride of the query tiles: 304-byte rows at head dim 128
-  // (as RS); at head dim 64, 144-byte rows, which keep the row reads
-  // conflict-free and let two workgroups share a CU.
-  constexpr int RS = D == 64 ? D + 8 : kRS;
+  // Query tiles in LDS: rows of D + 8 elements in the slots of
+  // tile_slot (see there).
+  constexpr int RS = D + 8;
   constexpr int QE = kBQ2 * RS;                  // elements per tile stage
+  auto prm = [](int r) -> int { return tile_slot(r); };
   constexpr int THREADS = 256;
   __shared__ __attribute__((aligned(16))) uint16_t lds_q[4][QE];
   __shared__ __attribute__((aligned(16))) uint16_t lds_g[4][QE];   // dO
@@ -821,7 +839,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_pipe_kernel(
   unsigned toff[TIW];
 #pragma unroll
   for (int u = 0; u < TIW; ++u) {
-    const int p = 64 * (w + 4 * u) + lane, row = p / RCH, c = p % RCH;
+    // slot p / RCH holds row prm(p / RCH) (prm is its own inverse)
+    const int p = 64 * (w + 4 * u) + lane, row = prm(p / RCH), c = p % RCH;
     toff[u] = c < D / 8 ? (unsigned)((row * D + 8 * c) * 2) : (1u << 30);
   }
   const unsigned lds_q0 = lds_addr(&lds_q[0][0]);
@@ -919,7 +938,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_pipe_kernel(
       const int ai = BF ? i - kB : i;
       const int kk = ai / 2;
       const uint16_t* t = (ai % 2 == 0) ? lds_q[sta] : lds_g[sta];
-      return *(const bf16x8*)(&t[(32 * ca + l32) * RS + 16 * kk + 8 * hh]);
+      return *(const bf16x8*)(&t[(32 * ca + prm(l32)) * RS + 16 * kk + 8 * hh]);
     }
     const int bi = BF ? i : i - kA;
     const int which = bi / (kB / 2);           // 0: dO^T (dV), 1: Q^T (dK)
@@ -927,8 +946,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_pipe_kernel(
     const uint16_t* t = which == 0 ? lds_g[stb] : lds_q[stb];
     const int col = 32 * db + 16 * dsub + 4 * (r16 & 3);
     const int row = 32 * cb + 16 * h + 4 * hh + (r16 >> 2);
-    return join_bf16(lds_read_tr16(&t[row * RS + col]),
-                     lds_read_tr16(&t[(row + 8) * RS + col]));
+    return join_bf16(lds_read_tr16(&t[prm(row) * RS + col]),
+                     lds_read_tr16(&t[prm(row + 8) * RS + col]));
   };
   // LSE of the lane's 16 rows of block cv, -D of those of block ca (and,
   // with dropout, of block cv): register r <-> row 32 c + 8 (r / 4) + 4 hh
@@ -1067,8 +1086,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_pipe_kernel(
       const uint16_t* t = which == 0 ? lds_g[stb] : lds_q[stb];
       const int col = 32 * db + 16 * dsub + 4 * (r16 & 3);
       const int row = 32 + 16 * h + 4 * hh + (r16 >> 2);
-      const bf16x8 a = join_bf16(lds_read_tr16(&t[row * RS + col]),
-                                 lds_read_tr16(&t[(row + 8) * RS + col]));
+      const bf16x8 a = join_bf16(lds_read_tr16(&t[prm(row) * RS + col]),
+                                 lds_read_tr16(&t[prm(row + 8) * RS + col]));
       if (which == 0)
         mfma_agpr(dv_acc[db], a, pb[1][h]);
       else
@@ -1110,7 +1129,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_pipe_kernel(
     }
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const int o = l32 * RS + 16 * kk + 8 * hh;
+      const int o = prm(l32) * RS + 16 * kk + 8 * hh;
       s[0] = mfma32x16(*(const bf16x8*)(&lds_q[0][o]), kf[kk], kk == 0 ? f32x16{} : s[0]);
       dp[0] = mfma32x16(*(const bf16x8*)(&lds_g[0][o]), vf[kk], kk == 0 ? negd0 : dp[0]);
     }
@@ -1210,8 +1229,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
     const int32_t* __restrict__ kv_len = nullptr) {
   static_assert(!SPARSE || kDqPBR == FA_SPARSE_BQ, "a workgroup is a mask row");
   static_assert(D == kD || (D == 64 && !DROP), "head dimension");
-  // Padded row stride of the K/V tiles (as in the dK/dV kernel).
-  constexpr int RS = D == 64 ? D + 8 : kRS;
+  // K/V tiles in LDS: rows of D + 8 elements in the slots of tile_slot.
+  constexpr int RS = D + 8;
   constexpr int TE = kDqBC * RS;                  // elements per tile stage
   constexpr int THREADS = 512;
   constexpr int NW = THREADS / 64;
@@ -1339,7 +1358,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
   unsigned toff[TIW];
 #pragma unroll
   for (int u = 0; u < TIW; ++u) {
-    const int p = 64 * (w + NW * u) + lane, row = p / RCH, c = p % RCH;
+    // slot p / RCH holds row tile_slot(p / RCH) (the map is an involution)
+    const int p = 64 * (w + NW * u) + lane, row = tile_slot(p / RCH), c = p % RCH;
     toff[u] = c < D / 8 ? (unsigned)((row * D + 8 * c) * 2) : (1u << 30);
   }
   const unsigned lds_k0 = lds_addr(&lds_k[0][0]);
@@ -1394,15 +1414,15 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
     static_assert(kG * (kN - 2) >= 16, "the VALU pipeline fits the step");
     auto fetch = [&](int i) -> bf16x8 {
       if (i < kS)
-        return *(const bf16x8*)(&lds_k[stn][(32 * kbn + lq) * RS + 8 * hh + 16 * i]);
+        return *(const bf16x8*)(&lds_k[stn][(32 * kbn + tile_slot(lq)) * RS + 8 * hh + 16 * i]);
       if (i < 2 * kS)
-        return *(const bf16x8*)(&lds_v[stn][(32 * kbn + lq) * RS + 8 * hh + 16 * (i - kS)]);
+        return *(const bf16x8*)(&lds_v[stn][(32 * kbn + tile_slot(lq)) * RS + 8 * hh + 16 * (i - kS)]);
       const int pi = i - 2 * kS;
       const int h = pi / (D / 32), db = pi % (D / 32);
       const int col = 32 * db + 16 * dsub + 4 * (r16 & 3);
       const int row = 32 * kbc + 16 * h + 4 * hh + (r16 >> 2);
-      return join_bf16(lds_read_tr16(&lds_k[stc][row * RS + col]),
-                       lds_read_tr16(&lds_k[stc][(row + 8) * RS + col]));
+      return join_bf16(lds_read_tr16(&lds_k[stc][tile_slot(row) * RS + col]),
+                       lds_read_tr16(&lds_k[stc][tile_slot(row + 8) * RS + col]));
     };
     // Operand of slot m: the S^T and dP^T products alternate (S_0, dP_0,
     // S_1, dP_1, ...) so that no MFMA is issued right after one that
@@ -1511,7 +1531,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pipe_kernel(
       dp[0] = negd;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const int o = lq * RS + 8 * hh + 16 * kk;
+        const int o = tile_slot(lq) * RS + 8 * hh + 16 * kk;
         s[0] = mfma32x16(*(const bf16x8*)(&lds_k[0][o]), qf[kk], s[0]);
         dp[0] = mfma32x16(*(const bf16x8*)(&lds_v[0][o]), gf[kk], dp[0]);
       }
