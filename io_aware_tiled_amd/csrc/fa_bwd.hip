@@ -731,11 +731,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_pipe_kernel(
     float c_log2, float scale, Dropout drop,
     const int32_t* __restrict__ kv_len = nullptr) {
   static_assert(D == kD || (D == 64 && !DROP), "head dimension");
-  // Query tiles in LDS: rows of D + 8 elements in the slots of
-  // tile_slot (see there).
+  // Query tiles in LDS: rows of D + 8 elements in the slots of tile_slot.
   constexpr int RS = D + 8;
   constexpr int QE = kBQ2 * RS;                  // elements per tile stage
-  auto prm = [](int r) -> int { return tile_slot(r); };
   constexpr int THREADS = 256;
   __shared__ __attribute__((aligned(16))) uint16_t lds_q[4][QE];
   __shared__ __attribute__((aligned(16))) uint16_t lds_g[4][QE];   // dO
@@ -839,8 +837,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_pipe_kernel(
   unsigned toff[TIW];
 #pragma unroll
   for (int u = 0; u < TIW; ++u) {
-    // slot p / RCH holds row prm(p / RCH) (prm is its own inverse)
-    const int p = 64 * (w + 4 * u) + lane, row = prm(p / RCH), c = p % RCH;
+    // slot p / RCH holds row tile_slot(p / RCH) (the map is an involution)
+    const int p = 64 * (w + 4 * u) + lane, row = tile_slot(p / RCH), c = p % RCH;
     toff[u] = c < D / 8 ? (unsigned)((row * D + 8 * c) * 2) : (1u << 30);
   }
   const unsigned lds_q0 = lds_addr(&lds_q[0][0]);
@@ -938,7 +936,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_pipe_kernel(
       const int ai = BF ? i - kB : i;
       const int kk = ai / 2;
       const uint16_t* t = (ai % 2 == 0) ? lds_q[sta] : lds_g[sta];
-      return *(const bf16x8*)(&t[(32 * ca + prm(l32)) * RS + 16 * kk + 8 * hh]);
+      return *(const bf16x8*)(&t[(32 * ca + tile_slot(l32)) * RS + 16 * kk + 8 * hh]);
     }
     const int bi = BF ? i : i - kA;
     const int which = bi / (kB / 2);           // 0: dO^T (dV), 1: Q^T (dK)
@@ -946,8 +944,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_pipe_kernel(
     const uint16_t* t = which == 0 ? lds_g[stb] : lds_q[stb];
     const int col = 32 * db + 16 * dsub + 4 * (r16 & 3);
     const int row = 32 * cb + 16 * h + 4 * hh + (r16 >> 2);
-    return join_bf16(lds_read_tr16(&t[prm(row) * RS + col]),
-                     lds_read_tr16(&t[prm(row + 8) * RS + col]));
+    return join_bf16(lds_read_tr16(&t[tile_slot(row) * RS + col]),
+                     lds_read_tr16(&t[tile_slot(row + 8) * RS + col]));
   };
   // LSE of the lane's 16 rows of block cv, -D of those of block ca (and,
   // with dropout, of block cv): register r <-> row 32 c + 8 (r / 4) + 4 hh
@@ -1086,8 +1084,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_pipe_kernel(
       const uint16_t* t = which == 0 ? lds_g[stb] : lds_q[stb];
       const int col = 32 * db + 16 * dsub + 4 * (r16 & 3);
       const int row = 32 + 16 * h + 4 * hh + (r16 >> 2);
-      const bf16x8 a = join_bf16(lds_read_tr16(&t[prm(row) * RS + col]),
-                                 lds_read_tr16(&t[prm(row + 8) * RS + col]));
+      const bf16x8 a = join_bf16(lds_read_tr16(&t[tile_slot(row) * RS + col]),
+                                 lds_read_tr16(&t[tile_slot(row + 8) * RS + col]));
       if (which == 0)
         mfma_agpr(dv_acc[db], a, pb[1][h]);
       else
@@ -1129,7 +1127,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_pipe_kernel(
     }
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const int o = prm(l32) * RS + 16 * kk + 8 * hh;
+      const int o = tile_slot(l32) * RS + 16 * kk + 8 * hh;
       s[0] = mfma32x16(*(const bf16x8*)(&lds_q[0][o]), kf[kk], kk == 0 ? f32x16{} : s[0]);
       dp[0] = mfma32x16(*(const bf16x8*)(&lds_g[0][o]), vf[kk], kk == 0 ? negd0 : dp[0]);
     }
